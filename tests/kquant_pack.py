@@ -1,0 +1,108 @@
+"""Test-only packers and a grid quantizer for Q4_K / Q6_K super-blocks.
+
+They encode fields into bytes (the inverse direction of every decoder), written
+from the format description:
+
+Q4_K (144 B): fp16 d @0, fp16 dmin @2, 12 packed bytes @4, 128 code bytes @16.
+  Packed bytes 0-3 hold the low 6 bits of scales 0-3, bytes 4-7 the low 6 bits
+  of mins 0-3, bytes 8-11 the low nibbles of scales 4-7 (low half of the byte)
+  and mins 4-7 (high half); the high 2 bits of scales 4-7 sit in the top bits
+  of bytes 0-3 and those of mins 4-7 in the top bits of bytes 4-7. Code chunk c
+  (32 bytes) gives its low nibbles to sub-block 2c and its high nibbles to
+  sub-block 2c+1.
+Q6_K (210 B): low-nibble plane @0 (128 B), high-2-bit plane @128 (64 B),
+  16 int8 scales @192, fp16 d @208; bit placement as read in the oracle.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+
+def fp16_bits(v: float) -> int:
+    return int(np.array([v], dtype="<f2").view("<u2")[0])
+
+
+def fp16_value(bits: int) -> float:
+    return float(np.array([bits], dtype="<u2").view("<f2")[0])
+
+
+def pack_q4k(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
+    sc = [int(v) for v in sc]
+    mn = [int(v) for v in mn]
+    q = np.asarray(q, dtype=np.int64)
+    assert len(sc) == 8 and len(mn) == 8 and q.shape == (256,)
+    assert all(0 <= v < 64 for v in sc + mn) and q.min() >= 0 and q.max() < 16
+    b = np.zeros(144, dtype=np.uint8)
+    b[0], b[1] = d_bits & 255, d_bits >> 8
+    b[2], b[3] = dmin_bits & 255, dmin_bits >> 8
+    s = np.zeros(12, dtype=np.int64)
+    for j in range(4):
+        s[j] |= sc[j] & 63
+        s[j + 4] |= mn[j] & 63
+    for j in range(4, 8):
+        s[j + 4] |= (sc[j] & 15) | ((mn[j] & 15) << 4)
+        s[j - 4] |= (sc[j] >> 4) << 6
+        s[j] |= (mn[j] >> 4) << 6
+    b[4:16] = s
+    for j in range(8):
+        c, hi = j // 2, j % 2
+        for l in range(32):
+            b[16 + 32 * c + l] |= int(q[32 * j + l]) << (4 * hi)
+    return b
+
+
+def pack_q6k(d_bits: int, scales, q) -> np.ndarray:
+    scales = [int(v) for v in scales]
+    q = np.asarray(q, dtype=np.int64)
+    assert len(scales) == 16 and q.shape == (256,)
+    assert q.min() >= 0 and q.max() < 64
+    b = np.zeros(210, dtype=np.uint8)
+    for i in range(256):
+        h, r = divmod(i, 128)
+        g, l = divmod(r, 32)
+        lo, hi = int(q[i]) & 15, int(q[i]) >> 4
+        b[64 * h + 32 * (g % 2) + l] |= lo << (4 * (g // 2))
+        b[128 + 32 * h + l] |= hi << (2 * g)
+    b[192:208] = np.array(scales, dtype=np.int8).view(np.uint8)
+    b[208], b[209] = d_bits & 255, d_bits >> 8
+    return b
+
+
+def rn32(x: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32 (ties to even)."""
+    f64 = float(x)  # correctly rounded to float64
+    if Fraction(f64) != x:
+        # Would need a second, possibly different rounding: avoid silently.
+        raise AssertionError("value not exact in float64; test construction error")
+    return np.float32(f64)
+
+
+def q4k_exact_weights(d_bits, dmin_bits, sc, mn, q):
+    d, dmin = Fraction(fp16_value(d_bits)), Fraction(fp16_value(dmin_bits))
+    return [d * int(sc[i // 32]) * int(q[i]) - dmin * int(mn[i // 32]) for i in range(256)]
+
+
+def q6k_exact_weights(d_bits, scales, q):
+    d = Fraction(fp16_value(d_bits))
+    return [d * int(scales[i // 16]) * (int(q[i]) - 32) for i in range(256)]
+
+
+def grid_quantize_q4k(w: list[Fraction], d: Fraction, dmin: Fraction):
+    """Recover (sc, m, q) of a Q4_K block from exact weights on the grid
+    w = d*sc*q - dmin*m, for sub-blocks that contain both q = 0 and q = 15:
+    m = -min(w)/dmin, sc = (max(w) + dmin*m) / (15 d), q = (w + dmin*m)/(d*sc)."""
+    sc, mn, q = [], [], []
+    for j in range(8):
+        sub = w[32 * j:32 * j + 32]
+        m = -min(sub) / dmin
+        s = (max(sub) + dmin * m) / (15 * d)
+        assert m.denominator == 1 and s.denominator == 1
+        mn.append(int(m))
+        sc.append(int(s))
+        for v in sub:
+            qq = (v + dmin * m) / (d * s) if s else Fraction(0)
+            assert qq.denominator == 1
+            q.append(int(qq))
+    return sc, mn, q
