@@ -1,0 +1,376 @@
+"""Benchmark of the Q4_K / Q6_K dequantize-fused matmul on one MI355X.
+
+Headline (`value`): the Q4_K decode GEMV set at M = 1 with bf16 activations —
+fused QKV (K=5120, N=7168), fused gate+up (K=5120, N=34816) and down
+(K=17408, N=5120) — as effective GB/s: the algorithmic bytes of one step
+(packed weights + x + y of the three GEMVs) over the time of one step. A step
+is the three calls back to back; the timed region is `--steps` steps after
+`--warmup` untimed ones. Weight sets rotate over copies whose total exceeds
+twice the 256 MB MALL, so the rate is an HBM rate.
+
+The same JSON line carries the prefill GEMM (M = 512 and 4096, TFLOP/s
+against the bf16 MFMA peak), the Q6_K GEMVs and the MoE FFN as extra
+records, the roofline of the dominant kernel (the gate+up GEMV, timed per
+launch with HIP events on its stream) and the CPU oracle timed on the host as
+a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--sections ...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K GEMV GB/s (% HBM peak) at M=1; Q4_K GEMM TFLOP/s (% MFMA peak) M=512"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+MALL_BYTES = 256 << 20
+DECODE = [("qkv", 5120, 7168), ("gate_up", 5120, 34816), ("down", 17408, 5120)]
+Q4K_BPB, Q6K_BPB = 144, 210
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(N, K, M=1, bpb=Q4K_BPB, xbytes=2):
+    return N * (K // 256) * bpb + M * K * xbytes + M * N * 4
+
+
+def copies_for(nbytes):
+    return max(2, -(-2 * MALL_BYTES // nbytes))
+
+
+class Timer:
+    """HIP events on the current stream (the stream every call is enqueued on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quant_dequant_matmul_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", kernel_key + "_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha256_16") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to("cuda")
+
+
+def to_dev_bf16(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def rel(y, ref):
+    return float(np.linalg.norm(y.astype(np.float64) - ref) / np.linalg.norm(ref))
+
+
+# ---------------------------------------------------------------------------
+# sections
+# ---------------------------------------------------------------------------
+
+def bench_probe(torch, qdm):
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    for _ in range(3):
+        qdm.probe_copy(src, dst, nbytes)
+    tm = Timer(torch)
+    reps = 10
+    e0 = tm.event()
+    for _ in range(reps):
+        qdm.probe_copy(src, dst, nbytes)
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"copy_bytes": nbytes, "ms": ms, "read_plus_write_GBps": 2 * nbytes / ms / 1e6}
+
+
+def bench_decode(torch, qdm, synth, oracle, steps, warmup):
+    """The headline: QKV, gate+up, down per step, rotating weight copies."""
+    host_w, host_x, dev_x = {}, {}, {}
+    for name, K, N in DECODE:
+        w, x = synth.decode_gemv(name)
+        host_w[name], host_x[name] = w, x
+        dev_x[name] = to_dev_bf16(torch, x)
+    set_bytes = sum(host_w[n].nbytes for n, _, _ in DECODE)
+    ncopy = copies_for(set_bytes)
+    log("decode set: %.1f MB of weights x %d copies" % (set_bytes / 1e6, ncopy))
+    dev_w = []
+    base = {n: to_dev(torch, host_w[n]) for n, _, _ in DECODE}
+    for c in range(ncopy):
+        dev_w.append({n: (base[n] if c == 0 else base[n].clone()) for n, _, _ in DECODE})
+    ys = {n: torch.empty((1, N), dtype=torch.float32, device="cuda") for n, _, N in DECODE}
+
+    # parity of the exact launch configuration that is timed
+    errs = {}
+    for name, K, N in DECODE:
+        y = qdm.q4k_gemv(dev_w[0][name], dev_x[name], N, K, y=ys[name])
+        torch.cuda.synchronize()
+        errs[name] = rel(y.cpu().numpy(), oracle.q4k_matmul(host_w[name], host_x[name], N, K))
+    log("decode parity (normwise rel err):", errs)
+
+    def step(i):
+        wset = dev_w[i % ncopy]
+        for name, K, N in DECODE:
+            qdm.q4k_gemv(wset[name], dev_x[name], N, K, y=ys[name])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    ev = []
+    t0 = tm.event()
+    for i in range(steps):
+        wset = dev_w[i % ncopy]
+        row = []
+        for name, K, N in DECODE:
+            row.append(tm.event())
+            qdm.q4k_gemv(wset[name], dev_x[name], N, K, y=ys[name])
+        row.append(tm.event())
+        ev.append(row)
+    t1 = tm.event()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = {name: [] for name, _, _ in DECODE}
+    for row in ev:
+        for j, (name, _, _) in enumerate(DECODE):
+            per[name].append(row[j].elapsed_time(row[j + 1]))
+    step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
+    kernels = {}
+    for name, K, N in DECODE:
+        ms = float(np.mean(per[name]))
+        b = gemv_bytes(N, K)
+        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "median_ms": float(np.median(per[name])),
+                         "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
+                         "rel_err": errs[name]}
+    del dev_w
+    return {"ms_per_step": total_ms / steps, "step_bytes": step_bytes, "copies": ncopy,
+            "GBps": step_bytes / (total_ms / steps) / 1e6, "kernels": kernels,
+            "max_rel_err": max(errs.values())}
+
+
+def bench_gemm(torch, qdm, synth, oracle, M, reps):
+    K, N = 5120, 17408
+    w, x = synth.prefill_gemm(M)
+    wd, xd = to_dev(torch, w), to_dev_bf16(torch, x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qdm.q4k_gemm(wd, xd, N, K, y=y)
+    torch.cuda.synchronize()
+    cols = np.arange(0, N, 211)
+    rows = np.arange(0, M, max(1, M // 128))
+    err = rel(y.cpu().numpy()[np.ix_(rows, cols)], oracle.q4k_matmul(w[cols], x[rows], len(cols), K))
+    for _ in range(3):
+        qdm.q4k_gemm(wd, xd, N, K, y=y)
+    tm = Timer(torch)
+    evs = [tm.event()]
+    for _ in range(reps):
+        qdm.q4k_gemm(wd, xd, N, K, y=y)
+        evs.append(tm.event())
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    ms = float(np.mean(times))
+    flops = 2.0 * M * N * K
+    return {"M": M, "N": N, "K": K, "avg_ms": ms, "median_ms": float(np.median(times)),
+            "TFLOPs": flops / ms / 1e9, "frac_mfma_peak": flops / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS,
+            "rel_err_sampled": err}
+
+
+def bench_q6k(torch, qdm, synth, oracle, which, M, reps):
+    K, N = {"head": (5120, 151936), "down": (17408, 5120)}[which]
+    w, x = synth.q6k_gemv(which, M)
+    nbytes = w.nbytes
+    ncopy = copies_for(nbytes)
+    base = to_dev(torch, w)
+    ws = [base] + [base.clone() for _ in range(ncopy - 1)]
+    xd = to_dev_bf16(torch, x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qdm.q6k_gemv(ws[0], xd, N, K, y=y)
+    torch.cuda.synchronize()
+    rows = np.arange(0, N, 97 if N > 20000 else 1)
+    err = rel(y.cpu().numpy()[:, rows], oracle.q6k_matmul(w[rows], x, len(rows), K))
+    for i in range(3):
+        qdm.q6k_gemv(ws[i % ncopy], xd, N, K, y=y)
+    tm = Timer(torch)
+    evs = [tm.event()]
+    for i in range(reps):
+        qdm.q6k_gemv(ws[i % ncopy], xd, N, K, y=y)
+        evs.append(tm.event())
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    ms = float(np.mean(times))
+    b = gemv_bytes(N, K, M, Q6K_BPB)
+    del ws
+    return {"M": M, "N": N, "K": K, "copies": ncopy, "bytes": b, "avg_ms": ms,
+            "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
+            "rel_err_sampled": err}
+
+
+def bench_moe(torch, qdm, synth, oracle, T, reps):
+    E, H, F = 128, 2048, 768
+    d = synth.moe(T)
+    x, w13, w2 = to_dev_bf16(torch, d["x"]), to_dev(torch, d["w13"]), to_dev(torch, d["w2"])
+    ids = torch.from_numpy(d["ids"]).to("cuda")
+    gw = torch.from_numpy(d["gw"]).to("cuda")
+    sets = [(w13, w2), (w13.clone(), w2.clone())]
+    ws = torch.empty(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    qdm.moe_q4k_grouped_gemm(x, w13, w2, ids, gw, E, H, F, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 16).astype(int)
+    ref = oracle.moe_q4k(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F)
+    err = rel(y.cpu().numpy()[toks], ref)
+    for i in range(3):
+        a, b = sets[i % 2]
+        qdm.moe_q4k_grouped_gemm(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+    tm = Timer(torch)
+    evs = [tm.event()]
+    for i in range(reps):
+        a, b = sets[i % 2]
+        qdm.moe_q4k_grouped_gemm(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+        evs.append(tm.event())
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    ms = float(np.mean(times))
+    distinct = len(np.unique(d["ids"]))
+    per_expert = 2 * F * (H // 256) * 144 + H * (F // 256) * 144
+    touched = distinct * per_expert + T * H * 2 + T * H * 4
+    flops = 2.0 * T * 8 * (2 * F * H + H * F)
+    return {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
+            "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
+            "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
+
+
+def cpu_baseline(oracle, synth, budget_s=12.0):
+    """The oracle as it stands, on the host cores, over the decode set."""
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    work = [(synth.decode_gemv(n), K, N) for n, K, N in DECODE]
+    step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
+    t0 = time.perf_counter()
+    nsteps = 0
+    while True:
+        for (w, x), K, N in work:
+            oracle.q4k_matmul(w, x, N, K)
+        nsteps += 1
+        if time.perf_counter() - t0 >= budget_s or nsteps >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": step_bytes * nsteps / dt / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full decode-set steps (QKV + gate+up + down GEMV, M=1) in %.1f s"
+                      % (nsteps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sections", default="probe,decode,gemm,q6k,moe,cpu",
+                    help="comma list of: probe, decode, gemm, q6k, moe, cpu")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    sections = set(args.sections.split(","))
+
+    import torch
+
+    import oracle
+    import qdm_synth as synth
+    import quant_dequant_matmul_amd as qdm
+
+    qdm.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_name(0)
+    log("device:", dev_name)
+
+    extra = {}
+    if "probe" in sections:
+        extra["probe_copy"] = bench_probe(torch, qdm)
+        log("probe copy:", extra["probe_copy"])
+    dec = bench_decode(torch, qdm, synth, oracle, args.steps, args.warmup)
+    log("decode: %.1f GB/s per step" % dec["GBps"])
+    if "gemm" in sections:
+        for M, reps in ((512, 20), (4096, 5)):
+            extra["q4k_gemm_m%d" % M] = bench_gemm(torch, qdm, synth, oracle, M, reps)
+            log("gemm M=%d:" % M, extra["q4k_gemm_m%d" % M])
+    if "q6k" in sections:
+        for which, M, reps in (("head", 1, 20), ("head", 8, 20), ("down", 1, 50)):
+            key = "q6k_%s_m%d" % (which, M)
+            extra[key] = bench_q6k(torch, qdm, synth, oracle, which, M, reps)
+            log(key, extra[key])
+    if "moe" in sections:
+        for T, reps in ((1, 50), (8, 50), (512, 10)):
+            extra["moe_t%d" % T] = bench_moe(torch, qdm, synth, oracle, T, reps)
+            log("moe T=%d:" % T, extra["moe_t%d" % T])
+
+    gu = dec["kernels"]["gate_up"]
+    digest = src_digest("q4k_gemv.hip", "common.h")
+    roofline = {"kernel": "q4k_gemv_kernel (gate+up, K=5120 N=34816, M=1, bf16)",
+                "bound": "hbm", "achieved": gu["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gu["GBps"] / HBM_PEAK_GBS,
+                "traffic": read_traffic("q4k_gemv_gate_up", digest),
+                "algorithmic_bytes_per_launch": gu["bytes"], "avg_launch_ms": gu["avg_ms"],
+                "kernel_src_sha256_16": digest}
+    if "cpu" in sections:
+        cpu = cpu_baseline(oracle, synth)
+        log("cpu baseline:", cpu)
+    else:
+        cpu = None
+    rec = {"metric": METRIC, "value": dec["GBps"], "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "q4_k weights x bf16 activations -> f32 accumulate", "data": "synthetic",
+           "config": {"workload": "Q4_K decode GEMV set, M=1, bf16 x: QKV K=5120 N=7168; "
+                                  "gate+up K=5120 N=34816; down K=17408 N=5120 "
+                                  "(one step = the three calls; %d rotating weight copies)"
+                                  % dec["copies"],
+                      "frac_hbm_peak": dec["GBps"] / HBM_PEAK_GBS, "device": dev_name},
+           "roofline": roofline, "cpu_baseline": cpu, "decode_kernels": dec["kernels"],
+           "parity_max_rel_err": dec["max_rel_err"], "extra": extra}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

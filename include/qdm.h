@@ -1,0 +1,136 @@
+/*
+ * qdm.h — C ABI of the Q4_K / Q6_K dequantize-fused matmul library for
+ * MI355X (gfx950). Shared library: libqdm.so.
+ *
+ * What it computes. GGUF k-quant weights stay packed in HBM and are decoded on
+ * the fly inside the matmul: a GEMV for decode and a matrix-core GEMM for
+ * prefill over the same weights (hipEngine README, "Quickstart": WMMA prefill
+ * and GEMV decode; "GGUF Support": Q4_K and Q6_K tensor families of a Q4_K_M
+ * file, read by GGUF-specific quant readers), and an expert-grouped matmul for
+ * a routed MoE FFN (hipster README, "Verify the claims": MoE grouped GEMM
+ * micro-benchmark).
+ *
+ * Weight layout. A weight tensor W has N output rows of K weights; each row is
+ * K/256 consecutive super-blocks and rows are contiguous (row n starts at byte
+ * n * (K/256) * block_bytes). The value of weight (n, k) is:
+ *   Q4_K (144-byte block): fp16 d @0, fp16 dmin @2, 12 bytes of packed 6-bit
+ *     scales/mins @4, 128 bytes of 4-bit codes @16 (chunk c of 32 bytes holds
+ *     sub-block 2c in its low nibbles and 2c+1 in its high nibbles);
+ *     w = d * sc_j * q - dmin * m_j for the 32-weight sub-block j.
+ *   Q6_K (210-byte block): 128 bytes of low 4 bits @0, 64 bytes of high 2 bits
+ *     @128, 16 int8 scales @192 (one per 16 weights), fp16 d @208;
+ *     w = d * scale * (q - 32), q in 0..63.
+ *
+ * Matmul convention. X is [M][K] row-major (fp32 or bf16), Y = X * W^T is
+ * [M][N] fp32 row-major and is overwritten (no accumulation into Y).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are device pointers; `stream` is a hipStream_t passed
+ *    as void* (NULL = the null stream). Work is enqueued asynchronously; the
+ *    library never synchronizes, never allocates, never frees and never reads
+ *    device data on the host. The caller owns every buffer.
+ *  - Arguments are validated on the host before anything is launched. On a
+ *    failed check the call returns a negative status and enqueues nothing
+ *    (outputs are untouched). A launch error reported by the HIP runtime maps
+ *    to QDM_ERR_HIP. There is no fallback path of any kind.
+ *  - Alignment: w, x, y, out and workspace must be 16-byte aligned.
+ *  - Calls are stateless and may overlap on different streams as long as
+ *    their outputs and workspaces do not overlap.
+ */
+#ifndef QDM_H
+#define QDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* activation dtypes */
+#define QDM_F32 0
+#define QDM_BF16 1
+
+/* status codes */
+#define QDM_OK 0
+#define QDM_ERR_NULL (-1)      /* a required pointer is NULL */
+#define QDM_ERR_SHAPE (-2)     /* bad size (K % 256, non-positive, limits) */
+#define QDM_ERR_ALIGN (-3)     /* a pointer is not 16-byte aligned */
+#define QDM_ERR_DTYPE (-4)     /* unknown or unsupported activation dtype */
+#define QDM_ERR_WORKSPACE (-5) /* workspace missing or too small */
+#define QDM_ERR_HIP (-6)       /* the HIP runtime reported an error */
+
+/* Human-readable text for a status code (static storage). */
+const char *qdm_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int qdm_version(void);
+
+/*
+ * q4k_dequantize / q6k_dequantize: out[n][k] (fp32, [N][K] row-major) = the
+ * value of weight (n, k), bit-identical to the format formula evaluated in
+ * fp32 (every product in it is exact in fp32, so the result is the single
+ * correctly rounded value; Q6_K values are exact). Test-facing.
+ * N >= 1, K >= 256, K % 256 == 0.
+ */
+int q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
+int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
+
+/*
+ * q4k_gemv / q6k_gemv: decode-regime matmul, y[m][n] = sum_k x[m][k] * w(n,k)
+ * for 1 <= M <= 16. x_dtype is QDM_F32 or QDM_BF16. Accumulation is fp32.
+ * N >= 1, K >= 256, K % 256 == 0, K <= 65536 (bf16 x) or K <= 32768 (fp32 x):
+ * one activation row is staged in the 160 KiB LDS of a compute unit.
+ */
+int q4k_gemv(const void *w, const void *x, int x_dtype, float *y,
+             int64_t M, int64_t N, int64_t K, void *stream);
+int q6k_gemv(const void *w, const void *x, int x_dtype, float *y,
+             int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * q4k_gemm: prefill-regime matmul on the matrix cores. x is bf16 [M][K]; the
+ * Q4_K weights are decoded in fp32 and rounded to bf16 (nearest even) before
+ * the bf16 x bf16 -> fp32 MFMA contraction; y is fp32 [M][N].
+ * M >= 1, N >= 1, K >= 256, K % 256 == 0.
+ * workspace: q4k_gemm_workspace_bytes(M, N, K) bytes (may be 0, then
+ * workspace may be NULL).
+ */
+size_t q4k_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_q4k_grouped_gemm: routed MoE FFN with Q4_K experts, one call for the
+ * whole layer:
+ *   for every token t and slot s, e = topk_ids[t][s]:
+ *     u = W13[e] * x_t                  (2F values; W13[e] is [2F][H])
+ *     h = silu(u[0:F]) * u[F:2F]        (gate rows first, then up rows)
+ *     y_t += topk_w[t][s] * (W2[e] * h) (W2[e] is [H][F])
+ *   x: bf16 [T][H]; w_gate_up: E tensors of [2F][H/256] Q4_K blocks back to
+ *   back; w_down: E tensors of [H][F/256]; topk_ids int32 [T][top_k] (each in
+ *   [0, E), distinct within a row); topk_w fp32 [T][top_k]; y fp32 [T][H]
+ *   (overwritten). Tokens are grouped by expert on the device (histogram,
+ *   scan, scatter) so every expert's weights are streamed once per call.
+ *   Ids outside [0, E) are skipped (they contribute nothing).
+ *   1 <= T <= 2^24, 1 <= E <= 1024, 1 <= top_k <= 16, H and F multiples of
+ *   256 and at most 65536.
+ *   workspace: moe_q4k_workspace_bytes(T, E, top_k, H, F) bytes.
+ */
+size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
+int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,
+                         const int32_t *topk_ids, const float *topk_w, float *y,
+                         int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qdm_probe_copy: streaming copy of n_bytes from src to dst (n_bytes % 16 ==
+ * 0). A plain, known-size kernel used to calibrate memory-traffic counters
+ * and to measure the achievable HBM bandwidth of the device.
+ */
+int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDM_H */

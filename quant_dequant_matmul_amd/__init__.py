@@ -1,0 +1,186 @@
+"""Python binding of libqdm (include/qdm.h): Q4_K / Q6_K dequantize-fused
+matmul for MI355X (gfx950).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the computation runs in the HIP library. There
+is no CPU or torch fallback: a missing library or a tensor that is not on the
+GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqdm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "qdm.h")
+
+QDM_F32 = 0
+QDM_BF16 = 1
+Q4K_BLOCK_BYTES = 144
+Q6K_BLOCK_BYTES = 210
+
+_lib = None
+
+
+class QdmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqdm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqdm.so is not built (%s); run "
+                               "`python -m quant_dequant_matmul_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.qdm_status_string.argtypes = [i32]
+        L.qdm_status_string.restype = ctypes.c_char_p
+        L.qdm_version.restype = i32
+        for name in ("q4k_dequantize", "q6k_dequantize"):
+            f = getattr(L, name)
+            f.argtypes = [p, p, i64, i64, p]
+            f.restype = i32
+        for name in ("q4k_gemv", "q6k_gemv"):
+            f = getattr(L, name)
+            f.argtypes = [p, p, i32, p, i64, i64, i64, p]
+            f.restype = i32
+        L.q4k_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.q4k_gemm_workspace_bytes.restype = sz
+        L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
+        L.q4k_gemm.restype = i32
+        L.moe_q4k_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.moe_q4k_workspace_bytes.restype = sz
+        L.moe_q4k_grouped_gemm.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p, sz, p]
+        L.moe_q4k_grouped_gemm.restype = i32
+        L.qdm_probe_copy.argtypes = [p, p, i64, p]
+        L.qdm_probe_copy.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qdm_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise QdmError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (no CPU path exists)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _x_dtype(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return QDM_F32
+    if x.dtype == torch.bfloat16:
+        return QDM_BF16
+    raise ValueError("activations must be float32 or bfloat16")
+
+
+def _out(y, shape, device):
+    torch = _torch()
+    if y is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if tuple(y.shape) != tuple(shape) or y.dtype != torch.float32:
+        raise ValueError("y must be float32 %s" % (tuple(shape),))
+    return y
+
+
+def q4k_dequantize(w, N: int, K: int, out=None, stream=None):
+    out = _out(out, (N, K), w.device)
+    _check("q4k_dequantize", lib().q4k_dequantize(_dev_ptr(w, "w"), _dev_ptr(out, "out"),
+                                                  N, K, _stream(stream)))
+    return out
+
+
+def q6k_dequantize(w, N: int, K: int, out=None, stream=None):
+    out = _out(out, (N, K), w.device)
+    _check("q6k_dequantize", lib().q6k_dequantize(_dev_ptr(w, "w"), _dev_ptr(out, "out"),
+                                                  N, K, _stream(stream)))
+    return out
+
+
+def q4k_gemv(w, x, N: int, K: int, y=None, stream=None):
+    """y [M][N] fp32 = x [M][K] (fp32 or bf16) * W^T, W packed Q4_K [N][K/256]."""
+    M = x.shape[0]
+    y = _out(y, (M, N), x.device)
+    _check("q4k_gemv", lib().q4k_gemv(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _x_dtype(x),
+                                      _dev_ptr(y, "y"), M, N, K, _stream(stream)))
+    return y
+
+
+def q6k_gemv(w, x, N: int, K: int, y=None, stream=None):
+    """y [M][N] fp32 = x [M][K] (fp32 or bf16) * W^T, W packed Q6_K [N][K/256]."""
+    M = x.shape[0]
+    y = _out(y, (M, N), x.device)
+    _check("q6k_gemv", lib().q6k_gemv(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _x_dtype(x),
+                                      _dev_ptr(y, "y"), M, N, K, _stream(stream)))
+    return y
+
+
+def q4k_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().q4k_gemm_workspace_bytes(M, N, K))
+
+
+def q4k_gemm(w, x, N: int, K: int, y=None, workspace=None, stream=None):
+    """y [M][N] fp32 = x [M][K] bf16 * W^T on the matrix cores."""
+    torch = _torch()
+    M = x.shape[0]
+    y = _out(y, (M, N), x.device)
+    need = q4k_gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
+    _check("q4k_gemm", lib().q4k_gemm(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _dev_ptr(y, "y"),
+                                      M, N, K, wsp, wsb, _stream(stream)))
+    return y
+
+
+def moe_q4k_workspace_bytes(T: int, E: int, top_k: int, H: int, F: int) -> int:
+    return int(lib().moe_q4k_workspace_bytes(T, E, top_k, H, F))
+
+
+def moe_q4k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int, F: int,
+                         y=None, workspace=None, stream=None):
+    """Routed MoE FFN: y [T][H] = sum_s topk_w * W2[e] (silu(W13g x) * W13u x)."""
+    torch = _torch()
+    T, top_k = topk_ids.shape
+    y = _out(y, (T, H), x.device)
+    need = moe_q4k_workspace_bytes(T, E, top_k, H, F)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check("moe_q4k_grouped_gemm", lib().moe_q4k_grouped_gemm(
+        _dev_ptr(x, "x"), _dev_ptr(w_gate_up, "w_gate_up"), _dev_ptr(w_down, "w_down"),
+        _dev_ptr(topk_ids, "topk_ids"), _dev_ptr(topk_w, "topk_w"), _dev_ptr(y, "y"),
+        T, E, top_k, H, F, _dev_ptr(workspace, "workspace"), workspace.numel(),
+        _stream(stream)))
+    return y
+
+
+def probe_copy(src, dst, n_bytes: int, stream=None):
+    _check("qdm_probe_copy", lib().qdm_probe_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"),
+                                                  n_bytes, _stream(stream)))

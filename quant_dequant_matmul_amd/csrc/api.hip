@@ -1,0 +1,136 @@
+// C ABI of libqdm (declared in include/qdm.h): host-side validation, then the
+// launches. Nothing here allocates, synchronizes or reads device memory.
+//
+// Unsupported arguments fail with a status code instead of falling back to
+// another path (hipEngine README, "Quickstart": unsupported combinations fail
+// instead of falling back).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qdm.h"
+#include "launch.h"
+
+#define QDM_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;      // bf16 activations (x staged in LDS)
+constexpr int64_t kMaxKF32 = 32768;   // fp32 activations
+
+inline bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+inline int finish_launch() {
+  return hipGetLastError() == hipSuccess ? QDM_OK : QDM_ERR_HIP;
+}
+
+inline bool bad_k(int64_t K) { return K < 256 || K % 256 != 0; }
+
+}  // namespace
+
+QDM_EXPORT const char *qdm_status_string(int status) {
+  switch (status) {
+    case QDM_OK: return "ok";
+    case QDM_ERR_NULL: return "a required pointer is NULL";
+    case QDM_ERR_SHAPE: return "invalid size argument";
+    case QDM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QDM_ERR_DTYPE: return "unsupported activation dtype";
+    case QDM_ERR_WORKSPACE: return "workspace missing or too small";
+    case QDM_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+QDM_EXPORT int qdm_version(void) { return 100; }
+
+QDM_EXPORT int q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream) {
+  if (!w || !out) return QDM_ERR_NULL;
+  if (N < 1 || bad_k(K)) return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(out)) return QDM_ERR_ALIGN;
+  qdm::launch_q4k_dequantize(w, out, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream) {
+  if (!w || !out) return QDM_ERR_NULL;
+  if (N < 1 || bad_k(K)) return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(out)) return QDM_ERR_ALIGN;
+  qdm::launch_q6k_dequantize(w, out, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+static int check_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
+                      int64_t N, int64_t K) {
+  if (!w || !x || !y) return QDM_ERR_NULL;
+  if (M < 1 || M > 16 || N < 1 || N > INT32_MAX || bad_k(K) || K > kMaxK) return QDM_ERR_SHAPE;
+  if (x_dtype != QDM_F32 && x_dtype != QDM_BF16) return QDM_ERR_DTYPE;
+  if (x_dtype == QDM_F32 && K > kMaxKF32) return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(x) || misaligned(y)) return QDM_ERR_ALIGN;
+  return QDM_OK;
+}
+
+QDM_EXPORT int q4k_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+  const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
+  if (rc) return rc;
+  qdm::launch_q4k_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int q6k_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+  const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
+  if (rc) return rc;
+  qdm::launch_q6k_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT size_t q4k_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || bad_k(K)) return 0;
+  return qdm::q4k_gemm_workspace(M, N, K);
+}
+
+QDM_EXPORT int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N,
+                        int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!w || !x || !y) return QDM_ERR_NULL;
+  if (M < 1 || M > INT32_MAX || N < 1 || N > INT32_MAX || bad_k(K) || K > INT32_MAX ||
+      ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX)
+    return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(x) || misaligned(y)) return QDM_ERR_ALIGN;
+  const size_t need = qdm::q4k_gemm_workspace(M, N, K);
+  if (need && (!workspace || workspace_bytes < need)) return QDM_ERR_WORKSPACE;
+  if (need && misaligned(workspace)) return QDM_ERR_ALIGN;
+  qdm::launch_q4k_gemm(w, x, y, M, N, K, workspace, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H,
+                                          int64_t F) {
+  if (T < 1 || E < 1 || top_k < 1 || top_k > 16 || bad_k(H) || bad_k(F)) return 0;
+  return qdm::moe_workspace(T, E, top_k, H, F);
+}
+
+QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,
+                                    const int32_t *topk_ids, const float *topk_w, float *y,
+                                    int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !w_gate_up || !w_down || !topk_ids || !topk_w || !y) return QDM_ERR_NULL;
+  if (T < 1 || T > (1 << 24) || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || bad_k(H) ||
+      bad_k(F) || H > kMaxK || F > kMaxK)
+    return QDM_ERR_SHAPE;
+  if (misaligned(x) || misaligned(w_gate_up) || misaligned(w_down) || misaligned(y))
+    return QDM_ERR_ALIGN;
+  const size_t need = qdm::moe_workspace(T, E, top_k, H, F);
+  if (!workspace || workspace_bytes < need) return QDM_ERR_WORKSPACE;
+  if (misaligned(workspace)) return QDM_ERR_ALIGN;
+  qdm::launch_moe_q4k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F, workspace,
+                      (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void *stream) {
+  if (!src || !dst) return QDM_ERR_NULL;
+  if (n_bytes < 16 || n_bytes % 16) return QDM_ERR_SHAPE;
+  if (misaligned(src) || misaligned(dst)) return QDM_ERR_ALIGN;
+  qdm::launch_probe_copy(src, dst, n_bytes, (hipStream_t)stream);
+  return finish_launch();
+}

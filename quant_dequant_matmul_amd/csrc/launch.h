@@ -1,0 +1,30 @@
+// Host-side launchers (internal to libqdm; the public ABI is include/qdm.h).
+// Each launcher assumes validated arguments and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qdm {
+
+void launch_q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
+void launch_q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
+
+void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s);
+void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s);
+
+size_t q4k_gemm_workspace(int64_t M, int64_t N, int64_t K);
+void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
+                     void *workspace, hipStream_t s);
+
+size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
+void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                    const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
+                    int64_t F, void *workspace, hipStream_t s);
+
+void launch_probe_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
+
+}  // namespace qdm

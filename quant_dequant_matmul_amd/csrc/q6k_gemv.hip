@@ -1,0 +1,307 @@
+// Q6_K GEMV: y[m][n] = sum_k x[m][k] * w(n, k) for M in 1..16 (VALU path).
+//
+// Q6_K is the output-head / mixed tensor type of a Q4_K_M file (hipEngine
+// README, "GGUF Support", payload table). Weight i of a 210-byte block, with
+// h = i/128, g = (i%128)/32, l = i%32: low nibble from QL[64h + 32(g%2) + l]
+// (high half when g >= 2), high pair from bits 2g..2g+1 of QH[32h + l],
+// w = d * scale[i/16] * (q - 32).
+//
+// Mapping (wave64): a lane owns half h = c/2 and the 16 positions
+// l0 = 16(c%2) .. l0+15 of a block, i.e. 64 weights (4 groups g of 16, each
+// one sub-block with its own scale). 4 lanes per block; rows split across the
+// 16 lane-groups of a wave as in the Q4_K GEMV (G = gcd(K/256, 16) groups per
+// row, R = 16/G rows per wave).
+//
+// Alignment: blocks are 210 bytes, so a block starts at an even offset; all
+// field offsets a lane reads (64h + l0, 64h + 32 + l0, 128 + 32h + l0, 192 +
+// 8h, 208) are even too. Each field is read as 4-byte-aligned dwords covering
+// it and shifted down by 0 or 2 bytes with v_alignbyte.
+//
+// bf16 x: codes become exact bf16 values 128 + q (q < 64 fits the 7-bit
+// mantissa at exponent 7), summed with v_dot2_f32_bf16 against x pairs
+// (l, l+2) / (l+1, l+3) (x staged in LDS with groups of four permuted), then
+//   sum_l x_l (q_l - 32) = s - 160 * sum_l x_l.
+#include "common.h"
+#include "launch.h"
+
+namespace qdm {
+
+namespace {
+
+constexpr int Q6_THREADS = 256;
+constexpr int Q6_WAVES = Q6_THREADS / WAVE;
+
+template <bool XBF16, int MT>
+__device__ __forceinline__ void q6_stage_x(const void *__restrict__ x, int K, uint32_t *lds_x,
+                                           float *lds_sum) {
+  const int tid = threadIdx.x;
+  if constexpr (XBF16) {
+    const int nchunk = MT * K / 8;  // 8 bf16 per chunk, 2 chunks per 16-sum
+    const u32x4 *src = (const u32x4 *)x;
+    for (int base = 0; base < nchunk; base += Q6_THREADS) {
+      const int c = base + tid;
+      float s = 0.f;
+      if (c < nchunk) {
+        const u32x4 v = src[c];
+        u32x4 p;
+        p.x = (v.x & 0xFFFFu) | (v.y << 16);
+        p.y = (v.x >> 16) | (v.y & 0xFFFF0000u);
+        p.z = (v.z & 0xFFFFu) | (v.w << 16);
+        p.w = (v.z >> 16) | (v.w & 0xFFFF0000u);
+        ((u32x4 *)lds_x)[c] = p;
+        s = bf16_bits_to_float(v.x) + bf16_bits_to_float(v.x >> 16) +
+            bf16_bits_to_float(v.y) + bf16_bits_to_float(v.y >> 16) +
+            bf16_bits_to_float(v.z) + bf16_bits_to_float(v.z >> 16) +
+            bf16_bits_to_float(v.w) + bf16_bits_to_float(v.w >> 16);
+      }
+      s += __shfl_xor(s, 1, WAVE);
+      if (c < nchunk && (c & 1) == 0) lds_sum[c >> 1] = s;
+    }
+  } else {
+    const int nchunk = MT * K / 4;  // 4 fp32 per chunk, 4 chunks per 16-sum
+    const f32x4 *src = (const f32x4 *)x;
+    for (int base = 0; base < nchunk; base += Q6_THREADS) {
+      const int c = base + tid;
+      float s = 0.f;
+      if (c < nchunk) {
+        const f32x4 v = src[c];
+        ((f32x4 *)lds_x)[c] = v;
+        s = (v.x + v.y) + (v.z + v.w);
+      }
+      s += __shfl_xor(s, 1, WAVE);
+      s += __shfl_xor(s, 2, WAVE);
+      if (c < nchunk && (c & 3) == 0) lds_sum[c >> 2] = s;
+    }
+  }
+}
+
+// 4-byte-aligned dword loads (the compiler must not assume more alignment).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// 16 bytes starting at an even byte offset `off` from the 16-aligned base:
+// five aligned dwords [off & ~3, (off & ~3) + 20), shifted down by (off & 2)
+// bytes. Callers keep off + 18 inside the block.
+__device__ __forceinline__ u32x4 load16_even(const uint8_t *__restrict__ base, int64_t off) {
+  const int64_t a = off & ~(int64_t)3;
+  const u32x4 lo = *(const u32x4_a4 *)(base + a);
+  const uint32_t hi = *(const uint32_t *)(base + a + 16);
+  const uint32_t sh = (uint32_t)(off & 2);
+  u32x4 r;
+  r.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, sh);
+  r.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, sh);
+  r.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, sh);
+  r.w = __builtin_amdgcn_alignbyte(hi, lo.w, sh);
+  return r;
+}
+
+// 4 bytes at an even offset: the dwords holding its first and last byte
+// (the same dword when off is 4-aligned). Never reads past off + 6.
+__device__ __forceinline__ uint32_t load4_even(const uint8_t *__restrict__ base, int64_t off) {
+  const uint32_t lo = *(const uint32_t *)(base + (off & ~(int64_t)3));
+  const uint32_t hi = *(const uint32_t *)(base + ((off + 2) & ~(int64_t)3));
+  return __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(off & 2));
+}
+
+struct Q6Lane {
+  u32x4 qa, qb, qh;  // QL[64h+l0..], QL[64h+32+l0..], QH[32h+l0..]
+  uint32_t s0, s1;   // scale bytes 8h .. 8h+7
+  uint32_t dbits;    // fp16 d in the low half
+};
+
+__device__ __forceinline__ Q6Lane q6_load(const uint8_t *__restrict__ w, int64_t blk_off, int h,
+                                          int l0) {
+  Q6Lane L;
+  L.qa = load16_even(w, blk_off + 64 * h + l0);
+  L.qb = load16_even(w, blk_off + 64 * h + 32 + l0);
+  L.qh = load16_even(w, blk_off + 128 + 32 * h + l0);
+  L.s0 = load4_even(w, blk_off + 192 + 8 * h);
+  L.s1 = load4_even(w, blk_off + 196 + 8 * h);
+  L.dbits = *(const uint16_t *)(w + blk_off + 208);  // 2-aligned; the last field
+  return L;
+}
+
+template <bool XBF16, int MT, int PF>
+__global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
+    const uint8_t *__restrict__ w, const void *__restrict__ x, float *__restrict__ y, int N,
+    int K, int G, int ldy) {
+  extern __shared__ uint32_t lds[];
+  uint32_t *lds_x = lds;
+  float *lds_sum = (float *)(lds + (XBF16 ? MT * K / 2 : MT * K));
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 2, c = lane & 3;
+  const int h = c >> 1, l0 = 16 * (c & 1);
+  const int R = 16 / G;
+  const int row = (blockIdx.x * Q6_WAVES + wave) * R + g / G;
+  const int gg = g % G;
+  const int nb = K / QK;
+  const int iters = nb / G;
+  const bool active = row < N;
+  const int64_t row_off = (int64_t)(active ? row : 0) * nb * Q6K_BYTES;
+
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++) acc[m] = 0.f;
+
+  Q6Lane buf[PF];
+#pragma unroll
+  for (int p = 0; p < PF; p++)
+    if (active && p < iters) buf[p] = q6_load(w, row_off + (int64_t)(p * G + gg) * Q6K_BYTES, h, l0);
+
+  q6_stage_x<XBF16, MT>(x, K, lds_x, lds_sum);
+  __syncthreads();
+
+  if (active) {
+    for (int it0 = 0; it0 < iters; it0 += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; p++) {
+        const int it = it0 + p;
+        if (it < iters) {
+          const int kb = it * G + gg;
+          const Q6Lane L = buf[p];
+          if (it + PF < iters)
+            buf[p] = q6_load(w, row_off + (int64_t)((it + PF) * G + gg) * Q6K_BYTES, h, l0);
+          const float d = half_bits_to_float(L.dbits);
+          // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
+          // of the 8 scale bytes s0|s1.
+          const int sb = l0 >> 4;
+          float dsc[4];
+#pragma unroll
+          for (int gq = 0; gq < 4; gq++) {
+            const int bi = 2 * gq + sb;
+            const uint32_t word = bi < 4 ? L.s0 : L.s1;
+            dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+          }
+          const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+          const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+          const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+          if constexpr (XBF16) {
+            // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
+            uint32_t pr[4][8];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+              const uint32_t a = qa[k], b = qb[k], hh = qh[k];
+              pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
+              pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
+              pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
+              pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
+              pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
+              pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
+              pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
+              pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
+            }
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              float r = acc[m];
+#pragma unroll
+              for (int gq = 0; gq < 4; gq++) {
+                const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;  // first x element
+                const u32x4 *xv = (const u32x4 *)(lds_x + e0 / 2);
+                const float xs = lds_sum[e0 / 16];
+                const u32x4 x0 = xv[0], x1 = xv[1];  // l0..l0+7, l0+8..l0+15
+                float s = 0.f;
+                s = dot2_bf16(pr[gq][0], x0.x, s);
+                s = dot2_bf16(pr[gq][1], x0.y, s);
+                s = dot2_bf16(pr[gq][2], x0.z, s);
+                s = dot2_bf16(pr[gq][3], x0.w, s);
+                s = dot2_bf16(pr[gq][4], x1.x, s);
+                s = dot2_bf16(pr[gq][5], x1.y, s);
+                s = dot2_bf16(pr[gq][6], x1.z, s);
+                s = dot2_bf16(pr[gq][7], x1.w, s);
+                r = fmaf(dsc[gq], fmaf(-160.f, xs, s), r);
+              }
+              acc[m] = r;
+            }
+          } else {
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              float r = acc[m];
+#pragma unroll
+              for (int gq = 0; gq < 4; gq++) {
+                const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;
+                const f32x4 *xv = (const f32x4 *)((const float *)lds_x + e0);
+                float s = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                  const f32x4 xx = xv[k];
+                  const uint32_t src = (gq & 1) ? qb[k] : qa[k];
+                  const int nsh = (gq >> 1) * 4;
+#pragma unroll
+                  for (int e = 0; e < 4; e++) {
+                    const int lo = (int)((src >> (8 * e + nsh)) & 15u);
+                    const int hi = (int)((qh[k] >> (8 * e + 2 * gq)) & 3u);
+                    s = fmaf(xx[e], (float)((lo | (hi << 4)) - 32), s);
+                  }
+                }
+                r = fmaf(dsc[gq], s, r);
+              }
+              acc[m] = r;
+            }
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < MT; m++) {
+    float v = group_sum(acc[m], 4 * G);
+    if (active && (lane & (4 * G - 1)) == 0) y[(int64_t)m * ldy + row] = v;
+  }
+}
+
+int gcd16(int nb) {
+  int g = 16;
+  while (g > 1 && nb % g) g >>= 1;
+  return g;
+}
+
+template <bool XBF16, int MT>
+void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, int64_t ldy,
+                  hipStream_t s) {
+  const int nb = (int)(K / QK);
+  const int G = gcd16(nb);
+  const int R = 16 / G;
+  const int64_t rows_per_wg = (int64_t)Q6_WAVES * R;
+  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
+  const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 16) * 4;
+  constexpr int PF = 2;
+  auto kern = q6k_gemv_kernel<XBF16, MT, PF>;
+  if (lds > 65536) hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Q6_THREADS), lds, s, (const uint8_t *)w, x, y,
+                     (int)N, (int)K, G, (int)ldy);
+}
+
+}  // namespace
+
+void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s) {
+  const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 16) * 4;
+  const size_t elt = x_bf16 ? 2 : 4;
+  int64_t m0 = 0;
+  while (m0 < M) {
+    const int64_t rem = M - m0;
+    int mt = 8;
+    while (mt > 1 && (mt > rem || (size_t)mt * per_row > 65536)) mt >>= 1;
+    const void *xm = (const char *)x + (size_t)m0 * K * elt;
+    float *ym = y + m0 * N;
+    if (x_bf16) {
+      switch (mt) {
+        case 8: launch_chunk<true, 8>(w, xm, ym, N, K, N, s); break;
+        case 4: launch_chunk<true, 4>(w, xm, ym, N, K, N, s); break;
+        case 2: launch_chunk<true, 2>(w, xm, ym, N, K, N, s); break;
+        default: launch_chunk<true, 1>(w, xm, ym, N, K, N, s); break;
+      }
+    } else {
+      switch (mt) {
+        case 8: launch_chunk<false, 8>(w, xm, ym, N, K, N, s); break;
+        case 4: launch_chunk<false, 4>(w, xm, ym, N, K, N, s); break;
+        case 2: launch_chunk<false, 2>(w, xm, ym, N, K, N, s); break;
+        default: launch_chunk<false, 1>(w, xm, ym, N, K, N, s); break;
+      }
+    }
+    m0 += mt;
+  }
+}
+
+}  // namespace qdm

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/qdm.h declares, and rejects bad arguments with the documented
+status codes before anything is launched.
+
+Only argument combinations that fail validation are passed here: pointers in
+these calls are never dereferenced, and no call reaches a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quant_dequant_matmul_amd as qdm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+A = ctypes.c_void_p(1 << 20)       # 16-byte aligned fake address (never dereferenced)
+A2 = ctypes.c_void_p((1 << 20) + 4096)
+MIS = ctypes.c_void_p((1 << 20) + 8)  # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qdm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "defined"})
+
+
+def test_header_symbols_exported():
+    lib = ctypes.CDLL(qdm.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP):
+        assert qdm.status_string(code)
+    assert qdm.status_string(12345) == "unknown status"
+    assert qdm.lib().qdm_version() >= 100
+
+
+@pytest.mark.parametrize("fn", ["q4k_gemv", "q6k_gemv"])
+def test_gemv_validation(fn):
+    f = getattr(qdm.lib(), fn)
+    assert f(NUL, A, 0, A2, 1, 8, 256, NUL) == ENULL
+    assert f(A, NUL, 0, A2, 1, 8, 256, NUL) == ENULL
+    assert f(A, A, 0, NUL, 1, 8, 256, NUL) == ENULL
+    for (M, N, K) in [(0, 8, 256), (17, 8, 256), (1, 0, 256), (1, 8, 0), (1, 8, 255),
+                      (1, 8, 384), (1, 8, 65536 + 256), (-1, 8, 256)]:
+        assert f(A, A, 0, A2, M, N, K, NUL) == ESHAPE, (M, N, K)
+    assert f(A, A, 0, A2, 1, 8, 32768 + 256, NUL) == ESHAPE  # fp32 x: K <= 32768
+    assert f(A, A, 2, A2, 1, 8, 256, NUL) == EDTYPE
+    assert f(A, A, -1, A2, 1, 8, 256, NUL) == EDTYPE
+    assert f(MIS, A, 1, A2, 1, 8, 256, NUL) == EALIGN
+    assert f(A, MIS, 1, A2, 1, 8, 256, NUL) == EALIGN
+    assert f(A, A, 1, MIS, 1, 8, 256, NUL) == EALIGN
+
+
+@pytest.mark.parametrize("fn", ["q4k_dequantize", "q6k_dequantize"])
+def test_dequant_validation(fn):
+    f = getattr(qdm.lib(), fn)
+    assert f(NUL, A, 4, 256, NUL) == ENULL
+    assert f(A, NUL, 4, 256, NUL) == ENULL
+    assert f(A, A2, 0, 256, NUL) == ESHAPE
+    assert f(A, A2, 4, 500, NUL) == ESHAPE
+    assert f(MIS, A2, 4, 256, NUL) == EALIGN
+    assert f(A, MIS, 4, 256, NUL) == EALIGN
+
+
+def test_gemm_validation():
+    L = qdm.lib()
+    need = L.q4k_gemm_workspace_bytes(512, 17408, 5120)
+    assert L.q4k_gemm_workspace_bytes(0, 8, 256) == 0
+    assert L.q4k_gemm(NUL, A, A2, 4, 8, 256, NUL, 0, NUL) == ENULL
+    assert L.q4k_gemm(A, A, A2, 0, 8, 256, NUL, 0, NUL) == ESHAPE
+    assert L.q4k_gemm(A, A, A2, 4, 8, 300, NUL, 0, NUL) == ESHAPE
+    assert L.q4k_gemm(A, MIS, A2, 4, 8, 256, NUL, 0, NUL) == EALIGN
+    if need:
+        assert L.q4k_gemm(A, A, A2, 512, 17408, 5120, NUL, 0, NUL) == EWS
+        assert L.q4k_gemm(A, A, A2, 512, 17408, 5120, A, need - 1, NUL) == EWS
+
+
+def test_moe_validation():
+    L = qdm.lib()
+    T, E, k, H, F = 8, 128, 8, 2048, 768
+    need = L.moe_q4k_workspace_bytes(T, E, k, H, F)
+    assert need > 0
+    assert L.moe_q4k_workspace_bytes(T, E, 17, H, F) == 0
+    assert L.moe_q4k_workspace_bytes(T, E, k, 300, F) == 0
+    args = [A, A, A, A, A, A2]
+    assert L.moe_q4k_grouped_gemm(NUL, *args[1:], T, E, k, H, F, A, need, NUL) == ENULL
+    assert L.moe_q4k_grouped_gemm(*args, 0, E, k, H, F, A, need, NUL) == ESHAPE
+    assert L.moe_q4k_grouped_gemm(*args, T, 0, k, H, F, A, need, NUL) == ESHAPE
+    assert L.moe_q4k_grouped_gemm(*args, T, 2048, k, H, F, A, need, NUL) == ESHAPE
+    assert L.moe_q4k_grouped_gemm(*args, T, E, 0, H, F, A, need, NUL) == ESHAPE
+    assert L.moe_q4k_grouped_gemm(*args, T, E, k, 2000, F, A, need, NUL) == ESHAPE
+    assert L.moe_q4k_grouped_gemm(MIS, *args[1:], T, E, k, H, F, A, need, NUL) == EALIGN
+    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, NUL, need, NUL) == EWS
+    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, A, need - 1, NUL) == EWS
+    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, MIS, need, NUL) == EALIGN
+
+
+def test_probe_validation():
+    L = qdm.lib()
+    assert L.qdm_probe_copy(NUL, A, 1024, NUL) == ENULL
+    assert L.qdm_probe_copy(A, A2, 1000, NUL) == ESHAPE
+    assert L.qdm_probe_copy(MIS, A2, 1024, NUL) == EALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(144, dtype=torch.uint8)
+    x = torch.zeros(1, 256, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        qdm.q4k_gemv(w, x, 1, 256, y=torch.empty(1, 1))

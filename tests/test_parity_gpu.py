@@ -1,0 +1,318 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: dequantized weights bit-exact; matmuls within a normwise relative error
+of 1e-5 (fp32 activations) or 8e-3 (bf16 activations), over the whole output
+of a call (or over the sampled rows/columns where the oracle is run on a
+subset at full size). The fp32-accumulating GEMV/MoE paths must also stay
+within 1e-5 with bf16 activations.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qdm_synth as synth
+from gpu_helpers import (GUARD_VALU, TOL_BF16, TOL_F32, bf16_to_f32, dev_bytes, dev_x,
+                         f32_to_bf16_f32, host, rel_err, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import quant_dequant_matmul_amd as qdm  # noqa: E402
+
+
+# --------------------------------------------------------------------------
+# dequant exports: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (37, 768, 5), (5, 17408, 6), (129, 1280, 7)])
+def test_q4k_dequant_bit_exact(N, K, seed):
+    say("q4k_dequantize", N, K, seed)
+    w = synth.q4k_blocks(np.random.default_rng(seed), N, K)
+    out = host(qdm.q4k_dequantize(dev_bytes(w), N, K))
+    ref = oracle.q4k_dequantize(w, N, K)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,seed", [(16, 256, 0), (37, 768, 5), (3, 5120, 6), (7, 17408, 8)])
+def test_q6k_dequant_bit_exact(N, K, seed):
+    say("q6k_dequantize", N, K, seed)
+    w = synth.q6k_blocks(np.random.default_rng(seed), N, K)
+    out = host(qdm.q6k_dequantize(dev_bytes(w), N, K))
+    ref = oracle.q6k_dequantize(w, N, K)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# Q4_K GEMV
+# --------------------------------------------------------------------------
+
+def test_q4k_gemv_tiny_fp32():
+    say("q4k_gemv tiny N=K=256 M=1 fp32 seed 0")
+    w, x = synth.tiny_gemv()
+    y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), 256, 256))
+    ref = oracle.q4k_matmul(w, x, 256, 256)
+    assert rel_err(y, ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("which", ["qkv", "gate_up", "down"])
+def test_q4k_gemv_decode_set_full(which):
+    w, x = synth.decode_gemv(which)
+    N, K = {"qkv": (7168, 5120), "gate_up": (34816, 5120), "down": (5120, 17408)}[which]
+    say("q4k_gemv decode", which, "N", N, "K", K)
+    y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q4k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16 and e <= GUARD_VALU
+
+
+GEMV_CASES = [(1, 1, 256), (1, 37, 768), (3, 1000, 1280), (5, 129, 2304), (16, 64, 4096),
+              (8, 333, 512), (2, 17, 8192), (1, 4099, 256), (7, 250, 768 * 3), (1, 31, 32768)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+def test_q4k_gemv_ragged(M, N, K, dt):
+    say("q4k_gemv", M, N, K, dt)
+    rng = np.random.default_rng(M * 1000 + N + K)
+    w = synth.q4k_blocks(rng, N, K)
+    x = synth.normal_f32(rng, (M, K)) if dt == "f32" else synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q4k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+
+
+def test_q4k_gemv_longest_k_bf16():
+    M, N, K = 1, 31, 65536
+    say("q4k_gemv", M, N, K, "bf16")
+    rng = np.random.default_rng(77)
+    w = synth.q4k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), N, K))
+    assert rel_err(y, oracle.q4k_matmul(w, x, N, K)) <= GUARD_VALU
+
+
+def test_q4k_gemv_one_hot_rows_bit_exact():
+    """x = e_k (fp32) gives y[n] = W[n, k] exactly."""
+    N, K = 300, 1280
+    w = synth.q4k_blocks(np.random.default_rng(3), N, K)
+    W = oracle.q4k_dequantize(w, N, K)
+    wd = dev_bytes(w)
+    for k in [0, 1, 31, 32, 63, 64, 255, 256, 700, 1279]:
+        say("q4k_gemv one-hot k", k)
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        y = host(qdm.q4k_gemv(wd, dev_x(x), N, K))[0]
+        assert np.array_equal(y, W[:, k]), k
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_q4k_gemv_power_of_two_scaling(dt):
+    N, K = 512, 2048
+    rng = np.random.default_rng(9)
+    w = dev_bytes(synth.q4k_blocks(rng, N, K))
+    x = synth.normal_f32(rng, (1, K)) if dt == "f32" else synth.normal_bf16(rng, (1, K))
+    xd = dev_x(x)
+    say("q4k_gemv pow2 scaling", dt)
+    y1 = host(qdm.q4k_gemv(w, xd, N, K))
+    y2 = host(qdm.q4k_gemv(w, xd * 8, N, K))
+    assert np.array_equal(y2, y1 * 8)
+
+
+# --------------------------------------------------------------------------
+# Q6_K GEMV
+# --------------------------------------------------------------------------
+
+Q6_CASES = [(1, 16, 256), (1, 37, 768), (8, 129, 1280), (3, 1000, 5120), (16, 40, 2304),
+            (5, 77, 17408), (1, 4097, 512)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", Q6_CASES)
+def test_q6k_gemv_ragged(M, N, K, dt):
+    say("q6k_gemv", M, N, K, dt)
+    rng = np.random.default_rng(M * 7 + N + K)
+    w = synth.q6k_blocks(rng, N, K)
+    x = synth.normal_f32(rng, (M, K)) if dt == "f32" else synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q6k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+
+
+def test_q6k_gemv_one_hot_rows_bit_exact():
+    N, K = 100, 768
+    w = synth.q6k_blocks(np.random.default_rng(4), N, K)
+    W = oracle.q6k_dequantize(w, N, K)
+    wd = dev_bytes(w)
+    for k in [0, 15, 16, 31, 32, 127, 128, 200, 255, 256, 767]:
+        say("q6k_gemv one-hot k", k)
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        y = host(qdm.q6k_gemv(wd, dev_x(x), N, K))[0]
+        assert np.array_equal(y, W[:, k]), k
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_q6k_gemv_head_full_sampled(M):
+    """Output head K=5120, N=151936: GPU computes all rows; the oracle checks
+    every 53rd row."""
+    w, x = synth.q6k_gemv("head", M)
+    N, K = 151936, 5120
+    say("q6k_gemv head M", M)
+    y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
+    rows = np.arange(0, N, 53)
+    ref = oracle.q6k_matmul(w[rows], x, len(rows), K)
+    e = rel_err(y[:, rows], ref)
+    say("  rel err", e)
+    assert e <= min(TOL_BF16, GUARD_VALU)
+
+
+def test_q6k_gemv_down_full():
+    w, x = synth.q6k_gemv("down", 1)
+    N, K = 5120, 17408
+    say("q6k_gemv down")
+    y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q6k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= min(TOL_BF16, GUARD_VALU)
+
+
+# --------------------------------------------------------------------------
+# Q4_K GEMM (matrix cores)
+# --------------------------------------------------------------------------
+
+GEMM_CASES = [(1, 17, 256), (5, 128, 768), (130, 200, 1280), (257, 129, 512), (128, 128, 256),
+              (64, 1000, 2304), (512, 256, 5120), (33, 4099, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+def test_q4k_gemm_ragged(M, N, K):
+    say("q4k_gemm", M, N, K)
+    rng = np.random.default_rng(M + 3 * N + K)
+    w = synth.q4k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q4k_gemm(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q4k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
+def test_q4k_gemm_one_hot_gives_bf16_weights():
+    """x rows e_k: y[m, n] = bf16(W[n, k_m]) exactly (one nonzero product)."""
+    N, K = 200, 1280
+    w = synth.q4k_blocks(np.random.default_rng(12), N, K)
+    W = oracle.q4k_dequantize(w, N, K)
+    ks = [0, 1, 31, 32, 63, 64, 100, 255, 256, 511, 512, 700, 1000, 1100, 1278, 1279]
+    x = np.zeros((len(ks), K), dtype=np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80  # bf16 1.0
+    say("q4k_gemm one-hot")
+    y = host(qdm.q4k_gemm(dev_bytes(w), dev_x(x), N, K))
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i], f32_to_bf16_f32(W[:, k])), k
+
+
+@pytest.mark.parametrize("M", [512, 4096])
+def test_q4k_gemm_prefill_full_sampled(M):
+    """K=5120, N=17408: every output is computed; the oracle checks sampled
+    columns (every 67th) and, at M=4096, every 8th row."""
+    w, x = synth.prefill_gemm(M)
+    N, K = 17408, 5120
+    say("q4k_gemm prefill M", M)
+    y = host(qdm.q4k_gemm(dev_bytes(w), dev_x(x), N, K))
+    cols = np.arange(0, N, 67)
+    rows = np.arange(0, M, 1 if M <= 512 else 8)
+    ref = oracle.q4k_matmul(w[cols], x[rows], len(cols), K)
+    e = rel_err(y[np.ix_(rows, cols)], ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+    assert np.isfinite(y).all()
+
+
+# --------------------------------------------------------------------------
+# MoE
+# --------------------------------------------------------------------------
+
+def _moe_dev(d):
+    return (dev_x(d["x"]), dev_bytes(d["w13"]), dev_bytes(d["w2"]),
+            torch.from_numpy(d["ids"]).to("cuda"), torch.from_numpy(d["gw"]).to("cuda"))
+
+
+@pytest.mark.parametrize("T,E,H,F,top_k", [(5, 6, 256, 256, 3), (1, 4, 512, 256, 2),
+                                           (33, 16, 256, 512, 4), (64, 8, 768, 256, 8)])
+def test_moe_small_full(T, E, H, F, top_k):
+    say("moe small", T, E, H, F, top_k)
+    d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T + E)
+    y = host(qdm.moe_q4k_grouped_gemm(*_moe_dev(d), E, H, F))
+    ref = oracle.moe_q4k(d["x"], d["w13"], d["w2"], d["ids"], d["gw"], E, H, F)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [1, 8, 512])
+def test_moe_full_shape(T):
+    """128 experts, H=2048, F=768, top-8. The GPU runs all T tokens; the oracle
+    checks all of them for T <= 8 and 24 sampled tokens at T = 512."""
+    E, H, F = 128, 2048, 768
+    say("moe full T", T)
+    d = synth.moe(T)
+    y = host(qdm.moe_q4k_grouped_gemm(*_moe_dev(d), E, H, F))
+    toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 24).astype(int)
+    ref = oracle.moe_q4k(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F)
+    e = rel_err(y[toks], ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
+def test_moe_skips_out_of_range_ids():
+    E, H, F, T = 6, 256, 256, 4
+    d = synth.moe(T, E=E, H=H, F=F, top_k=2, seed=11)
+    ids = d["ids"].copy()
+    ids[1, 1] = E + 3
+    ids[3, 0] = -1
+    gw = d["gw"].copy()
+    say("moe bad ids")
+    xd, w13, w2, _, _ = _moe_dev(d)
+    y = host(qdm.moe_q4k_grouped_gemm(xd, w13, w2, torch.from_numpy(ids).to("cuda"),
+                                      torch.from_numpy(gw).to("cuda"), E, H, F))
+    gw_ref = gw.copy()
+    ids_ref = ids.copy()
+    gw_ref[1, 1] = 0.0
+    gw_ref[3, 0] = 0.0
+    ids_ref[1, 1] = 0
+    ids_ref[3, 0] = 0
+    ref = oracle.moe_q4k(d["x"], d["w13"], d["w2"], ids_ref, gw_ref, E, H, F)
+    assert rel_err(y, ref) <= TOL_BF16
+
+
+# --------------------------------------------------------------------------
+# determinism (race detector): identical calls give identical bits
+# --------------------------------------------------------------------------
+
+def test_determinism_all_entry_points():
+    rng = np.random.default_rng(99)
+    N, K, M = 4096, 5120, 1
+    w = dev_bytes(synth.q4k_blocks(rng, N, K))
+    x = dev_x(synth.normal_bf16(rng, (M, K)))
+    say("determinism gemv")
+    a, b = host(qdm.q4k_gemv(w, x, N, K)), host(qdm.q4k_gemv(w, x, N, K))
+    assert np.array_equal(a, b)
+    xg = dev_x(synth.normal_bf16(rng, (300, K)))
+    say("determinism gemm")
+    a, b = host(qdm.q4k_gemm(w, xg, N, K)), host(qdm.q4k_gemm(w, xg, N, K))
+    assert np.array_equal(a, b)
+    d = synth.moe(64)
+    args = _moe_dev(d)
+    say("determinism moe")
+    a = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
+    b = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
+    assert np.array_equal(a, b)
