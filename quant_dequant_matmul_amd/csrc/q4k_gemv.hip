@@ -5,23 +5,25 @@
 // micro-benchmark reported in GB/s). Every 144-byte super-block is read from
 // HBM exactly once with 16-byte loads and decoded in registers.
 //
-// Work mapping (wave64):
-//  * a lane owns one 32-byte code chunk c (sub-blocks 2c and 2c+1) of a
-//    super-block, so 4 lanes cover a block and a wave covers 16 blocks;
-//  * the 16 lane-groups of a wave are split into R = 16/G rows with G groups
-//    per row, G = gcd(K/256, 16): every lane stays on one row, walks that row's
-//    blocks with stride G, and no iteration is ragged;
-//  * per block a lane loads the 16-byte header and its 32 code bytes.
-// Arithmetic per lane and sub-block j (32 weights), with sums over the lane's
-// 32 positions:
+// Work split (balanced for any K):
+//  * workgroup b owns rows [r0, r1) (row counts differ by at most one), i.e.
+//    the contiguous block range [r0*nb, r1*nb) of the tensor (nb = K/256);
+//  * its waves split that block range evenly; one wave iteration covers 16
+//    consecutive blocks, 4 lanes per block, and a lane owns one 32-byte code
+//    chunk c (sub-blocks 2c and 2c+1) of its block;
+//  * each block's contribution (summed over its 4 lanes) goes to an LDS slot,
+//    and the workgroup finally sums each row's slots in block order, so the
+//    result does not depend on timing (bitwise deterministic).
+// Arithmetic per lane and sub-block j (32 weights, sums over its positions):
 //   sum_l x_l * w_l = a_j * sum_l x_l q_l - b_j * sum_l x_l,
-//   a_j = d*sc_j, b_j = dmin*m_j  (the per-sub-block scale is hoisted).
-// For bf16 x the code sum uses v_dot2_f32_bf16 on exact bf16 values
-// (128 + q) built with one AND-OR per two codes, then removes 128 * sum_l x_l.
-// For fp32 x the codes are converted with byte-to-float conversions.
-// x and its 32-element sums are staged once per workgroup in LDS; the bf16
-// copy is stored with each group of four permuted to (x0, x2, x1, x3) so the
-// code pairs (l, l+2), which one AND-OR extracts, meet matching x pairs.
+//   a_j = d*sc_j, b_j = dmin*m_j  (per-sub-block scale hoisted out).
+// bf16 x: two codes become the exact bf16 values (128 + q_l, 128 + q_l+2) with
+// one v_and_or_b32 (0x43 in a bf16's high byte is the exponent of 128 with a
+// mantissa step of 1), multiplied with v_dot2_f32_bf16 against x pairs
+// (x_l, x_l+2), and 128 * sum_l x_l is removed with the sub-block x sum.
+// fp32 x: codes are converted with byte-to-float conversions.
+// x and its 32-element sums are staged in LDS once per workgroup; the bf16
+// copy stores each group of four as (x0, x2, x1, x3) to match the code pairs.
 #include "common.h"
 #include "launch.h"
 
@@ -29,26 +31,31 @@ namespace qdm {
 
 namespace {
 
-constexpr int GEMV_THREADS = 256;
-constexpr int GEMV_WAVES = GEMV_THREADS / WAVE;
+constexpr int GV_THREADS = 256;
+constexpr int GV_WAVES = GV_THREADS / WAVE;
+constexpr int GV_PF = 4;  // wave iterations of loads kept in flight
+constexpr int GV_TARGET_WGS = 1024;  // 4 per compute unit
 
-// Stage MT rows of x into LDS. bf16: [MT][K] halves, groups of four permuted;
-// fp32: [MT][K] natural. Then the 32-element sums xs[MT][K/32].
+// A value the compiler cannot see through, so it stays in a VGPR and the
+// AND-OR below is formed as one v_and_or_b32 (VOP3 takes no literals here).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <bool XBF16, int MT>
 __device__ __forceinline__ void stage_x(const void *__restrict__ x, int K, uint32_t *lds_x,
                                         float *lds_sum) {
   const int tid = threadIdx.x;
   if constexpr (XBF16) {
-    // chunks of 8 bf16 (16 bytes); 4 chunks make one 32-element sum
-    const int nchunk = MT * K / 8;
+    const int nchunk = MT * K / 8;  // 8 bf16 per chunk, 4 chunks per 32-sum
     const u32x4 *src = (const u32x4 *)x;
-    for (int base = 0; base < nchunk; base += GEMV_THREADS) {
+    for (int base = 0; base < nchunk; base += GV_THREADS) {
       const int c = base + tid;
       float s = 0.f;
       if (c < nchunk) {
         const u32x4 v = src[c];
-        // element pairs: v.x = (e0,e1), v.y = (e2,e3) -> (e0,e2), (e1,e3)
-        u32x4 p;
+        u32x4 p;  // (e0,e1),(e2,e3) -> (e0,e2),(e1,e3)
         p.x = (v.x & 0xFFFFu) | (v.y << 16);
         p.y = (v.x >> 16) | (v.y & 0xFFFF0000u);
         p.z = (v.z & 0xFFFFu) | (v.w << 16);
@@ -64,10 +71,9 @@ __device__ __forceinline__ void stage_x(const void *__restrict__ x, int K, uint3
       if (c < nchunk && (c & 3) == 0) lds_sum[c >> 2] = s;
     }
   } else {
-    // chunks of 4 fp32 (16 bytes); 8 chunks make one 32-element sum
-    const int nchunk = MT * K / 4;
+    const int nchunk = MT * K / 4;  // 4 fp32 per chunk, 8 chunks per 32-sum
     const f32x4 *src = (const f32x4 *)x;
-    for (int base = 0; base < nchunk; base += GEMV_THREADS) {
+    for (int base = 0; base < nchunk; base += GV_THREADS) {
       const int c = base + tid;
       float s = 0.f;
       if (c < nchunk) {
@@ -83,116 +89,151 @@ __device__ __forceinline__ void stage_x(const void *__restrict__ x, int K, uint3
   }
 }
 
-template <bool XBF16, int MT, int PF>
-__global__ __launch_bounds__(GEMV_THREADS) void q4k_gemv_kernel(
+// Per-lane constants of the 6-bit scale/min decode for sub-blocks 2c, 2c+1.
+struct ScaleDecode {
+  uint32_t lo_sc0, lo_m0, lo_sc1, lo_m1;  // offsets of the low field
+  uint32_t lo_w;                          // width of the low field (6 or 4)
+  uint32_t hi_sc0, hi_m0, hi_sc1, hi_m1;  // offsets of the high 2 bits
+  uint32_t hi_w;                          // 0 (j < 4) or 2 (j >= 4)
+  bool upper;                             // sub-blocks 4..7
+};
+
+__device__ __forceinline__ ScaleDecode make_scale_decode(int c) {
+  ScaleDecode s;
+  const int j0 = 2 * c;
+  s.upper = j0 >= 4;
+  if (!s.upper) {
+    s.lo_sc0 = 8 * j0; s.lo_m0 = 8 * j0; s.lo_sc1 = 8 * j0 + 8; s.lo_m1 = 8 * j0 + 8;
+    s.lo_w = 6; s.hi_w = 0;
+    s.hi_sc0 = s.hi_m0 = s.hi_sc1 = s.hi_m1 = 0;
+  } else {
+    const int jj = j0 - 4;
+    s.lo_sc0 = 8 * jj; s.lo_m0 = 8 * jj + 4; s.lo_sc1 = 8 * jj + 8; s.lo_m1 = 8 * jj + 12;
+    s.lo_w = 4; s.hi_w = 2;
+    s.hi_sc0 = 8 * jj + 6; s.hi_m0 = 8 * jj + 6; s.hi_sc1 = 8 * jj + 14; s.hi_m1 = 8 * jj + 14;
+  }
+  return s;
+}
+
+// S0 = packed bytes 0..3, S1 = 4..7, S2 = 8..11. j < 4: sc from S0, m from
+// S1 (6 bits). j >= 4: low 4 bits from S2 (sc low nibble, m high nibble),
+// high 2 bits from the top of S0 (sc) / S1 (m).
+__device__ __forceinline__ void decode_scales(const ScaleDecode &s, uint32_t S0, uint32_t S1,
+                                              uint32_t S2, uint32_t &sc0, uint32_t &m0,
+                                              uint32_t &sc1, uint32_t &m1) {
+  const uint32_t Asc = s.upper ? S2 : S0;
+  const uint32_t Am = s.upper ? S2 : S1;
+  sc0 = bfe(Asc, s.lo_sc0, s.lo_w) | (bfe(S0, s.hi_sc0, s.hi_w) << 4);
+  m0 = bfe(Am, s.lo_m0, s.lo_w) | (bfe(S1, s.hi_m0, s.hi_w) << 4);
+  sc1 = bfe(Asc, s.lo_sc1, s.lo_w) | (bfe(S0, s.hi_sc1, s.hi_w) << 4);
+  m1 = bfe(Am, s.lo_m1, s.lo_w) | (bfe(S1, s.hi_m1, s.hi_w) << 4);
+}
+
+template <bool XBF16, int MT>
+__global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
     const uint8_t *__restrict__ w, const void *__restrict__ x, float *__restrict__ y, int N,
-    int K, int G, int ldy) {
+    int K, int ldy, int rows_q, int rows_rem, int max_wg_blocks) {
   extern __shared__ uint32_t lds[];
   uint32_t *lds_x = lds;
   float *lds_sum = (float *)(lds + (XBF16 ? MT * K / 2 : MT * K));
+  float *lds_part = lds_sum + MT * (K / 32);  // [MT][max_wg_blocks]
+
+  const int nb = K / QK;
+  const int bid = blockIdx.x;
+  const int r0 = bid * rows_q + min(bid, rows_rem);
+  const int r1 = r0 + rows_q + (bid < rows_rem ? 1 : 0);
+  const int64_t B0 = (int64_t)r0 * nb;
+  const int nblk = (r1 - r0) * nb;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 2, c = lane & 3;  // lane group (16 per wave), code chunk
-  const int R = 16 / G;                   // rows per wave
-  const int row = (blockIdx.x * GEMV_WAVES + wave) * R + g / G;
-  const int gg = g % G;
-  const int nb = K / QK;
-  const int iters = nb / G;
-  const bool active = row < N;
-  const uint8_t *rowp = w + (int64_t)(active ? row : 0) * nb * Q4K_BYTES;
+  const int g = lane >> 2, c = lane & 3;
+  const int wb0 = (int)(((int64_t)wave * nblk) / GV_WAVES);
+  const int wb1 = (int)(((int64_t)(wave + 1) * nblk) / GV_WAVES);
+  const int iters = (wb1 - wb0 + 15) >> 4;
 
-  // Per-lane constants of the scale/min decode: sub-blocks j0 = 2c, j1 = 2c+1.
-  const int j0 = 2 * c;
+  // block index (relative to B0) and column block of this lane, iteration 0
+  int fb = wb0 + g;
+  const uint8_t *fptr = w + (B0 + fb) * Q4K_BYTES;
+  const int64_t fstep = 16 * Q4K_BYTES;
 
-  float acc[MT];
+  u32x4 H[GV_PF], A[GV_PF], Bq[GV_PF];
 #pragma unroll
-  for (int m = 0; m < MT; m++) acc[m] = 0.f;
-
-  // Issue the first batch of weight loads before staging x.
-  u32x4 H[PF], A[PF], B[PF];
-#pragma unroll
-  for (int p = 0; p < PF; p++) {
-    if (active && p < iters) {
-      const uint8_t *blk = rowp + (int64_t)(p * G + gg) * Q4K_BYTES;
-      H[p] = __builtin_nontemporal_load((const u32x4 *)blk);
-      A[p] = __builtin_nontemporal_load((const u32x4 *)(blk + 16 + 32 * c));
-      B[p] = __builtin_nontemporal_load((const u32x4 *)(blk + 32 + 32 * c));
+  for (int p = 0; p < GV_PF; p++) {
+    if (p < iters && fb + 16 * p < wb1) {
+      const uint8_t *blk = fptr + p * fstep;
+      H[p] = *(const u32x4 *)blk;
+      A[p] = *(const u32x4 *)(blk + 16 + 32 * c);
+      Bq[p] = *(const u32x4 *)(blk + 32 + 32 * c);
     }
   }
 
   stage_x<XBF16, MT>(x, K, lds_x, lds_sum);
   __syncthreads();
 
-  if (active) {
-    for (int it0 = 0; it0 < iters; it0 += PF) {
+  const ScaleDecode sd = make_scale_decode(c);
+  const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
+  const int s16 = 16 % nb;
+  int kb = fb % nb;  // column block of this lane's current block
+  int cb = fb;       // current block (relative to B0)
+
+  for (int it0 = 0; it0 < iters; it0 += GV_PF) {
 #pragma unroll
-      for (int p = 0; p < PF; p++) {
-        const int it = it0 + p;
-        if (it < iters) {
-          const int kb = it * G + gg;
+    for (int p = 0; p < GV_PF; p++) {
+      const int it = it0 + p;
+      if (it < iters) {
+        const bool valid = cb < wb1;
+        float contrib[MT];
+#pragma unroll
+        for (int m = 0; m < MT; m++) contrib[m] = 0.f;
+        if (valid) {
           const u32x4 hdr = H[p];
-          const uint32_t q[8] = {A[p].x, A[p].y, A[p].z, A[p].w,
-                                 B[p].x, B[p].y, B[p].z, B[p].w};
-          // prefetch the block PF iterations ahead into this slot
-          if (it + PF < iters) {
-            const uint8_t *blk = rowp + (int64_t)((it + PF) * G + gg) * Q4K_BYTES;
-            H[p] = __builtin_nontemporal_load((const u32x4 *)blk);
-            A[p] = __builtin_nontemporal_load((const u32x4 *)(blk + 16 + 32 * c));
-            B[p] = __builtin_nontemporal_load((const u32x4 *)(blk + 32 + 32 * c));
-          }
           const float d = half_bits_to_float(hdr.x);
           const float dmin = half_bits_to_float(hdr.x >> 16);
           uint32_t sc0, m0, sc1, m1;
-          q4k_scale_min(hdr.y, hdr.z, hdr.w, j0, sc0, m0);
-          q4k_scale_min(hdr.y, hdr.z, hdr.w, j0 + 1, sc1, m1);
+          decode_scales(sd, hdr.y, hdr.z, hdr.w, sc0, m0, sc1, m1);
           const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
           const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-
+          const uint32_t q[8] = {A[p].x, A[p].y, A[p].z, A[p].w,
+                                 Bq[p].x, Bq[p].y, Bq[p].z, Bq[p].w};
+          const int e0 = kb * QK + 64 * c;  // first x element of sub-block 2c
           if constexpr (XBF16) {
-            uint32_t np[32];
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-              np[4 * i + 0] = nib_pair_bf16(q[i]);        // sub-block j0, l = 4i, 4i+2
-              np[4 * i + 1] = nib_pair_bf16(q[i] >> 8);   // j0, 4i+1, 4i+3
-              np[4 * i + 2] = nib_pair_bf16(q[i] >> 4);   // j1, 4i, 4i+2
-              np[4 * i + 3] = nib_pair_bf16(q[i] >> 12);  // j1, 4i+1, 4i+3
-            }
             const float c0 = fmaf(128.f, a0, b0), c1 = fmaf(128.f, a1, b1);
 #pragma unroll
             for (int m = 0; m < MT; m++) {
-              const u32x4 *xv = (const u32x4 *)(lds_x + (m * K + kb * QK + 32 * j0) / 2);
-              const float2 xs = *(const float2 *)(lds_sum + m * (K / 32) + kb * 8 + j0);
+              const u32x4 *xv = (const u32x4 *)(lds_x + (m * K + e0) / 2);
+              const float2 xs = *(const float2 *)(lds_sum + m * (K / 32) + (e0 >> 5));
               float s0 = 0.f, s1 = 0.f;
 #pragma unroll
               for (int i = 0; i < 4; i++) {
-                const u32x4 x0 = xv[i];      // j0 pairs for l = 8i .. 8i+7
-                const u32x4 x1 = xv[4 + i];  // j1 pairs
-                s0 = dot2_bf16(np[8 * i + 0], x0.x, s0);
-                s0 = dot2_bf16(np[8 * i + 1], x0.y, s0);
-                s0 = dot2_bf16(np[8 * i + 4], x0.z, s0);
-                s0 = dot2_bf16(np[8 * i + 5], x0.w, s0);
-                s1 = dot2_bf16(np[8 * i + 2], x1.x, s1);
-                s1 = dot2_bf16(np[8 * i + 3], x1.y, s1);
-                s1 = dot2_bf16(np[8 * i + 6], x1.z, s1);
-                s1 = dot2_bf16(np[8 * i + 7], x1.w, s1);
+                const u32x4 x0 = xv[i];      // sub-block 2c, l = 8i .. 8i+7
+                const u32x4 x1 = xv[4 + i];  // sub-block 2c+1
+                const uint32_t qa = q[2 * i], qb = q[2 * i + 1];
+                const uint32_t qa4 = qa >> 4, qb4 = qb >> 4;
+                s0 = dot2_bf16((qa & MASK) | MAGIC, x0.x, s0);
+                s0 = dot2_bf16(((qa >> 8) & MASK) | MAGIC, x0.y, s0);
+                s0 = dot2_bf16((qb & MASK) | MAGIC, x0.z, s0);
+                s0 = dot2_bf16(((qb >> 8) & MASK) | MAGIC, x0.w, s0);
+                s1 = dot2_bf16((qa4 & MASK) | MAGIC, x1.x, s1);
+                s1 = dot2_bf16(((qa4 >> 8) & MASK) | MAGIC, x1.y, s1);
+                s1 = dot2_bf16((qb4 & MASK) | MAGIC, x1.z, s1);
+                s1 = dot2_bf16(((qb4 >> 8) & MASK) | MAGIC, x1.w, s1);
               }
-              float r = acc[m];
-              r = fmaf(a0, s0, r);
+              float r = a0 * s0;
               r = fmaf(-c0, xs.x, r);
               r = fmaf(a1, s1, r);
               r = fmaf(-c1, xs.y, r);
-              acc[m] = r;
+              contrib[m] = r;
             }
           } else {
 #pragma unroll
             for (int m = 0; m < MT; m++) {
-              const f32x4 *xv = (const f32x4 *)((const float *)lds_x + m * K + kb * QK + 32 * j0);
-              const float2 xs = *(const float2 *)(lds_sum + m * (K / 32) + kb * 8 + j0);
+              const f32x4 *xv = (const f32x4 *)((const float *)lds_x + m * K + e0);
+              const float2 xs = *(const float2 *)(lds_sum + m * (K / 32) + (e0 >> 5));
               float s0 = 0.f, s1 = 0.f;
 #pragma unroll
               for (int i = 0; i < 8; i++) {
-                const f32x4 x0 = xv[i];      // j0, l = 4i .. 4i+3
-                const f32x4 x1 = xv[8 + i];  // j1
+                const f32x4 x0 = xv[i];
+                const f32x4 x1 = xv[8 + i];
                 const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
                 s0 = fmaf(x0.x, (float)(lo & 255u), s0);
                 s0 = fmaf(x0.y, (float)((lo >> 8) & 255u), s0);
@@ -203,55 +244,335 @@ __global__ __launch_bounds__(GEMV_THREADS) void q4k_gemv_kernel(
                 s1 = fmaf(x1.z, (float)((hi >> 16) & 255u), s1);
                 s1 = fmaf(x1.w, (float)(hi >> 24), s1);
               }
-              float r = acc[m];
-              r = fmaf(a0, s0, r);
+              float r = a0 * s0;
               r = fmaf(-b0, xs.x, r);
               r = fmaf(a1, s1, r);
               r = fmaf(-b1, xs.y, r);
-              acc[m] = r;
+              contrib[m] = r;
             }
           }
+        }
+        // refill this slot with the block GV_PF iterations ahead
+        const int nfb = cb + 16 * GV_PF;
+        if (it + GV_PF < iters && nfb < wb1) {
+          const uint8_t *blk = fptr + (it + GV_PF) * fstep;
+          H[p] = *(const u32x4 *)blk;
+          A[p] = *(const u32x4 *)(blk + 16 + 32 * c);
+          Bq[p] = *(const u32x4 *)(blk + 32 + 32 * c);
+        }
+        // sum the block's 4 lanes; one lane stores the block's contribution
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+          float v = contrib[m];
+          v += __shfl_xor(v, 1, WAVE);
+          v += __shfl_xor(v, 2, WAVE);
+          if (valid && c == 0) lds_part[m * max_wg_blocks + cb] = v;
+        }
+        cb += 16;
+        kb += s16;
+        if (kb >= nb) kb -= nb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // y[row] = sum of the row's block contributions, in block order.
+  const int nrows = r1 - r0;
+  for (int t = threadIdx.x; t < MT * nrows; t += GV_THREADS) {
+    const int m = t / nrows, r = t - m * nrows;
+    const float *pp = lds_part + m * max_wg_blocks + r * nb;
+    float s = 0.f;
+    for (int k = 0; k < nb; k++) s += pp[k];
+    y[(int64_t)m * ldy + r0 + r] = s;
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// M = 1, bf16 x: dense-span kernel (the decode hot path).
+//
+// Every wave instruction reads 1 KiB of consecutive bytes: a wave loads a
+// span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB) with
+// non-temporal 16-byte loads, keeps up to three spans in flight in registers,
+// and moves each span through its own LDS buffer so that lane l receives
+// whole block l. One lane then decodes a whole super-block: the header once
+// per 256 weights, the codes with one v_and_or_b32 per two codes and
+// v_dot2_f32_bf16 against x.
+// x lives in LDS as 560-byte records per 256-element column block: 512 bytes
+// of bf16 (groups of four stored as x0, x2, x1, x3), the eight 32-element sums,
+// and 16 bytes of padding so that lanes reading consecutive column blocks hit
+// distinct LDS banks.
+// ---------------------------------------------------------------------------
+constexpr int DN_SPAN = 64;                           // blocks per span, one per lane
+constexpr int DN_SPAN_BYTES = DN_SPAN * Q4K_BYTES;    // 9216 = 9 x 1 KiB
+constexpr int DN_XREC = 560;                          // LDS bytes per x column block
+constexpr int DN_TARGET_WGS = 256;                    // one workgroup per CU
+constexpr int DN_MAX_WG_BLOCKS = 8192;
+constexpr size_t DN_LDS_LIMIT = 160 * 1024;
+#ifndef QDM_DN_WAVES
+#define QDM_DN_WAVES 8  // waves per workgroup of the dense kernel (2 per SIMD)
+#endif
+#ifndef QDM_DN_NBUF
+#define QDM_DN_NBUF 2   // spans held in registers per wave (one in flight)
+#endif
+#ifndef QDM_DN_PHASED
+#define QDM_DN_PHASED 1  // keep each sub-block pair's LDS reads next to its math
+#endif
+
+struct Span {
+  u32x4 r[9];
+};
+
+// Loads are unconditional so the compiler can count outstanding loads and
+// wait for exactly the span it needs (a load behind a branch forces it to wait
+// for every load in flight). Chunks past the end of a partial span re-read the
+// span's last chunk, which is already in flight.
+__device__ __forceinline__ void load_span(Span &sp, const uint8_t *__restrict__ base,
+                                          int nbytes, int lane) {
+#pragma unroll
+  for (int j = 0; j < 9; j++) {
+    const int off = min(1024 * j + 16 * lane, nbytes - 16);
+    sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
+  }
+}
+
+// x staging in two phases: every x load is issued first (before any weight
+// load, so waiting for x never waits for weights), then the chunks are
+// permuted into their records and summed.
+constexpr int DN_XCHUNKS = 16;  // 16-byte x chunks per thread (K <= 16 * 8 * threads)
+
+template <int THREADS>
+struct XStage {
+  u32x4 v[DN_XCHUNKS];
+
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int K) {
+    const int nchunk = K / 8;
+#pragma unroll
+    for (int i = 0; i < DN_XCHUNKS; i++) {
+      const int c = min(i * THREADS + (int)threadIdx.x, nchunk - 1);
+      v[i] = ((const u32x4 *)x)[c];
+    }
+  }
+
+  __device__ __forceinline__ void store(int K, uint8_t *xrec) const {
+    const int nchunk = K / 8;  // 32 chunks per 256-element record
+#pragma unroll
+    for (int i = 0; i < DN_XCHUNKS; i++) {
+      if (i * THREADS < nchunk) {  // uniform
+        const int c = i * THREADS + threadIdx.x;
+        const u32x4 e = v[i];
+        u32x4 p;
+        p.x = (e.x & 0xFFFFu) | (e.y << 16);
+        p.y = (e.x >> 16) | (e.y & 0xFFFF0000u);
+        p.z = (e.z & 0xFFFFu) | (e.w << 16);
+        p.w = (e.z >> 16) | (e.w & 0xFFFF0000u);
+        float s = bf16_bits_to_float(e.x) + bf16_bits_to_float(e.x >> 16) +
+                  bf16_bits_to_float(e.y) + bf16_bits_to_float(e.y >> 16) +
+                  bf16_bits_to_float(e.z) + bf16_bits_to_float(e.z >> 16) +
+                  bf16_bits_to_float(e.w) + bf16_bits_to_float(e.w >> 16);
+        s += __shfl_xor(s, 1, WAVE);
+        s += __shfl_xor(s, 2, WAVE);
+        if (c < nchunk) {
+          *(u32x4 *)(xrec + (c >> 5) * DN_XREC + (c & 31) * 16) = p;
+          if ((c & 3) == 0) *(float *)(xrec + (c >> 5) * DN_XREC + 512 + 4 * ((c & 31) >> 2)) = s;
         }
       }
     }
   }
+};
 
-  // Reduce over the 4G lanes of each row (aligned lane groups).
+// sum_k x[k] * w(k) over one super-block held in LDS (blk), x record xr.
+__device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const uint8_t *xr,
+                                                    uint32_t MASK, uint32_t MAGIC) {
+  const u32x4 hdr = *(const u32x4 *)blk;
+  const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
+  const f32x4 xsa = *(const f32x4 *)(xr + 512), xsb = *(const f32x4 *)(xr + 528);
+  const float xs[8] = {xsa.x, xsa.y, xsa.z, xsa.w, xsb.x, xsb.y, xsb.z, xsb.w};
+  float r = 0.f;
 #pragma unroll
-  for (int m = 0; m < MT; m++) {
-    float v = group_sum(acc[m], 4 * G);
-    if (active && (lane & (4 * G - 1)) == 0) y[(int64_t)m * ldy + row] = v;
+  for (int cc = 0; cc < 4; cc++) {
+    const int j0 = 2 * cc;
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, j0, sc0, m0);
+    q4k_scale_min(hdr.y, hdr.z, hdr.w, j0 + 1, sc1, m1);
+    const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
+    const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
+    const u32x4 qa = *(const u32x4 *)(blk + 16 + 32 * cc);
+    const u32x4 qb = *(const u32x4 *)(blk + 32 + 32 * cc);
+    const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    const u32x4 *xv0 = (const u32x4 *)(xr + 64 * j0);
+    const u32x4 *xv1 = (const u32x4 *)(xr + 64 * (j0 + 1));
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const u32x4 x0 = xv0[t], x1 = xv1[t];
+      const uint32_t qd0 = q[2 * t], qd1 = q[2 * t + 1];
+      const uint32_t qd04 = qd0 >> 4, qd14 = qd1 >> 4;
+      s0 = dot2_bf16((qd0 & MASK) | MAGIC, x0.x, s0);
+      s0 = dot2_bf16(((qd0 >> 8) & MASK) | MAGIC, x0.y, s0);
+      s0 = dot2_bf16((qd1 & MASK) | MAGIC, x0.z, s0);
+      s0 = dot2_bf16(((qd1 >> 8) & MASK) | MAGIC, x0.w, s0);
+      s1 = dot2_bf16((qd04 & MASK) | MAGIC, x1.x, s1);
+      s1 = dot2_bf16(((qd04 >> 8) & MASK) | MAGIC, x1.y, s1);
+      s1 = dot2_bf16((qd14 & MASK) | MAGIC, x1.z, s1);
+      s1 = dot2_bf16(((qd14 >> 8) & MASK) | MAGIC, x1.w, s1);
+    }
+    r = fmaf(a0, s0, r);
+    r = fmaf(-fmaf(128.f, a0, b0), xs[j0], r);
+    r = fmaf(a1, s1, r);
+    r = fmaf(-fmaf(128.f, a1, b1), xs[j0 + 1], r);
+#if QDM_DN_PHASED
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+  }
+  return r;
+}
+
+// WAVES waves per workgroup; NBUF spans held in registers per wave (the
+// current one and NBUF - 1 in flight).
+template <int WAVES, int NBUF>
+__global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y,
+    int K, int rows_q, int rows_rem) {
+  constexpr int DN_WAVES = WAVES, DN_THREADS = WAVES * WAVE;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nb = K / QK;
+  uint8_t *spanbuf = smem;                              // [waves][9216]
+  uint8_t *xrec = smem + DN_WAVES * DN_SPAN_BYTES;      // [nb][560]
+  float *part = (float *)(xrec + nb * DN_XREC);         // [blocks of this workgroup]
+
+  const int bid = blockIdx.x;
+  const int r0 = bid * rows_q + min(bid, rows_rem);
+  const int r1 = r0 + rows_q + (bid < rows_rem ? 1 : 0);
+  const int64_t B0 = (int64_t)r0 * nb;
+  const int nblk = (r1 - r0) * nb;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wb0 = (int)(((int64_t)wave * nblk) / DN_WAVES);
+  const int wb1 = (int)(((int64_t)(wave + 1) * nblk) / DN_WAVES);
+  const int nspan = (wb1 - wb0 + DN_SPAN - 1) / DN_SPAN;
+  const uint8_t *wbase = w + (B0 + wb0) * Q4K_BYTES;
+  auto span_bytes = [&](int sidx) {
+    return min(DN_SPAN, wb1 - wb0 - DN_SPAN * sidx) * Q4K_BYTES;
+  };
+
+  // Spans past the wave's last one alias that last span (already in flight).
+  auto span_ptr = [&](int sidx) {
+    return wbase + (int64_t)min(sidx, nspan - 1) * DN_SPAN_BYTES;
+  };
+  auto span_len = [&](int sidx) { return span_bytes(min(sidx, nspan - 1)); };
+
+  XStage<DN_THREADS> xst;
+  xst.load(x, K);
+
+  Span R[NBUF];
+  if (nspan > 0) {
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; p++) load_span(R[p], span_ptr(p), span_len(p), lane);
+  }
+
+  xst.store(K, xrec);
+  __syncthreads();
+
+  const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
+  uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
+  const int s64 = DN_SPAN % nb;
+  int kb = (wb0 + lane) % nb;
+
+  if (nspan > 0) {
+    for (int sb = 0; sb < nspan; sb += NBUF) {
+#pragma unroll
+      for (int p = 0; p < NBUF; p++) {
+        const int sidx = sb + p;
+        load_span(R[(p + NBUF - 1) % NBUF], span_ptr(sidx + NBUF - 1), span_len(sidx + NBUF - 1),
+                  lane);
+        if (sidx < nspan) {
+          const int nbytes = span_bytes(sidx);
+#pragma unroll
+          for (int j = 0; j < 9; j++) {
+            const int off = 1024 * j + 16 * lane;
+            if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
+          }
+          const int rb = wb0 + DN_SPAN * sidx + lane;
+          if (rb < wb1)
+            part[rb] = q4k_block_dot_bf16(mybuf + Q4K_BYTES * lane, xrec + kb * DN_XREC, MASK,
+                                          MAGIC);
+          kb += s64;
+          if (kb >= nb) kb -= nb;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nrows = r1 - r0;
+  for (int t = threadIdx.x; t < nrows; t += DN_THREADS) {
+    const float *pp = part + t * nb;
+    float sacc = 0.f;
+    for (int k = 0; k < nb; k++) sacc += pp[k];
+    y[r0 + t] = sacc;
   }
 }
 
-int gcd16(int nb) {
-  int g = 16;
-  while (g > 1 && nb % g) g >>= 1;
-  return g;
+// Launch geometry of the dense kernel, or false if its LDS does not fit.
+template <int DN_WAVES>
+bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, size_t &lds) {
+  const int64_t nb = K / QK;
+  nwg = DN_TARGET_WGS;
+  const int64_t need = (N * nb + DN_MAX_WG_BLOCKS - 1) / DN_MAX_WG_BLOCKS;
+  if (need > nwg) nwg = need;
+  if (nwg > N) nwg = N;
+  rows_q = (int)(N / nwg);
+  rows_rem = (int)(N % nwg);
+  const int64_t max_blocks = (rows_q + (rows_rem ? 1 : 0)) * nb;
+  lds = (size_t)DN_WAVES * DN_SPAN_BYTES + (size_t)nb * DN_XREC + (size_t)max_blocks * 4;
+  return lds <= DN_LDS_LIMIT && K / 8 <= (int64_t)DN_XCHUNKS * DN_WAVES * WAVE;
 }
 
 template <bool XBF16, int MT>
 void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, int64_t ldy,
                   hipStream_t s) {
-  const int nb = (int)(K / QK);
-  const int G = gcd16(nb);
-  const int R = 16 / G;
-  const int64_t rows_per_wg = (int64_t)GEMV_WAVES * R;
-  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
-  const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 32) * 4;
-  constexpr int PF = 2;
-  auto kern = q4k_gemv_kernel<XBF16, MT, PF>;
-  if (lds > 65536) hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMV_THREADS), lds, s, (const uint8_t *)w, x, y,
-                     (int)N, (int)K, G, (int)ldy);
+  const int64_t nb = K / QK;
+  // Enough workgroups to fill the device; more when a workgroup's block slots
+  // (MT per block) would exceed 8192 floats of LDS.
+  int64_t nwg = GV_TARGET_WGS;
+  const int64_t cap = 8192 / MT;
+  const int64_t need = (N * nb + cap - 1) / cap;
+  if (need > nwg) nwg = need;
+  if (nwg > N) nwg = N;
+  const int rows_q = (int)(N / nwg), rows_rem = (int)(N % nwg);
+  const int max_wg_blocks = (int)((rows_q + (rows_rem ? 1 : 0)) * nb);
+  const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 32) * 4 +
+                     (size_t)MT * max_wg_blocks * 4;
+  auto kern = q4k_gemv_kernel<XBF16, MT>;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(GV_THREADS), lds, s, (const uint8_t *)w, x,
+                     y, (int)N, (int)K, (int)ldy, rows_q, rows_rem, max_wg_blocks);
 }
 
 }  // namespace
 
-// Rows of x are processed in chunks of MT (1, 2, 4 or 8) per launch, as many
-// as fit a 64 KiB LDS budget (one chunk of 1 row may use up to 136 KiB).
+// M = 1 with bf16 x runs the dense-span kernel whenever its LDS plan fits
+// (K up to about 26K); other cases (fp32 x, M > 1, longer K) process rows of x
+// in chunks of MT (1, 2, 4 or 8) per launch of the general kernel, as many as
+// fit a 64 KiB LDS budget for x.
 void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
+  if (M == 1 && x_bf16) {
+    int64_t nwg;
+    int rows_q, rows_rem;
+    size_t lds;
+    if (dense_plan<QDM_DN_WAVES>(N, K, nwg, rows_q, rows_rem, lds)) {
+      auto kern = q4k_gemv_m1_kernel<QDM_DN_WAVES, QDM_DN_NBUF>;
+      (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+      hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(QDM_DN_WAVES * WAVE), lds, s,
+                         (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem);
+      return;
+    }
+  }
   const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 32) * 4;
   const size_t elt = x_bf16 ? 2 : 4;
   int64_t m0 = 0;
