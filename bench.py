@@ -4,9 +4,11 @@ Headline (`value`): the Q4_K decode GEMV set at M = 1 with bf16 activations —
 fused QKV (K=5120, N=7168), fused gate+up (K=5120, N=34816) and down
 (K=17408, N=5120) — as effective GB/s: the algorithmic bytes of one step
 (packed weights + x + y of the three GEMVs) over the time of one step. A step
-is the three calls back to back; the timed region is `--steps` steps after
-`--warmup` untimed ones. Weight sets rotate over copies whose total exceeds
-twice the 256 MB MALL, so the rate is an HBM rate.
+is the three calls launched back to back through the Python binding (the rate
+of the same step replayed from a captured HIP graph is reported beside it);
+the timed region is `--steps` steps after `--warmup` untimed ones. Weight
+sets rotate over copies whose total exceeds twice the 256 MB MALL, so the
+rate is an HBM rate.
 
 The same JSON line carries the prefill GEMM (M = 512 and 4096, TFLOP/s
 against the bf16 MFMA peak), the Q6_K GEMVs and the MoE FFN as extra
@@ -19,6 +21,7 @@ a reported baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -157,35 +160,65 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+
+    # Graph-replayed steps: one graph holds one step per weight copy (the
+    # decode loop of an engine replays captured launches).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in range(ncopy):
+            step(c)
+    graph.replay()
+    torch.cuda.synchronize()
+    for name, K, N in DECODE:  # replayed results equal the eager ones
+        if rel(ys[name].cpu().numpy(), oracle.q4k_matmul(host_w[name], host_x[name], N, K)) != errs[name]:
+            raise RuntimeError("graph replay differs from eager result (%s)" % name)
+    reps = max(1, steps // ncopy)
+    tg = Timer(torch)
+    g0 = tg.event()
+    for _ in range(reps):
+        graph.replay()
+    g1 = tg.event()
+    torch.cuda.synchronize()
+    graph_ms_per_step = g0.elapsed_time(g1) / (reps * ncopy)
+
+    # eager steps through the Python binding
     tm = Timer(torch)
-    ev = []
     t0 = tm.event()
     for i in range(steps):
-        wset = dev_w[i % ncopy]
-        row = []
-        for name, K, N in DECODE:
-            row.append(tm.event())
-            qdm.q4k_gemv(wset[name], dev_x[name], N, K, y=ys[name])
-        row.append(tm.event())
-        ev.append(row)
+        step(i)
     t1 = tm.event()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    per = {name: [] for name, _, _ in DECODE}
-    for row in ev:
-        for j, (name, _, _) in enumerate(DECODE):
-            per[name].append(row[j].elapsed_time(row[j + 1]))
-    step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
+
+    # Per-kernel launch duration: a batch of back-to-back launches of one
+    # kernel through the C ABI with pre-marshalled arguments (the queue stays
+    # ahead of the GPU), bracketed by two events on the launch stream.
+    lib = qdm.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     kernels = {}
+    nb = max(20, steps)
     for name, K, N in DECODE:
-        ms = float(np.mean(per[name]))
+        args = [(ctypes.c_void_p(dev_w[c][name].data_ptr()), ctypes.c_void_p(dev_x[name].data_ptr()),
+                 qdm.QDM_BF16, ctypes.c_void_p(ys[name].data_ptr()), 1, N, K, stream)
+                for c in range(ncopy)]
+        for a in args:
+            lib.q4k_gemv(*a)
+        k0 = tm.event()
+        for i in range(nb):
+            lib.q4k_gemv(*args[i % ncopy])
+        k1 = tm.event()
+        torch.cuda.synchronize()
+        ms = k0.elapsed_time(k1) / nb
         b = gemv_bytes(N, K)
-        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "median_ms": float(np.median(per[name])),
+        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb,
                          "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
                          "rel_err": errs[name]}
-    del dev_w
+    step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
+    del graph, dev_w
     return {"ms_per_step": total_ms / steps, "step_bytes": step_bytes, "copies": ncopy,
-            "GBps": step_bytes / (total_ms / steps) / 1e6, "kernels": kernels,
+            "GBps": step_bytes / (total_ms / steps) / 1e6,
+            "graph_ms_per_step": graph_ms_per_step, "graph_steps": reps * ncopy,
+            "graph_GBps": step_bytes / graph_ms_per_step / 1e6, "kernels": kernels,
             "max_rel_err": max(errs.values())}
 
 
@@ -330,7 +363,7 @@ def main():
         extra["probe_copy"] = bench_probe(torch, qdm)
         log("probe copy:", extra["probe_copy"])
     dec = bench_decode(torch, qdm, synth, oracle, args.steps, args.warmup)
-    log("decode: %.1f GB/s per step" % dec["GBps"])
+    log("decode: %.1f GB/s per step (eager), %.1f GB/s graph replay" % (dec["GBps"], dec["graph_GBps"]))
     if "gemm" in sections:
         for M, reps in ((512, 20), (4096, 5)):
             extra["q4k_gemm_m%d" % M] = bench_gemm(torch, qdm, synth, oracle, M, reps)
@@ -364,8 +397,8 @@ def main():
            "dtype": "q4_k weights x bf16 activations -> f32 accumulate", "data": "synthetic",
            "config": {"workload": "Q4_K decode GEMV set, M=1, bf16 x: QKV K=5120 N=7168; "
                                   "gate+up K=5120 N=34816; down K=17408 N=5120 "
-                                  "(one step = the three calls; %d rotating weight copies)"
-                                  % dec["copies"],
+                                  "(one step = the three calls launched back to back; %d "
+                                  "rotating weight copies)" % dec["copies"],
                       "frac_hbm_peak": dec["GBps"] / HBM_PEAK_GBS, "device": dev_name},
            "roofline": roofline, "cpu_baseline": cpu, "decode_kernels": dec["kernels"],
            "parity_max_rel_err": dec["max_rel_err"], "extra": extra}

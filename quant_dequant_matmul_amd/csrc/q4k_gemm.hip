@@ -3,20 +3,27 @@
 // Prefill over GGUF weights runs on matrix cores (hipEngine README,
 // "Quickstart": WMMA prefill, GEMV decode). On gfx950 the equivalent is the
 // bf16 MFMA: Q4_K tiles are decoded in fp32 (w = d*sc*q - dmin*m, exact
-// products, one rounding), rounded to bf16 (nearest even) into LDS next to the
-// bf16 activation tile, and contracted with v_mfma_f32_16x16x32_bf16 into fp32
-// accumulators.
+// products, one rounding), rounded to bf16 (nearest even, v_cvt_pk_bf16_f32)
+// into LDS next to the bf16 activation tile, and contracted with
+// v_mfma_f32_32x32x16_bf16 into fp32 accumulators.
 //
-// Tiling: a 256-thread workgroup owns a BM x BN = 128 x 128 tile of y; its 4
-// waves own 64 x 64 quadrants (4 x 4 MFMA tiles of 16 x 16). K advances in
-// stages of 64: stage (b, c) covers code chunk c (sub-blocks 2c, 2c+1) of
-// super-block b, so every stage decodes whole 32-byte code chunks. Stages are
-// double-buffered in LDS; global loads for stage s+1 are issued before the
-// MFMAs of stage s.
+// Tiling: a 256-thread workgroup (one per compute unit) owns a 256 x 256 tile
+// of y; each of its 4 waves owns a 128 x 128 quadrant = 4 x 4 MFMA tiles of
+// 32 x 32, i.e. 256 fp32 accumulators per lane. Every weight a workgroup
+// decodes feeds 256 rows of x, which keeps the decode (about 3 VALU
+// operations per weight) well below the MFMA time. K advances in stages of 64:
+// stage (b, c) is code chunk c (sub-blocks 2c, 2c+1) of super-block b, so each
+// thread decodes one row's 32 code bytes per stage. Stages are double-buffered
+// in LDS (rows padded to 144 bytes so that 16 consecutive rows hit distinct
+// banks); the global loads of stage s+1 are in flight during the MFMAs of
+// stage s. All global loads are unconditional (rows past M or N are clamped
+// and their values zeroed), so the compiler waits for exactly the loads it
+// needs.
 //
-// MFMA operand layout (16x16x32 bf16, wave64): lane l holds, for A, row l%16
-// and k = 8*(l/16) .. +7; for B, column l%16 and the same k; the 16x16 fp32
-// result gives lane l column l%16 and rows 4*(l/16) .. +3.
+// MFMA operand layout (32x32x16 bf16, wave64): lane l holds, for A, row l%32
+// and k = 8*(l/32) .. +7; for B, column l%32 and the same k. The 32x32 fp32
+// result gives lane l column l%32 and, in accumulator r, row
+// 8*(r/4) + 4*(l/32) + r%4.
 #include "common.h"
 #include "launch.h"
 
@@ -24,88 +31,172 @@ namespace qdm {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BKS = 64;
-constexpr int LDS_STRIDE = BKS + 8;  // bf16 per LDS row (16-byte pad against bank conflicts)
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LROW = BK + 8;  // bf16 per LDS row (144 bytes)
 constexpr int GEMM_THREADS = 256;
+constexpr int TILE_ELEMS = BM * LROW;  // per operand and stage (BM == BN)
 
-struct StageRegs {
-  u32x4 xa[4];      // 4 x 16 bytes of the x tile
-  u32x4 hdr, code;  // this thread's W row: block header and 16 code bytes
+
+struct XRegs {
+  u32x4 v[8];  // x tile: 8 x 16 bytes per thread
+};
+struct WRegs {
+  u32x4 hdr, qa, qb;  // this thread's W row: block header and 32 code bytes
+};
+static_assert(BM == BN && BM == GEMM_THREADS, "one W row per thread");
+
+// Per-lane 32-bit byte offsets of this thread's loads, relative to the
+// tile's uniform base addresses (the loads then use a scalar base and a vector
+// offset). Rows past M or N are clamped to the last row.
+struct LoadOffsets {
+  uint32_t x[8];  // x chunk i: row (tid/8 + 32i) of the tile, 16-byte column tid%8
+  uint32_t w;     // this thread's W row
 };
 
-__device__ __forceinline__ void load_stage(StageRegs &r, const uint8_t *__restrict__ w,
-                                           const uint16_t *__restrict__ x, int M, int N, int K,
-                                           int m0, int n0, int stage) {
-  const int tid = threadIdx.x;
-  const int b = stage >> 2, c = stage & 3;
-  const int kbase = b * QK + c * BKS;
+__device__ __forceinline__ LoadOffsets make_offsets(int M, int N, int K, int m0, int n0) {
+  LoadOffsets o;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int q = tid + GEMM_THREADS * i;
-    const int row = q >> 3, col8 = (q & 7) * 8;
-    const int gm = m0 + row;
-    if (gm < M)
-      r.xa[i] = *(const u32x4 *)(x + (int64_t)gm * K + kbase + col8);
-    else
-      r.xa[i] = u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 8; i++) {
+    const int q = threadIdx.x + GEMM_THREADS * i;
+    const int row = min(m0 + (q >> 3), M - 1) - m0;
+    o.x[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(q & 7) * 16u;
   }
-  const int wr = tid >> 1, hf = tid & 1;
-  const int gn = n0 + wr;
-  if (gn < N) {
-    const uint8_t *blk = w + ((int64_t)gn * (K / QK) + b) * Q4K_BYTES;
-    r.hdr = *(const u32x4 *)blk;
-    r.code = __builtin_nontemporal_load((const u32x4 *)(blk + 16 + 32 * c + 16 * hf));
+  o.w = (uint32_t)(min(n0 + (int)threadIdx.x, N - 1) - n0) * (uint32_t)(K / QK) * Q4K_BYTES;
+  return o;
+}
+
+__device__ __forceinline__ void load_x(XRegs &r, const LoadOffsets &o,
+                                       const uint8_t *__restrict__ xtile, int stage) {
+  const uint8_t *base = xtile + ((stage >> 2) * QK + (stage & 3) * BK) * 2;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = *(const u32x4 *)(base + o.x[i]);
+}
+
+__device__ __forceinline__ void load_w(WRegs &r, const LoadOffsets &o,
+                                       const uint8_t *__restrict__ wtile, int stage) {
+  const int b = stage >> 2, c = stage & 3;
+  const uint8_t *blk = wtile + b * Q4K_BYTES + o.w;
+  r.hdr = *(const u32x4 *)blk;
+  r.qa = *(const u32x4 *)(blk + 16 + 32 * c);
+  r.qb = *(const u32x4 *)(blk + 32 + 32 * c);
+}
+
+__device__ __forceinline__ void store_x(const XRegs &r, uint16_t *sx, int M, int m0) {
+  if (m0 + BM <= M) {  // uniform: the whole tile is inside M
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int q = threadIdx.x + GEMM_THREADS * i;
+      *(u32x4 *)(sx + (q >> 3) * LROW + (q & 7) * 8) = r.v[i];
+    }
   } else {
-    r.hdr = u32x4{0, 0, 0, 0};
-    r.code = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int q = threadIdx.x + GEMM_THREADS * i;
+      const int row = q >> 3;
+      const u32x4 v = (m0 + row < M) ? r.v[i] : u32x4{0, 0, 0, 0};
+      *(u32x4 *)(sx + row * LROW + (q & 7) * 8) = v;
+    }
   }
 }
 
-__device__ __forceinline__ void store_stage(const StageRegs &r, uint16_t *sx, uint16_t *sw,
-                                            int stage) {
-  const int tid = threadIdx.x;
-  const int c = stage & 3;
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Scales of the stage's two sub-blocks for this thread's W row.
+struct RowScales {
+  float a0, b0, a1, b1;
+};
+
+__device__ __forceinline__ RowScales row_scales(const WRegs &r, bool live, int c) {
+  const float d = live ? half_bits_to_float(r.hdr.x) : 0.f;
+  const float dmin = live ? half_bits_to_float(r.hdr.x >> 16) : 0.f;
+  uint32_t sc0, m0s, sc1, m1s;
+  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c, sc0, m0s);
+  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c + 1, sc1, m1s);
+  return RowScales{d * (float)sc0, dmin * (float)m0s, d * (float)sc1, dmin * (float)m1s};
+}
+
+// Part kk (0..3) of a W row's decode: code dwords 2kk, 2kk+1, i.e. positions
+// 8kk .. 8kk+7 of both sub-blocks, stored as bf16 into the row's LDS slots.
+__device__ __forceinline__ void store_w_part(const WRegs &r, const RowScales &sc, int kk,
+                                             uint16_t *sw) {
+  const uint32_t qd[2] = {kk < 2 ? r.qa[2 * kk] : r.qb[2 * kk - 4],
+                          kk < 2 ? r.qa[2 * kk + 1] : r.qb[2 * kk - 3]};
+  uint32_t lo[4], hi[4];
+  // an opaque mask keeps the nibbles byte-aligned, so each code converts with
+  // one v_cvt_f32_ubyteN instead of a field extract plus a conversion
+  uint32_t nib = 0x0F0F0F0Fu;
+  asm volatile("" : "+v"(nib));
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const uint32_t l4 = qd[u] & nib, h4 = (qd[u] >> 4) & nib;
+    lo[2 * u] = pack_bf16(sc.a0 * (float)(l4 & 255u) - sc.b0,
+                          sc.a0 * (float)((l4 >> 8) & 255u) - sc.b0);
+    lo[2 * u + 1] = pack_bf16(sc.a0 * (float)((l4 >> 16) & 255u) - sc.b0,
+                              sc.a0 * (float)(l4 >> 24) - sc.b0);
+    hi[2 * u] = pack_bf16(sc.a1 * (float)(h4 & 255u) - sc.b1,
+                          sc.a1 * (float)((h4 >> 8) & 255u) - sc.b1);
+    hi[2 * u + 1] = pack_bf16(sc.a1 * (float)((h4 >> 16) & 255u) - sc.b1,
+                              sc.a1 * (float)(h4 >> 24) - sc.b1);
+  }
+  uint16_t *dst = sw + threadIdx.x * LROW;
+  *(u32x4 *)(dst + 8 * kk) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  *(u32x4 *)(dst + 32 + 8 * kk) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One stage of MFMAs from LDS buffer (sx, swb), with the W decode of the next
+// stage (regs nw, stage ns, into nws; skipped when store_next is false) woven
+// between them: per 16 MFMAs, a quarter of the decode.
+__device__ __forceinline__ void mfma_stage(f32x16 (&acc)[4][4], const uint16_t *sx,
+                                           const uint16_t *swb, const WRegs &nw,
+                                           bool store_next, int ns, uint16_t *nws, int N,
+                                           int n0, int wm, int wn, int lane) {
+  const int arow = lane & 31, akoff = 8 * (lane >> 5);
+  const RowScales sc = row_scales(nw, n0 + (int)threadIdx.x < N, ns & 3);
+  const uint16_t *pa = sx + (wm * 128 + arow) * LROW + akoff;
+  const uint16_t *pb = swb + (wn * 128 + arow) * LROW + akoff;
+  // operand fragments of k-step kk are read one k-step ahead of their MFMAs
+  bf16x8 af[2][4], bfr[2][4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int q = tid + GEMM_THREADS * i;
-    const int row = q >> 3, col8 = (q & 7) * 8;
-    *(u32x4 *)(sx + row * LDS_STRIDE + col8) = r.xa[i];
+    af[0][i] = *(const bf16x8 *)(pa + i * 32 * LROW);
+    bfr[0][i] = *(const bf16x8 *)(pb + i * 32 * LROW);
   }
-  const int wr = tid >> 1, hf = tid & 1;
-  const float d = half_bits_to_float(r.hdr.x), dmin = half_bits_to_float(r.hdr.x >> 16);
-  uint32_t sc0, m0, sc1, m1;
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c, sc0, m0);
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c + 1, sc1, m1);
-  const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
-  const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-  const uint32_t q[4] = {r.code.x, r.code.y, r.code.z, r.code.w};
-  uint32_t lo[8], hi[8];  // bf16 pairs
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int kk = 0; kk < 4; kk++) {
+    const int cur = kk & 1;
+    if (kk < 3) {
 #pragma unroll
-    for (int e = 0; e < 2; e++) {
-      const uint32_t v = q[k] >> (16 * e);
-      const float l0 = a0 * (float)(v & 15u) - b0;
-      const float l1 = a0 * (float)((v >> 8) & 15u) - b0;
-      const float h0 = a1 * (float)((v >> 4) & 15u) - b1;
-      const float h1 = a1 * (float)((v >> 12) & 15u) - b1;
-      lo[2 * k + e] = f32_to_bf16_rne(l0) | (f32_to_bf16_rne(l1) << 16);
-      hi[2 * k + e] = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+      for (int i = 0; i < 4; i++) {
+        af[cur ^ 1][i] = *(const bf16x8 *)(pa + i * 32 * LROW + (kk + 1) * 16);
+        bfr[cur ^ 1][i] = *(const bf16x8 *)(pb + i * 32 * LROW + (kk + 1) * 16);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
+                                                            0, 0, 0);
+    if (store_next) store_w_part(nw, sc, kk, nws);
+#pragma unroll
+    for (int t = 0; t < 16; t++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  uint16_t *dst = sw + wr * LDS_STRIDE + 16 * hf;
-  *(u32x4 *)(dst) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-  *(u32x4 *)(dst + 8) = u32x4{lo[4], lo[5], lo[6], lo[7]};
-  *(u32x4 *)(dst + 32) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  *(u32x4 *)(dst + 40) = u32x4{hi[4], hi[5], hi[6], hi[7]};
 }
 
 __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(const uint8_t *__restrict__ w,
                                                                 const uint16_t *__restrict__ x,
                                                                 float *__restrict__ y, int M,
                                                                 int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * LDS_STRIDE];
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // stage buffer p: x tile at smem + 2p*TILE_ELEMS, W tile right after it
 
   const int ntn = (N + BN - 1) / BN;
   const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * BN;
@@ -113,54 +204,69 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(const uint8_t *_
   const int wm = wave >> 1, wn = wave & 1;
   const int stages = (K / QK) * 4;
 
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  StageRegs r;
-  load_stage(r, w, x, M, N, K, m0, n0, 0);
-  store_stage(r, sX[0], sW[0], 0);
+  // Stage s lives in LDS buffer s & 1. While stage s is multiplied: x and W
+  // of stage s+2 are in flight, W of stage s+1 is decoded into the other
+  // buffer and x of stage s+1 (loaded two stages earlier) is stored there.
+  const LoadOffsets lo = make_offsets(M, N, K, m0, n0);
+  const uint8_t *xtile = (const uint8_t *)(x + (int64_t)m0 * K);
+  const uint8_t *wtile = w + (int64_t)n0 * (K / QK) * Q4K_BYTES;
+  XRegs xa, xb;
+  WRegs wa, wb;
+  load_x(xa, lo, xtile, 0);
+  load_w(wa, lo, wtile, 0);
+  load_x(xb, lo, xtile, min(1, stages - 1));
+  load_w(wb, lo, wtile, min(1, stages - 1));
+  store_x(xa, smem, M, m0);
+  {
+    const RowScales sc = row_scales(wa, n0 + (int)threadIdx.x < N, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) store_w_part(wa, sc, kk, smem + TILE_ELEMS);
+  }
   __syncthreads();
 
-  const int arow = lane & 15, akoff = 8 * (lane >> 4);
-  for (int s = 0; s < stages; s++) {
-    const int buf = s & 1;
-    if (s + 1 < stages) load_stage(r, w, x, M, N, K, m0, n0, s + 1);
-    const uint16_t *sx = sX[buf], *sw = sW[buf];
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        af[i] = *(const bf16x8 *)(sx + (wm * 64 + i * 16 + arow) * LDS_STRIDE + kk * 32 + akoff);
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        bfr[j] = *(const bf16x8 *)(sw + (wn * 64 + j * 16 + arow) * LDS_STRIDE + kk * 32 + akoff);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < stages) store_stage(r, sX[buf ^ 1], sW[buf ^ 1], s + 1);
+  // stages = 4 * K/256 is even: the loop body covers an even and an odd stage.
+  // Past the last stage, loads are clamped to it and the decodes/stores go to
+  // the buffer that is no longer read.
+  for (int s = 0; s < stages; s += 2) {
+    // even stage s (buffer 0): W of s+1 (wb) decoded and x of s+1 (xb) stored into buffer 1
+    load_x(xa, lo, xtile, min(s + 2, stages - 1));
+    load_w(wa, lo, wtile, min(s + 2, stages - 1));
+    mfma_stage(acc, smem, smem + TILE_ELEMS, wb, true, s + 1, smem + 3 * TILE_ELEMS, N, n0, wm,
+               wn, lane);
+    store_x(xb, smem + 2 * TILE_ELEMS, M, m0);
+    __syncthreads();
+    // odd stage s+1 (buffer 1): W of s+2 (wa) and x of s+2 (xa) into buffer 0
+    load_x(xb, lo, xtile, min(s + 3, stages - 1));
+    load_w(wb, lo, wtile, min(s + 3, stages - 1));
+    mfma_stage(acc, smem + 2 * TILE_ELEMS, smem + 3 * TILE_ELEMS, wa, true,
+               min(s + 2, stages - 1), smem + TILE_ELEMS, N, n0, wm, wn, lane);
+    store_x(xa, smem, M, m0);
     __syncthreads();
   }
 
-  const int col = lane & 15, rq = 4 * (lane >> 4);
+  const int col = lane & 31, rq = 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const int gn = n0 + wn * 64 + j * 16 + col;
+      const int gn = n0 + wn * 128 + j * 32 + col;
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int gm = m0 + wm * 64 + i * 16 + rq + v;
+      for (int v = 0; v < 16; v++) {
+        const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + rq + (v & 3);
         if (gm < M && gn < N) y[(int64_t)gm * N + gn] = acc[i][j][v];
       }
     }
 }
+
+constexpr size_t GEMM_LDS = 4 * TILE_ELEMS * sizeof(uint16_t);  // 147456 bytes
 
 }  // namespace
 
@@ -169,7 +275,9 @@ size_t q4k_gemm_workspace(int64_t, int64_t, int64_t) { return 0; }
 void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
                      void *, hipStream_t s) {
   const dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM)));
-  hipLaunchKernelGGL(q4k_gemm_kernel, grid, dim3(GEMM_THREADS), 0, s, (const uint8_t *)w,
+  (void)hipFuncSetAttribute((const void *)q4k_gemm_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
+  hipLaunchKernelGGL(q4k_gemm_kernel, grid, dim3(GEMM_THREADS), GEMM_LDS, s, (const uint8_t *)w,
                      (const uint16_t *)x, y, (int)M, (int)N, (int)K);
 }
 

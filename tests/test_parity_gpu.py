@@ -316,3 +316,43 @@ def test_determinism_all_entry_points():
     a = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
     b = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture and replay of a decode step
+# --------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager():
+    """Capture q4k_gemv + q6k_gemv + q4k_gemm on torch's capture stream, replay
+    several times with eager work and synchronizations between replays; every
+    replay must equal the eager result bit for bit."""
+    rng = np.random.default_rng(123)
+    N, K = 2048, 5120
+    w4 = dev_bytes(synth.q4k_blocks(rng, N, K))
+    w6 = dev_bytes(synth.q6k_blocks(rng, N, K))
+    x = dev_x(synth.normal_bf16(rng, (1, K)))
+    xg = dev_x(synth.normal_bf16(rng, (64, K)))
+    y4 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y6 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    yg = torch.empty((64, N), dtype=torch.float32, device="cuda")
+    say("graph: eager reference")
+    qdm.q4k_gemv(w4, x, N, K, y=y4)
+    qdm.q6k_gemv(w6, x, N, K, y=y6)
+    qdm.q4k_gemm(w4, xg, N, K, y=yg)
+    ref = [host(y4).copy(), host(y6).copy(), host(yg).copy()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qdm.q4k_gemv(w4, x, N, K, y=y4)
+        qdm.q6k_gemv(w6, x, N, K, y=y6)
+        qdm.q4k_gemm(w4, xg, N, K, y=yg)
+    for rep in range(4):
+        say("graph: replay", rep)
+        y4.zero_(), y6.zero_(), yg.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = [host(y4), host(y6), host(yg)]
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), rep
+        # eager work between replays
+        qdm.q4k_gemv(w4, x * 2, N, K, y=y4)
+        torch.cuda.synchronize()
