@@ -128,7 +128,7 @@ def bench_probe(torch, qdm):
     return {"copy_bytes": nbytes, "ms": ms, "read_plus_write_GBps": 2 * nbytes / ms / 1e6}
 
 
-def bench_decode(torch, qdm, synth, oracle, steps, warmup):
+def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
     """The headline: QKV, gate+up, down per step, rotating weight copies."""
     host_w, host_x, dev_x = {}, {}, {}
     for name, K, N in DECODE:
@@ -163,23 +163,26 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup):
 
     # Graph-replayed steps: one graph holds one step per weight copy (the
     # decode loop of an engine replays captured launches).
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for c in range(ncopy):
-            step(c)
-    graph.replay()
-    torch.cuda.synchronize()
-    for name, K, N in DECODE:  # replayed results equal the eager ones
-        if rel(ys[name].cpu().numpy(), oracle.q4k_matmul(host_w[name], host_x[name], N, K)) != errs[name]:
-            raise RuntimeError("graph replay differs from eager result (%s)" % name)
-    reps = max(1, steps // ncopy)
-    tg = Timer(torch)
-    g0 = tg.event()
-    for _ in range(reps):
+    graph, graph_ms_per_step, graph_steps = None, None, 0
+    if with_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(ncopy):
+                step(c)
         graph.replay()
-    g1 = tg.event()
-    torch.cuda.synchronize()
-    graph_ms_per_step = g0.elapsed_time(g1) / (reps * ncopy)
+        torch.cuda.synchronize()
+        for name, K, N in DECODE:  # replayed results equal the eager ones
+            if rel(ys[name].cpu().numpy(), oracle.q4k_matmul(host_w[name], host_x[name], N, K)) != errs[name]:
+                raise RuntimeError("graph replay differs from eager result (%s)" % name)
+        reps = max(1, steps // ncopy)
+        tg = Timer(torch)
+        g0 = tg.event()
+        for _ in range(reps):
+            graph.replay()
+        g1 = tg.event()
+        torch.cuda.synchronize()
+        graph_ms_per_step = g0.elapsed_time(g1) / (reps * ncopy)
+        graph_steps = reps * ncopy
 
     # eager steps through the Python binding
     tm = Timer(torch)
@@ -217,8 +220,9 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup):
     del graph, dev_w
     return {"ms_per_step": total_ms / steps, "step_bytes": step_bytes, "copies": ncopy,
             "GBps": step_bytes / (total_ms / steps) / 1e6,
-            "graph_ms_per_step": graph_ms_per_step, "graph_steps": reps * ncopy,
-            "graph_GBps": step_bytes / graph_ms_per_step / 1e6, "kernels": kernels,
+            "graph_ms_per_step": graph_ms_per_step, "graph_steps": graph_steps,
+            "graph_GBps": step_bytes / graph_ms_per_step / 1e6 if graph_ms_per_step else None,
+            "kernels": kernels,
             "max_rel_err": max(errs.values())}
 
 
@@ -338,8 +342,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="probe,decode,gemm,q6k,moe,cpu",
-                    help="comma list of: probe, decode, gemm, q6k, moe, cpu")
+    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,moe,cpu",
+                    help="comma list of: probe, decode, graph, gemm, q6k, moe, cpu "
+                         "(decode always runs: it is the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -362,8 +367,8 @@ def main():
     if "probe" in sections:
         extra["probe_copy"] = bench_probe(torch, qdm)
         log("probe copy:", extra["probe_copy"])
-    dec = bench_decode(torch, qdm, synth, oracle, args.steps, args.warmup)
-    log("decode: %.1f GB/s per step (eager), %.1f GB/s graph replay" % (dec["GBps"], dec["graph_GBps"]))
+    dec = bench_decode(torch, qdm, synth, oracle, args.steps, args.warmup, "graph" in sections)
+    log("decode: %.1f GB/s per step (eager), graph replay: %s GB/s" % (dec["GBps"], dec["graph_GBps"]))
     if "gemm" in sections:
         for M, reps in ((512, 20), (4096, 5)):
             extra["q4k_gemm_m%d" % M] = bench_gemm(torch, qdm, synth, oracle, M, reps)
