@@ -92,8 +92,16 @@ int q6k_gemv(const void *w, const void *x, int x_dtype, float *y,
  * Q4_K weights are decoded in fp32 and rounded to bf16 (nearest even) before
  * the bf16 x bf16 -> fp32 MFMA contraction; y is fp32 [M][N].
  * M >= 1, N >= 1, K >= 256, K % 256 == 0.
- * workspace: q4k_gemm_workspace_bytes(M, N, K) bytes (may be 0, then
- * workspace may be NULL).
+ * The tile x K iteration space is split evenly over one workgroup per
+ * compute unit; a tile computed by several workgroups is summed in a fixed
+ * order (results are deterministic).
+ * workspace: q4k_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, on the
+ * device of the call: a flag word per workgroup, then one fp32 256 x 256
+ * partial tile per workgroup. It must be zero-filled before its first use;
+ * every call leaves the flag words zero again, so one buffer serves any
+ * number of calls in stream order. Two calls that overlap in time (different
+ * streams) need different workspaces. The size depends on the current
+ * device's compute-unit count (256 if no device is visible).
  */
 size_t q4k_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,

@@ -145,14 +145,35 @@ def q4k_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().q4k_gemm_workspace_bytes(M, N, K))
 
 
+_gemm_ws = {}
+
+
+def _cached_gemm_workspace(need: int, device):
+    """A zero-filled workspace per device, grown on demand and reused (every
+    q4k_gemm call leaves its flag words zero again). Shared by all calls that
+    pass no workspace: calls running concurrently on different streams must
+    pass their own."""
+    torch = _torch()
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _gemm_ws.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("q4k_gemm: no workspace of %d bytes cached for this device; "
+                               "call it once before graph capture or pass workspace=" % need)
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _gemm_ws[key] = ws
+    return ws
+
+
 def q4k_gemm(w, x, N: int, K: int, y=None, workspace=None, stream=None):
-    """y [M][N] fp32 = x [M][K] bf16 * W^T on the matrix cores."""
+    """y [M][N] fp32 = x [M][K] bf16 * W^T on the matrix cores. A workspace
+    passed in must have been zero-filled before its first use."""
     torch = _torch()
     M = x.shape[0]
     y = _out(y, (M, N), x.device)
     need = q4k_gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _cached_gemm_workspace(need, x.device)
     wsp = _dev_ptr(workspace, "workspace") if workspace is not None else None
     wsb = workspace.numel() if workspace is not None else 0
     _check("q4k_gemm", lib().q4k_gemm(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _dev_ptr(y, "y"),

@@ -20,6 +20,23 @@
 // and their values zeroed), so the compiler waits for exactly the loads it
 // needs.
 //
+// Work split (stream-K): the 256 x 256 tiles times the K/128 stage pairs of
+// each form one iteration space that is cut into equal contiguous ranges, one
+// per workgroup. With at least as many tiles as compute units there is one
+// workgroup per unit; a range then covers the end of one tile, whole tiles,
+// and the start of another, so every unit gets the same number of MFMAs and
+// the last wave of tiles is not left to a few units. With fewer tiles than
+// units, each workgroup gets exactly one tile (no split). The unit that computes the last stage pair of
+// a tile owns it: it adds the fp32 partial tiles left in the workspace by the
+// units that computed its earlier pairs (always units with a smaller index, in
+// decreasing index order, so the sum is deterministic) and stores y. A
+// contributor writes its partial, fences at device scope and raises its flag;
+// the owner waits on the flag (bounded), reads the partial and lowers the flag
+// again, so the workspace flags are zero between calls. Workgroups start in
+// index order and a unit only waits on units with a smaller index, which have
+// started before it; each unit computes the segment others wait for before
+// the one that waits: the waits cannot deadlock and do not form chains.
+//
 // MFMA operand layout (32x32x16 bf16, wave64): lane l holds, for A, row l%32
 // and k = 8*(l/32) .. +7; for B, column l%32 and the same k. The 32x32 fp32
 // result gives lane l column l%32 and, in accumulator r, row
@@ -191,20 +208,13 @@ __device__ __forceinline__ void mfma_stage(f32x16 (&acc)[4][4], const uint16_t *
   }
 }
 
-__global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(const uint8_t *__restrict__ w,
-                                                                const uint16_t *__restrict__ x,
-                                                                float *__restrict__ y, int M,
-                                                                int N, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // stage buffer p: x tile at smem + 2p*TILE_ELEMS, W tile right after it
-
-  const int ntn = (N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * BN;
+// Multiplies stage range [s0, s1) (s1 - s0 even, >= 2) of tile (m0, n0) into acc.
+__device__ __forceinline__ void run_segment(f32x16 (&acc)[4][4], uint16_t *smem,
+                                            const uint8_t *__restrict__ w,
+                                            const uint16_t *__restrict__ x, int M, int N, int K,
+                                            int m0, int n0, int s0, int s1, uint32_t *publish) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int stages = (K / QK) * 4;
-
-  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -212,73 +222,244 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(const uint8_t *_
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  // Stage s lives in LDS buffer s & 1. While stage s is multiplied: x and W
-  // of stage s+2 are in flight, W of stage s+1 is decoded into the other
+  // Stage s lives in LDS buffer (s - s0) & 1. While stage s is multiplied: x
+  // and W of stage s+2 are in flight, W of stage s+1 is decoded into the other
   // buffer and x of stage s+1 (loaded two stages earlier) is stored there.
   const LoadOffsets lo = make_offsets(M, N, K, m0, n0);
   const uint8_t *xtile = (const uint8_t *)(x + (int64_t)m0 * K);
   const uint8_t *wtile = w + (int64_t)n0 * (K / QK) * Q4K_BYTES;
+  const int last = s1 - 1;
   XRegs xa, xb;
   WRegs wa, wb;
-  load_x(xa, lo, xtile, 0);
-  load_w(wa, lo, wtile, 0);
-  load_x(xb, lo, xtile, min(1, stages - 1));
-  load_w(wb, lo, wtile, min(1, stages - 1));
+  load_x(xa, lo, xtile, s0);
+  load_w(wa, lo, wtile, s0);
+  load_x(xb, lo, xtile, s0 + 1);
+  load_w(wb, lo, wtile, s0 + 1);
+  __syncthreads();  // the previous segment's last MFMAs have read the buffers
   store_x(xa, smem, M, m0);
   {
-    const RowScales sc = row_scales(wa, n0 + (int)threadIdx.x < N, 0);
+    const RowScales sc = row_scales(wa, n0 + (int)threadIdx.x < N, s0 & 3);
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) store_w_part(wa, sc, kk, smem + TILE_ELEMS);
   }
   __syncthreads();
 
-  // stages = 4 * K/256 is even: the loop body covers an even and an odd stage.
-  // Past the last stage, loads are clamped to it and the decodes/stores go to
-  // the buffer that is no longer read.
-  for (int s = 0; s < stages; s += 2) {
+  // The loop body covers an even and an odd stage. Past the segment's last
+  // stage, loads are clamped to it and the decodes/stores go to the buffer
+  // that is no longer read.
+  for (int s = s0; s < s1; s += 2) {
     // even stage s (buffer 0): W of s+1 (wb) decoded and x of s+1 (xb) stored into buffer 1
-    load_x(xa, lo, xtile, min(s + 2, stages - 1));
-    load_w(wa, lo, wtile, min(s + 2, stages - 1));
+    load_x(xa, lo, xtile, min(s + 2, last));
+    load_w(wa, lo, wtile, min(s + 2, last));
     mfma_stage(acc, smem, smem + TILE_ELEMS, wb, true, s + 1, smem + 3 * TILE_ELEMS, N, n0, wm,
                wn, lane);
     store_x(xb, smem + 2 * TILE_ELEMS, M, m0);
     __syncthreads();
     // odd stage s+1 (buffer 1): W of s+2 (wa) and x of s+2 (xa) into buffer 0
-    load_x(xb, lo, xtile, min(s + 3, stages - 1));
-    load_w(wb, lo, wtile, min(s + 3, stages - 1));
-    mfma_stage(acc, smem + 2 * TILE_ELEMS, smem + 3 * TILE_ELEMS, wa, true,
-               min(s + 2, stages - 1), smem + TILE_ELEMS, N, n0, wm, wn, lane);
+    load_x(xb, lo, xtile, min(s + 3, last));
+    load_w(wb, lo, wtile, min(s + 3, last));
+    mfma_stage(acc, smem + 2 * TILE_ELEMS, smem + 3 * TILE_ELEMS, wa, true, min(s + 2, last),
+               smem + TILE_ELEMS, N, n0, wm, wn, lane);
     store_x(xa, smem, M, m0);
     __syncthreads();
+    if (publish != nullptr && s == s0) {
+      // the partial tile stored before this segment has long been written:
+      // make it visible device-wide and raise its flag
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(publish, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+}
 
-  const int col = lane & 31, rq = 4 * (lane >> 5);
+constexpr uint32_t SPIN_LIMIT = 1u << 24;  // ~1 s of polling before giving up
+
+__global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int M,
+    int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags, int units) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // stage buffer p: x tile at smem + 2p*TILE_ELEMS, W tile right after it
+  __shared__ uint32_t timed_out;
+
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  const int P = K / (2 * BK);  // stage pairs per tile
+  const int64_t total = (int64_t)ntm * ntn * P;
+  const int unit = blockIdx.x;
+  const int64_t begin = total * unit / units, end = total * (unit + 1) / units;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[4][4];
+  uint32_t *pending = nullptr;  // flag of a partial tile stored but not yet published
+  // The range is walked from its end: the segment that starts a later tile
+  // (the only one whose partial another unit waits for) comes first, the
+  // segment that finishes an earlier tile (the only one that waits) comes last.
+  // So no unit's partial waits behind its own wait, and waits do not chain.
+  for (int64_t hi = end; hi > begin;) {
+    // tiles are ordered with the two (or more) M tiles of one N tile adjacent,
+    // so the units sharing a W tile run at the same time
+    const int tile = (int)((hi - 1) / P);
+    const int pe = (int)(hi - (int64_t)tile * P);
+    const int pb = (int)max(begin - (int64_t)tile * P, (int64_t)0);
+    const int m0 = (tile % ntm) * BM, n0 = (tile / ntm) * BN;
+    run_segment(acc, smem, w, x, M, N, K, m0, n0, 2 * pb, 2 * pe, pending);
+    pending = nullptr;
+    hi = (int64_t)tile * P + pb;
+
+    // The owner of a tile (the unit that computed its last stage pair) stores
+    // its part into y; a contributor stores its part as a row-major 256 x 256
+    // partial tile in its workspace slot and then raises its flag. Both use
+    // the same store loop.
+    const bool owner = pe == P;
+    {
+      float *dst = owner ? y + (int64_t)m0 * N + n0 : partials + (size_t)unit * BM * BN;
+      const int ld = owner ? N : BN;
+      const int rows = owner ? M - m0 : BM, cols = owner ? N - n0 : BN;
+      // lane coordinates pass through an opaque move, so the per-element
+      // address arithmetic is not hoisted out of the tile loop (where it would
+      // hold a register per element for the whole kernel)
+      int col = wn * 128 + (lane & 31), rq = wm * 128 + 4 * (lane >> 5);
+      asm volatile("" : "+v"(col), "+v"(rq));
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int gn = n0 + wn * 128 + j * 32 + col;
+        for (int j = 0; j < 4; j++) {
+          const int c = j * 32 + col;
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + rq + (v & 3);
-        if (gm < M && gn < N) y[(int64_t)gm * N + gn] = acc[i][j][v];
+          for (int v = 0; v < 16; v++) {
+            const int r = i * 32 + 8 * (v >> 2) + rq + (v & 3);
+            if (r < rows && c < cols) dst[(int64_t)r * ld + c] = acc[i][j][v];
+          }
+        }
+    }
+    if (!owner) {
+      // The partial is published during the next segment (after its first
+      // stage pair), so its stores drain behind MFMA work; if there is no
+      // next segment, right after the loop.
+      pending = &flags[unit];
+      continue;
+    }
+    if (pb == 0) continue;  // the owner computed the whole tile
+    // Earlier units [lowest, unit) worked on this tile: wait for their flags,
+    // then y += the sum of their partials (highest unit first), element-wise
+    // over the tile with no accumulator live.
+    int lowest = unit;
+    while (lowest > 0 && total * lowest / units > (int64_t)tile * P) lowest--;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t spins = 0;
+      for (int u = unit - 1; u >= lowest; u--) {
+        while (__hip_atomic_load(&flags[u], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+               ++spins < SPIN_LIMIT)
+          __builtin_amdgcn_s_sleep(2);
+        __hip_atomic_store(&flags[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      timed_out = spins >= SPIN_LIMIT;
+    }
+    __syncthreads();  // also orders this unit's own y stores before the re-reads below
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const bool bad = timed_out != 0u;  // a partial that never arrived poisons the tile
+    const int rows = min(M - m0, BM), cols = min(N - n0, BN);
+    float *yt = y + (int64_t)m0 * N + n0;
+    const bool vec = (N & 3) == 0;  // y rows of the tile are 16-byte aligned
+    constexpr int PB = 8;           // float4 per thread in flight
+    for (int base = 0; base < BM * BN / 4; base += PB * GEMM_THREADS) {
+      f32x4 sum[PB];
+#pragma unroll
+      for (int k = 0; k < PB; k++) sum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = unit - 1; u >= lowest; u--) {
+        const f32x4 *pt = (const f32x4 *)(partials + (size_t)u * BM * BN);
+#pragma unroll
+        for (int k = 0; k < PB; k++) {
+          const f32x4 v = pt[base + k * GEMM_THREADS + threadIdx.x];
+          sum[k].x += v.x;
+          sum[k].y += v.y;
+          sum[k].z += v.z;
+          sum[k].w += v.w;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PB; k++) {
+        const int e4 = base + k * GEMM_THREADS + threadIdx.x;
+        const int r = e4 / (BN / 4), c = (e4 % (BN / 4)) * 4;
+        if (r >= rows) continue;
+        float *py = yt + (int64_t)r * N + c;
+        if (vec) {
+          if (c < cols) {
+            const f32x4 o = *(const f32x4 *)py;
+            const float nan = __builtin_nanf("");
+            *(f32x4 *)py = bad ? f32x4{nan, nan, nan, nan}
+                               : f32x4{o.x + sum[k].x, o.y + sum[k].y, o.z + sum[k].z, o.w + sum[k].w};
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            if (c + q < cols) py[q] = bad ? __builtin_nanf("") : py[q] + sum[k][q];
+        }
       }
     }
+  }
+  if (pending != nullptr) {  // the last segment left a partial: publish it now
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(pending, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 constexpr size_t GEMM_LDS = 4 * TILE_ELEMS * sizeof(uint16_t);  // 147456 bytes
 
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Compute units of the current device (one workgroup each); 256 if unknown.
+int device_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Workgroups of a call. With fewer tiles than compute units, one workgroup
+// per tile: splitting them costs more in partial-tile traffic and in clock
+// (every unit busy) than the idle units leave on the table (measured at
+// M = 512, N = 17408, K = 5120: 136 tiles, 166 us whole versus 190 us split).
+// With at least as many tiles as units, the stream-K split evens out the
+// last wave of tiles.
+int gemm_units(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t cus = device_units();
+  if (tiles < cus) return (int)tiles;
+  const int64_t total = tiles * (K / (2 * BK));
+  return (int)(total < cus ? total : cus);
+}
+
 }  // namespace
 
-size_t q4k_gemm_workspace(int64_t, int64_t, int64_t) { return 0; }
+// Workspace: one flag word per unit (256-byte aligned block), then one fp32
+// partial tile per unit.
+size_t q4k_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  const size_t units = (size_t)gemm_units(M, N, K);
+  return align256(units * sizeof(uint32_t)) + units * BM * BN * sizeof(float);
+}
 
 void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
-                     void *, hipStream_t s) {
-  const dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM)));
+                     void *workspace, hipStream_t s) {
+  const int units = gemm_units(M, N, K);
+  uint32_t *flags = (uint32_t *)workspace;
+  float *partials = (float *)((char *)workspace + align256((size_t)units * sizeof(uint32_t)));
   (void)hipFuncSetAttribute((const void *)q4k_gemm_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
-  hipLaunchKernelGGL(q4k_gemm_kernel, grid, dim3(GEMM_THREADS), GEMM_LDS, s, (const uint8_t *)w,
-                     (const uint16_t *)x, y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL(q4k_gemm_kernel, dim3((unsigned)units), dim3(GEMM_THREADS), GEMM_LDS, s,
+                     (const uint8_t *)w, (const uint16_t *)x, y, (int)M, (int)N, (int)K, partials,
+                     flags, units);
 }
 
 }  // namespace qdm

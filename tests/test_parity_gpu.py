@@ -205,6 +205,52 @@ def test_q4k_gemm_ragged(M, N, K):
     assert e <= TOL_BF16
 
 
+def _gemm_units(M, N, K):
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return tiles if tiles < cus else min(cus, tiles * (K // 128))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 65536), (4352, 4096, 512), (4097, 4100, 768)])
+def test_q4k_gemm_split_tiles(M, N, K):
+    """Long K in one tile, and tile counts above the unit count, where tiles
+    are split between workgroups (272 tiles of 4 stage pairs over 256 units;
+    289 ragged tiles of 6): sampled outputs against the oracle, every output
+    finite, and every flag word of the workspace zero after the call."""
+    say("q4k_gemm split", M, N, K, "units", _gemm_units(M, N, K))
+    rng = np.random.default_rng(K + N)
+    w = synth.q4k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    need = qdm.q4k_gemm_workspace_bytes(M, N, K)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y = host(qdm.q4k_gemm(dev_bytes(w), dev_x(x), N, K, workspace=ws))
+    rows = np.unique(np.r_[np.arange(0, M, max(1, M // 97)), M - 1])
+    cols = np.unique(np.r_[np.arange(0, N, max(1, N // 101)), N - 1])
+    e = rel_err(y[np.ix_(rows, cols)], oracle.q4k_matmul(w[cols], x[rows], len(cols), K))
+    say("  rel err", e)
+    assert e <= TOL_BF16
+    assert np.isfinite(y).all()
+    flags = host(ws[: 4 * _gemm_units(M, N, K)].view(torch.int32))
+    assert not flags.any()
+
+
+def test_q4k_gemm_workspace_reused_across_shapes():
+    """One zero-filled workspace, used by calls of different shapes in turn,
+    gives the same bits as a fresh workspace per call."""
+    rng = np.random.default_rng(5)
+    shapes = [(4352, 4096, 512), (40, 700, 2560), (4352, 4096, 512), (4097, 4100, 768)]
+    big = max(qdm.q4k_gemm_workspace_bytes(*s) for s in shapes)
+    shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for M, N, K in shapes:
+        say("q4k_gemm reuse", M, N, K)
+        w = dev_bytes(synth.q4k_blocks(rng, N, K))
+        x = dev_x(synth.normal_bf16(rng, (M, K)))
+        a = host(qdm.q4k_gemm(w, x, N, K, workspace=shared))
+        fresh = torch.zeros(qdm.q4k_gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+        b = host(qdm.q4k_gemm(w, x, N, K, workspace=fresh))
+        assert np.array_equal(a, b)
+
+
 def test_q4k_gemm_one_hot_gives_bf16_weights():
     """x rows e_k: y[m, n] = bf16(W[n, k_m]) exactly (one nonzero product)."""
     N, K = 200, 1280
