@@ -293,9 +293,9 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 //
 // Every wave instruction reads 1 KiB of consecutive bytes: a wave loads a
 // span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB) with
-// non-temporal 16-byte loads, keeps up to three spans in flight in registers,
-// and moves each span through its own LDS buffer so that lane l receives
-// whole block l. One lane then decodes a whole super-block: the header once
+// non-temporal 16-byte loads, keeps two spans in flight in registers while it
+// computes a third, and moves each span through its own LDS buffer so that
+// lane l receives whole block l. One lane then decodes a whole super-block: the header once
 // per 256 weights, the codes with one v_and_or_b32 per two codes and
 // v_dot2_f32_bf16 against x.
 // x lives in LDS as 560-byte records per 256-element column block: 512 bytes
@@ -306,14 +306,14 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 constexpr int DN_SPAN = 64;                           // blocks per span, one per lane
 constexpr int DN_SPAN_BYTES = DN_SPAN * Q4K_BYTES;    // 9216 = 9 x 1 KiB
 constexpr int DN_XREC = 560;                          // LDS bytes per x column block
-constexpr int DN_TARGET_WGS = 256;                    // one workgroup per CU
+#ifndef QDM_DN_TARGET_WGS
+#define QDM_DN_TARGET_WGS 256
+#endif
+constexpr int DN_TARGET_WGS = QDM_DN_TARGET_WGS;      // workgroups per launch (one per CU)
 constexpr int DN_MAX_WG_BLOCKS = 8192;
 constexpr size_t DN_LDS_LIMIT = 160 * 1024;
 #ifndef QDM_DN_WAVES
-#define QDM_DN_WAVES 8  // waves per workgroup of the dense kernel (2 per SIMD)
-#endif
-#ifndef QDM_DN_NBUF
-#define QDM_DN_NBUF 2   // spans held in registers per wave (one in flight)
+#define QDM_DN_WAVES 4  // waves per workgroup of the dense kernel
 #endif
 #ifndef QDM_DN_PHASED
 #define QDM_DN_PHASED 1  // keep each sub-block pair's LDS reads next to its math
@@ -338,17 +338,16 @@ __device__ __forceinline__ void load_span(Span &sp, const uint8_t *__restrict__ 
 
 // x staging in two phases: every x load is issued first (before any weight
 // load, so waiting for x never waits for weights), then the chunks are
-// permuted into their records and summed.
-constexpr int DN_XCHUNKS = 16;  // 16-byte x chunks per thread (K <= 16 * 8 * threads)
-
-template <int THREADS>
+// permuted into their records and summed. XC 16-byte chunks per thread
+// (K <= 8 * XC * threads); loads past the end re-read the last chunk.
+template <int THREADS, int XC>
 struct XStage {
-  u32x4 v[DN_XCHUNKS];
+  u32x4 v[XC];
 
   __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int K) {
     const int nchunk = K / 8;
 #pragma unroll
-    for (int i = 0; i < DN_XCHUNKS; i++) {
+    for (int i = 0; i < XC; i++) {
       const int c = min(i * THREADS + (int)threadIdx.x, nchunk - 1);
       v[i] = ((const u32x4 *)x)[c];
     }
@@ -357,7 +356,7 @@ struct XStage {
   __device__ __forceinline__ void store(int K, uint8_t *xrec) const {
     const int nchunk = K / 8;  // 32 chunks per 256-element record
 #pragma unroll
-    for (int i = 0; i < DN_XCHUNKS; i++) {
+    for (int i = 0; i < XC; i++) {
       if (i * THREADS < nchunk) {  // uniform
         const int c = i * THREADS + threadIdx.x;
         const u32x4 e = v[i];
@@ -428,79 +427,74 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
   return r;
 }
 
-// WAVES waves per workgroup; NBUF spans held in registers per wave (the
-// current one and NBUF - 1 in flight).
-template <int WAVES, int NBUF>
+// WAVES waves per workgroup. Each wave holds two spans in registers: while it
+// computes one span (from its LDS buffer), the next two are in flight. Spans
+// are handed out in order from a workgroup counter, so a wave whose data
+// arrived late takes fewer spans and the waves finish together.
+template <int WAVES, int XC>
 __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y,
     int K, int rows_q, int rows_rem) {
-  constexpr int DN_WAVES = WAVES, DN_THREADS = WAVES * WAVE;
+  constexpr int DN_THREADS = WAVES * WAVE;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int next_span;
   const int nb = K / QK;
-  uint8_t *spanbuf = smem;                              // [waves][9216]
-  uint8_t *xrec = smem + DN_WAVES * DN_SPAN_BYTES;      // [nb][560]
-  float *part = (float *)(xrec + nb * DN_XREC);         // [blocks of this workgroup]
+  uint8_t *spanbuf = smem;                            // [waves][9216]
+  uint8_t *xrec = smem + WAVES * DN_SPAN_BYTES;       // [nb][560]
+  float *part = (float *)(xrec + nb * DN_XREC);       // [blocks of this workgroup]
 
   const int bid = blockIdx.x;
   const int r0 = bid * rows_q + min(bid, rows_rem);
   const int r1 = r0 + rows_q + (bid < rows_rem ? 1 : 0);
-  const int64_t B0 = (int64_t)r0 * nb;
   const int nblk = (r1 - r0) * nb;
-
+  const int nspan = (nblk + DN_SPAN - 1) / DN_SPAN;
+  const uint8_t *wbase = w + (int64_t)r0 * nb * Q4K_BYTES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wb0 = (int)(((int64_t)wave * nblk) / DN_WAVES);
-  const int wb1 = (int)(((int64_t)(wave + 1) * nblk) / DN_WAVES);
-  const int nspan = (wb1 - wb0 + DN_SPAN - 1) / DN_SPAN;
-  const uint8_t *wbase = w + (B0 + wb0) * Q4K_BYTES;
-  auto span_bytes = [&](int sidx) {
-    return min(DN_SPAN, wb1 - wb0 - DN_SPAN * sidx) * Q4K_BYTES;
+
+  // A span index past the end loads the last span again (its bytes are
+  // already on their way), so every wave issues the same loads in every
+  // iteration and the compiler can wait for exactly the span it needs.
+  auto issue = [&](Span &r, int sidx) {
+    const int si = min(sidx, nspan - 1);
+    load_span(r, wbase + (int64_t)si * DN_SPAN_BYTES, min(DN_SPAN, nblk - DN_SPAN * si) * Q4K_BYTES,
+              lane);
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_span, 1);
+    return __builtin_amdgcn_readfirstlane(v);
   };
 
-  // Spans past the wave's last one alias that last span (already in flight).
-  auto span_ptr = [&](int sidx) {
-    return wbase + (int64_t)min(sidx, nspan - 1) * DN_SPAN_BYTES;
-  };
-  auto span_len = [&](int sidx) { return span_bytes(min(sidx, nspan - 1)); };
-
-  XStage<DN_THREADS> xst;
+  XStage<DN_THREADS, XC> xst;
   xst.load(x, K);
-
-  Span R[NBUF];
-  if (nspan > 0) {
-#pragma unroll
-    for (int p = 0; p < NBUF - 1; p++) load_span(R[p], span_ptr(p), span_len(p), lane);
-  }
-
+  if (threadIdx.x == 0) next_span = 2 * WAVES;
+  int sidx[2] = {wave, WAVES + wave};
+  Span R[2];
+  issue(R[0], sidx[0]);
+  issue(R[1], sidx[1]);
   xst.store(K, xrec);
   __syncthreads();
 
   const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
   uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
-  const int s64 = DN_SPAN % nb;
-  int kb = (wb0 + lane) % nb;
-
-  if (nspan > 0) {
-    for (int sb = 0; sb < nspan; sb += NBUF) {
+  while (sidx[0] < nspan || sidx[1] < nspan) {
 #pragma unroll
-      for (int p = 0; p < NBUF; p++) {
-        const int sidx = sb + p;
-        load_span(R[(p + NBUF - 1) % NBUF], span_ptr(sidx + NBUF - 1), span_len(sidx + NBUF - 1),
-                  lane);
-        if (sidx < nspan) {
-          const int nbytes = span_bytes(sidx);
+    for (int p = 0; p < 2; p++) {
+      const int cur = sidx[p];
+      const int nbytes = cur < nspan ? min(DN_SPAN, nblk - DN_SPAN * cur) * Q4K_BYTES : 0;
 #pragma unroll
-          for (int j = 0; j < 9; j++) {
-            const int off = 1024 * j + 16 * lane;
-            if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
-          }
-          const int rb = wb0 + DN_SPAN * sidx + lane;
-          if (rb < wb1)
-            part[rb] = q4k_block_dot_bf16(mybuf + Q4K_BYTES * lane, xrec + kb * DN_XREC, MASK,
-                                          MAGIC);
-          kb += s64;
-          if (kb >= nb) kb -= nb;
-        }
+      for (int j = 0; j < 9; j++) {
+        const int off = 1024 * j + 16 * lane;
+        if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
       }
+      // refill this slot right away: two spans stay in flight during the math
+      const int nxt = cur < nspan ? grab() : nspan;
+      issue(R[p], nxt);
+      sidx[p] = nxt;
+      const int b = DN_SPAN * cur + lane;
+      if (cur < nspan && b < nblk)
+        part[b] = q4k_block_dot_bf16(mybuf + Q4K_BYTES * lane, xrec + (b % nb) * DN_XREC, MASK,
+                                     MAGIC);
     }
   }
   __syncthreads();
@@ -526,7 +520,18 @@ bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, 
   rows_rem = (int)(N % nwg);
   const int64_t max_blocks = (rows_q + (rows_rem ? 1 : 0)) * nb;
   lds = (size_t)DN_WAVES * DN_SPAN_BYTES + (size_t)nb * DN_XREC + (size_t)max_blocks * 4;
-  return lds <= DN_LDS_LIMIT && K / 8 <= (int64_t)DN_XCHUNKS * DN_WAVES * WAVE;
+  return lds <= DN_LDS_LIMIT && K / 8 <= (int64_t)16 * DN_WAVES * WAVE;
+}
+
+// x chunks per thread for K (the smallest instantiated count that covers it).
+template <int DN_WAVES, int XC>
+void launch_dense(const void *w, const void *x, float *y, int64_t K, int64_t nwg, int rows_q,
+                  int rows_rem, size_t lds, hipStream_t s) {
+  auto kern = q4k_gemv_m1_kernel<DN_WAVES, XC>;
+  (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(DN_WAVES * WAVE), lds, s,
+                     (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem);
 }
 
 template <bool XBF16, int MT>
@@ -565,11 +570,17 @@ void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
     int rows_q, rows_rem;
     size_t lds;
     if (dense_plan<QDM_DN_WAVES>(N, K, nwg, rows_q, rows_rem, lds)) {
-      auto kern = q4k_gemv_m1_kernel<QDM_DN_WAVES, QDM_DN_NBUF>;
-      (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-      hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(QDM_DN_WAVES * WAVE), lds, s,
-                         (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem);
+      const int64_t per_thread = (K / 8 + QDM_DN_WAVES * WAVE - 1) / (QDM_DN_WAVES * WAVE);
+      if (per_thread <= 2)
+        launch_dense<QDM_DN_WAVES, 2>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+      else if (per_thread <= 3)
+        launch_dense<QDM_DN_WAVES, 3>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+      else if (per_thread <= 5)
+        launch_dense<QDM_DN_WAVES, 5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+      else if (per_thread <= 8)
+        launch_dense<QDM_DN_WAVES, 8>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+      else
+        launch_dense<QDM_DN_WAVES, 16>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
       return;
     }
   }
