@@ -289,7 +289,7 @@ def bench_moe(torch, qdm, synth, oracle, T, reps):
     ids = torch.from_numpy(d["ids"]).to("cuda")
     gw = torch.from_numpy(d["gw"]).to("cuda")
     sets = [(w13, w2), (w13.clone(), w2.clone())]
-    ws = torch.empty(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8, device="cuda")
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     qdm.moe_q4k_grouped_gemm(x, w13, w2, ids, gw, E, H, F, y=y, workspace=ws)
     torch.cuda.synchronize()

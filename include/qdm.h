@@ -122,7 +122,13 @@ int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64
  *   Ids outside [0, E) are skipped (they contribute nothing).
  *   1 <= T <= 2^24, 1 <= E <= 1024, 1 <= top_k <= 16, H and F multiples of
  *   256 and at most 65536.
- *   workspace: moe_q4k_workspace_bytes(T, E, top_k, H, F) bytes.
+ *   workspace: moe_q4k_workspace_bytes(T, E, top_k, H, F) bytes, 16-byte
+ *   aligned, on the device of the call (scratch; no initial contents
+ *   needed). Calls that overlap in time need different workspaces.
+ *   With T * top_k <= 64 (decode) the call is three kernels: gate+up+SwiGLU
+ *   and down, each of which routes the few entries itself, and the combine.
+ *   Above that: a routing kernel, two grouped matrix-core kernels and the
+ *   combine.
  */
 size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
 int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,

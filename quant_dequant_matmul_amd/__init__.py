@@ -145,23 +145,23 @@ def q4k_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().q4k_gemm_workspace_bytes(M, N, K))
 
 
-_gemm_ws = {}
+_ws_cache = {}
 
 
-def _cached_gemm_workspace(need: int, device):
-    """A zero-filled workspace per device, grown on demand and reused (every
-    q4k_gemm call leaves its flag words zero again). Shared by all calls that
-    pass no workspace: calls running concurrently on different streams must
-    pass their own."""
+def _cached_workspace(kind: str, need: int, device):
+    """A zero-filled workspace per device and entry point, grown on demand and
+    reused (q4k_gemm and moe_q4k_grouped_gemm leave their flag and counter
+    words zero again). Shared by all calls that pass no workspace: calls
+    running concurrently on different streams must pass their own."""
     torch = _torch()
-    key = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _gemm_ws.get(key)
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
         if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError("q4k_gemm: no workspace of %d bytes cached for this device; "
-                               "call it once before graph capture or pass workspace=" % need)
+            raise RuntimeError("%s: no workspace of %d bytes cached for this device; call it "
+                               "once before graph capture or pass workspace=" % (kind, need))
         ws = torch.zeros(need, dtype=torch.uint8, device=device)
-        _gemm_ws[key] = ws
+        _ws_cache[key] = ws
     return ws
 
 
@@ -173,7 +173,7 @@ def q4k_gemm(w, x, N: int, K: int, y=None, workspace=None, stream=None):
     y = _out(y, (M, N), x.device)
     need = q4k_gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
-        workspace = _cached_gemm_workspace(need, x.device)
+        workspace = _cached_workspace("q4k_gemm", need, x.device)
     wsp = _dev_ptr(workspace, "workspace") if workspace is not None else None
     wsb = workspace.numel() if workspace is not None else 0
     _check("q4k_gemm", lib().q4k_gemm(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _dev_ptr(y, "y"),
@@ -187,13 +187,14 @@ def moe_q4k_workspace_bytes(T: int, E: int, top_k: int, H: int, F: int) -> int:
 
 def moe_q4k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int, F: int,
                          y=None, workspace=None, stream=None):
-    """Routed MoE FFN: y [T][H] = sum_s topk_w * W2[e] (silu(W13g x) * W13u x)."""
+    """Routed MoE FFN: y [T][H] = sum_s topk_w * W2[e] (silu(W13g x) * W13u x).
+    A workspace passed in must have been zero-filled before its first use."""
     torch = _torch()
     T, top_k = topk_ids.shape
     y = _out(y, (T, H), x.device)
     need = moe_q4k_workspace_bytes(T, E, top_k, H, F)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _cached_workspace("moe", need, x.device)
     _check("moe_q4k_grouped_gemm", lib().moe_q4k_grouped_gemm(
         _dev_ptr(x, "x"), _dev_ptr(w_gate_up, "w_gate_up"), _dev_ptr(w_down, "w_down"),
         _dev_ptr(topk_ids, "topk_ids"), _dev_ptr(topk_w, "topk_w"), _dev_ptr(y, "y"),

@@ -319,6 +319,48 @@ def test_moe_full_shape(T):
     assert e <= TOL_BF16
 
 
+@pytest.mark.parametrize("T,E,H,F,top_k", [(16, 3, 512, 256, 2), (64, 4, 256, 512, 1),
+                                           (9, 8, 256, 256, 7)])
+def test_moe_decode_many_entries_per_expert(T, E, H, F, top_k):
+    """At most 64 (token, slot) entries but more than 8 per expert, so the
+    decode kernels take several passes over an expert's entries."""
+    say("moe decode passes", T, E, H, F, top_k)
+    d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=3 * T + E)
+    y = host(qdm.moe_q4k_grouped_gemm(*_moe_dev(d), E, H, F))
+    ref = oracle.moe_q4k(d["x"], d["w13"], d["w2"], d["ids"], d["gw"], E, H, F)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [2, 20])
+def test_moe_all_ids_out_of_range_gives_zero(T):
+    E, H, F, k = 4, 256, 256, 4
+    d = synth.moe(T, E=E, H=H, F=F, top_k=k, seed=T)
+    ids = np.full_like(d["ids"], -1)
+    ids[::2, ::2] = E + 5
+    say("moe all ids bad", T)
+    xd, w13, w2, _, gw = _moe_dev(d)
+    y = host(qdm.moe_q4k_grouped_gemm(xd, w13, w2, torch.from_numpy(ids).to("cuda"), gw, E, H, F))
+    assert not y.any()
+
+
+def test_moe_workspace_reused_across_regimes():
+    """One zero-filled workspace serves decode-sized and prefill-sized calls in
+    turn and gives the bits of a fresh workspace each time."""
+    E, H, F = 16, 512, 256
+    calls = [synth.moe(T, E=E, H=H, F=F, top_k=4, seed=T) for T in (8, 40, 3, 40, 8)]
+    need = max(qdm.moe_q4k_workspace_bytes(d["ids"].shape[0], E, 4, H, F) for d in calls)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for d in calls:
+        say("moe reuse T", d["ids"].shape[0])
+        args = _moe_dev(d)
+        a = host(qdm.moe_q4k_grouped_gemm(*args, E, H, F, workspace=shared))
+        fresh = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        b = host(qdm.moe_q4k_grouped_gemm(*args, E, H, F, workspace=fresh))
+        assert np.array_equal(a, b)
+
+
 def test_moe_skips_out_of_range_ids():
     E, H, F, T = 6, 256, 256, 4
     d = synth.moe(T, E=E, H=H, F=F, top_k=2, seed=11)
@@ -356,12 +398,13 @@ def test_determinism_all_entry_points():
     say("determinism gemm")
     a, b = host(qdm.q4k_gemm(w, xg, N, K)), host(qdm.q4k_gemm(w, xg, N, K))
     assert np.array_equal(a, b)
-    d = synth.moe(64)
-    args = _moe_dev(d)
-    say("determinism moe")
-    a = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
-    b = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
-    assert np.array_equal(a, b)
+    for T in (8, 64):  # decode and matrix-core regimes
+        d = synth.moe(T)
+        args = _moe_dev(d)
+        say("determinism moe T", T)
+        a = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
+        b = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
+        assert np.array_equal(a, b)
 
 
 # --------------------------------------------------------------------------
