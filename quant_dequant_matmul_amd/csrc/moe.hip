@@ -2,262 +2,42 @@
 // matmul; hipster README, "Verify the claims": MoE grouped GEMM).
 //
 //   y_t = sum_s gw[t][s] * W2[e] * (silu(W13[e][0:F] x_t) * W13[e][F:2F] x_t),
-//   e = ids[t][s].
+//   e = ids[t][s]   (entries whose id is outside [0, E) contribute nothing).
 //
-// Pipeline (all on one stream, no host round trip):
-//  1. route: histogram of the ids over experts, exclusive scan, then a stable
-//     scatter of the (token, slot) entries into expert order (ties keep
-//     (t, s) order), plus the compact list of experts that received entries.
-//  2. gate+up: for each active expert, every W13 row is streamed once and
-//     multiplied with all the gathered tokens of that expert -> U [8T][2F].
-//  3. SwiGLU: h = silu(U[:, :F]) * U[:, F:] (fp32).
-//  4. down: for each active expert, W2 rows times its h rows -> O [8T][H].
-//  5. combine: y_t = sum over s in slot order of gw[t][s] * O[pos(t, s)];
-//     deterministic, no atomics.
+// Two regimes, chosen on the host from the entry count n = T * top_k.
+//
+// Decode (n <= 64): every workgroup routes the few entries itself (bitmap of
+// the experts present; the a-th of them in increasing id order; its entries
+// in (t, s) order), so there is no routing launch. Workgroup (chunk, a)
+// streams its row chunk of the a-th active expert's weights once and
+// multiplies it with all that expert's entries, whose inputs it holds in LDS.
+//  1. gate+up+SwiGLU: rows f of the gate half and F + f of the up half in one
+//     workgroup; h[entry][f] = silu(g) * u, fp32.
+//  2. down: o[entry][r], fp32.
+//  3. combine: y[t][r] = sum over s in slot order of gw[t][s] * o[t*k+s][r].
+//
+// Matrix cores (n > 64):
+//  1. route (one workgroup): histogram of the ids, exclusive scan, stable
+//     scatter of the entries into expert order (perm).
+//  2. gate+up+SwiGLU: workgroup (f tile of 128, e) decodes 128 gate rows and
+//     the matching 128 up rows of W13[e] to bf16 in LDS, 64 K at a time, and
+//     multiplies them with up to 128 gathered x rows of e's entries per pass
+//     (v_mfma_f32_32x32x16_bf16, fp32 accumulators); the gate and up values
+//     of one (entry, f) land in the same lane, so h = silu(g) * u is formed
+//     in registers and stored as bf16 by entry.
+//  3. down: workgroup (row tile of 256, e): W2[e] rows times the h rows of
+//     e's entries -> o[entry][r], fp32.
+//  4. combine as above.
 #include "common.h"
 #include "launch.h"
+#include "q4k_tile.h"
 
 namespace qdm {
 
 namespace {
 
-constexpr int ROUTE_THREADS = 1024;
-constexpr int MOE_GEMV_THREADS = 256;
-constexpr int MOE_WAVES = MOE_GEMV_THREADS / WAVE;
-constexpr int MOE_MT = 4;  // tokens per pass in the gathered GEMV
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-struct MoeWs {
-  int32_t *counts;   // [E]
-  int32_t *offsets;  // [E+1]
-  int32_t *active;   // [E] compact list of experts with entries
-  int32_t *meta;     // [0] = number of active experts, [1] = skipped (bad) ids
-  int32_t *perm;     // [n] sorted position -> entry (t*top_k + s)
-  int32_t *pos;      // [n] entry -> sorted position, -1 if skipped
-  float *u;          // [n][2F]
-  float *h;          // [n][F]
-  float *o;          // [n][H]
-  size_t total;
-};
-
-MoeWs carve(void *base, int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) {
-  const int64_t n = T * top_k;
-  MoeWs ws;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const size_t o_counts = take(sizeof(int32_t) * E);
-  const size_t o_offsets = take(sizeof(int32_t) * (E + 1));
-  const size_t o_active = take(sizeof(int32_t) * E);
-  const size_t o_meta = take(sizeof(int32_t) * 4);
-  const size_t o_perm = take(sizeof(int32_t) * n);
-  const size_t o_pos = take(sizeof(int32_t) * n);
-  const size_t o_u = take(sizeof(float) * n * 2 * F);
-  const size_t o_h = take(sizeof(float) * n * F);
-  const size_t o_o = take(sizeof(float) * n * H);
-  char *b = (char *)base;
-  ws.counts = (int32_t *)(b + o_counts);
-  ws.offsets = (int32_t *)(b + o_offsets);
-  ws.active = (int32_t *)(b + o_active);
-  ws.meta = (int32_t *)(b + o_meta);
-  ws.perm = (int32_t *)(b + o_perm);
-  ws.pos = (int32_t *)(b + o_pos);
-  ws.u = (float *)(b + o_u);
-  ws.h = (float *)(b + o_h);
-  ws.o = (float *)(b + o_o);
-  ws.total = off;
-  return ws;
-}
-
-// Single workgroup: counts, scan, active list and the stable scatter.
-__global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
-    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ active, int32_t *__restrict__ meta,
-    int32_t *__restrict__ perm, int32_t *__restrict__ pos) {
-  extern __shared__ int32_t sm[];
-  int32_t *cnt = sm;          // [E]
-  int32_t *run = sm + E;      // [E] running write position
-  __shared__ int32_t bad;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += ROUTE_THREADS) cnt[e] = 0;
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += ROUTE_THREADS) {
-    const int e = ids[i];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else
-      atomicAdd(&bad, 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0, na = 0;
-    for (int e = 0; e < E; e++) {
-      const int c = cnt[e];
-      offsets[e] = acc;
-      run[e] = acc;
-      counts[e] = c;
-      if (c > 0) active[na++] = e;
-      acc += c;
-    }
-    offsets[E] = acc;
-    meta[0] = na;
-    meta[1] = bad;
-  }
-  __syncthreads();
-  // Stable scatter by wave 0: 64 entries at a time, in entry order. Within a
-  // batch, lanes with the same expert are ranked by lane index via ballots.
-  if (tid < WAVE) {
-    const int lane = tid;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < n; base += WAVE) {
-      const int i = base + lane;
-      int e = i < n ? ids[i] : -1;
-      const bool valid = i < n && e >= 0 && e < E;
-      if (i < n && !valid) pos[i] = -1;
-      bool pending = valid;
-      while (__ballot(pending) != 0ull) {
-        const uint64_t pmask = __ballot(pending);
-        const int leader = __builtin_ctzll(pmask);
-        const int ev = __shfl(e, leader, WAVE);
-        const bool mine = pending && e == ev;
-        const uint64_t mmask = __ballot(mine);
-        const int start = run[ev];
-        if (mine) {
-          const int p = start + __popcll(mmask & lt);
-          pos[i] = p;
-          perm[p] = i;
-          pending = false;
-        }
-        if (lane == leader) run[ev] = start + __popcll(mmask);
-      }
-    }
-  }
-}
-
-// Gathered Q4_K GEMV over the rows of one expert: for the a-th active expert
-// e and the sorted entries p in [offsets[e], offsets[e+1]):
-//   out[p][r] = sum_k xrow(p)[k] * W_e(r, k)
-// xrow(p) = x[perm[p] / top_k] (bf16, gate+up) or x[p] (fp32, down).
-// Lane mapping as in the dense GEMV: 4 lanes per block, G groups per row.
-template <bool XBF16>
-__global__ __launch_bounds__(MOE_GEMV_THREADS) void moe_gemv_kernel(
-    const uint8_t *__restrict__ wbase, int64_t expert_stride, int Nr, int K,
-    const void *__restrict__ x, const int32_t *__restrict__ perm, int top_k,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ meta, float *__restrict__ out, int G) {
-  const int a = blockIdx.y;
-  if (a >= meta[0]) return;
-  const int e = active[a];
-  const int p_begin = offsets[e], p_end = offsets[e + 1];
-  const uint8_t *w = wbase + (int64_t)e * expert_stride;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 2, c = lane & 3;
-  const int R = 16 / G;
-  const int row = (blockIdx.x * MOE_WAVES + wave) * R + g / G;
-  const int gg = g % G;
-  const int nb = K / QK;
-  const int iters = nb / G;
-  const bool active_row = row < Nr;
-  const uint8_t *rowp = w + (int64_t)(active_row ? row : 0) * nb * Q4K_BYTES;
-  const int j0 = 2 * c;
-
-  for (int p0 = p_begin; p0 < p_end; p0 += MOE_MT) {
-    float acc[MOE_MT];
-    int64_t xoff[MOE_MT];
-#pragma unroll
-    for (int m = 0; m < MOE_MT; m++) {
-      acc[m] = 0.f;
-      const int p = p0 + m < p_end ? p0 + m : p_end - 1;
-      xoff[m] = XBF16 ? (int64_t)(perm[p] / top_k) * K : (int64_t)p * K;
-    }
-    if (active_row) {
-      for (int it = 0; it < iters; it++) {
-        const int kb = it * G + gg;
-        const uint8_t *blk = rowp + (int64_t)kb * Q4K_BYTES;
-        const u32x4 hdr = *(const u32x4 *)blk;
-        const u32x4 qa = *(const u32x4 *)(blk + 16 + 32 * c);
-        const u32x4 qb = *(const u32x4 *)(blk + 32 + 32 * c);
-        const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
-        uint32_t sc0, m0, sc1, m1;
-        q4k_scale_min(hdr.y, hdr.z, hdr.w, j0, sc0, m0);
-        q4k_scale_min(hdr.y, hdr.z, hdr.w, j0 + 1, sc1, m1);
-        const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
-        const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-        const int k0 = kb * QK + 32 * j0;
-#pragma unroll
-        for (int m = 0; m < MOE_MT; m++) {
-          float s0 = 0.f, s1 = 0.f, x0s = 0.f, x1s = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; i++) {
-            float xa[4], xb[4];
-            if constexpr (XBF16) {
-              const u32x2 va = *(const u32x2 *)((const uint16_t *)x + xoff[m] + k0 + 4 * i);
-              const u32x2 vb = *(const u32x2 *)((const uint16_t *)x + xoff[m] + k0 + 32 + 4 * i);
-              xa[0] = bf16_bits_to_float(va.x); xa[1] = bf16_bits_to_float(va.x >> 16);
-              xa[2] = bf16_bits_to_float(va.y); xa[3] = bf16_bits_to_float(va.y >> 16);
-              xb[0] = bf16_bits_to_float(vb.x); xb[1] = bf16_bits_to_float(vb.x >> 16);
-              xb[2] = bf16_bits_to_float(vb.y); xb[3] = bf16_bits_to_float(vb.y >> 16);
-            } else {
-              const f32x4 va = *(const f32x4 *)((const float *)x + xoff[m] + k0 + 4 * i);
-              const f32x4 vb = *(const f32x4 *)((const float *)x + xoff[m] + k0 + 32 + 4 * i);
-              xa[0] = va.x; xa[1] = va.y; xa[2] = va.z; xa[3] = va.w;
-              xb[0] = vb.x; xb[1] = vb.y; xb[2] = vb.z; xb[3] = vb.w;
-            }
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-              s0 = fmaf(xa[t], (float)((q[i] >> (8 * t)) & 15u), s0);
-              s1 = fmaf(xb[t], (float)((q[i] >> (8 * t + 4)) & 15u), s1);
-              x0s += xa[t];
-              x1s += xb[t];
-            }
-          }
-          acc[m] += a0 * s0 - b0 * x0s + a1 * s1 - b1 * x1s;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MOE_MT; m++) {
-      const float v = group_sum(acc[m], 4 * G);
-      if (active_row && p0 + m < p_end && (lane & (4 * G - 1)) == 0)
-        out[(int64_t)(p0 + m) * Nr + row] = v;
-    }
-  }
-}
-
-__global__ void moe_swiglu_kernel(const float *__restrict__ u, float *__restrict__ h,
-                                  const int32_t *__restrict__ offsets, int E, int F) {
-  const int64_t n = offsets[E];
-  const int64_t total = n * F;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = i / F, f = i % F;
-    const float gt = u[p * 2 * F + f], up = u[p * 2 * F + F + f];
-    h[i] = gt / (1.0f + __expf(-gt)) * up;
-  }
-}
-
-__global__ void moe_combine_kernel(const float *__restrict__ o, const int32_t *__restrict__ pos,
-                                   const float *__restrict__ gw, float *__restrict__ y, int T,
-                                   int top_k, int H) {
-  const int64_t total = (int64_t)T * H;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / H, r = i % H;
-    float acc = 0.f;
-    for (int s = 0; s < top_k; s++) {
-      const int p = pos[t * top_k + s];
-      if (p >= 0) acc = fmaf(gw[t * top_k + s], o[(int64_t)p * H + r], acc);
-    }
-    y[i] = acc;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Decode regime (n = T * top_k <= 64 entries).
@@ -616,20 +396,252 @@ __global__ void moe_combine_entries_kernel(const float *__restrict__ o,
   }
 }
 
-int gcd16(int nb) {
-  int g = 16;
-  while (g > 1 && nb % g) g >>= 1;
-  return g;
+// ---------------------------------------------------------------------------
+// Matrix-core regime (n > 64).
+// ---------------------------------------------------------------------------
+constexpr int ROUTE_THREADS = 1024;
+constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
+
+// One workgroup: offsets[e] = first sorted position of expert e (exclusive
+// scan of the counts, offsets[E] = valid entries), perm[pos] = entry index,
+// entries of one expert in increasing (t, s) order. The scatter takes 1024
+// entries at a time: each wave ranks its lanes among equal ids (ballots of the
+// id bits), the per-wave counts of every id go to LDS, and an entry's position
+// is the expert's running offset + the counts of earlier waves + its rank.
+__global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
+    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm) {
+  extern __shared__ int32_t rsm[];
+  int32_t *run = rsm;       // [E] running offsets
+  int32_t *cntw = rsm + E;  // [ROUTE_WAVES][E] per-wave counts of a chunk
+  __shared__ int32_t wsum[ROUTE_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += ROUTE_THREADS) run[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += ROUTE_THREADS) {
+    const int id = ids[i];
+    if (id >= 0 && id < E) atomicAdd(&run[id], 1);
+  }
+  __syncthreads();
+  const int v = tid < E ? run[tid] : 0;  // E <= 1024: one count per thread
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int u = __shfl_up(incl, o, WAVE);
+    if (lane >= o) incl += u;
+  }
+  if (lane == WAVE - 1) wsum[wave] = incl;
+  __syncthreads();
+  int wpre = 0, total = 0;
+  for (int w = 0; w < ROUTE_WAVES; w++) {
+    if (w < wave) wpre += wsum[w];
+    total += wsum[w];
+  }
+  if (tid < E) {
+    offsets[tid] = wpre + incl - v;
+    run[tid] = wpre + incl - v;
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = 0; base < n; base += ROUTE_THREADS) {
+    for (int j = tid; j < ROUTE_WAVES * E; j += ROUTE_THREADS) cntw[j] = 0;
+    __syncthreads();
+    const int i = base + tid;
+    int id = i < n ? ids[i] : -1;
+    if (id >= E) id = -1;
+    uint64_t match = __ballot(id >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 10; bit++) {  // E <= 1024
+      const uint64_t ones = __ballot(id >= 0 && ((id >> bit) & 1));
+      match &= ((id >> bit) & 1) ? ones : ~ones;
+    }
+    const int rank = __popcll(match & below);
+    if (id >= 0 && rank == 0) cntw[wave * E + id] = __popcll(match);
+    __syncthreads();
+    if (id >= 0) {
+      int pos = run[id] + rank;
+      for (int w = 0; w < wave; w++) pos += cntw[w * E + id];
+      perm[pos] = i;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += ROUTE_THREADS) {
+      int add = 0;
+      for (int w = 0; w < ROUTE_WAVES; w++) add += cntw[w * E + e];
+      run[e] += add;
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int MX_THREADS = 256;
+constexpr int MX_MS = 4;                    // 32-row entry subtiles per pass
+constexpr int MX_ROWS = 32 * MX_MS;         // entries per pass
+constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t);  // 55,296 B
+
+// Grouped matrix-core kernel. Workgroup (tile, e), for the entries
+// perm[offsets[e] ..] of expert e in passes of 128:
+//   GATEUP: A = x rows (token = entry / top_k), K = H; weight tile = gate rows
+//           f0 .. f0+127 and up rows F+f0 .. of W13[e]; hb[entry][f] = bf16 of
+//           silu(g) * u.
+//   DOWN:   A = hb rows (by entry), K = F; weight tile = rows r0 .. r0+255 of
+//           W2[e]; o[entry][r] fp32.
+// Per stage of 64 K: each thread loads and decodes one weight row into LDS
+// and 64 bytes of the A tile; the loads of the next stage are in flight during
+// the MFMAs of this one. Wave w owns weight columns (GATEUP) gate 32w .. and
+// up 32w .. (so g and u of one (entry, f) share a lane), or (DOWN) 64w ..
+// 64w+63; every wave covers all entry subtiles of the pass.
+template <bool GATEUP>
+__global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
+    const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int K,
+    int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t msm[];
+  uint16_t *sw = msm;                     // [256][TILE_LROW] weight rows (bf16)
+  uint16_t *sa = msm + 256 * TILE_LROW;   // [MX_ROWS][TILE_LROW] A rows (bf16)
+  const int e = blockIdx.y;
+  const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+  if (cnt == 0) return;
+  const int nbk = K / QK, stages = K / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int wrow;
+  if constexpr (GATEUP) {
+    const int f0 = blockIdx.x * 128;
+    wrow = tid < 128 ? f0 + tid : F + f0 + (tid - 128);
+  } else {
+    wrow = blockIdx.x * 256 + tid;
+  }
+  const uint8_t *wr = wq + ((int64_t)e * NR + wrow) * nbk * Q4K_BYTES;
+  // B operand rows of this lane's two 32-column tiles, A operand k offset
+  const int brow0 = GATEUP ? 32 * wave + (lane & 31) : 64 * wave + (lane & 31);
+  const int brow1 = GATEUP ? 128 + 32 * wave + (lane & 31) : 64 * wave + 32 + (lane & 31);
+  const int koff = 8 * (lane >> 5);
+
+  for (int p0 = 0; p0 < cnt; p0 += MX_ROWS) {
+    const int rows = min(MX_ROWS, cnt - p0);
+    const int ms = (rows + 31) >> 5;
+    // A chunks of this thread: row q/8, 16-byte column q%8 for q = tid + 256j
+    const uint16_t *arow[4];
+    bool alive[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int r = (tid + 256 * j) >> 3;
+      alive[j] = r < rows;
+      const int ent = perm[beg + p0 + (alive[j] ? r : 0)];
+      arow[j] = a_src + (int64_t)(GATEUP ? ent / top_k : ent) * K + 8 * ((tid + 256 * j) & 7);
+    }
+    f32x16 acc[MX_MS][2];
+#pragma unroll
+    for (int i = 0; i < MX_MS; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    auto load_w = [&](WRegs &r, int st) {
+      const uint8_t *blk = wr + (st >> 2) * Q4K_BYTES;
+      r.hdr = *(const u32x4 *)blk;
+      r.qa = *(const u32x4 *)(blk + 16 + 32 * (st & 3));
+      r.qb = *(const u32x4 *)(blk + 32 + 32 * (st & 3));
+    };
+    auto load_a = [&](u32x4 (&ra)[4], int st) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) ra[j] = *(const u32x4 *)(arow[j] + 64 * st);
+    };
+    WRegs wcur;
+    u32x4 acur[4];
+    load_w(wcur, 0);
+    load_a(acur, 0);
+    for (int st = 0; st < stages; st++) {
+      __syncthreads();  // the previous stage's MFMAs are done with LDS
+      {
+        const RowScales sc = row_scales(wcur, true, st & 3);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) store_w_part(wcur, sc, kk, sw);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int q = tid + 256 * j;
+          *(u32x4 *)(sa + (q >> 3) * TILE_LROW + 8 * (q & 7)) =
+              alive[j] ? acur[j] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      const int nx = min(st + 1, stages - 1);  // next stage (the last one reloads itself)
+      load_w(wcur, nx);
+      load_a(acur, nx);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        const bf16x8 b0 = *(const bf16x8 *)(sw + brow0 * TILE_LROW + 16 * kk + koff);
+        const bf16x8 b1 = *(const bf16x8 *)(sw + brow1 * TILE_LROW + 16 * kk + koff);
+#pragma unroll
+        for (int i = 0; i < MX_MS; i++) {
+          if (i < ms) {  // uniform
+            const bf16x8 a = *(const bf16x8 *)(sa + (32 * i + (lane & 31)) * TILE_LROW + 16 * kk + koff);
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // epilogue: lane holds column (lane & 31) of each 32-column tile and rows
+    // 32i + 8(v/4) + 4(lane/32) + v%4
+#pragma unroll
+    for (int i = 0; i < MX_MS; i++) {
+      if (i < ms) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (r < rows) {
+            const int ent = perm[beg + p0 + r];
+            if constexpr (GATEUP) {
+              const float g = acc[i][0][v], u = acc[i][1][v];
+              const float hv = g / (1.0f + expf(-g)) * u;
+              hb[(int64_t)ent * F + blockIdx.x * 128 + 32 * wave + (lane & 31)] =
+                  (uint16_t)f32_to_bf16_rne(hv);
+            } else {
+              float *orow = o + (int64_t)ent * H + blockIdx.x * 256 + 64 * wave + (lane & 31);
+              orow[0] = acc[i][0][v];
+              orow[32] = acc[i][1][v];
+            }
+          }
+        }
+      }
+    }
+  }
 }
 
 }  // namespace
 
-// Workspace: h [n][F] and o [n][H] (fp32, by entry) of the decode regime,
-// then the regions of the matrix-core regime.
-size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) {
+// Workspace: o [n][H] fp32 by entry (both regimes), then h [n][F] fp32 by
+// entry (decode) and offsets [E+1], perm [n], hb [n][F] bf16 by entry
+// (matrix cores).
+struct MoeWs {
+  float *o, *h;
+  int32_t *offsets, *perm;
+  uint16_t *hb;
+  size_t total;
+};
+
+MoeWs carve(void *base, int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) {
   const int64_t n = T * top_k;
-  return align256(sizeof(float) * n * F) + align256(sizeof(float) * n * H) +
-         carve(nullptr, T, E, top_k, H, F).total;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return (char *)base + at;
+  };
+  MoeWs ws;
+  ws.o = (float *)take(sizeof(float) * n * H);
+  ws.h = (float *)take(sizeof(float) * n * F);
+  ws.offsets = (int32_t *)take(sizeof(int32_t) * (E + 1));
+  ws.perm = (int32_t *)take(sizeof(int32_t) * n);
+  ws.hb = (uint16_t *)take(sizeof(uint16_t) * n * F);
+  ws.total = off;
+  return ws;
+}
+
+size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) {
+  return carve(nullptr, T, E, top_k, H, F).total;
 }
 
 // Entries processed per pass by the decode kernels, or 0 if the decode regime
@@ -677,46 +689,35 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
                     const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                     int64_t F, void *workspace, hipStream_t s) {
   const int64_t n64 = T * top_k;
-  char *base = (char *)workspace;
-  float *hbuf = (float *)base;
-  float *obuf = (float *)((char *)hbuf + align256(sizeof(float) * n64 * F));
+  const MoeWs ws = carve(workspace, T, E, top_k, H, F);
   size_t lds1 = 0, lds2 = 0;
   switch (dec_mt(T, n64, H, F, lds1, lds2)) {
-    case 8: launch_dec<8>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, hbuf, obuf, lds1, lds2, s); return;
-    case 4: launch_dec<4>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, hbuf, obuf, lds1, lds2, s); return;
-    case 2: launch_dec<2>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, hbuf, obuf, lds1, lds2, s); return;
-    case 1: launch_dec<1>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, hbuf, obuf, lds1, lds2, s); return;
+    case 8: launch_dec<8>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
+    case 4: launch_dec<4>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
+    case 2: launch_dec<2>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
+    case 1: launch_dec<1>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
     default: break;
   }
-  const MoeWs ws = carve((char *)obuf + align256(sizeof(float) * n64 * H), T, E, top_k, H, F);
-  const int n = (int)(T * top_k);
-  const size_t route_lds = sizeof(int32_t) * 2 * E;
+  const int n = (int)n64;
+  const size_t route_lds = sizeof(int32_t) * (1 + ROUTE_WAVES) * E;
+  (void)hipFuncSetAttribute((const void *)moe_route_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, s, ids, n,
-                     (int)E, ws.counts, ws.offsets, ws.active, ws.meta, ws.perm, ws.pos);
-  const int e_cap = (int)(E < n ? E : n);
-
-  // gate+up: rows 2F, K = H
-  {
-    const int nb = (int)(H / QK), G = gcd16(nb), R = 16 / G;
-    const int rows_wg = MOE_WAVES * R;
-    const dim3 grid((unsigned)((2 * F + rows_wg - 1) / rows_wg), (unsigned)e_cap);
-    hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(MOE_GEMV_THREADS), 0, s,
-                       (const uint8_t *)w13, (int64_t)2 * F * nb * Q4K_BYTES, (int)(2 * F),
-                       (int)H, x, ws.perm, (int)top_k, ws.offsets, ws.active, ws.meta, ws.u, G);
-  }
-  hipLaunchKernelGGL(moe_swiglu_kernel, dim3(1024), dim3(256), 0, s, ws.u, ws.h, ws.offsets,
-                     (int)E, (int)F);
-  // down: rows H, K = F
-  {
-    const int nb = (int)(F / QK), G = gcd16(nb), R = 16 / G;
-    const int rows_wg = MOE_WAVES * R;
-    const dim3 grid((unsigned)((H + rows_wg - 1) / rows_wg), (unsigned)e_cap);
-    hipLaunchKernelGGL(moe_gemv_kernel<false>, grid, dim3(MOE_GEMV_THREADS), 0, s,
-                       (const uint8_t *)w2, (int64_t)H * nb * Q4K_BYTES, (int)H, (int)F, ws.h,
-                       ws.perm, (int)top_k, ws.offsets, ws.active, ws.meta, ws.o, G);
-  }
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(1024), dim3(256), 0, s, ws.o, ws.pos, gw, y,
-                     (int)T, (int)top_k, (int)H);
+                     (int)E, ws.offsets, ws.perm);
+  auto k1 = moe_mfma_kernel<true>;
+  auto k2 = moe_mfma_kernel<false>;
+  (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
+  (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
+  hipLaunchKernelGGL(k1, dim3((unsigned)(F / 128), (unsigned)E), dim3(MX_THREADS), MX_LDS, s,
+                     (const uint16_t *)x, (const uint8_t *)w13, ws.offsets, ws.perm, (int)top_k,
+                     (int)H, (int)F, (int)(2 * F), ws.hb, (float *)nullptr, (int)H);
+  hipLaunchKernelGGL(k2, dim3((unsigned)(H / 256), (unsigned)E), dim3(MX_THREADS), MX_LDS, s,
+                     (const uint16_t *)ws.hb, (const uint8_t *)w2, ws.offsets, ws.perm,
+                     (int)top_k, (int)F, (int)F, (int)H, (uint16_t *)nullptr, ws.o, (int)H);
+  const int64_t total = T * H;
+  hipLaunchKernelGGL(moe_combine_entries_kernel,
+                     dim3((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)),
+                     dim3(256), 0, s, ws.o, ids, gw, y, (int)T, (int)top_k, (int)E, (int)H);
 }
 
 }  // namespace qdm

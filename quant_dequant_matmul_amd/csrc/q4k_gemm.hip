@@ -43,22 +43,20 @@
 // 8*(r/4) + 4*(l/32) + r%4.
 #include "common.h"
 #include "launch.h"
+#include "q4k_tile.h"
 
 namespace qdm {
 
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LROW = BK + 8;  // bf16 per LDS row (144 bytes)
+constexpr int LROW = TILE_LROW;  // bf16 per LDS row (144 bytes)
 constexpr int GEMM_THREADS = 256;
 constexpr int TILE_ELEMS = BM * LROW;  // per operand and stage (BM == BN)
 
 
 struct XRegs {
   u32x4 v[8];  // x tile: 8 x 16 bytes per thread
-};
-struct WRegs {
-  u32x4 hdr, qa, qb;  // this thread's W row: block header and 32 code bytes
 };
 static_assert(BM == BN && BM == GEMM_THREADS, "one W row per thread");
 
@@ -114,54 +112,6 @@ __device__ __forceinline__ void store_x(const XRegs &r, uint16_t *sx, int M, int
       *(u32x4 *)(sx + row * LROW + (q & 7) * 8) = v;
     }
   }
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Scales of the stage's two sub-blocks for this thread's W row.
-struct RowScales {
-  float a0, b0, a1, b1;
-};
-
-__device__ __forceinline__ RowScales row_scales(const WRegs &r, bool live, int c) {
-  const float d = live ? half_bits_to_float(r.hdr.x) : 0.f;
-  const float dmin = live ? half_bits_to_float(r.hdr.x >> 16) : 0.f;
-  uint32_t sc0, m0s, sc1, m1s;
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c, sc0, m0s);
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c + 1, sc1, m1s);
-  return RowScales{d * (float)sc0, dmin * (float)m0s, d * (float)sc1, dmin * (float)m1s};
-}
-
-// Part kk (0..3) of a W row's decode: code dwords 2kk, 2kk+1, i.e. positions
-// 8kk .. 8kk+7 of both sub-blocks, stored as bf16 into the row's LDS slots.
-__device__ __forceinline__ void store_w_part(const WRegs &r, const RowScales &sc, int kk,
-                                             uint16_t *sw) {
-  const uint32_t qd[2] = {kk < 2 ? r.qa[2 * kk] : r.qb[2 * kk - 4],
-                          kk < 2 ? r.qa[2 * kk + 1] : r.qb[2 * kk - 3]};
-  uint32_t lo[4], hi[4];
-  // an opaque mask keeps the nibbles byte-aligned, so each code converts with
-  // one v_cvt_f32_ubyteN instead of a field extract plus a conversion
-  uint32_t nib = 0x0F0F0F0Fu;
-  asm volatile("" : "+v"(nib));
-#pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const uint32_t l4 = qd[u] & nib, h4 = (qd[u] >> 4) & nib;
-    lo[2 * u] = pack_bf16(sc.a0 * (float)(l4 & 255u) - sc.b0,
-                          sc.a0 * (float)((l4 >> 8) & 255u) - sc.b0);
-    lo[2 * u + 1] = pack_bf16(sc.a0 * (float)((l4 >> 16) & 255u) - sc.b0,
-                              sc.a0 * (float)(l4 >> 24) - sc.b0);
-    hi[2 * u] = pack_bf16(sc.a1 * (float)(h4 & 255u) - sc.b1,
-                          sc.a1 * (float)((h4 >> 8) & 255u) - sc.b1);
-    hi[2 * u + 1] = pack_bf16(sc.a1 * (float)((h4 >> 16) & 255u) - sc.b1,
-                              sc.a1 * (float)(h4 >> 24) - sc.b1);
-  }
-  uint16_t *dst = sw + threadIdx.x * LROW;
-  *(u32x4 *)(dst + 8 * kk) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-  *(u32x4 *)(dst + 32 + 8 * kk) = u32x4{hi[0], hi[1], hi[2], hi[3]};
 }
 
 // One stage of MFMAs from LDS buffer (sx, swb), with the W decode of the next
