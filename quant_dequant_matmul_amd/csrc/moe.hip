@@ -475,30 +475,35 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
 }
 
 constexpr int MX_THREADS = 256;
-constexpr int MX_MS = 4;                    // 32-row entry subtiles per pass
+constexpr int MX_MS = 2;                    // 32-row entry subtiles per pass
 constexpr int MX_ROWS = 32 * MX_MS;         // entries per pass
-constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t);  // 55,296 B
+constexpr int MX_AJ = MX_ROWS * 8 / MX_THREADS;  // 16-byte A chunks per thread and stage
+constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t) +
+                          MX_ROWS * sizeof(int32_t);  // 46,336 B: two workgroups per CU
 
 // Grouped matrix-core kernel. Workgroup (tile, e), for the entries
-// perm[offsets[e] ..] of expert e in passes of 128:
+// perm[offsets[e] ..] of expert e in passes of MX_ROWS:
 //   GATEUP: A = x rows (token = entry / top_k), K = H; weight tile = gate rows
 //           f0 .. f0+127 and up rows F+f0 .. of W13[e]; hb[entry][f] = bf16 of
 //           silu(g) * u.
 //   DOWN:   A = hb rows (by entry), K = F; weight tile = rows r0 .. r0+255 of
 //           W2[e]; o[entry][r] fp32.
-// Per stage of 64 K: each thread loads and decodes one weight row into LDS
-// and 64 bytes of the A tile; the loads of the next stage are in flight during
-// the MFMAs of this one. Wave w owns weight columns (GATEUP) gate 32w .. and
-// up 32w .. (so g and u of one (entry, f) share a lane), or (DOWN) 64w ..
-// 64w+63; every wave covers all entry subtiles of the pass.
+// Per stage of 64 K each thread decodes one weight row into LDS and stores
+// its share of the A tile; the global loads of the next two stages are in
+// flight meanwhile (two register sets), and two workgroups share a compute
+// unit, so one decodes while the other multiplies. Wave w owns weight
+// columns (GATEUP) gate 32w .. and up 32w .. (g and u of one (entry, f) then
+// share a lane), or (DOWN) 64w .. 64w+63; every wave covers all entry
+// subtiles of the pass.
 template <bool GATEUP>
-__global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
+__global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int K,
     int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
   extern __shared__ __attribute__((aligned(16))) uint16_t msm[];
-  uint16_t *sw = msm;                     // [256][TILE_LROW] weight rows (bf16)
-  uint16_t *sa = msm + 256 * TILE_LROW;   // [MX_ROWS][TILE_LROW] A rows (bf16)
+  uint16_t *sw = msm;                       // [256][TILE_LROW] weight rows (bf16)
+  uint16_t *sa = msm + 256 * TILE_LROW;     // [MX_ROWS][TILE_LROW] A rows (bf16)
+  int32_t *sent = (int32_t *)(sa + MX_ROWS * TILE_LROW);  // [MX_ROWS] entries of the pass
   const int e = blockIdx.y;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
@@ -520,15 +525,18 @@ __global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
   for (int p0 = 0; p0 < cnt; p0 += MX_ROWS) {
     const int rows = min(MX_ROWS, cnt - p0);
     const int ms = (rows + 31) >> 5;
+    __syncthreads();  // the previous pass's epilogue is done with sent
+    if (tid < MX_ROWS) sent[tid] = perm[beg + p0 + min(tid, rows - 1)];
+    __syncthreads();
     // A chunks of this thread: row q/8, 16-byte column q%8 for q = tid + 256j
-    const uint16_t *arow[4];
-    bool alive[4];
+    const uint16_t *arow[MX_AJ];
+    bool alive[MX_AJ];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int r = (tid + 256 * j) >> 3;
-      alive[j] = r < rows;
-      const int ent = perm[beg + p0 + (alive[j] ? r : 0)];
-      arow[j] = a_src + (int64_t)(GATEUP ? ent / top_k : ent) * K + 8 * ((tid + 256 * j) & 7);
+    for (int j = 0; j < MX_AJ; j++) {
+      const int q = tid + MX_THREADS * j;
+      alive[j] = (q >> 3) < rows;
+      const int ent = sent[q >> 3];
+      arow[j] = a_src + (int64_t)(GATEUP ? ent / top_k : ent) * K + 8 * (q & 7);
     }
     f32x16 acc[MX_MS][2];
 #pragma unroll
@@ -538,36 +546,30 @@ __global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    auto load_w = [&](WRegs &r, int st) {
+    struct Stage {
+      WRegs w;
+      u32x4 a[MX_AJ];
+    };
+    auto load = [&](Stage &r, int st) {
       const uint8_t *blk = wr + (st >> 2) * Q4K_BYTES;
-      r.hdr = *(const u32x4 *)blk;
-      r.qa = *(const u32x4 *)(blk + 16 + 32 * (st & 3));
-      r.qb = *(const u32x4 *)(blk + 32 + 32 * (st & 3));
-    };
-    auto load_a = [&](u32x4 (&ra)[4], int st) {
+      r.w.hdr = *(const u32x4 *)blk;
+      r.w.qa = *(const u32x4 *)(blk + 16 + 32 * (st & 3));
+      r.w.qb = *(const u32x4 *)(blk + 32 + 32 * (st & 3));
 #pragma unroll
-      for (int j = 0; j < 4; j++) ra[j] = *(const u32x4 *)(arow[j] + 64 * st);
+      for (int j = 0; j < MX_AJ; j++) r.a[j] = *(const u32x4 *)(arow[j] + 64 * st);
     };
-    WRegs wcur;
-    u32x4 acur[4];
-    load_w(wcur, 0);
-    load_a(acur, 0);
-    for (int st = 0; st < stages; st++) {
+    auto step = [&](Stage &r, int st) {
       __syncthreads();  // the previous stage's MFMAs are done with LDS
-      {
-        const RowScales sc = row_scales(wcur, true, st & 3);
+      const RowScales sc = row_scales(r.w, true, st & 3);
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) store_w_part(wcur, sc, kk, sw);
+      for (int kk = 0; kk < 4; kk++) store_w_part(r.w, sc, kk, sw);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int q = tid + 256 * j;
-          *(u32x4 *)(sa + (q >> 3) * TILE_LROW + 8 * (q & 7)) =
-              alive[j] ? acur[j] : u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int j = 0; j < MX_AJ; j++) {
+        const int q = tid + MX_THREADS * j;
+        *(u32x4 *)(sa + (q >> 3) * TILE_LROW + 8 * (q & 7)) =
+            alive[j] ? r.a[j] : u32x4{0u, 0u, 0u, 0u};
       }
-      const int nx = min(st + 1, stages - 1);  // next stage (the last one reloads itself)
-      load_w(wcur, nx);
-      load_a(acur, nx);
+      load(r, min(st + 2, stages - 1));  // two stages ahead (the tail reloads the last)
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < 4; kk++) {
@@ -576,12 +578,21 @@ __global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < MX_MS; i++) {
           if (i < ms) {  // uniform
-            const bf16x8 a = *(const bf16x8 *)(sa + (32 * i + (lane & 31)) * TILE_LROW + 16 * kk + koff);
+            const bf16x8 a =
+                *(const bf16x8 *)(sa + (32 * i + (lane & 31)) * TILE_LROW + 16 * kk + koff);
             acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
             acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
           }
         }
       }
+    };
+    Stage ra, rb;
+    load(ra, 0);
+    load(rb, min(1, stages - 1));
+    // stages = K/64 is a multiple of 4: the loop body takes an even and an odd stage
+    for (int st = 0; st < stages; st += 2) {
+      step(ra, st);
+      step(rb, st + 1);
     }
     // epilogue: lane holds column (lane & 31) of each 32-column tile and rows
     // 32i + 8(v/4) + 4(lane/32) + v%4
@@ -592,7 +603,7 @@ __global__ __launch_bounds__(MX_THREADS) void moe_mfma_kernel(
         for (int v = 0; v < 16; v++) {
           const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (r < rows) {
-            const int ent = perm[beg + p0 + r];
+            const int ent = sent[r];
             if constexpr (GATEUP) {
               const float g = acc[i][0][v], u = acc[i][1][v];
               const float hv = g / (1.0f + expf(-g)) * u;
