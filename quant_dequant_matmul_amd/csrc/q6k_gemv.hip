@@ -120,6 +120,11 @@ __device__ __forceinline__ Q6Lane q6_load(const uint8_t *__restrict__ w, int64_t
   return L;
 }
 
+// Each workgroup stages x once and then streams row groups blockIdx.x,
+// blockIdx.x + gridDim.x, ... (a row group = Q6_WAVES * R rows). A wave walks
+// its (row group, block iteration) pairs as one flat sequence with PF of them
+// in flight, so loads run ahead across row-group boundaries. Loads are
+// unconditional (indices clamped) so the waits are exact.
 template <bool XBF16, int MT, int PF>
 __global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
     const uint8_t *__restrict__ w, const void *__restrict__ x, float *__restrict__ y, int N,
@@ -132,121 +137,134 @@ __global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
   const int g = lane >> 2, c = lane & 3;
   const int h = c >> 1, l0 = 16 * (c & 1);
   const int R = 16 / G;
-  const int row = (blockIdx.x * Q6_WAVES + wave) * R + g / G;
   const int gg = g % G;
   const int nb = K / QK;
   const int iters = nb / G;
-  const bool active = row < N;
-  const int64_t row_off = (int64_t)(active ? row : 0) * nb * Q6K_BYTES;
+  const int rows_rg = Q6_WAVES * R;
+  const int nrg = (N + rows_rg - 1) / rows_rg;
+  const int mine = (int)blockIdx.x < nrg ? (nrg - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int64_t nf = (int64_t)mine * iters;  // this wave's (row group, iteration) pairs
+  auto row_of = [&](int64_t f) {
+    const int j = (int)(f / iters);
+    return ((int)blockIdx.x + j * (int)gridDim.x) * rows_rg + wave * R + g / G;
+  };
+  auto blk_off = [&](int64_t f) {
+    const int64_t fc = f < nf ? f : nf - 1;
+    const int it = (int)(fc % iters);
+    const int row = min(row_of(fc), N - 1);
+    return ((int64_t)row * nb + it * G + gg) * Q6K_BYTES;
+  };
 
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; m++) acc[m] = 0.f;
 
   Q6Lane buf[PF];
+  if (nf > 0) {
 #pragma unroll
-  for (int p = 0; p < PF; p++)
-    if (active && p < iters) buf[p] = q6_load(w, row_off + (int64_t)(p * G + gg) * Q6K_BYTES, h, l0);
+    for (int p = 0; p < PF; p++) buf[p] = q6_load(w, blk_off(p), h, l0);
+  }
 
   q6_stage_x<XBF16, MT>(x, K, lds_x, lds_sum);
   __syncthreads();
 
-  if (active) {
-    for (int it0 = 0; it0 < iters; it0 += PF) {
+  for (int64_t f0 = 0; f0 < nf; f0 += PF) {
 #pragma unroll
-      for (int p = 0; p < PF; p++) {
-        const int it = it0 + p;
-        if (it < iters) {
-          const int kb = it * G + gg;
-          const Q6Lane L = buf[p];
-          if (it + PF < iters)
-            buf[p] = q6_load(w, row_off + (int64_t)((it + PF) * G + gg) * Q6K_BYTES, h, l0);
-          const float d = half_bits_to_float(L.dbits);
-          // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
-          // of the 8 scale bytes s0|s1.
-          const int sb = l0 >> 4;
-          float dsc[4];
+    for (int p = 0; p < PF; p++) {
+      const int64_t f = f0 + p;
+      if (f < nf) {
+        const int it = (int)(f % iters);
+        const int kb = it * G + gg;
+        const Q6Lane L = buf[p];
+        buf[p] = q6_load(w, blk_off(f + PF), h, l0);
+        const float d = half_bits_to_float(L.dbits);
+        // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
+        // of the 8 scale bytes s0|s1.
+        const int sb = l0 >> 4;
+        float dsc[4];
 #pragma unroll
-          for (int gq = 0; gq < 4; gq++) {
-            const int bi = 2 * gq + sb;
-            const uint32_t word = bi < 4 ? L.s0 : L.s1;
-            dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+        for (int gq = 0; gq < 4; gq++) {
+          const int bi = 2 * gq + sb;
+          const uint32_t word = bi < 4 ? L.s0 : L.s1;
+          dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+        }
+        const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+        const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+        const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+        if constexpr (XBF16) {
+          // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
+          uint32_t pr[4][8];
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const uint32_t a = qa[k], b = qb[k], hh = qh[k];
+            pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
+            pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
+            pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
+            pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
+            pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
+            pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
+            pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
+            pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
           }
-          const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
-          const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-          const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
-          if constexpr (XBF16) {
-            // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
-            uint32_t pr[4][8];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-              const uint32_t a = qa[k], b = qb[k], hh = qh[k];
-              pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
-              pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
-              pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
-              pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
-              pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
-              pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
-              pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
-              pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
+          for (int m = 0; m < MT; m++) {
+            float r = acc[m];
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+              const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;  // first x element
+              const u32x4 *xv = (const u32x4 *)(lds_x + e0 / 2);
+              const float xs = lds_sum[e0 / 16];
+              const u32x4 x0 = xv[0], x1 = xv[1];  // l0..l0+7, l0+8..l0+15
+              float s = 0.f;
+              s = dot2_bf16(pr[gq][0], x0.x, s);
+              s = dot2_bf16(pr[gq][1], x0.y, s);
+              s = dot2_bf16(pr[gq][2], x0.z, s);
+              s = dot2_bf16(pr[gq][3], x0.w, s);
+              s = dot2_bf16(pr[gq][4], x1.x, s);
+              s = dot2_bf16(pr[gq][5], x1.y, s);
+              s = dot2_bf16(pr[gq][6], x1.z, s);
+              s = dot2_bf16(pr[gq][7], x1.w, s);
+              r = fmaf(dsc[gq], fmaf(-160.f, xs, s), r);
             }
+            acc[m] = r;
+          }
+        } else {
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
-              float r = acc[m];
+          for (int m = 0; m < MT; m++) {
+            float r = acc[m];
 #pragma unroll
-              for (int gq = 0; gq < 4; gq++) {
-                const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;  // first x element
-                const u32x4 *xv = (const u32x4 *)(lds_x + e0 / 2);
-                const float xs = lds_sum[e0 / 16];
-                const u32x4 x0 = xv[0], x1 = xv[1];  // l0..l0+7, l0+8..l0+15
-                float s = 0.f;
-                s = dot2_bf16(pr[gq][0], x0.x, s);
-                s = dot2_bf16(pr[gq][1], x0.y, s);
-                s = dot2_bf16(pr[gq][2], x0.z, s);
-                s = dot2_bf16(pr[gq][3], x0.w, s);
-                s = dot2_bf16(pr[gq][4], x1.x, s);
-                s = dot2_bf16(pr[gq][5], x1.y, s);
-                s = dot2_bf16(pr[gq][6], x1.z, s);
-                s = dot2_bf16(pr[gq][7], x1.w, s);
-                r = fmaf(dsc[gq], fmaf(-160.f, xs, s), r);
-              }
-              acc[m] = r;
-            }
-          } else {
+            for (int gq = 0; gq < 4; gq++) {
+              const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;
+              const f32x4 *xv = (const f32x4 *)((const float *)lds_x + e0);
+              float s = 0.f;
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
-              float r = acc[m];
+              for (int k = 0; k < 4; k++) {
+                const f32x4 xx = xv[k];
+                const uint32_t src = (gq & 1) ? qb[k] : qa[k];
+                const int nsh = (gq >> 1) * 4;
 #pragma unroll
-              for (int gq = 0; gq < 4; gq++) {
-                const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;
-                const f32x4 *xv = (const f32x4 *)((const float *)lds_x + e0);
-                float s = 0.f;
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                  const f32x4 xx = xv[k];
-                  const uint32_t src = (gq & 1) ? qb[k] : qa[k];
-                  const int nsh = (gq >> 1) * 4;
-#pragma unroll
-                  for (int e = 0; e < 4; e++) {
-                    const int lo = (int)((src >> (8 * e + nsh)) & 15u);
-                    const int hi = (int)((qh[k] >> (8 * e + 2 * gq)) & 3u);
-                    s = fmaf(xx[e], (float)((lo | (hi << 4)) - 32), s);
-                  }
+                for (int e = 0; e < 4; e++) {
+                  const int lo = (int)((src >> (8 * e + nsh)) & 15u);
+                  const int hi = (int)((qh[k] >> (8 * e + 2 * gq)) & 3u);
+                  s = fmaf(xx[e], (float)((lo | (hi << 4)) - 32), s);
                 }
-                r = fmaf(dsc[gq], s, r);
               }
-              acc[m] = r;
+              r = fmaf(dsc[gq], s, r);
             }
+            acc[m] = r;
+          }
+        }
+        if (it == iters - 1) {  // uniform: the row group ends, store its rows
+          const int row = row_of(f);
+#pragma unroll
+          for (int m = 0; m < MT; m++) {
+            const float v = group_sum(acc[m], 4 * G);
+            if (row < N && (lane & (4 * G - 1)) == 0) y[(int64_t)m * ldy + row] = v;
+            acc[m] = 0.f;
           }
         }
       }
     }
-  }
-
-#pragma unroll
-  for (int m = 0; m < MT; m++) {
-    float v = group_sum(acc[m], 4 * G);
-    if (active && (lane & (4 * G - 1)) == 0) y[(int64_t)m * ldy + row] = v;
   }
 }
 
@@ -262,9 +280,15 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   const int nb = (int)(K / QK);
   const int G = gcd16(nb);
   const int R = 16 / G;
-  const int64_t rows_per_wg = (int64_t)Q6_WAVES * R;
-  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
+  const int64_t rows_per_rg = (int64_t)Q6_WAVES * R;
+  const int64_t nrg = (N + rows_per_rg - 1) / rows_per_rg;
   const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 16) * 4;
+  // as many workgroups as stay resident (x is staged once per workgroup)
+  int64_t per_cu = (int64_t)(160 * 1024 / (lds + 1024));
+  if (per_cu < 1) per_cu = 1;
+  if (per_cu > 4) per_cu = 4;
+  const int64_t want = 256 * per_cu;
+  const unsigned grid = (unsigned)(nrg < want ? nrg : want);
   constexpr int PF = 2;
   auto kern = q6k_gemv_kernel<XBF16, MT, PF>;
   if (lds > 65536) hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -145,6 +145,20 @@ def test_q6k_gemv_ragged(M, N, K, dt):
     assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_q6k_gemv_longest_k_bf16(M):
+    """K = 65536 with bf16 x: the x staging fills the whole 160 KiB of LDS."""
+    N, K = 24, 65536
+    rng = np.random.default_rng(65 + M)
+    w = synth.q6k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    say("q6k_gemv longest K", M)
+    y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, oracle.q6k_matmul(w, x, N, K))
+    say("  rel err", e)
+    assert e <= GUARD_VALU
+
+
 def test_q6k_gemv_one_hot_rows_bit_exact():
     N, K = 100, 768
     w = synth.q6k_blocks(np.random.default_rng(4), N, K)
