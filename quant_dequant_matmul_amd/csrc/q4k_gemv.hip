@@ -469,10 +469,12 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   xst.load(x, K);
   if (threadIdx.x == 0) next_span = 2 * WAVES;
   int sidx[2] = {wave, WAVES + wave};
+  // x loads, the first span, the x records, then the second span: x does not
+  // wait behind the whole initial burst of weight loads (measured fastest)
   Span R[2];
   issue(R[0], sidx[0]);
-  issue(R[1], sidx[1]);
   xst.store(K, xrec);
+  issue(R[1], sidx[1]);
   __syncthreads();
 
   const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
