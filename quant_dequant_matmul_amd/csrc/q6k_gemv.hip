@@ -28,17 +28,15 @@ namespace qdm {
 
 namespace {
 
-constexpr int Q6_THREADS = 256;
-constexpr int Q6_WAVES = Q6_THREADS / WAVE;
 
-template <bool XBF16, int MT>
+template <bool XBF16, int MT, int THREADS>
 __device__ __forceinline__ void q6_stage_x(const void *__restrict__ x, int K, uint32_t *lds_x,
                                            float *lds_sum) {
   const int tid = threadIdx.x;
   if constexpr (XBF16) {
     const int nchunk = MT * K / 8;  // 8 bf16 per chunk, 2 chunks per 16-sum
     const u32x4 *src = (const u32x4 *)x;
-    for (int base = 0; base < nchunk; base += Q6_THREADS) {
+    for (int base = 0; base < nchunk; base += THREADS) {
       const int c = base + tid;
       float s = 0.f;
       if (c < nchunk) {
@@ -60,7 +58,7 @@ __device__ __forceinline__ void q6_stage_x(const void *__restrict__ x, int K, ui
   } else {
     const int nchunk = MT * K / 4;  // 4 fp32 per chunk, 4 chunks per 16-sum
     const f32x4 *src = (const f32x4 *)x;
-    for (int base = 0; base < nchunk; base += Q6_THREADS) {
+    for (int base = 0; base < nchunk; base += THREADS) {
       const int c = base + tid;
       float s = 0.f;
       if (c < nchunk) {
@@ -121,12 +119,12 @@ __device__ __forceinline__ Q6Lane q6_load(const uint8_t *__restrict__ w, int64_t
 }
 
 // Each workgroup stages x once and then streams row groups blockIdx.x,
-// blockIdx.x + gridDim.x, ... (a row group = Q6_WAVES * R rows). A wave walks
+// blockIdx.x + gridDim.x, ... (a row group = R rows per wave). A wave walks
 // its (row group, block iteration) pairs as one flat sequence with PF of them
 // in flight, so loads run ahead across row-group boundaries. Loads are
 // unconditional (indices clamped) so the waits are exact.
-template <bool XBF16, int MT, int PF>
-__global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
+template <bool XBF16, int MT, int PF, int THREADS>
+__global__ __launch_bounds__(THREADS) void q6k_gemv_kernel(
     const uint8_t *__restrict__ w, const void *__restrict__ x, float *__restrict__ y, int N,
     int K, int G, int ldy) {
   extern __shared__ uint32_t lds[];
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
   const int gg = g % G;
   const int nb = K / QK;
   const int iters = nb / G;
-  const int rows_rg = Q6_WAVES * R;
+  const int rows_rg = (THREADS / WAVE) * R;
   const int nrg = (N + rows_rg - 1) / rows_rg;
   const int mine = (int)blockIdx.x < nrg ? (nrg - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   const int64_t nf = (int64_t)mine * iters;  // this wave's (row group, iteration) pairs
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(Q6_THREADS) void q6k_gemv_kernel(
     for (int p = 0; p < PF; p++) buf[p] = q6_load(w, blk_off(p), h, l0);
   }
 
-  q6_stage_x<XBF16, MT>(x, K, lds_x, lds_sum);
+  q6_stage_x<XBF16, MT, THREADS>(x, K, lds_x, lds_sum);
   __syncthreads();
 
   for (int64_t f0 = 0; f0 < nf; f0 += PF) {
@@ -280,7 +278,10 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   const int nb = (int)(K / QK);
   const int G = gcd16(nb);
   const int R = 16 / G;
-  const int64_t rows_per_rg = (int64_t)Q6_WAVES * R;
+  // the 8-row chunk keeps all of x for 8 rows in LDS (one workgroup per
+  // compute unit), so it runs 8 waves per workgroup for latency hiding
+  constexpr int THREADS = MT == 8 ? 512 : 256;
+  const int64_t rows_per_rg = (int64_t)(THREADS / WAVE) * R;
   const int64_t nrg = (N + rows_per_rg - 1) / rows_per_rg;
   const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 16) * 4;
   // as many workgroups as stay resident (x is staged once per workgroup)
@@ -290,9 +291,9 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   const int64_t want = 256 * per_cu;
   const unsigned grid = (unsigned)(nrg < want ? nrg : want);
   constexpr int PF = 2;
-  auto kern = q6k_gemv_kernel<XBF16, MT, PF>;
+  auto kern = q6k_gemv_kernel<XBF16, MT, PF, THREADS>;
   if (lds > 65536) hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(Q6_THREADS), lds, s, (const uint8_t *)w, x, y,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds, s, (const uint8_t *)w, x, y,
                      (int)N, (int)K, G, (int)ldy);
 }
 
@@ -306,7 +307,7 @@ void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
   while (m0 < M) {
     const int64_t rem = M - m0;
     int mt = 8;
-    while (mt > 1 && (mt > rem || (size_t)mt * per_row > 65536)) mt >>= 1;
+    while (mt > 1 && (mt > rem || (size_t)mt * per_row > 150 * 1024)) mt >>= 1;
     const void *xm = (const char *)x + (size_t)m0 * K * elt;
     float *ym = y + m0 * N;
     if (x_bf16) {
