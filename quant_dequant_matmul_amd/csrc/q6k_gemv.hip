@@ -23,6 +23,7 @@
 //   sum_l x_l (q_l - 32) = s - 160 * sum_l x_l.
 #include "common.h"
 #include "launch.h"
+#include "q4k_tile.h"  // pack_bf16
 
 namespace qdm {
 
@@ -292,15 +293,319 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   const unsigned grid = (unsigned)(nrg < want ? nrg : want);
   constexpr int PF = 2;
   auto kern = q6k_gemv_kernel<XBF16, MT, PF, THREADS>;
-  if (lds > 65536) hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 65536) (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds, s, (const uint8_t *)w, x, y,
                      (int)N, (int)K, G, (int)ldy);
+}
+
+// ---------------------------------------------------------------------------
+// M >= 2 with bf16 x: matrix cores. At M = 8 the VALU path spends 8 dot
+// products per weight and is bound by them; here every weight is decoded to
+// bf16 once, w = d * scale * (q - 32) (exact in fp32, then rounded to nearest
+// even), and v_mfma_f32_16x16x32_bf16 multiplies it with all M rows of x.
+// A wave streams tiles of 16 weight rows. Lane (s, r) = (lane / 16, lane % 16)
+// loads, for row r of the tile, the same 64-weight slice (h, l0) = (s / 2,
+// 16 (s % 2)) of each super-block that a VALU lane loads, so a wave's loads
+// cover 16 rows x whole super-blocks. Step (g, e) of a super-block, g = 0..3,
+// e = 0..1, gives the lane's weights at positions 128h + 32g + l0 + 8e + j,
+// j = 0..7, as the A operand; the B operand is x row (lane % 16) at the same
+// positions, from LDS (rows of x past M repeat row M - 1; their outputs are
+// not stored). The matrix core pairs A and B by (lane / 16, j), so any K order
+// that both sides share gives the same contraction.
+// Work split: workgroup b owns an even share of the 16-row tiles, and its
+// waves split the share's (tile, super-block) items into equal contiguous
+// ranges, so every wave streams the same number of super-blocks. A tile cut
+// by a range boundary is finished by the wave that holds its first
+// super-block: the waves that continue it publish their portion (the first
+// portion of their range) in LDS, and the first wave adds those portions in
+// wave order before it stores. Loads run Q6M_PF items ahead.
+// ---------------------------------------------------------------------------
+#ifndef QDM_Q6_MFMA_MIN_M
+#define QDM_Q6_MFMA_MIN_M 2  // smallest M (bf16 x) that takes the matrix-core kernel
+#endif
+#ifndef QDM_Q6M_WAVES_CU
+#define QDM_Q6M_WAVES_CU 12  // waves per compute unit
+#endif
+#ifndef QDM_Q6M_PF
+#define QDM_Q6M_PF 2  // super-blocks in flight per wave
+#endif
+constexpr int Q6M_PF = QDM_Q6M_PF;
+constexpr size_t Q6M_FLAGS = 256;  // flag words, padded
+constexpr int Q6M_SPIN_LIMIT = 1 << 24;
+
+__host__ __device__ constexpr size_t q6m_head_bytes(int waves) {
+  return (size_t)waves * WAVE * sizeof(f32x4) + Q6M_FLAGS;
+}
+
+__device__ __forceinline__ uint32_t q6m_codes(uint32_t ql, uint32_t qh, int g) {
+  // four 6-bit codes of group g as bytes: low nibble (g < 2) or high nibble of
+  // ql, and bits 2g, 2g + 1 of qh as bits 4, 5
+  const uint32_t lo = g < 2 ? ql : ql >> 4;
+  const uint32_t hi = g == 0 ? qh << 4 : g == 1 ? qh << 2 : g == 2 ? qh : qh >> 2;
+  return (lo & 0x0F0F0F0Fu) | (hi & 0x30303030u);
+}
+
+// A lane's slice (h, l0) of one super-block as loaded: aligned dwords only,
+// so the loads stay in flight until the slice is decoded. The super-block
+// starts at an even byte offset; every field the slice reads starts at the
+// same offset mod 4, so one shift (0 or 2 bytes) realigns them all.
+struct Q6Raw {
+  u32x4 qa, qb, qh;           // 16 B from the dword holding QL[64h+l0], QL[64h+32+l0], QH[32h+l0]
+  uint32_t qa4, qb4, qh4;     // the dword after each
+  uint32_t sc0, sc1, sc2;     // dwords covering scale bytes 8h .. 8h+7
+  uint32_t dbits, sh;
+};
+
+__device__ __forceinline__ Q6Raw q6_load_raw(const uint8_t *__restrict__ w, int64_t blk_off,
+                                             int h, int l0) {
+  Q6Raw R;
+  const int64_t a = blk_off & ~(int64_t)3;
+  const int64_t fa = a + 64 * h + l0, fb = fa + 32, fh = a + 128 + 32 * h + l0;
+  R.qa = *(const u32x4_a4 *)(w + fa);
+  R.qa4 = *(const uint32_t *)(w + fa + 16);
+  R.qb = *(const u32x4_a4 *)(w + fb);
+  R.qb4 = *(const uint32_t *)(w + fb + 16);
+  R.qh = *(const u32x4_a4 *)(w + fh);
+  R.qh4 = *(const uint32_t *)(w + fh + 16);
+  // scale bytes [so, so + 8): dwords at so & ~3, +4, and (so + 6) & ~3, which
+  // is the third dword when so is 2 mod 4 and a re-read of the second
+  // otherwise (never past the super-block)
+  const int64_t so = blk_off + 192 + 8 * h;
+  typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+  const u32x2_a4 s01 = *(const u32x2_a4 *)(w + (so & ~(int64_t)3));
+  R.sc0 = s01.x;
+  R.sc1 = s01.y;
+  R.sc2 = *(const uint32_t *)(w + ((so + 6) & ~(int64_t)3));
+  R.dbits = *(const uint16_t *)(w + blk_off + 208);
+  R.sh = (uint32_t)(blk_off & 2);
+  return R;
+}
+
+__device__ __forceinline__ Q6Lane q6_finish(const Q6Raw &R) {
+  Q6Lane L;
+  auto al = [&](const u32x4 &v, uint32_t n) {
+    return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, R.sh), __builtin_amdgcn_alignbyte(v.z, v.y, R.sh),
+                 __builtin_amdgcn_alignbyte(v.w, v.z, R.sh), __builtin_amdgcn_alignbyte(n, v.w, R.sh)};
+  };
+  L.qa = al(R.qa, R.qa4);
+  L.qb = al(R.qb, R.qb4);
+  L.qh = al(R.qh, R.qh4);
+  L.s0 = __builtin_amdgcn_alignbyte(R.sc1, R.sc0, R.sh);
+  L.s1 = __builtin_amdgcn_alignbyte(R.sc2, R.sc1, R.sh);
+  L.dbits = R.dbits;
+  return L;
+}
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__restrict__ w,
+                                                           const uint16_t *__restrict__ x,
+                                                           float *__restrict__ y, int M, int N,
+                                                           int K, int xs) {
+  constexpr int WAVES = THREADS / WAVE;
+  extern __shared__ __attribute__((aligned(16))) uint8_t q6m_smem[];
+  f32x4 *part = (f32x4 *)q6m_smem;                                   // [WAVES][64]
+  int *flag = (int *)(q6m_smem + (size_t)WAVES * WAVE * sizeof(f32x4));  // [WAVES]
+  uint16_t *xl = (uint16_t *)(q6m_smem + q6m_head_bytes(WAVES));    // [M][xs] bf16
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform ranges
+  const int nb = K / QK;
+  const int tiles = (N + 15) / 16;
+  const int tq = tiles / (int)gridDim.x, tr = tiles % (int)gridDim.x;
+  const int bid = blockIdx.x;
+  const int t0 = bid * tq + min(bid, tr);
+  const int items = (tq + (bid < tr ? 1 : 0)) * nb;  // >= nb: every workgroup has a tile
+  auto start_of = [&](int v) { return (int)((int64_t)items * v / WAVES); };
+  const int i0 = start_of(wave), i1 = start_of(wave + 1);
+  const int s = lane >> 4, r = lane & 15;
+  const int h = s >> 1, l0 = 16 * (s & 1);
+
+  if (tid < WAVES) flag[tid] = 0;
+  auto load = [&](int i) {
+    const int ic = max(min(i, i1 - 1), 0);  // past the range: a valid dummy
+    const int tl = ic / nb;
+    const int row = min((t0 + tl) * 16 + r, N - 1);
+    return q6_load_raw(w, ((int64_t)row * nb + (ic - tl * nb)) * Q6K_BYTES, h, l0);
+  };
+  // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
+  // apart), eight 16-byte loads in flight per thread; the first batch of x
+  // loads goes out before the first weight loads, so its stores wait for x only
+  const int cpr = K / 8, total = M * cpr;
+  u32x4 xv[8];
+  auto x_load = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int c = min(base + j * THREADS + tid, total - 1);
+      const int m = c / cpr;
+      xv[j] = *(const u32x4 *)(x + (int64_t)m * K + 8 * (c - m * cpr));
+    }
+  };
+  auto x_store = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      // unconditional: a clamped chunk rewrites the last chunk with its own value
+      const int c = min(base + j * THREADS + tid, total - 1);
+      const int m = c / cpr;
+      *(u32x4 *)(xl + m * xs + 8 * (c - m * cpr)) = xv[j];
+    }
+  };
+  x_load(0);
+  Q6Raw buf[Q6M_PF];
+#pragma unroll
+  for (int p = 0; p < Q6M_PF; p++) buf[p] = load(i0 + p);
+  x_store(0);
+  for (int base = 8 * THREADS; base < total; base += 8 * THREADS) {
+    x_load(base);
+    x_store(base);
+  }
+  __syncthreads();
+
+  const uint16_t *xb = xl + min(r, M - 1) * xs + 128 * h + l0;
+  // two accumulators (steps e = 0 and e = 1) halve the MFMA dependency chain
+  f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // one item: decode the slice, 8 MFMAs; at the end of this wave's portion of
+  // a tile, publish it or complete and store the tile
+  auto item = [&](int ii, Q6Raw &slot, bool reload) {
+    const Q6Lane L = q6_finish(slot);
+    const int tl = ii / nb, b = ii - tl * nb;
+
+    const float d = half_bits_to_float(L.dbits);
+    const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+    const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+    const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+    const uint16_t *xk = xb + b * QK;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      // scale of sub-block 8h + 2g + l0/16: byte 2g + l0/16 of s0|s1
+      const int bi = 2 * g + (l0 >> 4);
+      const uint32_t word = bi < 4 ? L.s0 : L.s1;
+      const float ds = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+      const float nds = -32.f * ds;
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++) {
+          const int k = 2 * e + k2;
+          const uint32_t c4 = q6m_codes((g & 1) ? qb[k] : qa[k], qh[k], g);
+          pk[2 * k2] = pack_bf16(fmaf((float)(c4 & 255u), ds, nds),
+                                 fmaf((float)((c4 >> 8) & 255u), ds, nds));
+          pk[2 * k2 + 1] = pack_bf16(fmaf((float)((c4 >> 16) & 255u), ds, nds),
+                                     fmaf((float)(c4 >> 24), ds, nds));
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const bf16x8 bv = *(const bf16x8 *)(xk + 32 * g + 8 * e);
+        acc2[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc2[e], 0, 0, 0);
+      }
+    }
+    if (reload) slot = load(ii + Q6M_PF);
+
+    if (b == nb - 1 || ii == i1 - 1) {  // end of this wave's portion of a tile
+      f32x4 acc = acc2[0] + acc2[1];
+      const int tstart = tl * nb;
+      if (tstart < i0) {
+        // the tile began in an earlier wave's range: publish the portion
+        part[wave * WAVE + lane] = acc;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __hip_atomic_store(&flag[wave], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        // the rest of the tile is the first portion of the next ranges
+        for (int v = wave + 1; v < WAVES && start_of(v) < tstart + nb; v++) {
+          if (start_of(v) == start_of(v + 1)) continue;  // empty range
+          int spins = 0;
+          while (__hip_atomic_load(&flag[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+                     0 &&
+                 spins < Q6M_SPIN_LIMIT) {
+            __builtin_amdgcn_s_sleep(1);
+            spins++;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          const f32x4 o = part[v * WAVE + lane];
+          acc += o;
+          if (spins >= Q6M_SPIN_LIMIT) acc = f32x4{NAN, NAN, NAN, NAN};
+        }
+        // lane holds column m = lane % 16 and rows 4 (lane / 16) + q of the tile
+        const int m = lane & 15;
+        if (m < M) {
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = (t0 + tl) * 16 + 4 * s + q;
+            if (n < N) y[(int64_t)m * N + n] = acc[q];
+          }
+        }
+      }
+      acc2[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc2[1] = acc2[0];
+    }
+  };
+  // whole groups of Q6M_PF items run with every load unconditional, so each
+  // wait is for exactly one item's loads; then the last partial group
+  int i = i0;
+  for (; i + Q6M_PF <= i1; i += Q6M_PF) {
+#pragma unroll
+    for (int p = 0; p < Q6M_PF; p++) item(i + p, buf[p], true);
+  }
+#pragma unroll
+  for (int p = 0; p < Q6M_PF; p++)
+    if (i + p < i1) item(i + p, buf[p], false);
+}
+
+template <int THREADS>
+void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t N, int64_t K,
+                    size_t lds, int per_cu, hipStream_t s) {
+  const int64_t tiles = (N + 15) / 16;
+  int64_t grid = 256 * per_cu;
+  if (grid > tiles) grid = tiles;  // every workgroup owns at least one tile
+  auto kern = q6k_mfma_kernel<THREADS>;
+  (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), lds, s, (const uint8_t *)w, x,
+                     y, mc, (int)N, (int)K, (int)(K + 8));
+}
+
+// Rows of x in chunks whose padded LDS copy fits; each chunk streams all
+// weights. 12 waves per compute unit (3 per SIMD, as many as the registers
+// allow): 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
+void launch_q6k_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                     int64_t K, hipStream_t s) {
+  constexpr size_t LDS_CU = 160 * 1024, SLACK = 512;  // SLACK: static LDS, rounding
+  const size_t row_bytes = (size_t)(K + 8) * 2;
+  const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
+  const int64_t cap = (int64_t)(x_cap / row_bytes);  // >= 2 for K <= 65536
+  const int64_t chunks = (M + cap - 1) / cap;
+  const int64_t base = M / chunks, extra = M % chunks;
+  int64_t m0 = 0;
+  for (int64_t c = 0; c < chunks; c++) {
+    const int mc = (int)(base + (c < extra ? 1 : 0));
+    const size_t xb = (size_t)mc * row_bytes;
+    const uint16_t *xm = x + m0 * K;
+    float *ym = y + m0 * N;
+#if QDM_Q6M_WAVES_CU == 16
+    if (4 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
+      launch_q6_mfma<256>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 4, s);
+    else if (2 * (xb + q6m_head_bytes(8) + SLACK) <= LDS_CU)
+      launch_q6_mfma<512>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(8), 2, s);
+    else
+      launch_q6_mfma<1024>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(16), 1, s);
+#else
+    if (3 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
+      launch_q6_mfma<256>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 3, s);
+    else if (2 * (xb + q6m_head_bytes(6) + SLACK) <= LDS_CU)
+      launch_q6_mfma<384>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(6), 2, s);
+    else
+      launch_q6_mfma<768>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(12), 1, s);
+#endif
+    m0 += mc;
+  }
 }
 
 }  // namespace
 
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
+  if (x_bf16 && M >= QDM_Q6_MFMA_MIN_M) {
+    launch_q6k_mfma(w, (const uint16_t *)x, y, M, N, K, s);
+    return;
+  }
   const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 16) * 4;
   const size_t elt = x_bf16 ? 2 : 4;
   int64_t m0 = 0;

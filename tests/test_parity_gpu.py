@@ -129,7 +129,8 @@ def test_q4k_gemv_power_of_two_scaling(dt):
 # --------------------------------------------------------------------------
 
 Q6_CASES = [(1, 16, 256), (1, 37, 768), (8, 129, 1280), (3, 1000, 5120), (16, 40, 2304),
-            (5, 77, 17408), (1, 4097, 512)]
+            (5, 77, 17408), (1, 4097, 512), (2, 513, 1024), (16, 300, 512),
+            (4, 4096, 256)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -142,12 +143,20 @@ def test_q6k_gemv_ragged(M, N, K, dt):
     y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
     ref = oracle.q6k_matmul(w, x, N, K)
     e = rel_err(y, ref)
-    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+    assert e <= (TOL_F32 if dt == "f32" else q6k_bf16_tol(M)), e
+
+
+def q6k_bf16_tol(M):
+    """bf16 x: M = 1 runs the fp32-accumulating VALU kernel, far inside the bf16
+    bar; M >= 2 runs the matrix-core kernel (weights rounded to bf16), held to
+    the bf16 bar itself."""
+    return min(TOL_BF16, GUARD_VALU) if M == 1 else TOL_BF16
 
 
 @pytest.mark.parametrize("M", [1, 3])
 def test_q6k_gemv_longest_k_bf16(M):
-    """K = 65536 with bf16 x: the x staging fills the whole 160 KiB of LDS."""
+    """K = 65536 with bf16 x (at M = 1 the x staging fills the whole 160 KiB of
+    LDS; at M = 3 the matrix-core kernel walks 1024 K stages)."""
     N, K = 24, 65536
     rng = np.random.default_rng(65 + M)
     w = synth.q6k_blocks(rng, N, K)
@@ -156,7 +165,7 @@ def test_q6k_gemv_longest_k_bf16(M):
     y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
     e = rel_err(y, oracle.q6k_matmul(w, x, N, K))
     say("  rel err", e)
-    assert e <= GUARD_VALU
+    assert e <= q6k_bf16_tol(M)
 
 
 def test_q6k_gemv_one_hot_rows_bit_exact():
@@ -184,7 +193,7 @@ def test_q6k_gemv_head_full_sampled(M):
     ref = oracle.q6k_matmul(w[rows], x, len(rows), K)
     e = rel_err(y[:, rows], ref)
     say("  rel err", e)
-    assert e <= min(TOL_BF16, GUARD_VALU)
+    assert e <= q6k_bf16_tol(M)
 
 
 def test_q6k_gemv_down_full():
@@ -411,6 +420,11 @@ def test_determinism_all_entry_points():
     xg = dev_x(synth.normal_bf16(rng, (300, K)))
     say("determinism gemm")
     a, b = host(qdm.q4k_gemm(w, xg, N, K)), host(qdm.q4k_gemm(w, xg, N, K))
+    assert np.array_equal(a, b)
+    w6 = dev_bytes(synth.q6k_blocks(rng, 1000, K))
+    x6 = dev_x(synth.normal_bf16(rng, (8, K)))
+    say("determinism q6k M=8 (matrix cores, tiles split across waves)")
+    a, b = host(qdm.q6k_gemv(w6, x6, 1000, K)), host(qdm.q6k_gemv(w6, x6, 1000, K))
     assert np.array_equal(a, b)
     for T in (8, 64):  # decode and matrix-core regimes
         d = synth.moe(T)
