@@ -323,6 +323,14 @@ struct Span {
   u32x4 r[9];
 };
 
+// A full span: 9 KiB from one base, chunk j at byte 1024 j + 16 lane.
+__device__ __forceinline__ void load_span_full(Span &sp, const uint8_t *__restrict__ base,
+                                               int lane) {
+  const uint8_t *p = base + 16 * lane;
+#pragma unroll
+  for (int j = 0; j < 9; j++) sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(p + 1024 * j));
+}
+
 // Loads are unconditional so the compiler can count outstanding loads and
 // wait for exactly the span it needs (a load behind a branch forces it to wait
 // for every load in flight). Chunks past the end of a partial span re-read the
@@ -449,15 +457,21 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   const int nblk = (r1 - r0) * nb;
   const int nspan = (nblk + DN_SPAN - 1) / DN_SPAN;
   const uint8_t *wbase = w + (int64_t)r0 * nb * Q4K_BYTES;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // span indices stay scalar
+  const int nfull = nblk / DN_SPAN;  // spans before nfull are full
 
   // A span index past the end loads the last span again (its bytes are
   // already on their way), so every wave issues the same loads in every
-  // iteration and the compiler can wait for exactly the span it needs.
+  // iteration and the compiler can wait for exactly the span it needs. Both
+  // branches issue the same 9 loads into the same registers.
   auto issue = [&](Span &r, int sidx) {
     const int si = min(sidx, nspan - 1);
-    load_span(r, wbase + (int64_t)si * DN_SPAN_BYTES, min(DN_SPAN, nblk - DN_SPAN * si) * Q4K_BYTES,
-              lane);
+    const uint8_t *base = wbase + (int64_t)si * DN_SPAN_BYTES;
+    if (si < nfull)
+      load_span_full(r, base, lane);
+    else
+      load_span(r, base, (nblk - DN_SPAN * si) * Q4K_BYTES, lane);
   };
   auto grab = [&]() {
     int v = 0;
@@ -483,11 +497,16 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
 #pragma unroll
     for (int p = 0; p < 2; p++) {
       const int cur = sidx[p];
-      const int nbytes = cur < nspan ? min(DN_SPAN, nblk - DN_SPAN * cur) * Q4K_BYTES : 0;
+      if (cur < nfull) {
 #pragma unroll
-      for (int j = 0; j < 9; j++) {
-        const int off = 1024 * j + 16 * lane;
-        if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
+        for (int j = 0; j < 9; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R[p].r[j];
+      } else {
+        const int nbytes = cur < nspan ? (nblk - DN_SPAN * cur) * Q4K_BYTES : 0;
+#pragma unroll
+        for (int j = 0; j < 9; j++) {
+          const int off = 1024 * j + 16 * lane;
+          if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
+        }
       }
       // refill this slot right away: two spans stay in flight during the math
       const int nxt = cur < nspan ? grab() : nspan;
