@@ -488,13 +488,17 @@ constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t)
 //           silu(g) * u.
 //   DOWN:   A = hb rows (by entry), K = F; weight tile = rows r0 .. r0+255 of
 //           W2[e]; o[entry][r] fp32.
-// Per stage of 64 K each thread decodes one weight row into LDS and stores
-// its share of the A tile; the global loads of the next two stages are in
-// flight meanwhile (two register sets), and two workgroups share a compute
-// unit, so one decodes while the other multiplies. Wave w owns weight
-// columns (GATEUP) gate 32w .. and up 32w .. (g and u of one (entry, f) then
-// share a lane), or (DOWN) 64w .. 64w+63; every wave covers all entry
-// subtiles of the pass.
+// Weights arrive one super-block column at a time: the tile's 256 blocks of
+// column b (144 B each, one per weight row) are read as consecutive 16-byte
+// chunks (9 per block, so a wave's loads cover whole blocks of a few rows)
+// into LDS, and each thread then takes its own row's block from there. The
+// column's four stages of 64 K follow: each thread decodes 64 weights of its
+// row into the bf16 LDS tile, which reuses the raw column's bytes, and stores
+// its share of the A tile; the next column and the A tiles of the next two
+// stages are in flight meanwhile, and two workgroups share a compute unit, so
+// one decodes while the other multiplies. Wave w owns weight columns (GATEUP)
+// gate 32w .. and up 32w .. (g and u of one (entry, f) then share a lane), or
+// (DOWN) 64w .. 64w+63; every wave covers all entry subtiles of the pass.
 template <bool GATEUP>
 __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
@@ -502,21 +506,35 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
   extern __shared__ __attribute__((aligned(16))) uint16_t msm[];
   uint16_t *sw = msm;                       // [256][TILE_LROW] weight rows (bf16)
+  uint8_t *raw = (uint8_t *)msm;            // [256][144] raw block column (same bytes as sw)
   uint16_t *sa = msm + 256 * TILE_LROW;     // [MX_ROWS][TILE_LROW] A rows (bf16)
   int32_t *sent = (int32_t *)(sa + MX_ROWS * TILE_LROW);  // [MX_ROWS] entries of the pass
-  const int e = blockIdx.y;
+  // blockIdx.x = expert, blockIdx.y = tile: consecutive workgroup ids go to
+  // different XCDs, so the tiles of one expert share an XCD and its L2 holds
+  // that expert's A rows for all of them
+  const int e = blockIdx.x, tile = blockIdx.y;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int nbk = K / QK, stages = K / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int wrow;
-  if constexpr (GATEUP) {
-    const int f0 = blockIdx.x * 128;
-    wrow = tid < 128 ? f0 + tid : F + f0 + (tid - 128);
-  } else {
-    wrow = blockIdx.x * 256 + tid;
+  auto tile_row = [&](int t) {
+    if constexpr (GATEUP) {
+      const int f0 = tile * 128;
+      return t < 128 ? f0 + t : F + f0 + (t - 128);
+    } else {
+      return tile * 256 + t;
+    }
+  };
+  const uint8_t *wexp = wq + (int64_t)e * NR * nbk * Q4K_BYTES;
+  // raw chunk i of this thread: chunk c = tid + 256 i of the column, which is
+  // piece c % 9 of the block of tile row c / 9
+  int choff[9];
+#pragma unroll
+  for (int i = 0; i < 9; i++) {
+    const int c = tid + MX_THREADS * i;
+    const int row = c / 9;
+    choff[i] = tile_row(row) * nbk * Q4K_BYTES + 16 * (c - 9 * row);
   }
-  const uint8_t *wr = wq + ((int64_t)e * NR + wrow) * nbk * Q4K_BYTES;
   // B operand rows of this lane's two 32-column tiles, A operand k offset
   const int brow0 = GATEUP ? 32 * wave + (lane & 31) : 64 * wave + (lane & 31);
   const int brow1 = GATEUP ? 128 + 32 * wave + (lane & 31) : 64 * wave + 32 + (lane & 31);
@@ -546,30 +564,33 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    struct Stage {
-      WRegs w;
+    struct AStage {
       u32x4 a[MX_AJ];
     };
-    auto load = [&](Stage &r, int st) {
-      const uint8_t *blk = wr + (st >> 2) * Q4K_BYTES;
-      r.w.hdr = *(const u32x4 *)blk;
-      r.w.qa = *(const u32x4 *)(blk + 16 + 32 * (st & 3));
-      r.w.qb = *(const u32x4 *)(blk + 32 + 32 * (st & 3));
+    u32x4 rawv[9];
+    auto load_raw = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < 9; i++)
+        rawv[i] = *(const u32x4 *)(wexp + choff[i] + (int64_t)b * Q4K_BYTES);
+    };
+    auto load_a = [&](AStage &r, int st) {
 #pragma unroll
       for (int j = 0; j < MX_AJ; j++) r.a[j] = *(const u32x4 *)(arow[j] + 64 * st);
     };
-    auto step = [&](Stage &r, int st) {
-      __syncthreads();  // the previous stage's MFMAs are done with LDS
-      const RowScales sc = row_scales(r.w, true, st & 3);
+    // one stage of 64 K: decode this thread's row into sw, store the A tile,
+    // refill its A registers two stages ahead, then the MFMAs
+    auto stage = [&](const WRegs &wr, AStage &ar, int st) {
+      __syncthreads();  // every row is out of the raw column / the last MFMAs are done
+      const RowScales sc = row_scales(wr, true, st & 3);
 #pragma unroll
-      for (int kk = 0; kk < 4; kk++) store_w_part(r.w, sc, kk, sw);
+      for (int kk = 0; kk < 4; kk++) store_w_part(wr, sc, kk, sw);
 #pragma unroll
       for (int j = 0; j < MX_AJ; j++) {
         const int q = tid + MX_THREADS * j;
         *(u32x4 *)(sa + (q >> 3) * TILE_LROW + 8 * (q & 7)) =
-            alive[j] ? r.a[j] : u32x4{0u, 0u, 0u, 0u};
+            alive[j] ? ar.a[j] : u32x4{0u, 0u, 0u, 0u};
       }
-      load(r, min(st + 2, stages - 1));  // two stages ahead (the tail reloads the last)
+      load_a(ar, min(st + 2, stages - 1));  // the tail reloads the last stage
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < 4; kk++) {
@@ -586,13 +607,24 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
         }
       }
     };
-    Stage ra, rb;
-    load(ra, 0);
-    load(rb, min(1, stages - 1));
-    // stages = K/64 is a multiple of 4: the loop body takes an even and an odd stage
-    for (int st = 0; st < stages; st += 2) {
-      step(ra, st);
-      step(rb, st + 1);
+    AStage ra, rb;
+    load_raw(0);
+    load_a(ra, 0);
+    load_a(rb, min(1, stages - 1));
+    for (int b = 0; b < nbk; b++) {
+      __syncthreads();  // the last MFMAs are done with sw, which the raw column reuses
+#pragma unroll
+      for (int i = 0; i < 9; i++) *(u32x4 *)(raw + 16 * (tid + MX_THREADS * i)) = rawv[i];
+      load_raw(min(b + 1, nbk - 1));  // the last column reloads itself
+      __syncthreads();
+      u32x4 blk[9];
+#pragma unroll
+      for (int j = 0; j < 9; j++) blk[j] = *(const u32x4 *)(raw + Q4K_BYTES * tid + 16 * j);
+      // stages 4b .. 4b+3 (code chunk c holds sub-blocks 2c and 2c+1)
+      stage(WRegs{blk[0], blk[1], blk[2]}, ra, 4 * b);
+      stage(WRegs{blk[0], blk[3], blk[4]}, rb, 4 * b + 1);
+      stage(WRegs{blk[0], blk[5], blk[6]}, ra, 4 * b + 2);
+      stage(WRegs{blk[0], blk[7], blk[8]}, rb, 4 * b + 3);
     }
     // epilogue: lane holds column (lane & 31) of each 32-column tile and rows
     // 32i + 8(v/4) + 4(lane/32) + v%4
@@ -607,10 +639,10 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
             if constexpr (GATEUP) {
               const float g = acc[i][0][v], u = acc[i][1][v];
               const float hv = g / (1.0f + expf(-g)) * u;
-              hb[(int64_t)ent * F + blockIdx.x * 128 + 32 * wave + (lane & 31)] =
+              hb[(int64_t)ent * F + tile * 128 + 32 * wave + (lane & 31)] =
                   (uint16_t)f32_to_bf16_rne(hv);
             } else {
-              float *orow = o + (int64_t)ent * H + blockIdx.x * 256 + 64 * wave + (lane & 31);
+              float *orow = o + (int64_t)ent * H + tile * 256 + 64 * wave + (lane & 31);
               orow[0] = acc[i][0][v];
               orow[32] = acc[i][1][v];
             }
@@ -719,10 +751,10 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
   auto k2 = moe_mfma_kernel<false>;
   (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
   (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
-  hipLaunchKernelGGL(k1, dim3((unsigned)(F / 128), (unsigned)E), dim3(MX_THREADS), MX_LDS, s,
+  hipLaunchKernelGGL(k1, dim3((unsigned)E, (unsigned)(F / 128)), dim3(MX_THREADS), MX_LDS, s,
                      (const uint16_t *)x, (const uint8_t *)w13, ws.offsets, ws.perm, (int)top_k,
                      (int)H, (int)F, (int)(2 * F), ws.hb, (float *)nullptr, (int)H);
-  hipLaunchKernelGGL(k2, dim3((unsigned)(H / 256), (unsigned)E), dim3(MX_THREADS), MX_LDS, s,
+  hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), MX_LDS, s,
                      (const uint16_t *)ws.hb, (const uint8_t *)w2, ws.offsets, ws.perm,
                      (int)top_k, (int)F, (int)F, (int)H, (uint16_t *)nullptr, ws.o, (int)H);
   const int64_t total = T * H;
