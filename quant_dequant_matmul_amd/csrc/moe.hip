@@ -378,21 +378,30 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_down_kernel(
 
 // y[t][r] = sum over slots s in order of gw[t][s] * o[t*top_k+s][r], slots
 // with an id outside [0, E) skipped (o is indexed by entry).
-__global__ void moe_combine_entries_kernel(const float *__restrict__ o,
-                                           const int32_t *__restrict__ ids,
-                                           const float *__restrict__ gw, float *__restrict__ y,
-                                           int T, int top_k, int E, int H) {
-  const int64_t total = (int64_t)T * H;
+__global__ __launch_bounds__(256) void moe_combine_entries_kernel(
+    const float *__restrict__ o, const int32_t *__restrict__ ids, const float *__restrict__ gw,
+    float *__restrict__ y, int T, int top_k, int E, int H) {
+  // one thread per token t and 4 consecutive outputs (H % 4 == 0)
+  const int h4 = H / 4;
+  const int64_t total = (int64_t)T * h4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / H, r = i - t * H;
-    float acc = 0.f;
+    const int64_t t = i / h4;
+    const int c = (int)(i - t * h4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < top_k; s++) {
       const int64_t en = t * top_k + s;
       const int id = ids[en];
-      if (id >= 0 && id < E) acc = fmaf(gw[en], o[en * H + r], acc);
+      if (id >= 0 && id < E) {
+        const float g = gw[en];
+        const f32x4 v = *(const f32x4 *)(o + en * H + 4 * c);
+        acc.x = fmaf(g, v.x, acc.x);
+        acc.y = fmaf(g, v.y, acc.y);
+        acc.z = fmaf(g, v.z, acc.z);
+        acc.w = fmaf(g, v.w, acc.w);
+      }
     }
-    y[i] = acc;
+    *(f32x4 *)(y + t * H + 4 * c) = acc;
   }
 }
 
@@ -722,7 +731,7 @@ void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *i
   hipLaunchKernelGGL(k2, dim3((unsigned)((H + DEC_RW - 1) / DEC_RW), slots), dim3(DEC_THREADS),
                      lds2, s, hbuf, (const uint8_t *)w2, ids, obuf, n, (int)top_k, (int)E,
                      (int)H, (int)F);
-  const int64_t total = T * H;
+  const int64_t total = T * H / 4;
   hipLaunchKernelGGL(moe_combine_entries_kernel,
                      dim3((unsigned)((total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048)),
                      dim3(256), 0, s, obuf, ids, gw, y, (int)T, (int)top_k, (int)E, (int)H);
@@ -757,7 +766,7 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
   hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), MX_LDS, s,
                      (const uint16_t *)ws.hb, (const uint8_t *)w2, ws.offsets, ws.perm,
                      (int)top_k, (int)F, (int)F, (int)H, (uint16_t *)nullptr, ws.o, (int)H);
-  const int64_t total = T * H;
+  const int64_t total = T * H / 4;
   hipLaunchKernelGGL(moe_combine_entries_kernel,
                      dim3((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)),
                      dim3(256), 0, s, ws.o, ids, gw, y, (int)T, (int)top_k, (int)E, (int)H);
