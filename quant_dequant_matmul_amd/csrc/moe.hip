@@ -48,15 +48,15 @@ constexpr int DEC_MAX_N = 64;
 #ifndef QDM_DEC_PF
 #define QDM_DEC_PF 3
 #endif
-#ifndef QDM_DEC_FR
-#define QDM_DEC_FR 16
-#endif
-#ifndef QDM_DEC_RW
-#define QDM_DEC_RW 64
-#endif
 constexpr int DEC_PF = QDM_DEC_PF;  // wave iterations of weight loads in flight
-constexpr int DEC_FR = QDM_DEC_FR;  // gate/up row pairs per gate+up workgroup
-constexpr int DEC_RW = QDM_DEC_RW;  // W2 rows per down workgroup
+// Rows per decode workgroup: gate/up row pairs (FR) and W2 rows (RW). Few
+// tokens touch few experts, and small workgroups spread them over more compute
+// units; from 4 tokens on, larger workgroups spend less on their fixed costs
+// (measured at H = 2048, F = 768, 128 experts, top-8).
+constexpr int DEC_FR_SMALL = 16, DEC_RW_SMALL = 64;
+constexpr int DEC_FR_LARGE = 32, DEC_RW_LARGE = 128;
+constexpr int DEC_LARGE_FROM_T = 4;
+constexpr int DEC_MT_MAX = 4;  // entries per pass (more entries of one expert take more passes)
 
 // A value the compiler cannot see through (keeps v_and_or_b32 forms).
 __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
@@ -287,7 +287,7 @@ __device__ __forceinline__ RowsDot<XBF16, MT, BlkPtr> make_rows_dot(BlkPtr bp, i
 // Decode gate+up+SwiGLU: workgroup (f chunk, a) with e = the a-th active
 // expert; rows f0 .. f0+fr-1 (gate) and F+f0 .. (up) of W13[e], all entries
 // of e; h[entry][f] = silu(g) * u (fp32).
-template <int MT>
+template <int MT, int DEC_FR>
 __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w13,
     const int32_t *__restrict__ ids, int n, int top_k, int E, int H, int F,
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
 
 // Decode down: workgroup (row chunk, a): o[entry][r] for rows r0 .. r0+rw-1
 // of W2[e] and every entry of e (fp32).
-template <int MT>
+template <int MT, int DEC_RW>
 __global__ __launch_bounds__(DEC_THREADS) void moe_dec_down_kernel(
     const float *__restrict__ h, const uint8_t *__restrict__ w2, const int32_t *__restrict__ ids,
     float *__restrict__ o, int n, int top_k, int E, int H, int F) {
@@ -697,44 +697,57 @@ size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) 
 }
 
 // Entries processed per pass by the decode kernels, or 0 if the decode regime
-// does not apply (too many entries, or inputs too long for LDS).
-// An expert has at most T entries when the ids of a token are distinct, so
-// passes of min(8, T) entries (rounded up to a power of two) cover it at once.
-int dec_mt(int64_t T, int64_t n, int64_t H, int64_t F, size_t &lds1, size_t &lds2) {
+// does not apply (too many entries, or inputs too long for LDS). An expert has
+// at most T entries when the ids of a token are distinct; passes of
+// min(DEC_MT_MAX, T) entries (a power of two) cover a typical expert at once.
+int dec_mt(int64_t T, int64_t n, int64_t H, int64_t F, int fr, int rw, size_t &lds1,
+           size_t &lds2) {
   if (n > DEC_MAX_N) return 0;
   int start = 1;
-  while (start < 8 && start < T) start <<= 1;
+  while (start < DEC_MT_MAX && start < T) start <<= 1;
   for (int mt = start; mt >= 1; mt >>= 1) {
     lds1 = (size_t)mt * (H / QK) * REC_BF16 + (size_t)mt * (H / 8) +
-           (size_t)mt * 2 * DEC_FR * (H / QK) * 4 + (size_t)mt * 2 * DEC_FR * 4;
-    lds2 = (size_t)mt * (F / QK) * REC_F32 + (size_t)mt * (F / 8) +
-           (size_t)mt * DEC_RW * (F / QK) * 4;
+           (size_t)mt * 2 * fr * (H / QK) * 4 + (size_t)mt * 2 * fr * 4;
+    lds2 = (size_t)mt * (F / QK) * REC_F32 + (size_t)mt * (F / 8) + (size_t)mt * rw * (F / QK) * 4;
     if (lds1 <= 96 * 1024 && lds2 <= 96 * 1024) return mt;
   }
   return 0;
 }
 
-template <int MT>
+template <int MT, int FR, int RW>
 void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *ids,
                 const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                 int64_t F, float *hbuf, float *obuf, size_t lds1, size_t lds2,
                 hipStream_t s) {
   const int n = (int)(T * top_k);
   const unsigned slots = (unsigned)(E < n ? E : n);
-  auto k1 = moe_dec_gateup_kernel<MT>;
-  auto k2 = moe_dec_down_kernel<MT>;
+  auto k1 = moe_dec_gateup_kernel<MT, FR>;
+  auto k2 = moe_dec_down_kernel<MT, RW>;
   (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-  hipLaunchKernelGGL(k1, dim3((unsigned)((F + DEC_FR - 1) / DEC_FR), slots), dim3(DEC_THREADS),
-                     lds1, s, (const uint16_t *)x, (const uint8_t *)w13, ids, n, (int)top_k,
-                     (int)E, (int)H, (int)F, hbuf);
-  hipLaunchKernelGGL(k2, dim3((unsigned)((H + DEC_RW - 1) / DEC_RW), slots), dim3(DEC_THREADS),
-                     lds2, s, hbuf, (const uint8_t *)w2, ids, obuf, n, (int)top_k, (int)E,
-                     (int)H, (int)F);
+  hipLaunchKernelGGL(k1, dim3((unsigned)((F + FR - 1) / FR), slots), dim3(DEC_THREADS), lds1, s,
+                     (const uint16_t *)x, (const uint8_t *)w13, ids, n, (int)top_k, (int)E,
+                     (int)H, (int)F, hbuf);
+  hipLaunchKernelGGL(k2, dim3((unsigned)((H + RW - 1) / RW), slots), dim3(DEC_THREADS), lds2, s,
+                     hbuf, (const uint8_t *)w2, ids, obuf, n, (int)top_k, (int)E, (int)H, (int)F);
   const int64_t total = T * H / 4;
   hipLaunchKernelGGL(moe_combine_entries_kernel,
                      dim3((unsigned)((total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048)),
                      dim3(256), 0, s, obuf, ids, gw, y, (int)T, (int)top_k, (int)E, (int)H);
+}
+
+// Decode regime with tile sizes (FR, RW); false if it does not apply.
+template <int FR, int RW>
+bool try_dec(const void *x, const void *w13, const void *w2, const int32_t *ids, const float *gw,
+             float *y, int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+             const MoeWs &ws, hipStream_t s) {
+  size_t lds1 = 0, lds2 = 0;
+  switch (dec_mt(T, T * top_k, H, F, FR, RW, lds1, lds2)) {
+    case 4: launch_dec<4, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    case 2: launch_dec<2, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    case 1: launch_dec<1, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    default: return false;
+  }
 }
 
 void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
@@ -742,14 +755,10 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
                     int64_t F, void *workspace, hipStream_t s) {
   const int64_t n64 = T * top_k;
   const MoeWs ws = carve(workspace, T, E, top_k, H, F);
-  size_t lds1 = 0, lds2 = 0;
-  switch (dec_mt(T, n64, H, F, lds1, lds2)) {
-    case 8: launch_dec<8>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
-    case 4: launch_dec<4>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
-    case 2: launch_dec<2>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
-    case 1: launch_dec<1>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return;
-    default: break;
-  }
+  if (T >= DEC_LARGE_FROM_T
+          ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s)
+          : try_dec<DEC_FR_SMALL, DEC_RW_SMALL>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s))
+    return;
   const int n = (int)n64;
   const size_t route_lds = sizeof(int32_t) * (1 + ROUTE_WAVES) * E;
   (void)hipFuncSetAttribute((const void *)moe_route_kernel,
