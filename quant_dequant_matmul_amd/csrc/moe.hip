@@ -410,6 +410,7 @@ __global__ __launch_bounds__(256) void moe_combine_entries_kernel(
 // ---------------------------------------------------------------------------
 constexpr int ROUTE_THREADS = 1024;
 constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
+constexpr int ROUTE_IDS = 4;  // ids per thread and batch
 
 // One workgroup: offsets[e] = first sorted position of expert e (exclusive
 // scan of the counts, offsets[E] = valid entries), perm[pos] = entry index,
@@ -425,11 +426,25 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
   int32_t *cntw = rsm + E;  // [ROUTE_WAVES][E] per-wave counts of a chunk
   __shared__ int32_t wsum[ROUTE_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ids are read once per batch of ROUTE_IDS chunks (all loads in flight
+  // together) and serve both the histogram and the scatter
+  int idr[ROUTE_IDS];
+  auto load_batch = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < ROUTE_IDS; j++) {
+      const int i = base + ROUTE_THREADS * j + tid;
+      const int id = i < n ? ids[i] : -1;
+      idr[j] = (id >= 0 && id < E) ? id : -1;
+    }
+  };
   for (int e = tid; e < E; e += ROUTE_THREADS) run[e] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += ROUTE_THREADS) {
-    const int id = ids[i];
-    if (id >= 0 && id < E) atomicAdd(&run[id], 1);
+  constexpr int BATCH = ROUTE_THREADS * ROUTE_IDS;
+  for (int base = 0; base < n; base += BATCH) {
+    load_batch(base);
+#pragma unroll
+    for (int j = 0; j < ROUTE_IDS; j++)
+      if (idr[j] >= 0) atomicAdd(&run[idr[j]], 1);
   }
   __syncthreads();
   const int v = tid < E ? run[tid] : 0;  // E <= 1024: one count per thread
@@ -453,33 +468,38 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
   if (tid == 0) offsets[E] = total;
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int base = 0; base < n; base += ROUTE_THREADS) {
-    for (int j = tid; j < ROUTE_WAVES * E; j += ROUTE_THREADS) cntw[j] = 0;
-    __syncthreads();
-    const int i = base + tid;
-    int id = i < n ? ids[i] : -1;
-    if (id >= E) id = -1;
-    uint64_t match = __ballot(id >= 0);
+  for (int base = 0; base < n; base += BATCH) {
+    if (n > BATCH) load_batch(base);  // a single batch is still in registers
 #pragma unroll
-    for (int bit = 0; bit < 10; bit++) {  // E <= 1024
-      const uint64_t ones = __ballot(id >= 0 && ((id >> bit) & 1));
-      match &= ((id >> bit) & 1) ? ones : ~ones;
+    for (int j = 0; j < ROUTE_IDS; j++) {
+      if (base + ROUTE_THREADS * j >= n) break;  // uniform
+      for (int q = tid; q < ROUTE_WAVES * E; q += ROUTE_THREADS) cntw[q] = 0;
+      __syncthreads();
+      const int i = base + ROUTE_THREADS * j + tid;
+      const int id = idr[j];
+      // entries of this wave with the same id: match the 10 id bits by ballot
+      uint64_t match = __ballot(id >= 0);
+#pragma unroll
+      for (int bit = 0; bit < 10; bit++) {  // E <= 1024
+        const uint64_t ones = __ballot(id >= 0 && ((id >> bit) & 1));
+        match &= ((id >> bit) & 1) ? ones : ~ones;
+      }
+      const int rank = __popcll(match & below);
+      if (id >= 0 && rank == 0) cntw[wave * E + id] = __popcll(match);
+      __syncthreads();
+      if (id >= 0) {
+        int pos = run[id] + rank;
+        for (int w = 0; w < wave; w++) pos += cntw[w * E + id];
+        perm[pos] = i;
+      }
+      __syncthreads();
+      for (int e = tid; e < E; e += ROUTE_THREADS) {
+        int add = 0;
+        for (int w = 0; w < ROUTE_WAVES; w++) add += cntw[w * E + e];
+        run[e] += add;
+      }
+      __syncthreads();
     }
-    const int rank = __popcll(match & below);
-    if (id >= 0 && rank == 0) cntw[wave * E + id] = __popcll(match);
-    __syncthreads();
-    if (id >= 0) {
-      int pos = run[id] + rank;
-      for (int w = 0; w < wave; w++) pos += cntw[w * E + id];
-      perm[pos] = i;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += ROUTE_THREADS) {
-      int add = 0;
-      for (int w = 0; w < ROUTE_WAVES; w++) add += cntw[w * E + e];
-      run[e] += add;
-    }
-    __syncthreads();
   }
 }
 
