@@ -347,7 +347,7 @@ def main():
                          "(decode always runs: it is the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU; there is no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     sections = set(args.sections.split(","))
