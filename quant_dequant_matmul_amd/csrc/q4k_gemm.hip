@@ -27,9 +27,14 @@
 // and the start of another, so every unit gets the same number of MFMAs and
 // the last wave of tiles is not left to a few units. With fewer tiles than
 // units, each workgroup gets exactly one tile (no split). The unit that computes the last stage pair of
-// a tile owns it: it adds the fp32 partial tiles left in the workspace by the
-// units that computed its earlier pairs (always units with a smaller index, in
-// decreasing index order, so the sum is deterministic) and stores y. A
+// a tile owns it. A contributor (a unit that computed earlier pairs of the
+// tile) leaves its fp32 partial tile in the workspace in the accumulators' own
+// register order, so its stores and the owner's loads are whole 4 KiB lines
+// per instruction. The owner writes its accumulators into LDS, half a tile at a
+// time, adds there the partials of the contributors (always units with a
+// smaller index, in decreasing index order, so the sum is deterministic), and
+// stores y from LDS in 16-byte pieces of rows; a tile with no contributor goes
+// from the accumulators straight to y. A
 // contributor writes its partial, fences at device scope and raises its flag;
 // the owner waits on the flag (bounded), reads the partial and lowers the flag
 // again, so the workspace flags are zero between calls. Workgroups start in
@@ -225,6 +230,116 @@ __device__ __forceinline__ void run_segment(f32x16 (&acc)[4][4], uint16_t *smem,
 
 constexpr uint32_t SPIN_LIMIT = 1u << 24;  // ~1 s of polling before giving up
 
+// A partial tile in the accumulators' own layout: accumulator group
+// g = (i*4 + j)*4 + v/4 (64 groups of 4 floats per thread) of thread t sits at
+// float4 index g*256 + t, so each store or load instruction of the workgroup
+// covers 4 KiB of consecutive bytes.
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][4], float *__restrict__ slot) {
+  f32x4 *dst = (f32x4 *)slot;
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        dst[((i * 4 + j) * 4 + q) * GEMM_THREADS + t] =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                  acc[i][j][4 * q + 3]};
+}
+
+// y tile store straight from the accumulators (a tile no other unit worked
+// on): each lane writes its 32-column runs of rows; rows and columns past M, N
+// skipped.
+__device__ __forceinline__ void store_direct(const f32x16 (&acc)[4][4], float *yt, int ldy,
+                                             int rows, int cols) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // lane coordinates pass through an opaque move, so the per-element address
+  // arithmetic is not hoisted out of the tile loop (where it would hold a
+  // register per element for the whole kernel)
+  int col = wn * 128 + (lane & 31), rq = wm * 128 + 4 * (lane >> 5);
+  asm volatile("" : "+v"(col), "+v"(rq));
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int c = j * 32 + col;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int r = i * 32 + 8 * (v >> 2) + rq + (v & 3);
+        if (r < rows && c < cols) yt[(int64_t)r * ldy + c] = acc[i][j][v];
+      }
+    }
+}
+
+// y tile store through LDS (a tile with contributors): the two 128-row halves of the tile in turn are
+// written into LDS by the waves that hold them, plus the partial tiles of the
+// contributors (each thread adds the values at its own accumulator positions,
+// contributor by contributor in a fixed order), then every thread writes
+// whole 16-byte pieces of rows to y (rows and columns past M, N skipped).
+constexpr int EPI_LD = BN + 4;  // floats per LDS row (16 bytes of bank padding)
+
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], float *yt, int ldy,
+                                           int rows, int cols, uint16_t *smem, bool vec,
+                                           bool bad, const float *__restrict__ part0,
+                                           int nparts) {
+  float *st = (float *)smem;  // [128][EPI_LD]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    __syncthreads();  // the LDS is free (MFMAs done / previous half written out)
+    if (wm == h) {
+      // lane coordinates pass through an opaque move so the per-element
+      // address arithmetic is not hoisted (it would pin a register per element)
+      int col = wn * 128 + (lane & 31), rq = 4 * (lane >> 5);
+      asm volatile("" : "+v"(col), "+v"(rq));
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            st[(i * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] = acc[i][j][v];
+      for (int k = 0; k < nparts; k++) {
+        const f32x4 *src = (const f32x4 *)(part0 - (size_t)k * BM * BN);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            int off = (i * 4 + j) * 4 * GEMM_THREADS + (int)threadIdx.x;
+            asm volatile("" : "+v"(off));
+            f32x4 t[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) t[q] = src[off + q * GEMM_THREADS];
+#pragma unroll
+            for (int v = 0; v < 16; v++)
+              st[(i * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] += t[v >> 2][v & 3];
+          }
+      }
+    }
+    __syncthreads();
+    // 128 rows x 64 pieces of 16 bytes, 32 per thread
+    for (int e = threadIdx.x; e < 128 * (BN / 4); e += GEMM_THREADS) {
+      const int r = e / (BN / 4), c = 4 * (e % (BN / 4));
+      const int gr = 128 * h + r;
+      if (gr >= rows) continue;
+      f32x4 v = *(const f32x4 *)(st + r * EPI_LD + c);
+      if (bad) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      float *py = yt + (int64_t)gr * ldy + c;
+      if (vec && c + 3 < cols) {
+        *(f32x4 *)py = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (c + q < cols) py[q] = v[q];
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int M,
     int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags, int units) {
@@ -237,8 +352,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
   const int64_t total = (int64_t)ntm * ntn * P;
   const int unit = blockIdx.x;
   const int64_t begin = total * unit / units, end = total * (unit + 1) / units;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[4][4];
   uint32_t *pending = nullptr;  // flag of a partial tile stored but not yet published
@@ -257,46 +370,25 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     pending = nullptr;
     hi = (int64_t)tile * P + pb;
 
-    // The owner of a tile (the unit that computed its last stage pair) stores
-    // its part into y; a contributor stores its part as a row-major 256 x 256
-    // partial tile in its workspace slot and then raises its flag. Both use
-    // the same store loop.
-    const bool owner = pe == P;
-    {
-      float *dst = owner ? y + (int64_t)m0 * N + n0 : partials + (size_t)unit * BM * BN;
-      const int ld = owner ? N : BN;
-      const int rows = owner ? M - m0 : BM, cols = owner ? N - n0 : BN;
-      // lane coordinates pass through an opaque move, so the per-element
-      // address arithmetic is not hoisted out of the tile loop (where it would
-      // hold a register per element for the whole kernel)
-      int col = wn * 128 + (lane & 31), rq = wm * 128 + 4 * (lane >> 5);
-      asm volatile("" : "+v"(col), "+v"(rq));
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int c = j * 32 + col;
-#pragma unroll
-          for (int v = 0; v < 16; v++) {
-            const int r = i * 32 + 8 * (v >> 2) + rq + (v & 3);
-            if (r < rows && c < cols) dst[(int64_t)r * ld + c] = acc[i][j][v];
-          }
-        }
-    }
-    if (!owner) {
-      // The partial is published during the next segment (after its first
-      // stage pair), so its stores drain behind MFMA work; if there is no
-      // next segment, right after the loop.
+    if (pe != P) {
+      // A contributor (its range does not reach the tile's last stage pair)
+      // stores its part in its workspace slot; the flag is raised during the
+      // next segment (after its first stage pair), so the stores drain
+      // behind MFMA work; if there is no next segment, right after the loop.
+      store_partial(acc, partials + (size_t)unit * BM * BN);
       pending = &flags[unit];
       continue;
     }
-    if (pb == 0) continue;  // the owner computed the whole tile
-    // Earlier units [lowest, unit) worked on this tile: wait for their flags,
-    // then y += the sum of their partials (highest unit first), element-wise
-    // over the tile with no accumulator live.
+    float *yt = y + (int64_t)m0 * N + n0;
+    if (pb == 0) {  // the owner computed the whole tile
+      store_direct(acc, yt, N, M - m0, N - n0);
+      continue;
+    }
+    // Earlier units [lowest, unit) worked on this tile: wait for their flags;
+    // their partials are added while the tile goes out (highest unit first, a
+    // fixed order).
     int lowest = unit;
     while (lowest > 0 && total * lowest / units > (int64_t)tile * P) lowest--;
-    __syncthreads();
     if (threadIdx.x == 0) {
       uint32_t spins = 0;
       for (int u = unit - 1; u >= lowest; u--) {
@@ -307,48 +399,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
       }
       timed_out = spins >= SPIN_LIMIT;
     }
-    __syncthreads();  // also orders this unit's own y stores before the re-reads below
+    __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const bool bad = timed_out != 0u;  // a partial that never arrived poisons the tile
-    const int rows = min(M - m0, BM), cols = min(N - n0, BN);
-    float *yt = y + (int64_t)m0 * N + n0;
-    const bool vec = (N & 3) == 0;  // y rows of the tile are 16-byte aligned
-    constexpr int PB = 8;           // float4 per thread in flight
-    for (int base = 0; base < BM * BN / 4; base += PB * GEMM_THREADS) {
-      f32x4 sum[PB];
-#pragma unroll
-      for (int k = 0; k < PB; k++) sum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int u = unit - 1; u >= lowest; u--) {
-        const f32x4 *pt = (const f32x4 *)(partials + (size_t)u * BM * BN);
-#pragma unroll
-        for (int k = 0; k < PB; k++) {
-          const f32x4 v = pt[base + k * GEMM_THREADS + threadIdx.x];
-          sum[k].x += v.x;
-          sum[k].y += v.y;
-          sum[k].z += v.z;
-          sum[k].w += v.w;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < PB; k++) {
-        const int e4 = base + k * GEMM_THREADS + threadIdx.x;
-        const int r = e4 / (BN / 4), c = (e4 % (BN / 4)) * 4;
-        if (r >= rows) continue;
-        float *py = yt + (int64_t)r * N + c;
-        if (vec) {
-          if (c < cols) {
-            const f32x4 o = *(const f32x4 *)py;
-            const float nan = __builtin_nanf("");
-            *(f32x4 *)py = bad ? f32x4{nan, nan, nan, nan}
-                               : f32x4{o.x + sum[k].x, o.y + sum[k].y, o.z + sum[k].z, o.w + sum[k].w};
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            if (c + q < cols) py[q] = bad ? __builtin_nanf("") : py[q] + sum[k][q];
-        }
-      }
-    }
+    store_tile(acc, yt, N, M - m0, N - n0, smem, (N & 3) == 0, bad,
+               partials + (size_t)(unit - 1) * BM * BN, unit - lowest);
   }
   if (pending != nullptr) {  // the last segment left a partial: publish it now
     __threadfence();
@@ -357,6 +412,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
       __hip_atomic_store(pending, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+
 
 constexpr size_t GEMM_LDS = 4 * TILE_ELEMS * sizeof(uint16_t);  // 147456 bytes
 
