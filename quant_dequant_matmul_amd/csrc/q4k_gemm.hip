@@ -2,23 +2,38 @@
 //
 // Prefill over GGUF weights runs on matrix cores (hipEngine README,
 // "Quickstart": WMMA prefill, GEMV decode). On gfx950 the equivalent is the
-// bf16 MFMA: Q4_K tiles are decoded in fp32 (w = d*sc*q - dmin*m, exact
+// bf16 MFMA: Q4_K weights are decoded in fp32 (w = d*sc*q - dmin*m, exact
 // products, one rounding), rounded to bf16 (nearest even, v_cvt_pk_bf16_f32)
-// into LDS next to the bf16 activation tile, and contracted with
-// v_mfma_f32_32x32x16_bf16 into fp32 accumulators.
+// and contracted with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.
 //
 // Tiling: a 256-thread workgroup (one per compute unit) owns a 256 x 256 tile
-// of y; each of its 4 waves owns a 128 x 128 quadrant = 4 x 4 MFMA tiles of
-// 32 x 32, i.e. 256 fp32 accumulators per lane. Every weight a workgroup
-// decodes feeds 256 rows of x, which keeps the decode (about 3 VALU
-// operations per weight) well below the MFMA time. K advances in stages of 64:
-// stage (b, c) is code chunk c (sub-blocks 2c, 2c+1) of super-block b, so each
-// thread decodes one row's 32 code bytes per stage. Stages are double-buffered
-// in LDS (rows padded to 144 bytes so that 16 consecutive rows hit distinct
-// banks); the global loads of stage s+1 are in flight during the MFMAs of
-// stage s. All global loads are unconditional (rows past M or N are clamped
-// and their values zeroed), so the compiler waits for exactly the loads it
-// needs.
+// of y. Wave v owns all 256 rows of x and the 64 weight rows 64v .. 64v+63:
+// 8 x 2 MFMA tiles of 32 x 32, i.e. 256 fp32 accumulators per lane. Each
+// weight row is needed by one wave only, so every lane decodes its own two
+// rows straight into MFMA operand registers: weights never pass through LDS.
+// Only the x tile does (it is shared by the four waves): it is written once
+// and read four times per stage, which halves the LDS write traffic of a
+// layout that stages both operands (LDS writes run at half the read rate).
+// Every weight a workgroup decodes feeds 256 rows of x, which keeps the
+// decode (about 3 VALU operations per weight) below the MFMA time.
+//
+// K advances in stages of 64: stage (b, c) is code chunk c (sub-blocks 2c and
+// 2c+1) of super-block b. The k order inside a stage is permuted (the
+// contraction does not depend on it) so that each lane reads one contiguous
+// 16-byte run of codes per row: lanes 0..31 take code bytes 0..15, lanes
+// 32..63 bytes 16..31 of the chunk. In k-step kk (16 k per MFMA) lane half h
+// holds the low nibbles (kk = 0, 1) or high nibbles (kk = 2, 3) of code bytes
+// 16h + 8(kk&1) .. +7, i.e. k = 32(kk>>1) + 16h + 8(kk&1) .. +7 of the stage,
+// and reads x at the same k.
+//
+// Pipeline (one barrier per stage): x of stage s+2 and the codes of stage s+2
+// are loaded while stage s is multiplied; x of stage s+1 is stored into the
+// other LDS buffer during stage s; the weight operands of k-step kk+1 are
+// decoded while the MFMAs of k-step kk run. All global loads are
+// unconditional (rows past M or N are clamped; weight rows past N decode to
+// zero, x rows past M only feed y rows that are not stored), so the compiler
+// waits for exactly the loads it needs, and a stage has no branch that would
+// split its MFMA schedule.
 //
 // Work split (stream-K): the 256 x 256 tiles times the K/128 stage pairs of
 // each form one iteration space that is cut into equal contiguous ranges, one
@@ -26,15 +41,15 @@
 // workgroup per unit; a range then covers the end of one tile, whole tiles,
 // and the start of another, so every unit gets the same number of MFMAs and
 // the last wave of tiles is not left to a few units. With fewer tiles than
-// units, each workgroup gets exactly one tile (no split). The unit that computes the last stage pair of
-// a tile owns it. A contributor (a unit that computed earlier pairs of the
-// tile) leaves its fp32 partial tile in the workspace in the accumulators' own
-// register order, so its stores and the owner's loads are whole 4 KiB lines
-// per instruction. The owner writes its accumulators into LDS, half a tile at a
-// time, adds there the partials of the contributors (always units with a
-// smaller index, in decreasing index order, so the sum is deterministic), and
-// stores y from LDS in 16-byte pieces of rows; a tile with no contributor goes
-// from the accumulators straight to y. A
+// units, each workgroup gets exactly one tile (no split). The unit that
+// computes the last stage pair of a tile owns it. A contributor (a unit that
+// computed earlier pairs of the tile) leaves its fp32 partial tile in the
+// workspace in the accumulators' own register order, so its stores and the
+// owner's loads are whole 4 KiB lines per instruction. The owner writes its
+// accumulators into LDS, half a tile at a time, adds there the partials of the
+// contributors (always units with a smaller index, in decreasing index order,
+// so the sum is deterministic), and stores y from LDS in 16-byte pieces of
+// rows; a tile with no contributor goes from the accumulators straight to y. A
 // contributor writes its partial, fences at device scope and raises its flag;
 // the owner waits on the flag (bounded), reads the partial and lowers the flag
 // again, so the workspace flags are zero between calls. Workgroups start in
@@ -43,9 +58,9 @@
 // the one that waits: the waits cannot deadlock and do not form chains.
 //
 // MFMA operand layout (32x32x16 bf16, wave64): lane l holds, for A, row l%32
-// and k = 8*(l/32) .. +7; for B, column l%32 and the same k. The 32x32 fp32
-// result gives lane l column l%32 and, in accumulator r, row
-// 8*(r/4) + 4*(l/32) + r%4.
+// and 8 consecutive k; for B, column l%32 and the same 8 k (lane halves take
+// the two 8-k halves of the k-step). The 32x32 fp32 result gives lane l
+// column l%32 and, in accumulator r, row 8*(r/4) + 4*(l/32) + r%4.
 #include "common.h"
 #include "launch.h"
 #include "q4k_tile.h"
@@ -55,25 +70,42 @@ namespace qdm {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LROW = TILE_LROW;  // bf16 per LDS row (144 bytes)
+constexpr int LROW = TILE_LROW;  // bf16 per LDS x row (144 bytes)
 constexpr int GEMM_THREADS = 256;
-constexpr int TILE_ELEMS = BM * LROW;  // per operand and stage (BM == BN)
-
+constexpr int XTILE = BM * LROW;  // bf16 per LDS x buffer
+constexpr int WAVE_ROWS = BN / 4;  // weight rows per wave
+// VALU instructions placed after each MFMA in k-steps 0..2 and in k-step 3
+// (which also forms the next stage's scales); measured best of 2..4 / 4..8.
+constexpr int SCHED_VALU = 3, SCHED_VALU_K3 = 6;
 
 struct XRegs {
   u32x4 v[8];  // x tile: 8 x 16 bytes per thread
 };
-static_assert(BM == BN && BM == GEMM_THREADS, "one W row per thread");
+static_assert(BM == GEMM_THREADS, "x tile loads assume one row-eighth per thread and chunk");
+
+// This lane's two weight rows (j = 0, 1) for one stage: the block header and
+// the lane's 16 code bytes of the stage's chunk.
+struct WRaw {
+  u32x4 hdr[2], q[2];
+};
+
+// Scales of both rows for one stage (a0, a1 carry the factor 2^9 that the fp8
+// reading of the codes leaves out).
+struct Scales2 {
+  RowScales r[2];
+};
 
 // Per-lane 32-bit byte offsets of this thread's loads, relative to the
 // tile's uniform base addresses (the loads then use a scalar base and a vector
 // offset). Rows past M or N are clamped to the last row.
 struct LoadOffsets {
   uint32_t x[8];  // x chunk i: row (tid/8 + 32i) of the tile, 16-byte column tid%8
-  uint32_t w;     // this thread's W row
+  uint32_t w[2];  // weight row j of this lane: 64*wave + 32j + lane%32
+  uint32_t q;     // code bytes of this lane half within a stage's 32-byte chunk
 };
 
-__device__ __forceinline__ LoadOffsets make_offsets(int M, int N, int K, int m0, int n0) {
+__device__ __forceinline__ LoadOffsets make_offsets(int M, int N, int K, int m0, int n0,
+                                                    int wave, int lane) {
   LoadOffsets o;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -81,7 +113,12 @@ __device__ __forceinline__ LoadOffsets make_offsets(int M, int N, int K, int m0,
     const int row = min(m0 + (q >> 3), M - 1) - m0;
     o.x[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(q & 7) * 16u;
   }
-  o.w = (uint32_t)(min(n0 + (int)threadIdx.x, N - 1) - n0) * (uint32_t)(K / QK) * Q4K_BYTES;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int row = min(n0 + WAVE_ROWS * wave + 32 * j + (lane & 31), N - 1) - n0;
+    o.w[j] = (uint32_t)row * (uint32_t)(K / QK) * Q4K_BYTES;
+  }
+  o.q = 16u + 16u * (uint32_t)(lane >> 5);
   return o;
 }
 
@@ -92,131 +129,193 @@ __device__ __forceinline__ void load_x(XRegs &r, const LoadOffsets &o,
   for (int i = 0; i < 8; i++) r.v[i] = *(const u32x4 *)(base + o.x[i]);
 }
 
-__device__ __forceinline__ void load_w(WRegs &r, const LoadOffsets &o,
+__device__ __forceinline__ void load_w(WRaw &r, const LoadOffsets &o,
                                        const uint8_t *__restrict__ wtile, int stage) {
-  const int b = stage >> 2, c = stage & 3;
-  const uint8_t *blk = wtile + b * Q4K_BYTES + o.w;
-  r.hdr = *(const u32x4 *)blk;
-  r.qa = *(const u32x4 *)(blk + 16 + 32 * c);
-  r.qb = *(const u32x4 *)(blk + 32 + 32 * c);
-}
-
-__device__ __forceinline__ void store_x(const XRegs &r, uint16_t *sx, int M, int m0) {
-  if (m0 + BM <= M) {  // uniform: the whole tile is inside M
+  const uint8_t *blk = wtile + (stage >> 2) * Q4K_BYTES;
+  const uint32_t qo = o.q + 32u * (uint32_t)(stage & 3);
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int q = threadIdx.x + GEMM_THREADS * i;
-      *(u32x4 *)(sx + (q >> 3) * LROW + (q & 7) * 8) = r.v[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int q = threadIdx.x + GEMM_THREADS * i;
-      const int row = q >> 3;
-      const u32x4 v = (m0 + row < M) ? r.v[i] : u32x4{0, 0, 0, 0};
-      *(u32x4 *)(sx + row * LROW + (q & 7) * 8) = v;
-    }
+  for (int j = 0; j < 2; j++) {
+    r.hdr[j] = *(const u32x4 *)(blk + o.w[j]);
+    r.q[j] = *(const u32x4 *)(blk + o.w[j] + qo);
   }
 }
 
-// One stage of MFMAs from LDS buffer (sx, swb), with the W decode of the next
-// stage (regs nw, stage ns, into nws; skipped when store_next is false) woven
-// between them: per 16 MFMAs, a quarter of the decode.
-__device__ __forceinline__ void mfma_stage(f32x16 (&acc)[4][4], const uint16_t *sx,
-                                           const uint16_t *swb, const WRegs &nw,
-                                           bool store_next, int ns, uint16_t *nws, int N,
-                                           int n0, int wm, int wn, int lane) {
-  const int arow = lane & 31, akoff = 8 * (lane >> 5);
-  const RowScales sc = row_scales(nw, n0 + (int)threadIdx.x < N, ns & 3);
-  const uint16_t *pa = sx + (wm * 128 + arow) * LROW + akoff;
-  const uint16_t *pb = swb + (wn * 128 + arow) * LROW + akoff;
-  // operand fragments of k-step kk are read one k-step ahead of their MFMAs
-  bf16x8 af[2][4], bfr[2][4];
+// Scale and min of sub-block j (0..7) of a block header, without a branch on
+// j (the stage, hence j, is known only at run time, and a branch would split
+// the MFMA schedule): both packings are formed and the right one selected.
+__device__ __forceinline__ void scale_min_sel(const u32x4 &hdr, int j, uint32_t &sc,
+                                              uint32_t &m) {
+  const int sh = 8 * (j & 3);
+  const uint32_t b0 = hdr.y >> sh, b1 = hdr.z >> sh, b2 = hdr.w >> sh;
+  const uint32_t lo_sc = b0 & 63u, lo_m = b1 & 63u;
+  const uint32_t hi_sc = (b2 & 15u) | ((b0 >> 2) & 48u);
+  const uint32_t hi_m = ((b2 >> 4) & 15u) | ((b1 >> 2) & 48u);
+  sc = j < 4 ? lo_sc : hi_sc;
+  m = j < 4 ? lo_m : hi_m;
+}
+
+__device__ __forceinline__ Scales2 stage_scales(const WRaw &r, const bool (&live)[2], int stage) {
+  Scales2 s;
+  const int c = stage & 3;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    af[0][i] = *(const bf16x8 *)(pa + i * 32 * LROW);
-    bfr[0][i] = *(const bf16x8 *)(pb + i * 32 * LROW);
+  for (int j = 0; j < 2; j++) {
+    const float d = live[j] ? half_bits_to_float(r.hdr[j].x) : 0.f;
+    const float dmin = live[j] ? half_bits_to_float(r.hdr[j].x >> 16) : 0.f;
+    uint32_t sc0, m0s, sc1, m1s;
+    scale_min_sel(r.hdr[j], 2 * c, sc0, m0s);
+    scale_min_sel(r.hdr[j], 2 * c + 1, sc1, m1s);
+    const float d9 = d * 512.f;  // the fp8 code scale 2^-9 undone (exact)
+    s.r[j] = RowScales{d9 * (float)sc0, dmin * (float)m0s, d9 * (float)sc1, dmin * (float)m1s};
   }
+  return s;
+}
+
+// Weight operand of k-step kk for one row: 8 codes (two code words) scaled by
+// the sub-block's scale and min, rounded to bf16. A code byte 0..15 read as an
+// fp8 e4m3 value is exactly q * 2^-9 (the small ones as subnormals), so one
+// conversion turns two codes into floats; the scale a carries the factor 2^9
+// (exact), and a * (q * 2^-9) - b is the same single-rounding fma as
+// a * q - b.
+__device__ __forceinline__ bf16x8 decode_b(const u32x4 &q, const RowScales &sc, int kk) {
+  const bool hi = kk >= 2;
+  const uint32_t c0 = (kk & 1) ? q.z : q.x, c1 = (kk & 1) ? q.w : q.y;
+  const float a = hi ? sc.a1 : sc.a0, b = hi ? sc.b1 : sc.b0;
+  const uint32_t n0 = (hi ? c0 >> 4 : c0) & 0x0F0F0F0Fu, n1 = (hi ? c1 >> 4 : c1) & 0x0F0F0F0Fu;
+  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)n0, false);
+  const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)n0, true);
+  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)n1, false);
+  const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)n1, true);
+  u32x4 o;
+  o.x = pack_bf16(a * p0[0] - b, a * p0[1] - b);
+  o.y = pack_bf16(a * p1[0] - b, a * p1[1] - b);
+  o.z = pack_bf16(a * p2[0] - b, a * p2[1] - b);
+  o.w = pack_bf16(a * p3[0] - b, a * p3[1] - b);
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// x chunks i0 .. i0+3 of this thread into an LDS x buffer. Rows past M hold
+// copies of row M-1 (clamped loads): finite, and their y rows are never
+// stored, so they need no masking (and the stage has no branch).
+__device__ __forceinline__ void store_x_part(const XRegs &r, uint16_t *sx, int i0) {
+#pragma unroll
+  for (int i = i0; i < i0 + 4; i++) {
+    const int q = threadIdx.x + GEMM_THREADS * i;
+    *(u32x4 *)(sx + (q >> 3) * LROW + (q & 7) * 8) = r.v[i];
+  }
+}
+
+// LDS offset (in bf16) of this lane's x operand for k-step kk, row tile 0.
+__device__ __forceinline__ int a_koff(int kk, int lane) {
+  return 32 * (kk >> 1) + 16 * (lane >> 5) + 8 * (kk & 1);
+}
+
+// One stage. On entry bf[0] holds the weight operands of k-step 0 and
+// sc_cur the scales of this stage; the x tile of this stage is complete in sx.
+// During the stage: x of stage s+2 is loaded into xl, x of stage s+1 (xs) is
+// stored into nsx, the codes of stage s+2 are loaded into wcur once its last
+// operands are decoded, and the scales and k-step-0 operands of stage s+1
+// (wnext) are formed, so that on exit bf[0] and sc_next are ready.
+__device__ __forceinline__ void gemm_stage(f32x16 (&acc)[8][2], bf16x8 (&bf)[2][2],
+                                           const Scales2 &sc_cur, Scales2 &sc_next,
+                                           WRaw &wcur, const WRaw &wnext, int s_next,
+                                           int s_load, const XRegs &xs, XRegs &xl,
+                                           const uint16_t *sx, uint16_t *nsx,
+                                           const LoadOffsets &lo, const bool (&live)[2],
+                                           const uint8_t *__restrict__ xtile,
+                                           const uint8_t *__restrict__ wtile, int M, int m0,
+                                           int lane) {
+  load_x(xl, lo, xtile, s_load);
+  const uint16_t *pa = sx + (lane & 31) * LROW;
+  bf16x8 af[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) af[i] = *(const bf16x8 *)(pa + i * 32 * LROW + a_koff(0, lane));
 #pragma unroll
   for (int kk = 0; kk < 4; kk++) {
     const int cur = kk & 1;
     if (kk < 3) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        af[cur ^ 1][i] = *(const bf16x8 *)(pa + i * 32 * LROW + (kk + 1) * 16);
-        bfr[cur ^ 1][i] = *(const bf16x8 *)(pb + i * 32 * LROW + (kk + 1) * 16);
-      }
+      for (int j = 0; j < 2; j++) bf[cur ^ 1][j] = decode_b(wcur.q[j], sc_cur.r[j], kk + 1);
+    } else {
+      sc_next = stage_scales(wnext, live, s_next);
+#pragma unroll
+      for (int j = 0; j < 2; j++) bf[cur ^ 1][j] = decode_b(wnext.q[j], sc_next.r[j], 0);
+      load_w(wcur, lo, wtile, s_load);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 8; i++) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[cur][0], acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[cur][1], acc[i][1], 0, 0, 0);
+      if (kk < 3) af[i] = *(const bf16x8 *)(pa + i * 32 * LROW + a_koff(kk + 1, lane));
+    }
+    if (kk < 2) store_x_part(xs, nsx, 4 * kk);
+    // k-steps 0..2 carry one row pair's decode, k-step 3 also the next
+    // stage's scales: their VALU work is spread over the 16 MFMAs
+    if (kk < 3) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
-                                                            0, 0, 0);
-    if (store_next) store_w_part(nw, sc, kk, nws);
+      for (int t = 0; t < 16; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, SCHED_VALU, 0);  // VALU
+      }
+    } else {
 #pragma unroll
-    for (int t = 0; t < 16; t++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      for (int t = 0; t < 16; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, SCHED_VALU_K3, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();  // x of stage s+1 complete in nsx; sx free for stage s+2
 }
 
 // Multiplies stage range [s0, s1) (s1 - s0 even, >= 2) of tile (m0, n0) into acc.
-__device__ __forceinline__ void run_segment(f32x16 (&acc)[4][4], uint16_t *smem,
+__device__ __forceinline__ void run_segment(f32x16 (&acc)[8][2], uint16_t *smem,
                                             const uint8_t *__restrict__ w,
                                             const uint16_t *__restrict__ x, int M, int N, int K,
                                             int m0, int n0, int s0, int s1, uint32_t *publish) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 8; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  // Stage s lives in LDS buffer (s - s0) & 1. While stage s is multiplied: x
-  // and W of stage s+2 are in flight, W of stage s+1 is decoded into the other
-  // buffer and x of stage s+1 (loaded two stages earlier) is stored there.
-  const LoadOffsets lo = make_offsets(M, N, K, m0, n0);
+  const LoadOffsets lo = make_offsets(M, N, K, m0, n0, wave, lane);
+  bool live[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) live[j] = n0 + WAVE_ROWS * wave + 32 * j + (lane & 31) < N;
   const uint8_t *xtile = (const uint8_t *)(x + (int64_t)m0 * K);
   const uint8_t *wtile = w + (int64_t)n0 * (K / QK) * Q4K_BYTES;
   const int last = s1 - 1;
+  uint16_t *sx0 = smem, *sx1 = smem + XTILE;
   XRegs xa, xb;
-  WRegs wa, wb;
+  WRaw wa, wb;
+  Scales2 sca, scb;
+  bf16x8 bf[2][2];
   load_x(xa, lo, xtile, s0);
   load_w(wa, lo, wtile, s0);
   load_x(xb, lo, xtile, s0 + 1);
   load_w(wb, lo, wtile, s0 + 1);
-  __syncthreads();  // the previous segment's last MFMAs have read the buffers
-  store_x(xa, smem, M, m0);
-  {
-    const RowScales sc = row_scales(wa, n0 + (int)threadIdx.x < N, s0 & 3);
+  __syncthreads();  // the previous segment's last reads of the buffers are done
+  store_x_part(xa, sx0, 0);
+  store_x_part(xa, sx0, 4);
+  sca = stage_scales(wa, live, s0);
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) store_w_part(wa, sc, kk, smem + TILE_ELEMS);
-  }
+  for (int j = 0; j < 2; j++) bf[0][j] = decode_b(wa.q[j], sca.r[j], 0);
   __syncthreads();
 
-  // The loop body covers an even and an odd stage. Past the segment's last
-  // stage, loads are clamped to it and the decodes/stores go to the buffer
-  // that is no longer read.
+  // The loop body covers an even and an odd stage; register sets alternate.
+  // Past the segment's last stage, loads are clamped to it and the stores go
+  // to the buffer that is no longer read.
   for (int s = s0; s < s1; s += 2) {
-    // even stage s (buffer 0): W of s+1 (wb) decoded and x of s+1 (xb) stored into buffer 1
-    load_x(xa, lo, xtile, min(s + 2, last));
-    load_w(wa, lo, wtile, min(s + 2, last));
-    mfma_stage(acc, smem, smem + TILE_ELEMS, wb, true, s + 1, smem + 3 * TILE_ELEMS, N, n0, wm,
-               wn, lane);
-    store_x(xb, smem + 2 * TILE_ELEMS, M, m0);
-    __syncthreads();
-    // odd stage s+1 (buffer 1): W of s+2 (wa) and x of s+2 (xa) into buffer 0
-    load_x(xb, lo, xtile, min(s + 3, last));
-    load_w(wb, lo, wtile, min(s + 3, last));
-    mfma_stage(acc, smem + 2 * TILE_ELEMS, smem + 3 * TILE_ELEMS, wa, true, min(s + 2, last),
-               smem + TILE_ELEMS, N, n0, wm, wn, lane);
-    store_x(xa, smem, M, m0);
-    __syncthreads();
+    // even stage s: codes wa, x in sx0; x of s+1 (xb) into sx1; loads of s+2 into xa, wa
+    gemm_stage(acc, bf, sca, scb, wa, wb, s + 1, min(s + 2, last), xb, xa, sx0, sx1, lo, live,
+               xtile, wtile, M, m0, lane);
+    // odd stage s+1: codes wb, x in sx1; x of s+2 (xa) into sx0; loads of s+3 into xb, wb
+    gemm_stage(acc, bf, scb, sca, wb, wa, min(s + 2, last), min(s + 3, last), xa, xb, sx1, sx0,
+               lo, live, xtile, wtile, M, m0, lane);
     if (publish != nullptr && s == s0) {
       // the partial tile stored before this segment has long been written:
       // make it visible device-wide and raise its flag
@@ -231,20 +330,20 @@ __device__ __forceinline__ void run_segment(f32x16 (&acc)[4][4], uint16_t *smem,
 constexpr uint32_t SPIN_LIMIT = 1u << 24;  // ~1 s of polling before giving up
 
 // A partial tile in the accumulators' own layout: accumulator group
-// g = (i*4 + j)*4 + v/4 (64 groups of 4 floats per thread) of thread t sits at
+// g = (i*2 + j)*4 + v/4 (64 groups of 4 floats per thread) of thread t sits at
 // float4 index g*256 + t, so each store or load instruction of the workgroup
 // covers 4 KiB of consecutive bytes.
-__device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][4], float *__restrict__ slot) {
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[8][2], float *__restrict__ slot) {
   f32x4 *dst = (f32x4 *)slot;
   int t = (int)threadIdx.x;
   asm volatile("" : "+v"(t));
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 8; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int q = 0; q < 4; q++)
-        dst[((i * 4 + j) * 4 + q) * GEMM_THREADS + t] =
+        dst[((i * 2 + j) * 4 + q) * GEMM_THREADS + t] =
             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                   acc[i][j][4 * q + 3]};
 }
@@ -252,19 +351,18 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][4], float *
 // y tile store straight from the accumulators (a tile no other unit worked
 // on): each lane writes its 32-column runs of rows; rows and columns past M, N
 // skipped.
-__device__ __forceinline__ void store_direct(const f32x16 (&acc)[4][4], float *yt, int ldy,
+__device__ __forceinline__ void store_direct(const f32x16 (&acc)[8][2], float *yt, int ldy,
                                              int rows, int cols) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   // lane coordinates pass through an opaque move, so the per-element address
   // arithmetic is not hoisted out of the tile loop (where it would hold a
   // register per element for the whole kernel)
-  int col = wn * 128 + (lane & 31), rq = wm * 128 + 4 * (lane >> 5);
+  int col = WAVE_ROWS * wave + (lane & 31), rq = 4 * (lane >> 5);
   asm volatile("" : "+v"(col), "+v"(rq));
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 8; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < 2; j++) {
       const int c = j * 32 + col;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
@@ -274,49 +372,51 @@ __device__ __forceinline__ void store_direct(const f32x16 (&acc)[4][4], float *y
     }
 }
 
-// y tile store through LDS (a tile with contributors): the two 128-row halves of the tile in turn are
-// written into LDS by the waves that hold them, plus the partial tiles of the
-// contributors (each thread adds the values at its own accumulator positions,
-// contributor by contributor in a fixed order), then every thread writes
-// whole 16-byte pieces of rows to y (rows and columns past M, N skipped).
+// y tile store through LDS (a tile with contributors): the two 128-row halves
+// of the tile in turn are written into LDS by every wave (row tiles 4h..4h+3),
+// plus the partial tiles of the contributors (each thread adds the values at
+// its own accumulator positions, contributor by contributor in a fixed order),
+// then every thread writes whole 16-byte pieces of rows to y (rows and columns
+// past M, N skipped).
 constexpr int EPI_LD = BN + 4;  // floats per LDS row (16 bytes of bank padding)
 
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], float *yt, int ldy,
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[8][2], float *yt, int ldy,
                                            int rows, int cols, uint16_t *smem, bool vec,
                                            bool bad, const float *__restrict__ part0,
                                            int nparts) {
   float *st = (float *)smem;  // [128][EPI_LD]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int h = 0; h < 2; h++) {
     __syncthreads();  // the LDS is free (MFMAs done / previous half written out)
-    if (wm == h) {
+    {
       // lane coordinates pass through an opaque move so the per-element
       // address arithmetic is not hoisted (it would pin a register per element)
-      int col = wn * 128 + (lane & 31), rq = 4 * (lane >> 5);
+      int col = WAVE_ROWS * wave + (lane & 31), rq = 4 * (lane >> 5);
       asm volatile("" : "+v"(col), "+v"(rq));
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int ii = 0; ii < 4; ii++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
           for (int v = 0; v < 16; v++)
-            st[(i * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] = acc[i][j][v];
+            st[(ii * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] =
+                acc[4 * h + ii][j][v];
       for (int k = 0; k < nparts; k++) {
         const f32x4 *src = (const f32x4 *)(part0 - (size_t)k * BM * BN);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int ii = 0; ii < 4; ii++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            int off = (i * 4 + j) * 4 * GEMM_THREADS + (int)threadIdx.x;
+          for (int j = 0; j < 2; j++) {
+            int off = ((4 * h + ii) * 2 + j) * 4 * GEMM_THREADS + (int)threadIdx.x;
             asm volatile("" : "+v"(off));
             f32x4 t[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) t[q] = src[off + q * GEMM_THREADS];
 #pragma unroll
             for (int v = 0; v < 16; v++)
-              st[(i * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] += t[v >> 2][v & 3];
+              st[(ii * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] +=
+                  t[v >> 2][v & 3];
           }
       }
     }
@@ -344,7 +444,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int M,
     int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags, int units) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // stage buffer p: x tile at smem + 2p*TILE_ELEMS, W tile right after it
+  // x stage buffer p at smem + p*XTILE; the LDS store of a split tile reuses it
   __shared__ uint32_t timed_out;
 
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -353,7 +453,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
   const int unit = blockIdx.x;
   const int64_t begin = total * unit / units, end = total * (unit + 1) / units;
 
-  f32x16 acc[4][4];
+  f32x16 acc[8][2];
   uint32_t *pending = nullptr;  // flag of a partial tile stored but not yet published
   // The range is walked from its end: the segment that starts a later tile
   // (the only one whose partial another unit waits for) comes first, the
@@ -413,8 +513,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
   }
 }
 
-
-constexpr size_t GEMM_LDS = 4 * TILE_ELEMS * sizeof(uint16_t);  // 147456 bytes
+// Dynamic LDS: two x stage buffers (73728 bytes), or the 128-row fp32 staging
+// of a split tile's store (133120 bytes), whichever is larger.
+constexpr size_t GEMM_LDS_MAIN = 2 * XTILE * sizeof(uint16_t);
+constexpr size_t GEMM_LDS_EPI = 128 * EPI_LD * sizeof(float);
+constexpr size_t GEMM_LDS = GEMM_LDS_MAIN > GEMM_LDS_EPI ? GEMM_LDS_MAIN : GEMM_LDS_EPI;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 

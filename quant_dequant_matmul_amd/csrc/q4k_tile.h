@@ -28,13 +28,19 @@ struct RowScales {
   float a0, b0, a1, b1;
 };
 
-__device__ __forceinline__ RowScales row_scales(const WRegs &r, bool live, int c) {
-  const float d = live ? half_bits_to_float(r.hdr.x) : 0.f;
-  const float dmin = live ? half_bits_to_float(r.hdr.x >> 16) : 0.f;
+// From a block's 16-byte header (d, dmin, packed scales): the scales of code
+// chunk c's two sub-blocks; all zero for a row past N.
+__device__ __forceinline__ RowScales hdr_scales(const u32x4 &hdr, bool live, int c) {
+  const float d = live ? half_bits_to_float(hdr.x) : 0.f;
+  const float dmin = live ? half_bits_to_float(hdr.x >> 16) : 0.f;
   uint32_t sc0, m0s, sc1, m1s;
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c, sc0, m0s);
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, 2 * c + 1, sc1, m1s);
+  q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c, sc0, m0s);
+  q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, m1s);
   return RowScales{d * (float)sc0, dmin * (float)m0s, d * (float)sc1, dmin * (float)m1s};
+}
+
+__device__ __forceinline__ RowScales row_scales(const WRegs &r, bool live, int c) {
+  return hdr_scales(r.hdr, live, c);
 }
 
 // Part kk (0..3) of a W row's decode: code dwords 2kk, 2kk+1, i.e. positions
