@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
+BLOCK_BYTES = {4: 144, 5: 176, 6: 210}  # bytes per 256-weight super-block
+
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with the host C compiler (plain C, OpenMP)."""
@@ -40,12 +42,16 @@ def _load():
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_q4k_dequantize.argtypes = [p, i64, i64, p]
         lib.oracle_q4k_dequantize.restype = None
+        lib.oracle_q5k_dequantize.argtypes = [p, i64, i64, p]
+        lib.oracle_q5k_dequantize.restype = None
         lib.oracle_q6k_dequantize.argtypes = [p, i64, i64, p]
         lib.oracle_q6k_dequantize.restype = None
         lib.oracle_qmatmul.argtypes = [i32, p, p, i32, i64, i64, i64, p]
         lib.oracle_qmatmul.restype = i32
         lib.oracle_moe_q4k.argtypes = [p, i32, p, p, p, p, i64, i64, i64, i64, i64, p]
         lib.oracle_moe_q4k.restype = i32
+        lib.oracle_moe.argtypes = [p, i32, p, p, i32, p, p, i64, i64, i64, i64, i64, p]
+        lib.oracle_moe.restype = i32
         _lib = lib
     return _lib
 
@@ -68,6 +74,13 @@ def q4k_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
     return out
 
 
+def q5k_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
+    b = _blocks(blocks, N, K, 176)
+    out = np.empty((N, K), dtype=np.float32)
+    _load().oracle_q5k_dequantize(_ptr(b), N, K, _ptr(out))
+    return out
+
+
 def q6k_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
     b = _blocks(blocks, N, K, 210)
     out = np.empty((N, K), dtype=np.float32)
@@ -83,12 +96,12 @@ def _x(x: np.ndarray):
 
 
 def qmatmul(qtype: int, blocks: np.ndarray, x: np.ndarray, N: int, K: int) -> np.ndarray:
-    """float64 Y [M][N] = X [M][K] * dequant(W)^T; qtype 4 (Q4_K) or 6 (Q6_K)."""
+    """float64 Y [M][N] = X [M][K] * dequant(W)^T; qtype 4 (Q4_K), 5 (Q5_K) or 6 (Q6_K)."""
     xx, is_bf16 = _x(x)
     M = xx.shape[0]
     if xx.shape != (M, K):
         raise ValueError("x must be [M][K]")
-    b = _blocks(blocks, N, K, 144 if qtype == 4 else 210)
+    b = _blocks(blocks, N, K, BLOCK_BYTES[qtype])
     y = np.empty((M, N), dtype=np.float64)
     rc = _load().oracle_qmatmul(qtype, _ptr(b), _ptr(xx), is_bf16, M, N, K, _ptr(y))
     if rc:
@@ -100,23 +113,33 @@ def q4k_matmul(blocks, x, N, K):
     return qmatmul(4, blocks, x, N, K)
 
 
+def q5k_matmul(blocks, x, N, K):
+    return qmatmul(5, blocks, x, N, K)
+
+
 def q6k_matmul(blocks, x, N, K):
     return qmatmul(6, blocks, x, N, K)
 
 
-def moe_q4k(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, ids: np.ndarray,
-            gw: np.ndarray, E: int, H: int, F: int) -> np.ndarray:
-    """float64 routed MoE FFN output [T][H] (see oracle_moe_q4k in oracle.c)."""
+def moe(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, ids: np.ndarray,
+        gw: np.ndarray, E: int, H: int, F: int, down_qtype: int = 4) -> np.ndarray:
+    """float64 routed MoE FFN output [T][H] (see oracle_moe in oracle.c); the
+    gate+up experts are Q4_K, the down experts Q4_K (4) or Q5_K (5)."""
     xx, is_bf16 = _x(x)
     T = xx.shape[0]
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     gw = np.ascontiguousarray(gw, dtype=np.float32)
     top_k = ids.shape[1] if ids.ndim == 2 else 0
     b13 = _blocks(w13, E * 2 * F, H, 144)
-    b2 = _blocks(w2, E * H, F, 144)
+    b2 = _blocks(w2, E * H, F, BLOCK_BYTES[down_qtype])
     y = np.empty((T, H), dtype=np.float64)
-    rc = _load().oracle_moe_q4k(_ptr(xx), is_bf16, _ptr(b13), _ptr(b2), _ptr(ids),
-                                _ptr(gw), T, E, top_k, H, F, _ptr(y))
+    rc = _load().oracle_moe(_ptr(xx), is_bf16, _ptr(b13), _ptr(b2), down_qtype, _ptr(ids),
+                            _ptr(gw), T, E, top_k, H, F, _ptr(y))
     if rc:
-        raise RuntimeError("oracle_moe_q4k failed (%d)" % rc)
+        raise RuntimeError("oracle_moe failed (%d)" % rc)
     return y
+
+
+def moe_q4k(x, w13, w2, ids, gw, E: int, H: int, F: int) -> np.ndarray:
+    """float64 routed MoE FFN output [T][H] with Q4_K gate+up and down experts."""
+    return moe(x, w13, w2, ids, gw, E, H, F, 4)

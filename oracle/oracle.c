@@ -1,5 +1,5 @@
 /*
- * CPU oracle for the GGUF k-quant (Q4_K, Q6_K) dequantize-fused matmul.
+ * CPU oracle for the GGUF k-quant (Q4_K, Q5_K, Q6_K) dequantize-fused matmul.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this library. It shares no code, header or table
@@ -27,6 +27,13 @@
  *   nibbles to sub-block 2c+1 (weight l of a sub-block sits in byte 32c+l).
  *   w = d*sc_j*q - dmin*m_j.
  *
+ * Q5_K, 176 bytes (a reading: the pages name the type and its share of a
+ *   Q4_K_M file only): the Q4_K header (fp16 d @0, fp16 dmin @2, the same 12
+ *   packed scale/min bytes @4), a high-bit plane QH @16 (32 B) and the Q4_K
+ *   code bytes Q @48 (128 B). Weight l of sub-block j takes its low 4 bits as
+ *   in Q4_K and its fifth bit from bit j of QH[l]: q = lo | hi << 4 in 0..31.
+ *   w = d*sc_j*q - dmin*m_j.
+ *
  * Q6_K, 210 bytes: low-nibble plane QL @0 (128 B), high-2-bit plane QH @128
  *   (64 B), sixteen int8 scales @192 (one per 16 weights), fp16 d @208.
  *   Placement of the code bits (a reading; the pages name the type only):
@@ -37,10 +44,11 @@
  *
  * fp32 exactness of the dequant (why one fp32 formula is the reference):
  *   every product here is exact in fp32 (Q4_K d*sc*q has at most 11+6+4 = 21
- *   significant bits, dmin*m at most 17; Q6_K d*scale*(q-32) at most 11+7+5),
- *   so the Q4_K weight is the single correctly rounded value of the exact
- *   d*sc*q - dmin*m, whatever the evaluation order or FMA contraction, and the
- *   Q6_K weight is exact. Any correct fp32 implementation is bit-identical.
+ *   significant bits, Q5_K d*sc*q at most 11+6+5 = 22, dmin*m at most 17;
+ *   Q6_K d*scale*(q-32) at most 11+7+5), so a Q4_K or Q5_K weight is the
+ *   single correctly rounded value of the exact d*sc*q - dmin*m, whatever the
+ *   evaluation order or FMA contraction, and the Q6_K weight is exact. Any
+ *   correct fp32 implementation is bit-identical.
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +57,7 @@
 
 #define QK 256
 #define Q4K_BYTES 144
+#define Q5K_BYTES 176
 #define Q6K_BYTES 210
 
 /* IEEE 754 binary16 -> float, from the definition:
@@ -75,12 +84,9 @@ static float bf16_value(uint16_t b)
     return f;
 }
 
-static void q4k_block_dequant(const uint8_t *B, float *w)
+/* The 6-bit scales and mins of the eight sub-blocks (Q4_K and Q5_K). */
+static void kq_scales_mins(const uint8_t *S, int *sc, int *mn)
 {
-    const float d = fp16_value((uint16_t)(B[0] | B[1] << 8));
-    const float dmin = fp16_value((uint16_t)(B[2] | B[3] << 8));
-    const uint8_t *S = B + 4, *Q = B + 16;
-    int sc[8], mn[8];
     for (int j = 0; j < 4; j++) {
         sc[j] = S[j] & 63;
         mn[j] = S[j + 4] & 63;
@@ -89,14 +95,46 @@ static void q4k_block_dequant(const uint8_t *B, float *w)
         sc[j] = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
         mn[j] = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
     }
+}
+
+/* w = d*sc_j*q - dmin*m_j for the 256 codes q[i] (sub-block j = i/32). */
+static void kq_apply(const uint8_t *B, const int *q, float *w)
+{
+    const float d = fp16_value((uint16_t)(B[0] | B[1] << 8));
+    const float dmin = fp16_value((uint16_t)(B[2] | B[3] << 8));
+    int sc[8], mn[8];
+    kq_scales_mins(B + 4, sc, mn);
+    for (int i = 0; i < QK; i++) {
+        int j = i / 32;
+        float a = d * (float)sc[j];    /* exact */
+        float aq = a * (float)q[i];    /* exact */
+        float b = dmin * (float)mn[j]; /* exact */
+        w[i] = aq - b;                 /* the one rounding */
+    }
+}
+
+static void q4k_block_dequant(const uint8_t *B, float *w)
+{
+    const uint8_t *Q = B + 16;
+    int q[QK];
     for (int i = 0; i < QK; i++) {
         int j = i / 32, l = i % 32;
-        int q = (Q[32 * (j / 2) + l] >> (4 * (j % 2))) & 15;
-        float a = d * (float)sc[j];   /* exact */
-        float aq = a * (float)q;      /* exact */
-        float b = dmin * (float)mn[j]; /* exact */
-        w[i] = aq - b;                /* the one rounding */
+        q[i] = (Q[32 * (j / 2) + l] >> (4 * (j % 2))) & 15;
     }
+    kq_apply(B, q, w);
+}
+
+static void q5k_block_dequant(const uint8_t *B, float *w)
+{
+    const uint8_t *QH = B + 16, *Q = B + 48;
+    int q[QK];
+    for (int i = 0; i < QK; i++) {
+        int j = i / 32, l = i % 32;
+        int lo = (Q[32 * (j / 2) + l] >> (4 * (j % 2))) & 15;
+        int hi = (QH[l] >> j) & 1;
+        q[i] = lo | (hi << 4);
+    }
+    kq_apply(B, q, w);
 }
 
 static void q6k_block_dequant(const uint8_t *B, float *w)
@@ -124,6 +162,15 @@ void oracle_q4k_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *o
             q4k_block_dequant(blocks + (n * nb + b) * Q4K_BYTES, out + n * K + b * QK);
 }
 
+void oracle_q5k_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *out)
+{
+    const int64_t nb = K / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t b = 0; b < nb; b++)
+            q5k_block_dequant(blocks + (n * nb + b) * Q5K_BYTES, out + n * K + b * QK);
+}
+
 void oracle_q6k_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *out)
 {
     const int64_t nb = K / QK;
@@ -142,14 +189,15 @@ static void widen_x(const void *x, int x_is_bf16, int64_t M, int64_t K, double *
 }
 
 /* Y [M][N] float64 = X [M][K] * W^T for a quantized W [N][K].
- * qtype 4 = Q4_K, 6 = Q6_K. Each row of W is dequantized once into fp32, then
- * Y[m][n] = sum_k X[m][k] * W[n][k] in float64, k increasing. */
+ * qtype 4 = Q4_K, 5 = Q5_K, 6 = Q6_K. Each row of W is dequantized once into
+ * fp32, then Y[m][n] = sum_k X[m][k] * W[n][k] in float64, k increasing. */
 int oracle_qmatmul(int qtype, const uint8_t *blocks, const void *x, int x_is_bf16,
                    int64_t M, int64_t N, int64_t K, double *y)
 {
-    if (K % QK || M < 0 || N < 0 || (qtype != 4 && qtype != 6))
+    if (K % QK || M < 0 || N < 0 || (qtype != 4 && qtype != 5 && qtype != 6))
         return -1;
-    const int64_t nb = K / QK, bb = qtype == 4 ? Q4K_BYTES : Q6K_BYTES;
+    const int64_t nb = K / QK;
+    const int64_t bb = qtype == 4 ? Q4K_BYTES : qtype == 5 ? Q5K_BYTES : Q6K_BYTES;
     double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!xd)
         return -2;
@@ -163,6 +211,8 @@ int oracle_qmatmul(int qtype, const uint8_t *blocks, const void *x, int x_is_bf1
                 const uint8_t *blk = blocks + (n * nb + b) * bb;
                 if (qtype == 4)
                     q4k_block_dequant(blk, w + b * QK);
+                else if (qtype == 5)
+                    q5k_block_dequant(blk, w + b * QK);
                 else
                     q6k_block_dequant(blk, w + b * QK);
             }
@@ -182,11 +232,12 @@ int oracle_qmatmul(int qtype, const uint8_t *blocks, const void *x, int x_is_bf1
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
- * Routed MoE FFN with Q4_K experts, in float64.
+ * Routed MoE FFN with Q4_K gate+up experts, in float64.
  *   x      [T][H]  activations (bf16 bits or fp32)
  *   w13    [E][2F][H/256] Q4_K blocks: rows 0..F-1 are the gate projection,
  *          rows F..2F-1 the up projection (concatenated)
- *   w2     [E][H][F/256] Q4_K blocks: the down projection
+ *   w2     [E][H][F/256] blocks of type down_qtype (4 = Q4_K, 5 = Q5_K): the
+ *          down projection
  *   ids    [T][top_k] expert index per (token, slot), distinct within a row
  *   gw     [T][top_k] fp32 gate weight per (token, slot)
  *   y      [T][H] float64 output
@@ -196,12 +247,14 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * fp32 dequant is float64; silu(z) = z / (1 + exp(-z)).
  * Returns 0, or -1 for bad sizes / out-of-range ids.
  */
-int oracle_moe_q4k(const void *x, int x_is_bf16, const uint8_t *w13, const uint8_t *w2,
-                   const int32_t *ids, const float *gw, int64_t T, int64_t E,
-                   int64_t top_k, int64_t H, int64_t F, double *y)
+int oracle_moe(const void *x, int x_is_bf16, const uint8_t *w13, const uint8_t *w2,
+               int down_qtype, const int32_t *ids, const float *gw, int64_t T, int64_t E,
+               int64_t top_k, int64_t H, int64_t F, double *y)
 {
-    if (H % QK || F % QK || T < 0 || E <= 0 || top_k <= 0)
+    if (H % QK || F % QK || T < 0 || E <= 0 || top_k <= 0 ||
+        (down_qtype != 4 && down_qtype != 5))
         return -1;
+    const int64_t b2 = down_qtype == 4 ? Q4K_BYTES : Q5K_BYTES;
     for (int64_t i = 0; i < T * top_k; i++)
         if (ids[i] < 0 || ids[i] >= E)
             return -1;
@@ -224,7 +277,10 @@ int oracle_moe_q4k(const void *x, int x_is_bf16, const uint8_t *w13, const uint8
         if (!used)
             continue;
         oracle_q4k_dequantize(w13 + e * 2 * F * nbH * Q4K_BYTES, 2 * F, H, W13);
-        oracle_q4k_dequantize(w2 + e * H * nbF * Q4K_BYTES, H, F, W2);
+        if (down_qtype == 4)
+            oracle_q4k_dequantize(w2 + e * H * nbF * b2, H, F, W2);
+        else
+            oracle_q5k_dequantize(w2 + e * H * nbF * b2, H, F, W2);
 #pragma omp parallel
         {
             double *u = (double *)malloc(sizeof(double) * (size_t)(2 * F));
@@ -263,4 +319,11 @@ int oracle_moe_q4k(const void *x, int x_is_bf16, const uint8_t *w13, const uint8
         }
     free(xd); free(o); free(W13); free(W2);
     return 0;
+}
+
+int oracle_moe_q4k(const void *x, int x_is_bf16, const uint8_t *w13, const uint8_t *w2,
+                   const int32_t *ids, const float *gw, int64_t T, int64_t E,
+                   int64_t top_k, int64_t H, int64_t F, double *y)
+{
+    return oracle_moe(x, x_is_bf16, w13, w2, 4, ids, gw, T, E, top_k, H, F, y);
 }

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the Q4_K / Q6_K dequantize-fused matmul.
+"""Seeded synthetic inputs for the Q4_K / Q5_K / Q6_K dequantize-fused matmul.
 
 Both the CPU oracle (``oracle/``) and the HIP library are fed from this module,
 and it is the only thing they share. It holds none of the method's arithmetic:
@@ -13,12 +13,17 @@ Why random bytes are enough for the packed fields
   independent uniform values in 0..63. (The oracle tests check the bijection
   exhaustively through the oracle's own decoder.)
 * Q4_K codes: 128 uniform bytes are 256 independent uniform nibbles 0..15.
+* Q5_K codes: the 32 high-bit bytes and 128 low-nibble bytes carry exactly
+  256 x 5 bits, so uniform bytes give uniform codes 0..31; the scales/mins
+  are packed as in Q4_K.
 * Q6_K codes: the 128 low-nibble bytes and 64 high-2-bit bytes carry exactly
   256 x 6 bits; uniform bytes give uniform codes 0..63 under any one-to-one
   placement of the bits.
 
 Field placement (little-endian fp16):
   Q4_K, 144 B: d @0..1, dmin @2..3, packed scales/mins @4..15, codes @16..143.
+  Q5_K, 176 B: d @0..1, dmin @2..3, packed scales/mins @4..15,
+               high bits @16..47, low nibbles @48..175.
   Q6_K, 210 B: low nibbles @0..127, high 2 bits @128..191,
                int8 sub-block scales @192..207, d @208..209.
 
@@ -26,7 +31,7 @@ The Q4_K and Q6_K families are the GGUF k-quant tensor types that make up a
 Q4_K_M file (hipEngine README, "GGUF Support", payload-by-tensor-family table).
 
 Value distributions (per workload): d, dmin uniform in [1e-3, 1e-2]
-(Q4_K) or d uniform in [1e-4, 1e-3] (Q6_K), each drawn in float64 and rounded
+(Q4_K, Q5_K) or d uniform in [1e-4, 1e-3] (Q6_K), each drawn in float64 and rounded
 to fp16 (round to nearest even); Q6_K scales uniform int8 in [-64, 63];
 activations N(0, 1) drawn in float32, rounded to bf16 (nearest even) where the
 workload is bf16.
@@ -36,6 +41,7 @@ from __future__ import annotations
 import numpy as np
 
 Q4K_BLOCK_BYTES = 144
+Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 QK = 256  # weights per super-block
 
@@ -62,6 +68,19 @@ def q4k_blocks(rng: np.random.Generator, N: int, K: int,
     out[:, :, 0:2] = _fp16_bytes(rng.uniform(*d_range, size=(N, nb)))
     out[:, :, 2:4] = _fp16_bytes(rng.uniform(*dmin_range, size=(N, nb)))
     out[:, :, 4:] = rng.integers(0, 256, size=(N, nb, 140), dtype=np.uint8)
+    return out
+
+
+def q5k_blocks(rng: np.random.Generator, N: int, K: int,
+               d_range=(1e-3, 1e-2), dmin_range=(1e-3, 1e-2)) -> np.ndarray:
+    """Random Q5_K tensor: uint8 array [N, K/256, 176], rows contiguous."""
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    nb = K // QK
+    out = np.empty((N, nb, Q5K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = _fp16_bytes(rng.uniform(*d_range, size=(N, nb)))
+    out[:, :, 2:4] = _fp16_bytes(rng.uniform(*dmin_range, size=(N, nb)))
+    out[:, :, 4:] = rng.integers(0, 256, size=(N, nb, 172), dtype=np.uint8)
     return out
 
 
@@ -122,6 +141,10 @@ MOE = dict(name="moe_q4k_top8", seed=3, E=128, H=2048, F=768, top_k=8,
            Ts=(1, 8, 512))
 Q6K_MIX = dict(name="q6k_gemv", seed=4,
                shapes=[("head", 5120, 151936, (1, 8)), ("down", 17408, 5120, (1,))])
+# Q5_K: in a Q4_K_M file the MoE expert-down tensors are Q5_K. The dense GEMV
+# takes the decode set's down shape (K=17408, N=5120); the MoE workload is the
+# Q4_K one with its down experts drawn as Q5_K.
+Q5K_GEMV = dict(name="q5k_gemv", seed=5, K=17408, N=5120, Ms=(1, 8))
 
 
 def tiny_gemv():
@@ -149,12 +172,16 @@ def prefill_gemm(M: int):
 
 
 def moe(T: int, E: int = MOE["E"], H: int = MOE["H"], F: int = MOE["F"],
-        top_k: int = MOE["top_k"], seed: int = MOE["seed"]):
+        top_k: int = MOE["top_k"], seed: int = MOE["seed"], down_qtype: int = 4):
     """MoE FFN inputs: x bf16 [T][H]; gate+up Q4_K [E][2F][H/256];
-    down Q4_K [E][H][F/256]; routing ids/weights [T][top_k]."""
+    down Q4_K (down_qtype 4) or Q5_K (5) [E][H][F/256]; routing ids/weights
+    [T][top_k]."""
     g_13, g_2, g_x, g_r = streams(seed, 4)
     w13 = q4k_blocks(g_13, E * 2 * F, H).reshape(E, 2 * F, H // QK, Q4K_BLOCK_BYTES)
-    w2 = q4k_blocks(g_2, E * H, F).reshape(E, H, F // QK, Q4K_BLOCK_BYTES)
+    if down_qtype == 5:
+        w2 = q5k_blocks(g_2, E * H, F).reshape(E, H, F // QK, Q5K_BLOCK_BYTES)
+    else:
+        w2 = q4k_blocks(g_2, E * H, F).reshape(E, H, F // QK, Q4K_BLOCK_BYTES)
     x = normal_bf16(g_x, (T, H))
     ids, gw = routing(g_r, T, E, top_k)
     return dict(x=x, w13=w13, w2=w2, ids=ids, gw=gw)
@@ -166,4 +193,11 @@ def q6k_gemv(which: str, M: int):
     g = streams(Q6K_MIX["seed"], 2 * len(Q6K_MIX["shapes"]))
     w = q6k_blocks(g[2 * idx], N, K)
     x = normal_bf16(g[2 * idx + 1], (M, K))
+    return w, x
+
+
+def q5k_gemv(M: int):
+    g_w, g_x = streams(Q5K_GEMV["seed"], 2)
+    w = q5k_blocks(g_w, Q5K_GEMV["N"], Q5K_GEMV["K"])
+    x = normal_bf16(g_x, (M, Q5K_GEMV["K"]))
     return w, x

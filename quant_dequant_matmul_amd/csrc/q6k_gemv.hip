@@ -119,6 +119,92 @@ __device__ __forceinline__ Q6Lane q6_load(const uint8_t *__restrict__ w, int64_t
   return L;
 }
 
+// One block's contribution for every row m of x: lane (h, l0)'s 64 weights
+// against x staged in LDS, added to acc[m] (4 dot-product groups of 16, each
+// scaled by its sub-block scale).
+template <bool XBF16, int MT>
+__device__ __forceinline__ void q6_block(const Q6Lane &L, const uint32_t *lds_x,
+                                         const float *lds_sum, int K, int kb, int h, int l0,
+                                         float (&acc)[MT]) {
+  const float d = half_bits_to_float(L.dbits);
+  // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
+  // of the 8 scale bytes s0|s1.
+  const int sb = l0 >> 4;
+  float dsc[4];
+#pragma unroll
+  for (int gq = 0; gq < 4; gq++) {
+    const int bi = 2 * gq + sb;
+    const uint32_t word = bi < 4 ? L.s0 : L.s1;
+    dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+  }
+  const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+  const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+  const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+  if constexpr (XBF16) {
+    // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
+    uint32_t pr[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t a = qa[k], b = qb[k], hh = qh[k];
+      pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
+      pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
+      pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
+      pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
+      pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
+      pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
+      pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
+      pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      float r = acc[m];
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;  // first x element
+        const u32x4 *xv = (const u32x4 *)(lds_x + e0 / 2);
+        const float xs = lds_sum[e0 / 16];
+        const u32x4 x0 = xv[0], x1 = xv[1];  // l0..l0+7, l0+8..l0+15
+        float s = 0.f;
+        s = dot2_bf16(pr[gq][0], x0.x, s);
+        s = dot2_bf16(pr[gq][1], x0.y, s);
+        s = dot2_bf16(pr[gq][2], x0.z, s);
+        s = dot2_bf16(pr[gq][3], x0.w, s);
+        s = dot2_bf16(pr[gq][4], x1.x, s);
+        s = dot2_bf16(pr[gq][5], x1.y, s);
+        s = dot2_bf16(pr[gq][6], x1.z, s);
+        s = dot2_bf16(pr[gq][7], x1.w, s);
+        r = fmaf(dsc[gq], fmaf(-160.f, xs, s), r);
+      }
+      acc[m] = r;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      float r = acc[m];
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;
+        const f32x4 *xv = (const f32x4 *)((const float *)lds_x + e0);
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const f32x4 xx = xv[k];
+          const uint32_t src = (gq & 1) ? qb[k] : qa[k];
+          const int nsh = (gq >> 1) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int lo = (int)((src >> (8 * e + nsh)) & 15u);
+            const int hi = (int)((qh[k] >> (8 * e + 2 * gq)) & 3u);
+            s = fmaf(xx[e], (float)((lo | (hi << 4)) - 32), s);
+          }
+        }
+        r = fmaf(dsc[gq], s, r);
+      }
+      acc[m] = r;
+    }
+  }
+}
+
 // Each workgroup stages x once and then streams row groups blockIdx.x,
 // blockIdx.x + gridDim.x, ... (a row group = R rows per wave). A wave walks
 // its (row group, block iteration) pairs as one flat sequence with PF of them
@@ -176,83 +262,7 @@ __global__ __launch_bounds__(THREADS) void q6k_gemv_kernel(
         const int kb = it * G + gg;
         const Q6Lane L = buf[p];
         buf[p] = q6_load(w, blk_off(f + PF), h, l0);
-        const float d = half_bits_to_float(L.dbits);
-        // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
-        // of the 8 scale bytes s0|s1.
-        const int sb = l0 >> 4;
-        float dsc[4];
-#pragma unroll
-        for (int gq = 0; gq < 4; gq++) {
-          const int bi = 2 * gq + sb;
-          const uint32_t word = bi < 4 ? L.s0 : L.s1;
-          dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
-        }
-        const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
-        const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-        const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
-        if constexpr (XBF16) {
-          // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
-          uint32_t pr[4][8];
-#pragma unroll
-          for (int k = 0; k < 4; k++) {
-            const uint32_t a = qa[k], b = qb[k], hh = qh[k];
-            pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
-            pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
-            pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
-            pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
-            pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
-            pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
-            pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
-            pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
-          }
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            float r = acc[m];
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-              const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;  // first x element
-              const u32x4 *xv = (const u32x4 *)(lds_x + e0 / 2);
-              const float xs = lds_sum[e0 / 16];
-              const u32x4 x0 = xv[0], x1 = xv[1];  // l0..l0+7, l0+8..l0+15
-              float s = 0.f;
-              s = dot2_bf16(pr[gq][0], x0.x, s);
-              s = dot2_bf16(pr[gq][1], x0.y, s);
-              s = dot2_bf16(pr[gq][2], x0.z, s);
-              s = dot2_bf16(pr[gq][3], x0.w, s);
-              s = dot2_bf16(pr[gq][4], x1.x, s);
-              s = dot2_bf16(pr[gq][5], x1.y, s);
-              s = dot2_bf16(pr[gq][6], x1.z, s);
-              s = dot2_bf16(pr[gq][7], x1.w, s);
-              r = fmaf(dsc[gq], fmaf(-160.f, xs, s), r);
-            }
-            acc[m] = r;
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            float r = acc[m];
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-              const int e0 = m * K + kb * QK + 128 * h + 32 * gq + l0;
-              const f32x4 *xv = (const f32x4 *)((const float *)lds_x + e0);
-              float s = 0.f;
-#pragma unroll
-              for (int k = 0; k < 4; k++) {
-                const f32x4 xx = xv[k];
-                const uint32_t src = (gq & 1) ? qb[k] : qa[k];
-                const int nsh = (gq >> 1) * 4;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                  const int lo = (int)((src >> (8 * e + nsh)) & 15u);
-                  const int hi = (int)((qh[k] >> (8 * e + 2 * gq)) & 3u);
-                  s = fmaf(xx[e], (float)((lo | (hi << 4)) - 32), s);
-                }
-              }
-              r = fmaf(dsc[gq], s, r);
-            }
-            acc[m] = r;
-          }
-        }
+        q6_block<XBF16, MT>(L, lds_x, lds_sum, K, kb, h, l0, acc);
         if (it == iters - 1) {  // uniform: the row group ends, store its rows
           const int row = row_of(f);
 #pragma unroll

@@ -1,4 +1,4 @@
-"""Test-only packers and a grid quantizer for Q4_K / Q6_K super-blocks.
+"""Test-only packers and a grid quantizer for Q4_K / Q5_K / Q6_K super-blocks.
 
 They encode fields into bytes (the inverse direction of every decoder), written
 from the format description:
@@ -10,6 +10,8 @@ Q4_K (144 B): fp16 d @0, fp16 dmin @2, 12 packed bytes @4, 128 code bytes @16.
   of bytes 0-3 and those of mins 4-7 in the top bits of bytes 4-7. Code chunk c
   (32 bytes) gives its low nibbles to sub-block 2c and its high nibbles to
   sub-block 2c+1.
+Q5_K (176 B): the Q4_K header @0..15, a high-bit plane @16 (32 B: bit j of
+  byte l is the fifth bit of weight l of sub-block j), the Q4_K code bytes @48.
 Q6_K (210 B): low-nibble plane @0 (128 B), high-2-bit plane @128 (64 B),
   16 int8 scales @192, fp16 d @208; bit placement as read in the oracle.
 """
@@ -53,6 +55,22 @@ def pack_q4k(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
     return b
 
 
+def pack_q5k(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
+    """Q5_K (176 B): the Q4_K header, then the high-bit plane @16 (bit j of byte
+    l is the fifth bit of weight l of sub-block j), then the Q4_K code bytes of
+    the low 4 bits @48."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.shape == (256,) and q.min() >= 0 and q.max() < 32
+    b4 = pack_q4k(d_bits, dmin_bits, sc, mn, q & 15)
+    b = np.zeros(176, dtype=np.uint8)
+    b[0:16] = b4[0:16]
+    for j in range(8):
+        for l in range(32):
+            b[16 + l] |= (int(q[32 * j + l]) >> 4) << j
+    b[48:176] = b4[16:144]
+    return b
+
+
 def pack_q6k(d_bits: int, scales, q) -> np.ndarray:
     scales = [int(v) for v in scales]
     q = np.asarray(q, dtype=np.int64)
@@ -84,20 +102,25 @@ def q4k_exact_weights(d_bits, dmin_bits, sc, mn, q):
     return [d * int(sc[i // 32]) * int(q[i]) - dmin * int(mn[i // 32]) for i in range(256)]
 
 
+def q5k_exact_weights(d_bits, dmin_bits, sc, mn, q):
+    return q4k_exact_weights(d_bits, dmin_bits, sc, mn, q)  # same formula, q in 0..31
+
+
 def q6k_exact_weights(d_bits, scales, q):
     d = Fraction(fp16_value(d_bits))
     return [d * int(scales[i // 16]) * (int(q[i]) - 32) for i in range(256)]
 
 
-def grid_quantize_q4k(w: list[Fraction], d: Fraction, dmin: Fraction):
-    """Recover (sc, m, q) of a Q4_K block from exact weights on the grid
-    w = d*sc*q - dmin*m, for sub-blocks that contain both q = 0 and q = 15:
-    m = -min(w)/dmin, sc = (max(w) + dmin*m) / (15 d), q = (w + dmin*m)/(d*sc)."""
+def grid_quantize_q4k(w: list[Fraction], d: Fraction, dmin: Fraction, qmax: int = 15):
+    """Recover (sc, m, q) of a Q4_K (qmax 15) or Q5_K (qmax 31) block from exact
+    weights on the grid w = d*sc*q - dmin*m, for sub-blocks that contain both
+    q = 0 and q = qmax: m = -min(w)/dmin, sc = (max(w) + dmin*m) / (qmax d),
+    q = (w + dmin*m)/(d*sc)."""
     sc, mn, q = [], [], []
     for j in range(8):
         sub = w[32 * j:32 * j + 32]
         m = -min(sub) / dmin
-        s = (max(sub) + dmin * m) / (15 * d)
+        s = (max(sub) + dmin * m) / (qmax * d)
         assert m.denominator == 1 and s.denominator == 1
         mn.append(int(m))
         sc.append(int(s))

@@ -4,8 +4,10 @@ mathematics fix, never against the oracle itself.
 * Raw-byte placement: single bits/nibbles set directly in the block bytes land
   on exactly the weight the format description says (no packer involved).
 * Exhaustive 6-bit scale/min slots (16 slots x 64 values).
-* Closed forms: all-equal fields give w = d*sc*q - dmin*m (Q4_K) and
+* Closed forms: all-equal fields give w = d*sc*q - dmin*m (Q4_K, Q5_K) and
   w = d*scale*(q-32) (Q6_K), rounded once from the exact rational.
+* Q5_K against Q4_K: with an empty high-bit plane a Q5_K block decodes
+  exactly like the Q4_K block with the same header and code bytes.
 * fp16 decoding of d over every finite fp16 pattern vs numpy's conversion.
 * Round trip through an independent grid quantizer.
 * Matmul: exact rationals on tiny shapes within the fp64 summation bound,
@@ -22,8 +24,9 @@ import pytest
 
 import oracle
 import qdm_synth as synth
-from kquant_pack import (fp16_bits, fp16_value, grid_quantize_q4k, pack_q4k,
-                         pack_q6k, q4k_exact_weights, q6k_exact_weights, rn32)
+from kquant_pack import (fp16_bits, fp16_value, grid_quantize_q4k, pack_q4k, pack_q5k,
+                         pack_q6k, q4k_exact_weights, q5k_exact_weights, q6k_exact_weights,
+                         rn32)
 
 ONE = 0x3C00  # fp16 1.0
 
@@ -277,6 +280,115 @@ def test_q6k_round_trip_codes():
 
 
 # --------------------------------------------------------------------------
+# Q5_K
+# --------------------------------------------------------------------------
+
+def _blank_q5k(n, d=ONE, dmin=ONE):
+    b = np.zeros((n, 176), dtype=np.uint8)
+    b[:, 0], b[:, 1] = d & 255, d >> 8
+    b[:, 2], b[:, 3] = dmin & 255, dmin >> 8
+    b[:, 4:8] = 1    # sc_0..3 = 1
+    b[:, 12:16] = 1  # sc_4..7 = 1; every min 0
+    return b
+
+
+def test_q5k_code_bit_placement_from_bytes():
+    """Raw bytes, no packer (d = 1, sc = 1, m = 0, so w = q): the low nibble
+    of byte 48+32c+l is weight l of sub-block 2c and its high nibble weight l
+    of sub-block 2c+1 (value 15); bit j of byte 16+l is the fifth bit of weight
+    l of sub-block j (value 16)."""
+    cases = []
+    for c in range(4):
+        for l in range(32):
+            for hi in (0, 1):
+                b = _blank_q5k(1)[0]
+                b[48 + 32 * c + l] = 0xF0 if hi else 0x0F
+                cases.append((b, 64 * c + 32 * hi + l, 15.0))
+    for j in range(8):
+        for l in range(32):
+            b = _blank_q5k(1)[0]
+            b[16 + l] = 1 << j
+            cases.append((b, 32 * j + l, 16.0))
+    W = oracle.q5k_dequantize(np.stack([c[0] for c in cases]), len(cases), 256)
+    for (_, k, v), w in zip(cases, W):
+        exp = np.zeros(256, dtype=np.float32)
+        exp[k] = v
+        np.testing.assert_array_equal(w, exp)
+
+
+def test_q5k_empty_high_plane_decodes_as_q4k():
+    """Random headers (d, dmin, packed scales/mins) and code bytes with the
+    high-bit plane zero: the Q5_K weights equal the Q4_K weights of the block
+    made of the same header and code bytes (the Q4_K decode is pinned above)."""
+    rng = np.random.default_rng(51)
+    w4 = synth.q4k_blocks(rng, 64, 256)[:, 0]
+    w5 = np.zeros((64, 176), dtype=np.uint8)
+    w5[:, 0:16] = w4[:, 0:16]
+    w5[:, 48:176] = w4[:, 16:144]
+    np.testing.assert_array_equal(oracle.q5k_dequantize(w5, 64, 256),
+                                  oracle.q4k_dequantize(w4, 64, 256))
+
+
+def test_q5k_closed_form_all_equal():
+    rng = np.random.default_rng(52)
+    blocks, expect = [], []
+    for _ in range(400):
+        d = fp16_bits(rng.uniform(1e-3, 1e-2))
+        dm = fp16_bits(rng.uniform(1e-3, 1e-2))
+        s, m, q = int(rng.integers(0, 64)), int(rng.integers(0, 64)), int(rng.integers(0, 32))
+        blocks.append(pack_q5k(d, dm, [s] * 8, [m] * 8, [q] * 256))
+        expect.append(rn32(Fraction(fp16_value(d)) * s * q - Fraction(fp16_value(dm)) * m))
+    W = oracle.q5k_dequantize(np.stack(blocks), len(blocks), 256)
+    for w, e in zip(W, expect):
+        assert np.all(w == e) and w.dtype == np.float32
+
+
+def test_q5k_random_fields_single_rounding():
+    """Every weight is the correctly rounded fp32 value of the exact rational
+    d*sc*q - dmin*m (q in 0..31; at most 22 significant bits in d*sc*q)."""
+    rng = np.random.default_rng(53)
+    for _ in range(30):
+        d = fp16_bits(rng.uniform(1e-3, 1e-2))
+        dm = fp16_bits(rng.uniform(1e-3, 1e-2))
+        sc, mn = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+        q = rng.integers(0, 32, 256)
+        w = oracle.q5k_dequantize(pack_q5k(d, dm, sc, mn, q)[None], 1, 256)[0]
+        ex = q5k_exact_weights(d, dm, sc, mn, q)
+        assert all(w[i] == rn32(ex[i]) for i in range(256))
+
+
+def test_q5k_grid_round_trip():
+    """Exact grid weights (q in 0..31, each sub-block holding 0 and 31) ->
+    independent grid quantizer -> pack -> oracle: fields recovered exactly and
+    every weight bit-equal."""
+    rng = np.random.default_rng(54)
+    for _ in range(20):
+        d = fp16_bits(rng.uniform(1e-3, 1e-2))
+        dm = fp16_bits(rng.uniform(1e-3, 1e-2))
+        sc, mn = rng.integers(1, 64, 8), rng.integers(0, 64, 8)
+        q = rng.integers(0, 32, 256)
+        for j in range(8):
+            pos = rng.choice(32, 2, replace=False)
+            q[32 * j + pos[0]], q[32 * j + pos[1]] = 0, 31
+        exact = q5k_exact_weights(d, dm, sc, mn, q)
+        rs, rm, rq = grid_quantize_q4k(exact, Fraction(fp16_value(d)),
+                                       Fraction(fp16_value(dm)), qmax=31)
+        assert rs == list(sc) and rm == list(mn) and rq == list(q)
+        w = oracle.q5k_dequantize(pack_q5k(d, dm, rs, rm, rq)[None], 1, 256)[0]
+        assert all(w[i] == rn32(exact[i]) for i in range(256))
+
+
+def test_q5k_synthetic_fields_in_range():
+    """Synthetic blocks decode inside -dmin*63 <= w <= d*63*31, and every code
+    value 0..31 occurs (uniform bytes cover the 5-bit range)."""
+    w = synth.q5k_blocks(np.random.default_rng(2), 64, 512)
+    W = oracle.q5k_dequantize(w, 64, 512)
+    assert W.max() <= 1e-2 * 1.001 * 63 * 31 and W.min() >= -1e-2 * 1.001 * 63
+    hb = np.unpackbits(w[:, :, 16:48].reshape(-1, 32), axis=1, bitorder="little")
+    assert 0.45 < hb.mean() < 0.55
+
+
+# --------------------------------------------------------------------------
 # Matmul (fp64 accumulation)
 # --------------------------------------------------------------------------
 
@@ -284,17 +396,21 @@ def _bf16_to_f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("qtype", [4, 6])
+_GEN = {4: synth.q4k_blocks, 5: synth.q5k_blocks, 6: synth.q6k_blocks}
+_DEQ = {4: oracle.q4k_dequantize, 5: oracle.q5k_dequantize, 6: oracle.q6k_dequantize}
+
+
+@pytest.mark.parametrize("qtype", [4, 5, 6])
 @pytest.mark.parametrize("xbf16", [False, True])
 def test_matmul_exact_rationals(qtype, xbf16):
     """Oracle fp64 result vs the exact rational sum: within the fp64
     recursive-summation bound (K-1) 2^-53 sum|x w| (products are exact)."""
     rng = np.random.default_rng(31 + qtype + 2 * xbf16)
     N, K, M = 5, 512, 3
-    w = synth.q4k_blocks(rng, N, K) if qtype == 4 else synth.q6k_blocks(rng, N, K)
+    w = _GEN[qtype](rng, N, K)
     x = synth.normal_bf16(rng, (M, K)) if xbf16 else synth.normal_f32(rng, (M, K))
     xf = _bf16_to_f32(x) if xbf16 else x
-    W = (oracle.q4k_dequantize if qtype == 4 else oracle.q6k_dequantize)(w, N, K)
+    W = _DEQ[qtype](w, N, K)
     Y = oracle.qmatmul(qtype, w, x, N, K)
     for m in range(M):
         for n in range(N):
@@ -412,3 +528,35 @@ def test_moe_rejects_bad_ids():
     ids[1, 1] = 4
     with pytest.raises(RuntimeError):
         oracle.moe_q4k(d["x"], d["w13"], d["w2"], ids, d["gw"], 4, 256, 256)
+
+
+def test_moe_q5k_down_empty_high_plane_matches_q4k_down():
+    """Down experts as Q5_K with an empty high-bit plane and the same header and
+    code bytes as the Q4_K down experts: the same FFN, bit for bit."""
+    E, H, F, T = 4, 256, 256, 3
+    d = synth.moe(T, E=E, H=H, F=F, top_k=2, seed=9)
+    w2q4 = d["w2"]
+    w2q5 = np.zeros(w2q4.shape[:-1] + (176,), dtype=np.uint8)
+    w2q5[..., 0:16] = w2q4[..., 0:16]
+    w2q5[..., 48:176] = w2q4[..., 16:144]
+    y4 = oracle.moe(d["x"], d["w13"], w2q4, d["ids"], d["gw"], E, H, F, 4)
+    y5 = oracle.moe(d["x"], d["w13"], w2q5, d["ids"], d["gw"], E, H, F, 5)
+    np.testing.assert_array_equal(y4, y5)
+
+
+def test_moe_q5k_down_one_hot_gate_dense():
+    """Q5_K down experts, gate one-hot on slot 0: a single expert's FFN as
+    dense numpy products on the dequantized weights."""
+    E, H, F, T = 5, 256, 512, 4
+    d = synth.moe(T, E=E, H=H, F=F, top_k=3, seed=8, down_qtype=5)
+    gw1 = np.zeros_like(d["gw"])
+    gw1[:, 0] = 1.0
+    y1 = oracle.moe(d["x"], d["w13"], d["w2"], d["ids"], gw1, E, H, F, 5)
+    xf = _bf16_to_f32(d["x"]).astype(np.float64)
+    for t in range(T):
+        e = d["ids"][t, 0]
+        W13 = oracle.q4k_dequantize(d["w13"][e], 2 * F, H).astype(np.float64)
+        W2 = oracle.q5k_dequantize(d["w2"][e], H, F).astype(np.float64)
+        u = W13 @ xf[t]
+        h = u[:F] / (1 + np.exp(-u[:F])) * u[F:]
+        np.testing.assert_allclose(y1[t], W2 @ h, rtol=1e-11, atol=1e-11 * np.abs(W2 @ h).max())
