@@ -1,5 +1,5 @@
 /*
- * qdm.h — C ABI of the Q4_K / Q6_K dequantize-fused matmul library for
+ * qdm.h — C ABI of the Q4_K / Q5_K / Q6_K dequantize-fused matmul library for
  * MI355X (gfx950). Shared library: libqdm.so.
  *
  * What it computes. GGUF k-quant weights stay packed in HBM and are decoded on
@@ -17,6 +17,13 @@
  *     scales/mins @4, 128 bytes of 4-bit codes @16 (chunk c of 32 bytes holds
  *     sub-block 2c in its low nibbles and 2c+1 in its high nibbles);
  *     w = d * sc_j * q - dmin * m_j for the 32-weight sub-block j.
+ *   Q5_K (176-byte block): the Q4_K header (d @0, dmin @2, packed scales/mins
+ *     @4), 32 bytes of fifth code bits @16 (bit j of byte l belongs to weight l
+ *     of sub-block j), and the Q4_K arrangement of 128 bytes of low 4 bits
+ *     @48; q = low | fifth << 4 in 0..31 and w = d * sc_j * q - dmin * m_j.
+ *     The pages name Q5_K as the expert-down type of a Q4_K_M file (hipEngine
+ *     README, "GGUF Support", payload table) without its byte layout; this
+ *     layout is the reading the library and its tests share.
  *   Q6_K (210-byte block): 128 bytes of low 4 bits @0, 64 bytes of high 2 bits
  *     @128, 16 int8 scales @192 (one per 16 weights), fp16 d @208;
  *     w = d * scale * (q - 32), q in 0..63.
@@ -67,17 +74,19 @@ const char *qdm_status_string(int status);
 int qdm_version(void);
 
 /*
- * q4k_dequantize / q6k_dequantize: out[n][k] (fp32, [N][K] row-major) = the
- * value of weight (n, k), bit-identical to the format formula evaluated in
- * fp32 (every product in it is exact in fp32, so the result is the single
- * correctly rounded value; Q6_K values are exact). Test-facing.
+ * q4k_dequantize / q5k_dequantize / q6k_dequantize: out[n][k] (fp32, [N][K]
+ * row-major) = the value of weight (n, k), bit-identical to the format formula
+ * evaluated in fp32 (every product in it is exact in fp32, so the result is
+ * the single correctly rounded value; Q6_K values are exact). Test-facing.
  * N >= 1, K >= 256, K % 256 == 0.
  */
 int q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
+int q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
 int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
 
 /*
- * q4k_gemv / q6k_gemv: decode-regime matmul, y[m][n] = sum_k x[m][k] * w(n,k)
+ * q4k_gemv / q5k_gemv / q6k_gemv: decode-regime matmul,
+ * y[m][n] = sum_k x[m][k] * w(n,k)
  * for 1 <= M <= 16. x_dtype is QDM_F32 or QDM_BF16. Accumulation is fp32.
  * N >= 1, K >= 256, K % 256 == 0, K <= 65536 (bf16 x) or K <= 32768 (fp32 x):
  * one activation row is staged in the 160 KiB LDS of a compute unit.
@@ -87,6 +96,8 @@ int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream
  * weights in fp32. Results are deterministic.
  */
 int q4k_gemv(const void *w, const void *x, int x_dtype, float *y,
+             int64_t M, int64_t N, int64_t K, void *stream);
+int q5k_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);
 int q6k_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);

@@ -50,6 +50,14 @@ QDM_EXPORT int q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, v
   return finish_launch();
 }
 
+QDM_EXPORT int q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream) {
+  if (!w || !out) return QDM_ERR_NULL;
+  if (N < 1 || bad_k(K)) return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(out)) return QDM_ERR_ALIGN;
+  qdm::launch_q5k_dequantize(w, out, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
 QDM_EXPORT int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream) {
   if (!w || !out) return QDM_ERR_NULL;
   if (N < 1 || bad_k(K)) return QDM_ERR_SHAPE;
@@ -73,6 +81,14 @@ QDM_EXPORT int q4k_gemv(const void *w, const void *x, int x_dtype, float *y, int
   const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
   if (rc) return rc;
   qdm::launch_q4k_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int q5k_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+  const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
+  if (rc) return rc;
+  qdm::launch_q5k_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -8,6 +8,7 @@ namespace qdm {
 
 constexpr int QK = 256;          // weights per super-block
 constexpr int Q4K_BYTES = 144;   // Q4_K super-block
+constexpr int Q5K_BYTES = 176;   // Q5_K super-block: Q4_K header, 32 high-bit bytes, 128 code bytes
 constexpr int Q6K_BYTES = 210;   // Q6_K super-block
 constexpr int WAVE = 64;
 

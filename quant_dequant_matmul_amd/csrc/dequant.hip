@@ -1,7 +1,8 @@
-// Bit-exact dequantization of packed Q4_K / Q6_K tensors to fp32 [N][K].
+// Bit-exact dequantization of packed Q4_K / Q5_K / Q6_K tensors to fp32 [N][K].
 //
 // Weight formulas (GGUF k-quant tensor families named in the hipEngine README,
-// "GGUF Support"): Q4_K w = d*sc_j*q - dmin*m_j; Q6_K w = d*scale*(q-32).
+// "GGUF Support"): Q4_K and Q5_K w = d*sc_j*q - dmin*m_j (Q5_K codes carry a
+// fifth bit from a 32-byte high-bit plane); Q6_K w = d*scale*(q-32).
 // Every product is exact in fp32, so computing them in fp32 and subtracting
 // once gives the correctly rounded value whatever the evaluation order.
 #include "common.h"
@@ -33,6 +34,38 @@ __global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t *__restr
     r1[e] = a * (float)((q.y >> (8 * e + sh)) & 15u) - b;
   }
   // out is [N][K] with K = 256 * (blocks per row): block blk starts at blk*256.
+  f32x4 *o = (f32x4 *)(out + blk * QK + 32 * j + l0);
+  o[0] = r0;
+  o[1] = r1;
+}
+
+// Q5_K: as Q4_K, with the codes at byte 48 and the fifth bit of weight l of
+// sub-block j in bit j of high-bit byte 16 + l.
+__global__ __launch_bounds__(256) void q5k_dequant_kernel(const uint8_t *__restrict__ w,
+                                                          float *__restrict__ out,
+                                                          int64_t nblocks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = t >> 5;
+  if (blk >= nblocks) return;
+  const int i = (int)(t & 31);
+  const uint8_t *B = w + blk * Q5K_BYTES;
+  const u32x4 hdr = *(const u32x4 *)B;
+  const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
+  const int j = i >> 2, l0 = (i & 3) * 8;
+  uint32_t sc, m;
+  q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, m);
+  const float a = d * (float)sc, b = dmin * (float)m;
+  const u32x2 q = *(const u32x2 *)(B + 48 + 32 * (j >> 1) + l0);
+  const u32x2 qh = *(const u32x2 *)(B + 16 + l0);
+  const int sh = 4 * (j & 1);
+  f32x4 r0, r1;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const uint32_t q0 = ((q.x >> (8 * e + sh)) & 15u) | (((qh.x >> (8 * e + j)) & 1u) << 4);
+    const uint32_t q1 = ((q.y >> (8 * e + sh)) & 15u) | (((qh.y >> (8 * e + j)) & 1u) << 4);
+    r0[e] = a * (float)q0 - b;
+    r1[e] = a * (float)q1 - b;
+  }
   f32x4 *o = (f32x4 *)(out + blk * QK + 32 * j + l0);
   o[0] = r0;
   o[1] = r1;
@@ -72,6 +105,13 @@ void launch_q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipS
   const int64_t nblocks = N * (K / QK);
   const int64_t threads = nblocks * 32;
   hipLaunchKernelGGL(q4k_dequant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, (const uint8_t *)w, out, nblocks);
+}
+
+void launch_q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t nblocks = N * (K / QK);
+  const int64_t threads = nblocks * 32;
+  hipLaunchKernelGGL(q5k_dequant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      s, (const uint8_t *)w, out, nblocks);
 }
 

@@ -129,10 +129,17 @@ __device__ __forceinline__ void decode_scales(const ScaleDecode &s, uint32_t S0,
   m1 = bfe(Am, s.lo_m1, s.lo_w) | (bfe(S1, s.hi_m1, s.hi_w) << 4);
 }
 
-template <bool XBF16, int MT>
+// Q5 = true reads Q5_K blocks (176 B): the same header, a 32-byte high-bit
+// plane at byte 16 whose bit j of byte l is the fifth bit of weight l of
+// sub-block j, and the Q4_K code bytes at byte 48. Each lane also loads the
+// whole high-bit plane and merges bits 2c and 2c+1 into its code bytes.
+template <bool XBF16, int MT, bool Q5>
 __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
     const uint8_t *__restrict__ w, const void *__restrict__ x, float *__restrict__ y, int N,
     int K, int ldy, int rows_q, int rows_rem, int max_wg_blocks) {
+  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;  // bytes per super-block
+  constexpr int QOFF = Q5 ? 48 : 16;              // code bytes
+
   extern __shared__ uint32_t lds[];
   uint32_t *lds_x = lds;
   float *lds_sum = (float *)(lds + (XBF16 ? MT * K / 2 : MT * K));
@@ -153,17 +160,22 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 
   // block index (relative to B0) and column block of this lane, iteration 0
   int fb = wb0 + g;
-  const uint8_t *fptr = w + (B0 + fb) * Q4K_BYTES;
-  const int64_t fstep = 16 * Q4K_BYTES;
+  const uint8_t *fptr = w + (B0 + fb) * BB;
+  const int64_t fstep = 16 * BB;
 
   u32x4 H[GV_PF], A[GV_PF], Bq[GV_PF];
+  u32x4 Ha[Q5 ? GV_PF : 1], Hb[Q5 ? GV_PF : 1];  // Q5_K high-bit plane
 #pragma unroll
   for (int p = 0; p < GV_PF; p++) {
     if (p < iters && fb + 16 * p < wb1) {
       const uint8_t *blk = fptr + p * fstep;
       H[p] = *(const u32x4 *)blk;
-      A[p] = *(const u32x4 *)(blk + 16 + 32 * c);
-      Bq[p] = *(const u32x4 *)(blk + 32 + 32 * c);
+      A[p] = *(const u32x4 *)(blk + QOFF + 32 * c);
+      Bq[p] = *(const u32x4 *)(blk + QOFF + 16 + 32 * c);
+      if constexpr (Q5) {
+        Ha[p] = *(const u32x4 *)(blk + 16);
+        Hb[p] = *(const u32x4 *)(blk + 32);
+      }
     }
   }
 
@@ -171,7 +183,9 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
   __syncthreads();
 
   const ScaleDecode sd = make_scale_decode(c);
-  const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
+  // Q4_K codes are nibbles picked straight from the code words; Q5_K codes
+  // are first assembled into bytes (nibble | high bit << 4), then picked
+  const uint32_t MASK = opaque(Q5 ? 0x00FF00FFu : 0x000F000Fu), MAGIC = opaque(0x43004300u);
   const int s16 = 16 % nb;
   int kb = fb % nb;  // column block of this lane's current block
   int cb = fb;       // current block (relative to B0)
@@ -195,6 +209,23 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
           const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
           const uint32_t q[8] = {A[p].x, A[p].y, A[p].z, A[p].w,
                                  Bq[p].x, Bq[p].y, Bq[p].z, Bq[p].w};
+          // code words of sub-block 2c (lo) and 2c+1 (hi), positions 4i .. 4i+3:
+          // Q4_K keeps the raw words (the nibble is picked with the mask or a
+          // shift by 4); Q5_K builds bytes q = nibble | high bit << 4
+          uint32_t lo[8], hi[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            if constexpr (Q5) {
+              const uint32_t hbits[8] = {Ha[p].x, Ha[p].y, Ha[p].z, Ha[p].w,
+                                         Hb[p].x, Hb[p].y, Hb[p].z, Hb[p].w};
+              const uint32_t hh = hbits[i] >> (2 * c);
+              lo[i] = (q[i] & 0x0F0F0F0Fu) | ((hh << 4) & 0x10101010u);
+              hi[i] = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hh << 3) & 0x10101010u);
+            } else {
+              lo[i] = q[i];
+              hi[i] = q[i] >> 4;
+            }
+          }
           const int e0 = kb * QK + 64 * c;  // first x element of sub-block 2c
           if constexpr (XBF16) {
             const float c0 = fmaf(128.f, a0, b0), c1 = fmaf(128.f, a1, b1);
@@ -207,8 +238,8 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
               for (int i = 0; i < 4; i++) {
                 const u32x4 x0 = xv[i];      // sub-block 2c, l = 8i .. 8i+7
                 const u32x4 x1 = xv[4 + i];  // sub-block 2c+1
-                const uint32_t qa = q[2 * i], qb = q[2 * i + 1];
-                const uint32_t qa4 = qa >> 4, qb4 = qb >> 4;
+                const uint32_t qa = lo[2 * i], qb = lo[2 * i + 1];
+                const uint32_t qa4 = hi[2 * i], qb4 = hi[2 * i + 1];
                 s0 = dot2_bf16((qa & MASK) | MAGIC, x0.x, s0);
                 s0 = dot2_bf16(((qa >> 8) & MASK) | MAGIC, x0.y, s0);
                 s0 = dot2_bf16((qb & MASK) | MAGIC, x0.z, s0);
@@ -234,15 +265,16 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
               for (int i = 0; i < 8; i++) {
                 const f32x4 x0 = xv[i];
                 const f32x4 x1 = xv[8 + i];
-                const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
-                s0 = fmaf(x0.x, (float)(lo & 255u), s0);
-                s0 = fmaf(x0.y, (float)((lo >> 8) & 255u), s0);
-                s0 = fmaf(x0.z, (float)((lo >> 16) & 255u), s0);
-                s0 = fmaf(x0.w, (float)(lo >> 24), s0);
-                s1 = fmaf(x1.x, (float)(hi & 255u), s1);
-                s1 = fmaf(x1.y, (float)((hi >> 8) & 255u), s1);
-                s1 = fmaf(x1.z, (float)((hi >> 16) & 255u), s1);
-                s1 = fmaf(x1.w, (float)(hi >> 24), s1);
+                const uint32_t cl = Q5 ? lo[i] : lo[i] & 0x0F0F0F0Fu;
+                const uint32_t ch = Q5 ? hi[i] : hi[i] & 0x0F0F0F0Fu;
+                s0 = fmaf(x0.x, (float)(cl & 255u), s0);
+                s0 = fmaf(x0.y, (float)((cl >> 8) & 255u), s0);
+                s0 = fmaf(x0.z, (float)((cl >> 16) & 255u), s0);
+                s0 = fmaf(x0.w, (float)(cl >> 24), s0);
+                s1 = fmaf(x1.x, (float)(ch & 255u), s1);
+                s1 = fmaf(x1.y, (float)((ch >> 8) & 255u), s1);
+                s1 = fmaf(x1.z, (float)((ch >> 16) & 255u), s1);
+                s1 = fmaf(x1.w, (float)(ch >> 24), s1);
               }
               float r = a0 * s0;
               r = fmaf(-b0, xs.x, r);
@@ -257,8 +289,12 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
         if (it + GV_PF < iters && nfb < wb1) {
           const uint8_t *blk = fptr + (it + GV_PF) * fstep;
           H[p] = *(const u32x4 *)blk;
-          A[p] = *(const u32x4 *)(blk + 16 + 32 * c);
-          Bq[p] = *(const u32x4 *)(blk + 32 + 32 * c);
+          A[p] = *(const u32x4 *)(blk + QOFF + 32 * c);
+          Bq[p] = *(const u32x4 *)(blk + QOFF + 16 + 32 * c);
+          if constexpr (Q5) {
+            Ha[p] = *(const u32x4 *)(blk + 16);
+            Hb[p] = *(const u32x4 *)(blk + 32);
+          }
         }
         // sum the block's 4 lanes; one lane stores the block's contribution
 #pragma unroll
@@ -555,7 +591,7 @@ void launch_dense(const void *w, const void *x, float *y, int64_t K, int64_t nwg
                      (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem);
 }
 
-template <bool XBF16, int MT>
+template <bool XBF16, int MT, bool Q5>
 void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, int64_t ldy,
                   hipStream_t s) {
   const int64_t nb = K / QK;
@@ -570,12 +606,45 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   const int max_wg_blocks = (int)((rows_q + (rows_rem ? 1 : 0)) * nb);
   const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 32) * 4 +
                      (size_t)MT * max_wg_blocks * 4;
-  auto kern = q4k_gemv_kernel<XBF16, MT>;
+  auto kern = q4k_gemv_kernel<XBF16, MT, Q5>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(GV_THREADS), lds, s, (const uint8_t *)w, x,
                      y, (int)N, (int)K, (int)ldy, rows_q, rows_rem, max_wg_blocks);
+}
+
+// Rows of x in chunks of MT (1, 2, 4 or 8) per launch of the general kernel,
+// as many as fit a 64 KiB LDS budget for x.
+template <bool Q5>
+void launch_general(const void *w, const void *x, bool x_bf16, float *y, int64_t M, int64_t N,
+                    int64_t K, hipStream_t s) {
+  const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 32) * 4;
+  const size_t elt = x_bf16 ? 2 : 4;
+  int64_t m0 = 0;
+  while (m0 < M) {
+    const int64_t rem = M - m0;
+    int mt = 8;
+    while (mt > 1 && (mt > rem || (size_t)mt * per_row > 65536)) mt >>= 1;
+    const void *xm = (const char *)x + (size_t)m0 * K * elt;
+    float *ym = y + m0 * N;
+    if (x_bf16) {
+      switch (mt) {
+        case 8: launch_chunk<true, 8, Q5>(w, xm, ym, N, K, N, s); break;
+        case 4: launch_chunk<true, 4, Q5>(w, xm, ym, N, K, N, s); break;
+        case 2: launch_chunk<true, 2, Q5>(w, xm, ym, N, K, N, s); break;
+        default: launch_chunk<true, 1, Q5>(w, xm, ym, N, K, N, s); break;
+      }
+    } else {
+      switch (mt) {
+        case 8: launch_chunk<false, 8, Q5>(w, xm, ym, N, K, N, s); break;
+        case 4: launch_chunk<false, 4, Q5>(w, xm, ym, N, K, N, s); break;
+        case 2: launch_chunk<false, 2, Q5>(w, xm, ym, N, K, N, s); break;
+        default: launch_chunk<false, 1, Q5>(w, xm, ym, N, K, N, s); break;
+      }
+    }
+    m0 += mt;
+  }
 }
 
 }  // namespace
@@ -605,32 +674,13 @@ void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
       return;
     }
   }
-  const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 32) * 4;
-  const size_t elt = x_bf16 ? 2 : 4;
-  int64_t m0 = 0;
-  while (m0 < M) {
-    const int64_t rem = M - m0;
-    int mt = 8;
-    while (mt > 1 && (mt > rem || (size_t)mt * per_row > 65536)) mt >>= 1;
-    const void *xm = (const char *)x + (size_t)m0 * K * elt;
-    float *ym = y + m0 * N;
-    if (x_bf16) {
-      switch (mt) {
-        case 8: launch_chunk<true, 8>(w, xm, ym, N, K, N, s); break;
-        case 4: launch_chunk<true, 4>(w, xm, ym, N, K, N, s); break;
-        case 2: launch_chunk<true, 2>(w, xm, ym, N, K, N, s); break;
-        default: launch_chunk<true, 1>(w, xm, ym, N, K, N, s); break;
-      }
-    } else {
-      switch (mt) {
-        case 8: launch_chunk<false, 8>(w, xm, ym, N, K, N, s); break;
-        case 4: launch_chunk<false, 4>(w, xm, ym, N, K, N, s); break;
-        case 2: launch_chunk<false, 2>(w, xm, ym, N, K, N, s); break;
-        default: launch_chunk<false, 1>(w, xm, ym, N, K, N, s); break;
-      }
-    }
-    m0 += mt;
-  }
+  launch_general<false>(w, x, x_bf16, y, M, N, K, s);
+}
+
+// Q5_K runs the general kernel for every M and dtype.
+void launch_q5k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s) {
+  launch_general<true>(w, x, x_bf16, y, M, N, K, s);
 }
 
 }  // namespace qdm

@@ -125,6 +125,62 @@ def test_q4k_gemv_power_of_two_scaling(dt):
 
 
 # --------------------------------------------------------------------------
+# Q5_K dequant and GEMV
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (37, 768, 5), (5, 17408, 6), (129, 1280, 7)])
+def test_q5k_dequant_bit_exact(N, K, seed):
+    say("q5k_dequantize", N, K, seed)
+    w = synth.q5k_blocks(np.random.default_rng(seed), N, K)
+    out = host(qdm.q5k_dequantize(dev_bytes(w), N, K))
+    ref = oracle.q5k_dequantize(w, N, K)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+Q5_CASES = [(1, 1, 256), (1, 37, 768), (3, 1000, 1280), (5, 129, 2304), (16, 64, 4096),
+            (8, 333, 512), (2, 17, 8192), (1, 4099, 256), (1, 31, 32768)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", Q5_CASES)
+def test_q5k_gemv_ragged(M, N, K, dt):
+    say("q5k_gemv", M, N, K, dt)
+    rng = np.random.default_rng(M * 1000 + N + K + 5)
+    w = synth.q5k_blocks(rng, N, K)
+    x = synth.normal_f32(rng, (M, K)) if dt == "f32" else synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q5k_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q5k_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+
+
+def test_q5k_gemv_one_hot_rows_bit_exact():
+    """x = e_k (fp32) gives y[n] = W[n, k] exactly (every code bit position)."""
+    N, K = 300, 1280
+    w = synth.q5k_blocks(np.random.default_rng(4), N, K)
+    W = oracle.q5k_dequantize(w, N, K)
+    wd = dev_bytes(w)
+    for k in [0, 1, 2, 3, 31, 32, 63, 64, 95, 96, 160, 224, 255, 256, 700, 1279]:
+        say("q5k_gemv one-hot k", k)
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        y = host(qdm.q5k_gemv(wd, dev_x(x), N, K))[0]
+        assert np.array_equal(y, W[:, k]), k
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_q5k_gemv_down_full(M):
+    """The Q5_K GEMV workload: the decode down shape (K=17408, N=5120), bf16 x."""
+    w, x = synth.q5k_gemv(M)
+    N, K = synth.Q5K_GEMV["N"], synth.Q5K_GEMV["K"]
+    say("q5k_gemv down full M", M)
+    y = host(qdm.q5k_gemv(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, oracle.q5k_matmul(w, x, N, K))
+    say("  rel err", e)
+    assert e <= min(TOL_BF16, GUARD_VALU)
+
+
+# --------------------------------------------------------------------------
 # Q6_K GEMV
 # --------------------------------------------------------------------------
 
@@ -425,6 +481,10 @@ def test_determinism_all_entry_points():
     x6 = dev_x(synth.normal_bf16(rng, (8, K)))
     say("determinism q6k M=8 (matrix cores, tiles split across waves)")
     a, b = host(qdm.q6k_gemv(w6, x6, 1000, K)), host(qdm.q6k_gemv(w6, x6, 1000, K))
+    assert np.array_equal(a, b)
+    w5 = dev_bytes(synth.q5k_blocks(rng, 1000, K))
+    say("determinism q5k M=8")
+    a, b = host(qdm.q5k_gemv(w5, x6, 1000, K)), host(qdm.q5k_gemv(w5, x6, 1000, K))
     assert np.array_equal(a, b)
     for T in (8, 64):  # decode and matrix-core regimes
         d = synth.moe(T)
