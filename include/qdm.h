@@ -152,6 +152,19 @@ int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_dow
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_q4k_q5k_grouped_gemm: the same routed MoE FFN with Q4_K gate+up experts
+ * and Q5_K down experts (w_down: E tensors of [H][F/256] Q5_K blocks), the
+ * expert arrangement of a Q4_K_M file (hipEngine README, "GGUF Support":
+ * Q5_K holds the MoE expert-down payload). Arguments, limits, workspace
+ * (moe_q4k_workspace_bytes) and status codes are those of
+ * moe_q4k_grouped_gemm.
+ */
+int moe_q4k_q5k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,
+                             const int32_t *topk_ids, const float *topk_w, float *y,
+                             int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * qdm_probe_copy: streaming copy of n_bytes from src to dst (n_bytes % 16 ==
  * 0). A plain, known-size kernel used to calibrate memory-traffic counters
  * and to measure the achievable HBM bandwidth of the device.

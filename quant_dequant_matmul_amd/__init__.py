@@ -1,4 +1,4 @@
-"""Python binding of libqdm (include/qdm.h): Q4_K / Q6_K dequantize-fused
+"""Python binding of libqdm (include/qdm.h): Q4_K / Q5_K / Q6_K dequantize-fused
 matmul for MI355X (gfx950).
 
 Argument marshalling only: torch tensors provide device memory and the
@@ -55,8 +55,10 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemm.restype = i32
         L.moe_q4k_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         L.moe_q4k_workspace_bytes.restype = sz
-        L.moe_q4k_grouped_gemm.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p, sz, p]
-        L.moe_q4k_grouped_gemm.restype = i32
+        for name in ("moe_q4k_grouped_gemm", "moe_q4k_q5k_grouped_gemm"):
+            f = getattr(L, name)
+            f.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p, sz, p]
+            f.restype = i32
         L.qdm_probe_copy.argtypes = [p, p, i64, p]
         L.qdm_probe_copy.restype = i32
         _lib = L
@@ -201,22 +203,33 @@ def moe_q4k_workspace_bytes(T: int, E: int, top_k: int, H: int, F: int) -> int:
     return int(lib().moe_q4k_workspace_bytes(T, E, top_k, H, F))
 
 
-def moe_q4k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int, F: int,
-                         y=None, workspace=None, stream=None):
-    """Routed MoE FFN: y [T][H] = sum_s topk_w * W2[e] (silu(W13g x) * W13u x).
-    A workspace passed in must have been zero-filled before its first use."""
-    torch = _torch()
+def _moe(fn: str, x, w_gate_up, w_down, topk_ids, topk_w, E, H, F, y, workspace, stream):
     T, top_k = topk_ids.shape
     y = _out(y, (T, H), x.device)
     need = moe_q4k_workspace_bytes(T, E, top_k, H, F)
     if workspace is None:
         workspace = _cached_workspace("moe", need, x.device)
-    _check("moe_q4k_grouped_gemm", lib().moe_q4k_grouped_gemm(
+    _check(fn, getattr(lib(), fn)(
         _dev_ptr(x, "x"), _dev_ptr(w_gate_up, "w_gate_up"), _dev_ptr(w_down, "w_down"),
         _dev_ptr(topk_ids, "topk_ids"), _dev_ptr(topk_w, "topk_w"), _dev_ptr(y, "y"),
         T, E, top_k, H, F, _dev_ptr(workspace, "workspace"), workspace.numel(),
         _stream(stream)))
     return y
+
+
+def moe_q4k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int, F: int,
+                         y=None, workspace=None, stream=None):
+    """Routed MoE FFN: y [T][H] = sum_s topk_w * W2[e] (silu(W13g x) * W13u x),
+    Q4_K experts. The workspace is scratch (no initial contents needed)."""
+    return _moe("moe_q4k_grouped_gemm", x, w_gate_up, w_down, topk_ids, topk_w, E, H, F, y,
+                workspace, stream)
+
+
+def moe_q4k_q5k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int, F: int,
+                             y=None, workspace=None, stream=None):
+    """The same routed MoE FFN with Q4_K gate+up experts and Q5_K down experts."""
+    return _moe("moe_q4k_q5k_grouped_gemm", x, w_gate_up, w_down, topk_ids, topk_w, E, H, F, y,
+                workspace, stream)
 
 
 def probe_copy(src, dst, n_bytes: int, stream=None):

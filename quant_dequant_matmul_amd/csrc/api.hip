@@ -125,10 +125,10 @@ QDM_EXPORT size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, i
   return qdm::moe_workspace(T, E, top_k, H, F);
 }
 
-QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,
-                                    const int32_t *topk_ids, const float *topk_w, float *y,
-                                    int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+static int check_moe(const void *x, const void *w_gate_up, const void *w_down,
+                     const int32_t *topk_ids, const float *topk_w, float *y, int64_t T,
+                     int64_t E, int64_t top_k, int64_t H, int64_t F, void *workspace,
+                     size_t workspace_bytes) {
   if (!x || !w_gate_up || !w_down || !topk_ids || !topk_w || !y) return QDM_ERR_NULL;
   if (T < 1 || T > (1 << 24) || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || bad_k(H) ||
       bad_k(F) || H > kMaxK || F > kMaxK)
@@ -138,8 +138,31 @@ QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const 
   const size_t need = qdm::moe_workspace(T, E, top_k, H, F);
   if (!workspace || workspace_bytes < need) return QDM_ERR_WORKSPACE;
   if (misaligned(workspace)) return QDM_ERR_ALIGN;
+  return QDM_OK;
+}
+
+QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_down,
+                                    const int32_t *topk_ids, const float *topk_w, float *y,
+                                    int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = check_moe(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
+                           workspace, workspace_bytes);
+  if (rc) return rc;
   qdm::launch_moe_q4k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F, workspace,
                       (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int moe_q4k_q5k_grouped_gemm(const void *x, const void *w_gate_up,
+                                        const void *w_down, const int32_t *topk_ids,
+                                        const float *topk_w, float *y, int64_t T, int64_t E,
+                                        int64_t top_k, int64_t H, int64_t F, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  const int rc = check_moe(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
+                           workspace, workspace_bytes);
+  if (rc) return rc;
+  qdm::launch_moe_q4k_q5k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
+                          workspace, (hipStream_t)stream);
   return finish_launch();
 }
 

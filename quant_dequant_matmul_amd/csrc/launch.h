@@ -27,6 +27,9 @@ size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
 void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
                     const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                     int64_t F, void *workspace, hipStream_t s);
+void launch_moe_q4k_q5k(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                        const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
+                        int64_t H, int64_t F, void *workspace, hipStream_t s);
 
 void launch_probe_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
 

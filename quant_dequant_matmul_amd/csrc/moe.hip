@@ -1,5 +1,7 @@
 // Routed MoE FFN with Q4_K experts, one call per layer (expert-grouped
-// matmul; hipster README, "Verify the claims": MoE grouped GEMM).
+// matmul; hipster README, "Verify the claims": MoE grouped GEMM). The down
+// experts may also be Q5_K, the expert-down type of a Q4_K_M file (hipEngine
+// README, "GGUF Support", payload table).
 //
 //   y_t = sum_s gw[t][s] * W2[e] * (silu(W13[e][0:F] x_t) * W13[e][F:2F] x_t),
 //   e = ids[t][s]   (entries whose id is outside [0, E) contribute nothing).
@@ -170,11 +172,16 @@ __device__ __forceinline__ void stage_rows(SrcRow src_row, int mt, int K, uint8_
 // 2c and 2c+1), 16 blocks per wave iteration, DEC_PF iterations of loads in
 // flight; loads are unconditional (clamped) so waits are exact. prefetch()
 // issues the first loads (before the inputs are staged), run() the rest.
-template <bool XBF16, int MT, typename BlkPtr>
+// Q5 = true reads Q5_K blocks (176 B: the Q4_K header, a 32-byte high-bit
+// plane at 16, the code bytes at 48); each lane then also loads the plane and
+// merges bits 2c and 2c+1 into its code bytes.
+template <bool XBF16, int MT, bool Q5, typename BlkPtr>
 struct RowsDot {
+  static constexpr int QOFF = Q5 ? 48 : 16;
   BlkPtr blk_ptr;
   int nblk, wb0, wb1, iters, g, c;
   u32x4 Hd[DEC_PF], A[DEC_PF], Bq[DEC_PF];
+  u32x4 Ha[Q5 ? DEC_PF : 1], Hb[Q5 ? DEC_PF : 1];
 
   __device__ __forceinline__ RowsDot(BlkPtr bp, int nblk_) : blk_ptr(bp), nblk(nblk_) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -188,8 +195,12 @@ struct RowsDot {
   __device__ __forceinline__ void load(int slot, int it) {
     const uint8_t *blk = blk_ptr(min(wb0 + g + 16 * it, wb1 - 1));
     Hd[slot] = *(const u32x4 *)blk;
-    A[slot] = *(const u32x4 *)(blk + 16 + 32 * c);
-    Bq[slot] = *(const u32x4 *)(blk + 32 + 32 * c);
+    A[slot] = *(const u32x4 *)(blk + QOFF + 32 * c);
+    Bq[slot] = *(const u32x4 *)(blk + QOFF + 16 + 32 * c);
+    if constexpr (Q5) {
+      Ha[slot] = *(const u32x4 *)(blk + 16);
+      Hb[slot] = *(const u32x4 *)(blk + 32);
+    }
   }
 
   __device__ __forceinline__ void prefetch() {
@@ -203,7 +214,10 @@ struct RowsDot {
     constexpr int REC = XBF16 ? REC_BF16 : REC_F32;
     constexpr int PIECE = XBF16 ? PIECE_BF16 : PIECE_F32;
     if (iters == 0) return;
-    const uint32_t MASK = opaque_u32(0x000F000Fu), MAGIC = opaque_u32(0x43004300u);
+    // Q4_K codes are nibbles picked straight from the code words; Q5_K codes
+    // are assembled into bytes (nibble | high bit << 4) first
+    const uint32_t MASK = opaque_u32(Q5 ? 0x00FF00FFu : 0x000F000Fu);
+    const uint32_t MAGIC = opaque_u32(0x43004300u);
     for (int it0 = 0; it0 < iters; it0 += DEC_PF) {
 #pragma unroll
       for (int p = 0; p < DEC_PF; p++) {
@@ -214,6 +228,21 @@ struct RowsDot {
           const u32x4 hdr = Hd[p];
           const uint32_t q[8] = {A[p].x, A[p].y, A[p].z, A[p].w,
                                  Bq[p].x, Bq[p].y, Bq[p].z, Bq[p].w};
+          // code words of sub-blocks 2c (lo) and 2c+1 (hi), positions 4i .. 4i+3
+          uint32_t lo[8], hi[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            if constexpr (Q5) {
+              const uint32_t hbits[8] = {Ha[p].x, Ha[p].y, Ha[p].z, Ha[p].w,
+                                         Hb[p].x, Hb[p].y, Hb[p].z, Hb[p].w};
+              const uint32_t hh = hbits[i] >> (2 * c);
+              lo[i] = (q[i] & 0x0F0F0F0Fu) | ((hh << 4) & 0x10101010u);
+              hi[i] = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hh << 3) & 0x10101010u);
+            } else {
+              lo[i] = q[i];
+              hi[i] = q[i] >> 4;
+            }
+          }
           load(p, min(it + DEC_PF, iters - 1));  // refill the slot right away
           const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
           uint32_t sc0, m0, sc1, m1;
@@ -233,8 +262,8 @@ struct RowsDot {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                   const u32x4 x0 = xv[i], x1 = xv[4 + i];
-                  const uint32_t qa = q[2 * i], qb = q[2 * i + 1];
-                  const uint32_t qa4 = qa >> 4, qb4 = qb >> 4;
+                  const uint32_t qa = lo[2 * i], qb = lo[2 * i + 1];
+                  const uint32_t qa4 = hi[2 * i], qb4 = hi[2 * i + 1];
                   s0 = dot2_bf16((qa & MASK) | MAGIC, x0.x, s0);
                   s0 = dot2_bf16(((qa >> 8) & MASK) | MAGIC, x0.y, s0);
                   s0 = dot2_bf16((qb & MASK) | MAGIC, x0.z, s0);
@@ -253,15 +282,16 @@ struct RowsDot {
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                   const f32x4 x0 = xv[i], x1 = xv[8 + i];
-                  const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
-                  s0 = fmaf(x0.x, (float)(lo & 255u), s0);
-                  s0 = fmaf(x0.y, (float)((lo >> 8) & 255u), s0);
-                  s0 = fmaf(x0.z, (float)((lo >> 16) & 255u), s0);
-                  s0 = fmaf(x0.w, (float)(lo >> 24), s0);
-                  s1 = fmaf(x1.x, (float)(hi & 255u), s1);
-                  s1 = fmaf(x1.y, (float)((hi >> 8) & 255u), s1);
-                  s1 = fmaf(x1.z, (float)((hi >> 16) & 255u), s1);
-                  s1 = fmaf(x1.w, (float)(hi >> 24), s1);
+                  const uint32_t cl = Q5 ? lo[i] : lo[i] & 0x0F0F0F0Fu;
+                  const uint32_t ch = Q5 ? hi[i] : hi[i] & 0x0F0F0F0Fu;
+                  s0 = fmaf(x0.x, (float)(cl & 255u), s0);
+                  s0 = fmaf(x0.y, (float)((cl >> 8) & 255u), s0);
+                  s0 = fmaf(x0.z, (float)((cl >> 16) & 255u), s0);
+                  s0 = fmaf(x0.w, (float)(cl >> 24), s0);
+                  s1 = fmaf(x1.x, (float)(ch & 255u), s1);
+                  s1 = fmaf(x1.y, (float)((ch >> 8) & 255u), s1);
+                  s1 = fmaf(x1.z, (float)((ch >> 16) & 255u), s1);
+                  s1 = fmaf(x1.w, (float)(ch >> 24), s1);
                 }
                 r = a0 * s0;
                 r = fmaf(-b0, xs.x, r);
@@ -279,9 +309,9 @@ struct RowsDot {
   }
 };
 
-template <bool XBF16, int MT, typename BlkPtr>
-__device__ __forceinline__ RowsDot<XBF16, MT, BlkPtr> make_rows_dot(BlkPtr bp, int nblk) {
-  return RowsDot<XBF16, MT, BlkPtr>(bp, nblk);
+template <bool XBF16, int MT, bool Q5, typename BlkPtr>
+__device__ __forceinline__ RowsDot<XBF16, MT, Q5, BlkPtr> make_rows_dot(BlkPtr bp, int nblk) {
+  return RowsDot<XBF16, MT, Q5, BlkPtr>(bp, nblk);
 }
 
 // Decode gate+up+SwiGLU: workgroup (f chunk, a) with e = the a-th active
@@ -311,7 +341,7 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
     const int row = r < fr ? f0 + r : F + f0 + (r - fr);
     return we + ((int64_t)row * nb + (b - r * nb)) * Q4K_BYTES;
   };
-  auto rd = make_rows_dot<true, MT>(blk_ptr, nblk);
+  auto rd = make_rows_dot<true, MT, false>(blk_ptr, nblk);
   for (int c0 = 0; c0 < cnt; c0 += MT) {
     const int mt = min(MT, cnt - c0);
     rd.prefetch();  // weight loads fly while the x rows are staged
@@ -338,8 +368,8 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
 }
 
 // Decode down: workgroup (row chunk, a): o[entry][r] for rows r0 .. r0+rw-1
-// of W2[e] and every entry of e (fp32).
-template <int MT, int DEC_RW>
+// of W2[e] and every entry of e (fp32). W2 is Q4_K, or Q5_K when Q5.
+template <int MT, int DEC_RW, bool Q5>
 __global__ __launch_bounds__(DEC_THREADS) void moe_dec_down_kernel(
     const float *__restrict__ h, const uint8_t *__restrict__ w2, const int32_t *__restrict__ ids,
     float *__restrict__ o, int n, int top_k, int E, int H, int F) {
@@ -354,9 +384,10 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_down_kernel(
   uint8_t *lds_in = (uint8_t *)lds;                       // [MT][nb][REC_F32]
   float *lds_sum = (float *)(lds_in + MT * nb * REC_F32);  // [MT][F / 32]
   float *part = lds_sum + MT * (F / 32);           // [MT][DEC_RW nb]
-  const uint8_t *rows = w2 + ((int64_t)e * H + r0) * nb * Q4K_BYTES;
-  auto blk_ptr = [&](int b) { return rows + (int64_t)b * Q4K_BYTES; };
-  auto rd = make_rows_dot<false, MT>(blk_ptr, nblk);
+  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;
+  const uint8_t *rows = w2 + ((int64_t)e * H + r0) * nb * BB;
+  auto blk_ptr = [&](int b) { return rows + (int64_t)b * BB; };
+  auto rd = make_rows_dot<false, MT, Q5>(blk_ptr, nblk);
   for (int c0 = 0; c0 < cnt; c0 += MT) {
     const int mt = min(MT, cnt - c0);
     rd.prefetch();  // weight loads fly while the h rows are staged
@@ -507,8 +538,19 @@ constexpr int MX_THREADS = 256;
 constexpr int MX_MS = 2;                    // 32-row entry subtiles per pass
 constexpr int MX_ROWS = 32 * MX_MS;         // entries per pass
 constexpr int MX_AJ = MX_ROWS * 8 / MX_THREADS;  // 16-byte A chunks per thread and stage
-constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t) +
-                          MX_ROWS * sizeof(int32_t);  // 46,336 B: two workgroups per CU
+// LDS of the matrix-core kernel: the weight region holds either the bf16
+// weight tile (256 rows x 144 B) or the raw block column it is decoded from
+// (256 x 144 B for Q4_K, 256 x 176 B for Q5_K), then the A rows and the
+// entries of a pass. 46,336 B (Q4_K) or 54,528 B (Q5_K): two workgroups per CU.
+constexpr int mx_w_elems(bool q5) {
+  return (256 * (q5 ? Q5K_BYTES : Q4K_BYTES) / 2) > 256 * TILE_LROW
+             ? 256 * (q5 ? Q5K_BYTES : Q4K_BYTES) / 2
+             : 256 * TILE_LROW;
+}
+constexpr size_t mx_lds(bool q5) {
+  return (size_t)(mx_w_elems(q5) + MX_ROWS * TILE_LROW) * sizeof(uint16_t) +
+         MX_ROWS * sizeof(int32_t);
+}
 
 // Grouped matrix-core kernel. Workgroup (tile, e), for the entries
 // perm[offsets[e] ..] of expert e in passes of MX_ROWS:
@@ -528,15 +570,21 @@ constexpr size_t MX_LDS = (size_t)(256 + MX_ROWS) * TILE_LROW * sizeof(uint16_t)
 // one decodes while the other multiplies. Wave w owns weight columns (GATEUP)
 // gate 32w .. and up 32w .. (g and u of one (entry, f) then share a lane), or
 // (DOWN) 64w .. 64w+63; every wave covers all entry subtiles of the pass.
-template <bool GATEUP>
+// Q5 (DOWN only): W2 is Q5_K; a row's block is 11 chunks of 16 B (header,
+// two of the high-bit plane, eight of codes) instead of 9, and the decode
+// merges the plane's bits into the codes.
+template <bool GATEUP, bool Q5>
 __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int K,
     int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
+  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;  // bytes per block
+  constexpr int NCH = BB / 16;                    // 16-byte chunks per block
+  constexpr int QC = Q5 ? 3 : 1;                  // first code chunk
   extern __shared__ __attribute__((aligned(16))) uint16_t msm[];
   uint16_t *sw = msm;                       // [256][TILE_LROW] weight rows (bf16)
-  uint8_t *raw = (uint8_t *)msm;            // [256][144] raw block column (same bytes as sw)
-  uint16_t *sa = msm + 256 * TILE_LROW;     // [MX_ROWS][TILE_LROW] A rows (bf16)
+  uint8_t *raw = (uint8_t *)msm;            // [256][BB] raw block column (same bytes as sw)
+  uint16_t *sa = msm + mx_w_elems(Q5);      // [MX_ROWS][TILE_LROW] A rows (bf16)
   int32_t *sent = (int32_t *)(sa + MX_ROWS * TILE_LROW);  // [MX_ROWS] entries of the pass
   // blockIdx.x = expert, blockIdx.y = tile: consecutive workgroup ids go to
   // different XCDs, so the tiles of one expert share an XCD and its L2 holds
@@ -554,15 +602,15 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
       return tile * 256 + t;
     }
   };
-  const uint8_t *wexp = wq + (int64_t)e * NR * nbk * Q4K_BYTES;
+  const uint8_t *wexp = wq + (int64_t)e * NR * nbk * BB;
   // raw chunk i of this thread: chunk c = tid + 256 i of the column, which is
-  // piece c % 9 of the block of tile row c / 9
-  int choff[9];
+  // piece c % NCH of the block of tile row c / NCH
+  int choff[NCH];
 #pragma unroll
-  for (int i = 0; i < 9; i++) {
+  for (int i = 0; i < NCH; i++) {
     const int c = tid + MX_THREADS * i;
-    const int row = c / 9;
-    choff[i] = tile_row(row) * nbk * Q4K_BYTES + 16 * (c - 9 * row);
+    const int row = c / NCH;
+    choff[i] = tile_row(row) * nbk * BB + 16 * (c - NCH * row);
   }
   // B operand rows of this lane's two 32-column tiles, A operand k offset
   const int brow0 = GATEUP ? 32 * wave + (lane & 31) : 64 * wave + (lane & 31);
@@ -596,11 +644,11 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     struct AStage {
       u32x4 a[MX_AJ];
     };
-    u32x4 rawv[9];
+    u32x4 rawv[NCH];
     auto load_raw = [&](int b) {
 #pragma unroll
-      for (int i = 0; i < 9; i++)
-        rawv[i] = *(const u32x4 *)(wexp + choff[i] + (int64_t)b * Q4K_BYTES);
+      for (int i = 0; i < NCH; i++)
+        rawv[i] = *(const u32x4 *)(wexp + choff[i] + (int64_t)b * BB);
     };
     auto load_a = [&](AStage &r, int st) {
 #pragma unroll
@@ -608,11 +656,17 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     };
     // one stage of 64 K: decode this thread's row into sw, store the A tile,
     // refill its A registers two stages ahead, then the MFMAs
-    auto stage = [&](const WRegs &wr, AStage &ar, int st) {
+    auto stage = [&](const WRegs &wr, const u32x4 &qh0, const u32x4 &qh1, AStage &ar,
+                     int st) {
       __syncthreads();  // every row is out of the raw column / the last MFMAs are done
       const RowScales sc = row_scales(wr, true, st & 3);
 #pragma unroll
-      for (int kk = 0; kk < 4; kk++) store_w_part(wr, sc, kk, sw);
+      for (int kk = 0; kk < 4; kk++) {
+        if constexpr (Q5)
+          store_w_part5(wr, qh0, qh1, sc, kk, st & 3, sw);
+        else
+          store_w_part(wr, sc, kk, sw);
+      }
 #pragma unroll
       for (int j = 0; j < MX_AJ; j++) {
         const int q = tid + MX_THREADS * j;
@@ -643,17 +697,19 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
     for (int b = 0; b < nbk; b++) {
       __syncthreads();  // the last MFMAs are done with sw, which the raw column reuses
 #pragma unroll
-      for (int i = 0; i < 9; i++) *(u32x4 *)(raw + 16 * (tid + MX_THREADS * i)) = rawv[i];
+      for (int i = 0; i < NCH; i++) *(u32x4 *)(raw + 16 * (tid + MX_THREADS * i)) = rawv[i];
       load_raw(min(b + 1, nbk - 1));  // the last column reloads itself
       __syncthreads();
-      u32x4 blk[9];
+      u32x4 blk[NCH];
 #pragma unroll
-      for (int j = 0; j < 9; j++) blk[j] = *(const u32x4 *)(raw + Q4K_BYTES * tid + 16 * j);
-      // stages 4b .. 4b+3 (code chunk c holds sub-blocks 2c and 2c+1)
-      stage(WRegs{blk[0], blk[1], blk[2]}, ra, 4 * b);
-      stage(WRegs{blk[0], blk[3], blk[4]}, rb, 4 * b + 1);
-      stage(WRegs{blk[0], blk[5], blk[6]}, ra, 4 * b + 2);
-      stage(WRegs{blk[0], blk[7], blk[8]}, rb, 4 * b + 3);
+      for (int j = 0; j < NCH; j++) blk[j] = *(const u32x4 *)(raw + BB * tid + 16 * j);
+      // stages 4b .. 4b+3 (code chunk c holds sub-blocks 2c and 2c+1); for
+      // Q5_K chunks 1 and 2 are the high-bit plane
+      const u32x4 qh0 = blk[Q5 ? 1 : 0], qh1 = blk[Q5 ? 2 : 0];
+      stage(WRegs{blk[0], blk[QC], blk[QC + 1]}, qh0, qh1, ra, 4 * b);
+      stage(WRegs{blk[0], blk[QC + 2], blk[QC + 3]}, qh0, qh1, rb, 4 * b + 1);
+      stage(WRegs{blk[0], blk[QC + 4], blk[QC + 5]}, qh0, qh1, ra, 4 * b + 2);
+      stage(WRegs{blk[0], blk[QC + 6], blk[QC + 7]}, qh0, qh1, rb, 4 * b + 3);
     }
     // epilogue: lane holds column (lane & 31) of each 32-column tile and rows
     // 32i + 8(v/4) + 4(lane/32) + v%4
@@ -734,7 +790,7 @@ int dec_mt(int64_t T, int64_t n, int64_t H, int64_t F, int fr, int rw, size_t &l
   return 0;
 }
 
-template <int MT, int FR, int RW>
+template <int MT, int FR, int RW, bool Q5>
 void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *ids,
                 const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                 int64_t F, float *hbuf, float *obuf, size_t lds1, size_t lds2,
@@ -742,7 +798,7 @@ void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *i
   const int n = (int)(T * top_k);
   const unsigned slots = (unsigned)(E < n ? E : n);
   auto k1 = moe_dec_gateup_kernel<MT, FR>;
-  auto k2 = moe_dec_down_kernel<MT, RW>;
+  auto k2 = moe_dec_down_kernel<MT, RW, Q5>;
   (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
   hipLaunchKernelGGL(k1, dim3((unsigned)((F + FR - 1) / FR), slots), dim3(DEC_THREADS), lds1, s,
@@ -757,27 +813,28 @@ void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *i
 }
 
 // Decode regime with tile sizes (FR, RW); false if it does not apply.
-template <int FR, int RW>
+template <int FR, int RW, bool Q5>
 bool try_dec(const void *x, const void *w13, const void *w2, const int32_t *ids, const float *gw,
              float *y, int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
              const MoeWs &ws, hipStream_t s) {
   size_t lds1 = 0, lds2 = 0;
   switch (dec_mt(T, T * top_k, H, F, FR, RW, lds1, lds2)) {
-    case 4: launch_dec<4, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
-    case 2: launch_dec<2, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
-    case 1: launch_dec<1, FR, RW>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    case 4: launch_dec<4, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    case 2: launch_dec<2, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
+    case 1: launch_dec<1, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s); return true;
     default: return false;
   }
 }
 
-void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
-                    const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
-                    int64_t F, void *workspace, hipStream_t s) {
+template <bool Q5>
+void launch_moe(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
+                int64_t F, void *workspace, hipStream_t s) {
   const int64_t n64 = T * top_k;
   const MoeWs ws = carve(workspace, T, E, top_k, H, F);
   if (T >= DEC_LARGE_FROM_T
-          ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s)
-          : try_dec<DEC_FR_SMALL, DEC_RW_SMALL>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s))
+          ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s)
+          : try_dec<DEC_FR_SMALL, DEC_RW_SMALL, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s))
     return;
   const int n = (int)n64;
   const size_t route_lds = sizeof(int32_t) * (1 + ROUTE_WAVES) * E;
@@ -785,20 +842,33 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, s, ids, n,
                      (int)E, ws.offsets, ws.perm);
-  auto k1 = moe_mfma_kernel<true>;
-  auto k2 = moe_mfma_kernel<false>;
-  (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
-  (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MX_LDS);
-  hipLaunchKernelGGL(k1, dim3((unsigned)E, (unsigned)(F / 128)), dim3(MX_THREADS), MX_LDS, s,
+  auto k1 = moe_mfma_kernel<true, false>;
+  auto k2 = moe_mfma_kernel<false, Q5>;
+  constexpr size_t lds1 = mx_lds(false), lds2 = mx_lds(Q5);
+  (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+  hipLaunchKernelGGL(k1, dim3((unsigned)E, (unsigned)(F / 128)), dim3(MX_THREADS), lds1, s,
                      (const uint16_t *)x, (const uint8_t *)w13, ws.offsets, ws.perm, (int)top_k,
                      (int)H, (int)F, (int)(2 * F), ws.hb, (float *)nullptr, (int)H);
-  hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), MX_LDS, s,
+  hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), lds2, s,
                      (const uint16_t *)ws.hb, (const uint8_t *)w2, ws.offsets, ws.perm,
                      (int)top_k, (int)F, (int)F, (int)H, (uint16_t *)nullptr, ws.o, (int)H);
   const int64_t total = T * H / 4;
   hipLaunchKernelGGL(moe_combine_entries_kernel,
                      dim3((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)),
                      dim3(256), 0, s, ws.o, ids, gw, y, (int)T, (int)top_k, (int)E, (int)H);
+}
+
+void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                    const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
+                    int64_t F, void *workspace, hipStream_t s) {
+  launch_moe<false>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
+}
+
+void launch_moe_q4k_q5k(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                        const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
+                        int64_t H, int64_t F, void *workspace, hipStream_t s) {
+  launch_moe<true>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
 }
 
 }  // namespace qdm

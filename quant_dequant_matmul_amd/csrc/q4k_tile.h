@@ -1,4 +1,4 @@
-// Q4_K tile decode shared by the matrix-core kernels (gfx950): one thread
+// Q4_K (and Q5_K) tile decode shared by the matrix-core kernels (gfx950): one thread
 // owns one weight row of a 256-row tile and, per K stage of 64, decodes code
 // chunk c of a super-block (sub-blocks 2c and 2c+1) into bf16 LDS slots in
 // MFMA operand order. w = d*sc*q - dmin*m is formed in fp32 (the product is
@@ -65,6 +65,36 @@ __device__ __forceinline__ void store_w_part(const WRegs &r, const RowScales &sc
                           sc.a1 * (float)((h4 >> 8) & 255u) - sc.b1);
     hi[2 * u + 1] = pack_bf16(sc.a1 * (float)((h4 >> 16) & 255u) - sc.b1,
                               sc.a1 * (float)(h4 >> 24) - sc.b1);
+  }
+  uint16_t *dst = sw + threadIdx.x * TILE_LROW;
+  *(u32x4 *)(dst + 8 * kk) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  *(u32x4 *)(dst + 32 + 8 * kk) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Q5_K variant of store_w_part: the code words come from the block's code
+// bytes at 48 (wr.qa, wr.qb hold chunk c as for Q4_K) and the fifth bits from
+// the 32-byte high-bit plane (qh0 = bytes 0..15, qh1 = 16..31): bit 2c of byte
+// l for the low-nibble sub-block, bit 2c+1 for the high-nibble one.
+__device__ __forceinline__ void store_w_part5(const WRegs &r, const u32x4 &qh0, const u32x4 &qh1,
+                                              const RowScales &sc, int kk, int c, uint16_t *sw) {
+  const uint32_t qd[2] = {kk < 2 ? r.qa[2 * kk] : r.qb[2 * kk - 4],
+                          kk < 2 ? r.qa[2 * kk + 1] : r.qb[2 * kk - 3]};
+  const uint32_t hq[2] = {kk < 2 ? qh0[2 * kk] : qh1[2 * kk - 4],
+                          kk < 2 ? qh0[2 * kk + 1] : qh1[2 * kk - 3]};
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const uint32_t hh = hq[u] >> (2 * c);
+    const uint32_t l5 = (qd[u] & 0x0F0F0F0Fu) | ((hh << 4) & 0x10101010u);
+    const uint32_t h5 = ((qd[u] >> 4) & 0x0F0F0F0Fu) | ((hh << 3) & 0x10101010u);
+    lo[2 * u] = pack_bf16(sc.a0 * (float)(l5 & 255u) - sc.b0,
+                          sc.a0 * (float)((l5 >> 8) & 255u) - sc.b0);
+    lo[2 * u + 1] = pack_bf16(sc.a0 * (float)((l5 >> 16) & 255u) - sc.b0,
+                              sc.a0 * (float)(l5 >> 24) - sc.b0);
+    hi[2 * u] = pack_bf16(sc.a1 * (float)(h5 & 255u) - sc.b1,
+                          sc.a1 * (float)((h5 >> 8) & 255u) - sc.b1);
+    hi[2 * u + 1] = pack_bf16(sc.a1 * (float)((h5 >> 16) & 255u) - sc.b1,
+                              sc.a1 * (float)(h5 >> 24) - sc.b1);
   }
   uint16_t *dst = sw + threadIdx.x * TILE_LROW;
   *(u32x4 *)(dst + 8 * kk) = u32x4{lo[0], lo[1], lo[2], lo[3]};

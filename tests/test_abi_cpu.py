@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(qdm.LIB_PATH)
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 14
     for n in names:
         assert hasattr(lib, n), n
 
@@ -83,24 +83,26 @@ def test_gemm_validation():
         assert L.q4k_gemm(A, A, A2, 512, 17408, 5120, A, need - 1, NUL) == EWS
 
 
-def test_moe_validation():
+@pytest.mark.parametrize("fn", ["moe_q4k_grouped_gemm", "moe_q4k_q5k_grouped_gemm"])
+def test_moe_validation(fn):
     L = qdm.lib()
+    moe = getattr(L, fn)
     T, E, k, H, F = 8, 128, 8, 2048, 768
     need = L.moe_q4k_workspace_bytes(T, E, k, H, F)
     assert need > 0
     assert L.moe_q4k_workspace_bytes(T, E, 17, H, F) == 0
     assert L.moe_q4k_workspace_bytes(T, E, k, 300, F) == 0
     args = [A, A, A, A, A, A2]
-    assert L.moe_q4k_grouped_gemm(NUL, *args[1:], T, E, k, H, F, A, need, NUL) == ENULL
-    assert L.moe_q4k_grouped_gemm(*args, 0, E, k, H, F, A, need, NUL) == ESHAPE
-    assert L.moe_q4k_grouped_gemm(*args, T, 0, k, H, F, A, need, NUL) == ESHAPE
-    assert L.moe_q4k_grouped_gemm(*args, T, 2048, k, H, F, A, need, NUL) == ESHAPE
-    assert L.moe_q4k_grouped_gemm(*args, T, E, 0, H, F, A, need, NUL) == ESHAPE
-    assert L.moe_q4k_grouped_gemm(*args, T, E, k, 2000, F, A, need, NUL) == ESHAPE
-    assert L.moe_q4k_grouped_gemm(MIS, *args[1:], T, E, k, H, F, A, need, NUL) == EALIGN
-    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, NUL, need, NUL) == EWS
-    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, A, need - 1, NUL) == EWS
-    assert L.moe_q4k_grouped_gemm(*args, T, E, k, H, F, MIS, need, NUL) == EALIGN
+    assert moe(NUL, *args[1:], T, E, k, H, F, A, need, NUL) == ENULL
+    assert moe(*args, 0, E, k, H, F, A, need, NUL) == ESHAPE
+    assert moe(*args, T, 0, k, H, F, A, need, NUL) == ESHAPE
+    assert moe(*args, T, 2048, k, H, F, A, need, NUL) == ESHAPE
+    assert moe(*args, T, E, 0, H, F, A, need, NUL) == ESHAPE
+    assert moe(*args, T, E, k, 2000, F, A, need, NUL) == ESHAPE
+    assert moe(MIS, *args[1:], T, E, k, H, F, A, need, NUL) == EALIGN
+    assert moe(*args, T, E, k, H, F, NUL, need, NUL) == EWS
+    assert moe(*args, T, E, k, H, F, A, need - 1, NUL) == EWS
+    assert moe(*args, T, E, k, H, F, MIS, need, NUL) == EALIGN
 
 
 def test_probe_validation():

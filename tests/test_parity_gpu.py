@@ -440,6 +440,35 @@ def test_moe_workspace_reused_across_regimes():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("T,E,H,F,top_k", [(5, 6, 256, 256, 3), (33, 16, 256, 512, 4),
+                                           (64, 8, 768, 256, 8), (16, 3, 512, 256, 2)])
+def test_moe_q5k_down_small_full(T, E, H, F, top_k):
+    """Q4_K gate+up, Q5_K down experts; both regimes (<= 64 entries: decode
+    kernels, above: matrix cores)."""
+    say("moe q5k-down small", T, E, H, F, top_k)
+    d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T + E + 1, down_qtype=5)
+    y = host(qdm.moe_q4k_q5k_grouped_gemm(*_moe_dev(d), E, H, F))
+    ref = oracle.moe(d["x"], d["w13"], d["w2"], d["ids"], d["gw"], E, H, F, 5)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [1, 8, 512])
+def test_moe_q5k_down_full_shape(T):
+    """128 experts, H=2048, F=768, top-8, down experts Q5_K. The oracle checks
+    all tokens for T <= 8 and 24 sampled tokens at T = 512."""
+    E, H, F = 128, 2048, 768
+    say("moe q5k-down full T", T)
+    d = synth.moe(T, down_qtype=5)
+    y = host(qdm.moe_q4k_q5k_grouped_gemm(*_moe_dev(d), E, H, F))
+    toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 24).astype(int)
+    ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F, 5)
+    e = rel_err(y[toks], ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
 def test_moe_skips_out_of_range_ids():
     E, H, F, T = 6, 256, 256, 4
     d = synth.moe(T, E=E, H=H, F=F, top_k=2, seed=11)
@@ -492,6 +521,12 @@ def test_determinism_all_entry_points():
         say("determinism moe T", T)
         a = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
         b = host(qdm.moe_q4k_grouped_gemm(*args, 128, 2048, 768))
+        assert np.array_equal(a, b)
+        d5 = synth.moe(T, down_qtype=5)
+        args5 = _moe_dev(d5)
+        say("determinism moe q5k-down T", T)
+        a = host(qdm.moe_q4k_q5k_grouped_gemm(*args5, 128, 2048, 768))
+        b = host(qdm.moe_q4k_q5k_grouped_gemm(*args5, 128, 2048, 768))
         assert np.array_equal(a, b)
 
 
