@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 MALL_BYTES = 256 << 20
 DECODE = [("qkv", 5120, 7168), ("gate_up", 5120, 34816), ("down", 17408, 5120)]
-Q4K_BPB, Q6K_BPB = 144, 210
+Q4K_BPB, Q5K_BPB, Q6K_BPB = 144, 176, 210
 
 
 def log(*a):
@@ -261,61 +261,76 @@ def bench_gemm(torch, qdm, synth, oracle, M, reps):
 def bench_q6k(torch, qdm, synth, oracle, which, M, reps):
     K, N = {"head": (5120, 151936), "down": (17408, 5120)}[which]
     w, x = synth.q6k_gemv(which, M)
+    return bench_kgemv(torch, qdm.q6k_gemv, oracle.q6k_matmul, w, x, M, N, K, Q6K_BPB, reps)
+
+
+def bench_q5k(torch, qdm, synth, oracle, M, reps):
+    K, N = synth.Q5K_GEMV["K"], synth.Q5K_GEMV["N"]
+    w, x = synth.q5k_gemv(M)
+    return bench_kgemv(torch, qdm.q5k_gemv, oracle.q5k_matmul, w, x, M, N, K, Q5K_BPB, reps)
+
+
+def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
+    """A k-quant GEMV timed over rotating weight copies (larger than the
+    last-level cache together), checked on sampled rows against the oracle."""
     nbytes = w.nbytes
     ncopy = copies_for(nbytes)
     base = to_dev(torch, w)
     ws = [base] + [base.clone() for _ in range(ncopy - 1)]
     xd = to_dev_bf16(torch, x)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    qdm.q6k_gemv(ws[0], xd, N, K, y=y)
+    gemv(ws[0], xd, N, K, y=y)
     torch.cuda.synchronize()
     rows = np.arange(0, N, 97 if N > 20000 else 1)
-    err = rel(y.cpu().numpy()[:, rows], oracle.q6k_matmul(w[rows], x, len(rows), K))
+    err = rel(y.cpu().numpy()[:, rows], ref_matmul(w[rows], x, len(rows), K))
     for i in range(3):
-        qdm.q6k_gemv(ws[i % ncopy], xd, N, K, y=y)
+        gemv(ws[i % ncopy], xd, N, K, y=y)
     tm = Timer(torch)
     evs = [tm.event()]
     for i in range(reps):
-        qdm.q6k_gemv(ws[i % ncopy], xd, N, K, y=y)
+        gemv(ws[i % ncopy], xd, N, K, y=y)
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
     ms = float(np.mean(times))
-    b = gemv_bytes(N, K, M, Q6K_BPB)
+    b = gemv_bytes(N, K, M, bpb)
     del ws
     return {"M": M, "N": N, "K": K, "copies": ncopy, "bytes": b, "avg_ms": ms,
             "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
             "rel_err_sampled": err}
 
 
-def bench_moe(torch, qdm, synth, oracle, T, reps):
+def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4):
     E, H, F = 128, 2048, 768
-    d = synth.moe(T)
+    d = synth.moe(T, down_qtype=down_qtype)
+    run = qdm.moe_q4k_grouped_gemm if down_qtype == 4 else qdm.moe_q4k_q5k_grouped_gemm
     x, w13, w2 = to_dev_bf16(torch, d["x"]), to_dev(torch, d["w13"]), to_dev(torch, d["w2"])
     ids = torch.from_numpy(d["ids"]).to("cuda")
     gw = torch.from_numpy(d["gw"]).to("cuda")
     sets = [(w13, w2), (w13.clone(), w2.clone())]
     ws = torch.zeros(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8, device="cuda")
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    qdm.moe_q4k_grouped_gemm(x, w13, w2, ids, gw, E, H, F, y=y, workspace=ws)
+    run(x, w13, w2, ids, gw, E, H, F, y=y, workspace=ws)
     torch.cuda.synchronize()
     toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 16).astype(int)
-    ref = oracle.moe_q4k(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F)
+    ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F,
+                     down_qtype)
     err = rel(y.cpu().numpy()[toks], ref)
     for i in range(3):
         a, b = sets[i % 2]
-        qdm.moe_q4k_grouped_gemm(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+        run(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
     tm = Timer(torch)
     evs = [tm.event()]
     for i in range(reps):
         a, b = sets[i % 2]
-        qdm.moe_q4k_grouped_gemm(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+        run(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
     ms = float(np.mean(times))
     distinct = len(np.unique(d["ids"]))
-    per_expert = 2 * F * (H // 256) * 144 + H * (F // 256) * 144
+    per_expert = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
+                                                                   else Q5K_BPB)
     touched = distinct * per_expert + T * H * 2 + T * H * 4
     flops = 2.0 * T * 8 * (2 * F * H + H * F)
     return {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
@@ -348,8 +363,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,moe,cpu",
-                    help="comma list of: probe, decode, graph, gemm, q6k, moe, cpu "
+    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,moe,cpu",
+                    help="comma list of: probe, decode, graph, gemm, q6k, q5k, moe, cpu "
                          "(decode always runs: it is the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -384,10 +399,20 @@ def main():
             key = "q6k_%s_m%d" % (which, M)
             extra[key] = bench_q6k(torch, qdm, synth, oracle, which, M, reps)
             log(key, extra[key])
+    if "q5k" in sections:
+        for M, reps in ((1, 50), (8, 50)):
+            key = "q5k_down_m%d" % M
+            extra[key] = bench_q5k(torch, qdm, synth, oracle, M, reps)
+            log(key, extra[key])
     if "moe" in sections:
         for T, reps in ((1, 50), (8, 50), (512, 10)):
             extra["moe_t%d" % T] = bench_moe(torch, qdm, synth, oracle, T, reps)
             log("moe T=%d:" % T, extra["moe_t%d" % T])
+        if "q5k" in sections:
+            for T, reps in ((1, 50), (8, 50), (512, 10)):
+                key = "moe_q5kdown_t%d" % T
+                extra[key] = bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=5)
+                log("moe (Q5_K down) T=%d:" % T, extra[key])
 
     gu = dec["kernels"]["gate_up"]
     digest = src_digest("q4k_gemv.hip", "common.h")

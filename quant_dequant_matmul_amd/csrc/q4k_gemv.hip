@@ -328,7 +328,8 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 // M = 1, bf16 x: dense-span kernel (the decode hot path).
 //
 // Every wave instruction reads 1 KiB of consecutive bytes: a wave loads a
-// span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB) with
+// span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB; Q5_K 64 x 176 B
+// = 11 x 1 KiB) with
 // non-temporal 16-byte loads, keeps two spans in flight in registers while it
 // computes a third, and moves each span through its own LDS buffer so that
 // lane l receives whole block l. One lane then decodes a whole super-block: the header once
@@ -340,7 +341,13 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 // distinct LDS banks.
 // ---------------------------------------------------------------------------
 constexpr int DN_SPAN = 64;                           // blocks per span, one per lane
-constexpr int DN_SPAN_BYTES = DN_SPAN * Q4K_BYTES;    // 9216 = 9 x 1 KiB
+// span bytes: 64 x 144 = 9 x 1 KiB (Q4_K) or 64 x 176 = 11 x 1 KiB (Q5_K)
+template <bool Q5>
+constexpr int dn_block_bytes() { return Q5 ? Q5K_BYTES : Q4K_BYTES; }
+template <bool Q5>
+constexpr int dn_span_bytes() { return DN_SPAN * dn_block_bytes<Q5>(); }
+template <bool Q5>
+constexpr int dn_span_chunks() { return dn_span_bytes<Q5>() / 1024; }
 constexpr int DN_XREC = 560;                          // LDS bytes per x column block
 #ifndef QDM_DN_TARGET_WGS
 #define QDM_DN_TARGET_WGS 256
@@ -355,26 +362,30 @@ constexpr size_t DN_LDS_LIMIT = 160 * 1024;
 #define QDM_DN_PHASED 1  // keep each sub-block pair's LDS reads next to its math
 #endif
 
+template <int NCH>
 struct Span {
-  u32x4 r[9];
+  u32x4 r[NCH];
 };
 
-// A full span: 9 KiB from one base, chunk j at byte 1024 j + 16 lane.
-__device__ __forceinline__ void load_span_full(Span &sp, const uint8_t *__restrict__ base,
+// A full span: NCH KiB from one base, chunk j at byte 1024 j + 16 lane.
+template <int NCH>
+__device__ __forceinline__ void load_span_full(Span<NCH> &sp, const uint8_t *__restrict__ base,
                                                int lane) {
   const uint8_t *p = base + 16 * lane;
 #pragma unroll
-  for (int j = 0; j < 9; j++) sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(p + 1024 * j));
+  for (int j = 0; j < NCH; j++)
+    sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(p + 1024 * j));
 }
 
 // Loads are unconditional so the compiler can count outstanding loads and
 // wait for exactly the span it needs (a load behind a branch forces it to wait
 // for every load in flight). Chunks past the end of a partial span re-read the
 // span's last chunk, which is already in flight.
-__device__ __forceinline__ void load_span(Span &sp, const uint8_t *__restrict__ base,
+template <int NCH>
+__device__ __forceinline__ void load_span(Span<NCH> &sp, const uint8_t *__restrict__ base,
                                           int nbytes, int lane) {
 #pragma unroll
-  for (int j = 0; j < 9; j++) {
+  for (int j = 0; j < NCH; j++) {
     const int off = min(1024 * j + 16 * lane, nbytes - 16);
     sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
   }
@@ -425,8 +436,13 @@ struct XStage {
 };
 
 // sum_k x[k] * w(k) over one super-block held in LDS (blk), x record xr.
+// Q5_K (Q5): codes at 48 and the high-bit plane at 16; the code bytes are
+// assembled (nibble | bit 2cc or 2cc+1 of the plane << 4) and picked with
+// MASK = 0x00FF00FF instead of 0x000F000F.
+template <bool Q5>
 __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const uint8_t *xr,
                                                     uint32_t MASK, uint32_t MAGIC) {
+  constexpr int QOFF = Q5 ? 48 : 16;
   const u32x4 hdr = *(const u32x4 *)blk;
   const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
   const f32x4 xsa = *(const f32x4 *)(xr + 512), xsb = *(const f32x4 *)(xr + 528);
@@ -440,17 +456,35 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
     q4k_scale_min(hdr.y, hdr.z, hdr.w, j0 + 1, sc1, m1);
     const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
     const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-    const u32x4 qa = *(const u32x4 *)(blk + 16 + 32 * cc);
-    const u32x4 qb = *(const u32x4 *)(blk + 32 + 32 * cc);
+    const u32x4 qa = *(const u32x4 *)(blk + QOFF + 32 * cc);
+    const u32x4 qb = *(const u32x4 *)(blk + QOFF + 16 + 32 * cc);
     const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    // code words of sub-blocks 2cc (lo) and 2cc+1 (hi), positions 4i .. 4i+3
+    uint32_t lo[8], hi[8];
+    if constexpr (Q5) {
+      const u32x4 ha = *(const u32x4 *)(blk + 16), hb = *(const u32x4 *)(blk + 32);
+      const uint32_t hbits[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t hh = hbits[i] >> (2 * cc);
+        lo[i] = (q[i] & 0x0F0F0F0Fu) | ((hh << 4) & 0x10101010u);
+        hi[i] = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hh << 3) & 0x10101010u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        lo[i] = q[i];
+        hi[i] = q[i] >> 4;
+      }
+    }
     const u32x4 *xv0 = (const u32x4 *)(xr + 64 * j0);
     const u32x4 *xv1 = (const u32x4 *)(xr + 64 * (j0 + 1));
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       const u32x4 x0 = xv0[t], x1 = xv1[t];
-      const uint32_t qd0 = q[2 * t], qd1 = q[2 * t + 1];
-      const uint32_t qd04 = qd0 >> 4, qd14 = qd1 >> 4;
+      const uint32_t qd0 = lo[2 * t], qd1 = lo[2 * t + 1];
+      const uint32_t qd04 = hi[2 * t], qd14 = hi[2 * t + 1];
       s0 = dot2_bf16((qd0 & MASK) | MAGIC, x0.x, s0);
       s0 = dot2_bf16(((qd0 >> 8) & MASK) | MAGIC, x0.y, s0);
       s0 = dot2_bf16((qd1 & MASK) | MAGIC, x0.z, s0);
@@ -475,15 +509,18 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
 // computes one span (from its LDS buffer), the next two are in flight. Spans
 // are handed out in order from a workgroup counter, so a wave whose data
 // arrived late takes fewer spans and the waves finish together.
-template <int WAVES, int XC>
+template <int WAVES, int XC, bool Q5>
 __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y,
     int K, int rows_q, int rows_rem) {
   constexpr int DN_THREADS = WAVES * WAVE;
+  constexpr int BB = dn_block_bytes<Q5>();
+  constexpr int DN_SPAN_BYTES = dn_span_bytes<Q5>();
+  constexpr int NCH = dn_span_chunks<Q5>();
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int next_span;
   const int nb = K / QK;
-  uint8_t *spanbuf = smem;                            // [waves][9216]
+  uint8_t *spanbuf = smem;                            // [waves][span bytes]
   uint8_t *xrec = smem + WAVES * DN_SPAN_BYTES;       // [nb][560]
   float *part = (float *)(xrec + nb * DN_XREC);       // [blocks of this workgroup]
 
@@ -492,7 +529,7 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   const int r1 = r0 + rows_q + (bid < rows_rem ? 1 : 0);
   const int nblk = (r1 - r0) * nb;
   const int nspan = (nblk + DN_SPAN - 1) / DN_SPAN;
-  const uint8_t *wbase = w + (int64_t)r0 * nb * Q4K_BYTES;
+  const uint8_t *wbase = w + (int64_t)r0 * nb * BB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // span indices stay scalar
   const int nfull = nblk / DN_SPAN;  // spans before nfull are full
@@ -500,14 +537,14 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   // A span index past the end loads the last span again (its bytes are
   // already on their way), so every wave issues the same loads in every
   // iteration and the compiler can wait for exactly the span it needs. Both
-  // branches issue the same 9 loads into the same registers.
-  auto issue = [&](Span &r, int sidx) {
+  // branches issue the same NCH loads into the same registers.
+  auto issue = [&](Span<NCH> &r, int sidx) {
     const int si = min(sidx, nspan - 1);
     const uint8_t *base = wbase + (int64_t)si * DN_SPAN_BYTES;
     if (si < nfull)
-      load_span_full(r, base, lane);
+      load_span_full<NCH>(r, base, lane);
     else
-      load_span(r, base, (nblk - DN_SPAN * si) * Q4K_BYTES, lane);
+      load_span<NCH>(r, base, (nblk - DN_SPAN * si) * BB, lane);
   };
   auto grab = [&]() {
     int v = 0;
@@ -521,13 +558,13 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   int sidx[2] = {wave, WAVES + wave};
   // x loads, the first span, the x records, then the second span: x does not
   // wait behind the whole initial burst of weight loads (measured fastest)
-  Span R[2];
+  Span<NCH> R[2];
   issue(R[0], sidx[0]);
   xst.store(K, xrec);
   issue(R[1], sidx[1]);
   __syncthreads();
 
-  const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(0x43004300u);
+  const uint32_t MASK = opaque(Q5 ? 0x00FF00FFu : 0x000F000Fu), MAGIC = opaque(0x43004300u);
   uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
   while (sidx[0] < nspan || sidx[1] < nspan) {
 #pragma unroll
@@ -535,11 +572,11 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
       const int cur = sidx[p];
       if (cur < nfull) {
 #pragma unroll
-        for (int j = 0; j < 9; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R[p].r[j];
+        for (int j = 0; j < NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R[p].r[j];
       } else {
-        const int nbytes = cur < nspan ? (nblk - DN_SPAN * cur) * Q4K_BYTES : 0;
+        const int nbytes = cur < nspan ? (nblk - DN_SPAN * cur) * BB : 0;
 #pragma unroll
-        for (int j = 0; j < 9; j++) {
+        for (int j = 0; j < NCH; j++) {
           const int off = 1024 * j + 16 * lane;
           if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
         }
@@ -550,8 +587,8 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
       sidx[p] = nxt;
       const int b = DN_SPAN * cur + lane;
       if (cur < nspan && b < nblk)
-        part[b] = q4k_block_dot_bf16(mybuf + Q4K_BYTES * lane, xrec + (b % nb) * DN_XREC, MASK,
-                                     MAGIC);
+        part[b] = q4k_block_dot_bf16<Q5>(mybuf + BB * lane, xrec + (b % nb) * DN_XREC, MASK,
+                                         MAGIC);
     }
   }
   __syncthreads();
@@ -566,8 +603,9 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
 }
 
 // Launch geometry of the dense kernel, or false if its LDS does not fit.
-template <int DN_WAVES>
+template <int DN_WAVES, bool Q5>
 bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, size_t &lds) {
+  constexpr int DN_SPAN_BYTES = dn_span_bytes<Q5>();
   const int64_t nb = K / QK;
   nwg = DN_TARGET_WGS;
   const int64_t need = (N * nb + DN_MAX_WG_BLOCKS - 1) / DN_MAX_WG_BLOCKS;
@@ -581,10 +619,10 @@ bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, 
 }
 
 // x chunks per thread for K (the smallest instantiated count that covers it).
-template <int DN_WAVES, int XC>
+template <int DN_WAVES, int XC, bool Q5>
 void launch_dense(const void *w, const void *x, float *y, int64_t K, int64_t nwg, int rows_q,
                   int rows_rem, size_t lds, hipStream_t s) {
-  auto kern = q4k_gemv_m1_kernel<DN_WAVES, XC>;
+  auto kern = q4k_gemv_m1_kernel<DN_WAVES, XC, Q5>;
   (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(DN_WAVES * WAVE), lds, s,
@@ -596,16 +634,19 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
                   hipStream_t s) {
   const int64_t nb = K / QK;
   // Enough workgroups to fill the device; more when a workgroup's block slots
-  // (MT per block) would exceed 8192 floats of LDS.
+  // (MT floats per block) would exceed their LDS budget: 32 KiB, or what the
+  // 160 KiB of LDS leave beside x, less one row's slots (a workgroup holds up
+  // to one row more than the average).
   int64_t nwg = GV_TARGET_WGS;
-  const int64_t cap = 8192 / MT;
+  const size_t x_lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 32) * 4;
+  const size_t part_budget = x_lds < 128 * 1024 ? 32768 : 160 * 1024 - x_lds;
+  const int64_t cap = (int64_t)(part_budget / (4 * MT)) - nb;  // blocks per workgroup
   const int64_t need = (N * nb + cap - 1) / cap;
   if (need > nwg) nwg = need;
   if (nwg > N) nwg = N;
   const int rows_q = (int)(N / nwg), rows_rem = (int)(N % nwg);
   const int max_wg_blocks = (int)((rows_q + (rows_rem ? 1 : 0)) * nb);
-  const size_t lds = (size_t)MT * K * (XBF16 ? 2 : 4) + (size_t)MT * (K / 32) * 4 +
-                     (size_t)MT * max_wg_blocks * 4;
+  const size_t lds = x_lds + (size_t)MT * max_wg_blocks * 4;
   auto kern = q4k_gemv_kernel<XBF16, MT, Q5>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -615,7 +656,9 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 }
 
 // Rows of x in chunks of MT (1, 2, 4 or 8) per launch of the general kernel,
-// as many as fit a 64 KiB LDS budget for x.
+// as many as fit a 64 KiB LDS budget for x (several workgroups per compute
+// unit); when that budget holds a single row but more rows remain (long K),
+// up to 148 KiB (one workgroup per unit, fewer passes over the weights).
 template <bool Q5>
 void launch_general(const void *w, const void *x, bool x_bf16, float *y, int64_t M, int64_t N,
                     int64_t K, hipStream_t s) {
@@ -626,6 +669,10 @@ void launch_general(const void *w, const void *x, bool x_bf16, float *y, int64_t
     const int64_t rem = M - m0;
     int mt = 8;
     while (mt > 1 && (mt > rem || (size_t)mt * per_row > 65536)) mt >>= 1;
+    if (mt == 1 && rem > 1) {
+      mt = 8;
+      while (mt > 1 && (mt > rem || (size_t)mt * per_row > 148 * 1024)) mt >>= 1;
+    }
     const void *xm = (const char *)x + (size_t)m0 * K * elt;
     float *ym = y + m0 * N;
     if (x_bf16) {
@@ -650,36 +697,41 @@ void launch_general(const void *w, const void *x, bool x_bf16, float *y, int64_t
 }  // namespace
 
 // M = 1 with bf16 x runs the dense-span kernel whenever its LDS plan fits
-// (K up to about 26K); other cases (fp32 x, M > 1, longer K) process rows of x
-// in chunks of MT (1, 2, 4 or 8) per launch of the general kernel, as many as
-// fit a 64 KiB LDS budget for x.
+// (K up to about 26K for Q4_K); other cases (fp32 x, M > 1, longer K) process
+// rows of x in chunks of MT (1, 2, 4 or 8) per launch of the general kernel,
+// as many as fit a 64 KiB LDS budget for x.
+// The dense-span kernel for M = 1 with bf16 x, or false if its LDS plan does
+// not fit.
+template <bool Q5>
+bool try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, hipStream_t s) {
+  int64_t nwg;
+  int rows_q, rows_rem;
+  size_t lds;
+  if (!dense_plan<QDM_DN_WAVES, Q5>(N, K, nwg, rows_q, rows_rem, lds)) return false;
+  const int64_t per_thread = (K / 8 + QDM_DN_WAVES * WAVE - 1) / (QDM_DN_WAVES * WAVE);
+  if (per_thread <= 2)
+    launch_dense<QDM_DN_WAVES, 2, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+  else if (per_thread <= 3)
+    launch_dense<QDM_DN_WAVES, 3, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+  else if (per_thread <= 5)
+    launch_dense<QDM_DN_WAVES, 5, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+  else if (per_thread <= 8)
+    launch_dense<QDM_DN_WAVES, 8, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+  else
+    launch_dense<QDM_DN_WAVES, 16, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+  return true;
+}
+
 void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
-  if (M == 1 && x_bf16) {
-    int64_t nwg;
-    int rows_q, rows_rem;
-    size_t lds;
-    if (dense_plan<QDM_DN_WAVES>(N, K, nwg, rows_q, rows_rem, lds)) {
-      const int64_t per_thread = (K / 8 + QDM_DN_WAVES * WAVE - 1) / (QDM_DN_WAVES * WAVE);
-      if (per_thread <= 2)
-        launch_dense<QDM_DN_WAVES, 2>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
-      else if (per_thread <= 3)
-        launch_dense<QDM_DN_WAVES, 3>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
-      else if (per_thread <= 5)
-        launch_dense<QDM_DN_WAVES, 5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
-      else if (per_thread <= 8)
-        launch_dense<QDM_DN_WAVES, 8>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
-      else
-        launch_dense<QDM_DN_WAVES, 16>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
-      return;
-    }
-  }
+  if (M == 1 && x_bf16 && try_dense<false>(w, x, y, N, K, s)) return;
   launch_general<false>(w, x, x_bf16, y, M, N, K, s);
 }
 
-// Q5_K runs the general kernel for every M and dtype.
+// Q5_K: the same choice between the dense-span and the general kernel.
 void launch_q5k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
+  if (M == 1 && x_bf16 && try_dense<true>(w, x, y, N, K, s)) return;
   launch_general<true>(w, x, x_bf16, y, M, N, K, s);
 }
 
