@@ -52,6 +52,8 @@ def _load():
         lib.oracle_moe_q4k.restype = i32
         lib.oracle_moe.argtypes = [p, i32, p, p, i32, p, p, i64, i64, i64, i64, i64, p]
         lib.oracle_moe.restype = i32
+        lib.oracle_router_topk.argtypes = [p, i64, i64, i64, p, p]
+        lib.oracle_router_topk.restype = i32
         _lib = lib
     return _lib
 
@@ -143,3 +145,16 @@ def moe(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, ids: np.ndarray,
 def moe_q4k(x, w13, w2, ids, gw, E: int, H: int, F: int) -> np.ndarray:
     """float64 routed MoE FFN output [T][H] with Q4_K gate+up and down experts."""
     return moe(x, w13, w2, ids, gw, E, H, F, 4)
+
+
+def router_topk(logits: np.ndarray, k: int):
+    """Top-k experts per token (largest logit first, smaller index first among
+    equal logits) and the float64 softmax of the selected logits."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    rc = _load().oracle_router_topk(_ptr(lg), T, E, k, _ptr(ids), _ptr(w))
+    if rc:
+        raise RuntimeError("oracle_router_topk failed (%d)" % rc)
+    return ids, w

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the GGUF k-quant (Q4_K, Q5_K, Q6_K) dequantize-fused matmul.
+ * CPU oracle for the GGUF k-quant (Q4_K, Q5_K, Q6_K) dequantize-fused matmul
+ * and the top-k router in front of its MoE grouped matmul.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this library. It shares no code, header or table
@@ -326,4 +327,44 @@ int oracle_moe_q4k(const void *x, int x_is_bf16, const uint8_t *w13, const uint8
                    int64_t top_k, int64_t H, int64_t F, double *y)
 {
     return oracle_moe(x, x_is_bf16, w13, w2, 4, ids, gw, T, E, top_k, H, F, y);
+}
+
+/*
+ * MoE router: top-k selection and softmax from router logits (a reading: the
+ * pages name a routed MoE model but not its router). For each token t the k
+ * experts with the largest logits are taken, largest first; of equal logits
+ * the smaller expert index comes first. The gate weights are the softmax of
+ * the selected logits, in float64:
+ *   w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0),  l_0 the largest.
+ * logits [T][E] fp32 (finite), ids [T][k] int32, w [T][k] float64.
+ * Returns 0, or -1 for bad sizes (k < 1 or k > E).
+ */
+int oracle_router_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *ids,
+                       double *w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return -1;
+    char *taken = (char *)malloc((size_t)E);
+    if (!taken)
+        return -2;
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int64_t s = 0; s < k; s++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e; /* strict '>': the first of equal logits stays */
+            taken[best] = 1;
+            ids[t * k + s] = (int32_t)best;
+        }
+        const double l0 = (double)l[ids[t * k]];
+        double sum = 0.0;
+        for (int64_t s = 0; s < k; s++)
+            sum += exp((double)l[ids[t * k + s]] - l0);
+        for (int64_t s = 0; s < k; s++)
+            w[t * k + s] = exp((double)l[ids[t * k + s]] - l0) / sum;
+    }
+    free(taken);
+    return 0;
 }

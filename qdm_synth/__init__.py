@@ -114,6 +114,11 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(rng, shape))
 
 
+def router_logits(rng: np.random.Generator, T: int, E: int) -> np.ndarray:
+    """Router logits fp32 [T][E], N(0, 1) drawn in float32."""
+    return normal_f32(rng, (T, E))
+
+
 def routing(rng: np.random.Generator, T: int, E: int, top_k: int):
     """Top-k routing input: per token top_k distinct experts drawn uniformly
     without replacement, and softmax-normalised fp32 gate weights (softmax of
@@ -201,3 +206,9 @@ def q5k_gemv(M: int):
     w = q5k_blocks(g_w, Q5K_GEMV["N"], Q5K_GEMV["K"])
     x = normal_bf16(g_x, (M, Q5K_GEMV["K"]))
     return w, x
+
+
+def moe_router(T: int, E: int = MOE["E"], seed: int = MOE["seed"] + 10):
+    """Router logits for the MoE workload's token counts (seed 13)."""
+    (g,) = streams(seed, 1)
+    return router_logits(g, T, E)

@@ -13,6 +13,9 @@ mathematics fix, never against the oracle itself.
 * Matmul: exact rationals on tiny shapes within the fp64 summation bound,
   one-hot activations, bf16 widening, numpy cross-check.
 * MoE FFN: closed form with constant experts, token permutation, one-hot gate.
+* Router: hand-checked ties, a closed form on a ramp of logits, numpy's stable
+  argsort (an independent implementation of the same order), and the softmax
+  invariants (sum 1, ratios exp(l_i - l_j)).
 """
 from __future__ import annotations
 
@@ -560,3 +563,74 @@ def test_moe_q5k_down_one_hot_gate_dense():
         u = W13 @ xf[t]
         h = u[:F] / (1 + np.exp(-u[:F])) * u[F:]
         np.testing.assert_allclose(y1[t], W2 @ h, rtol=1e-11, atol=1e-11 * np.abs(W2 @ h).max())
+
+
+# --------------------------------------------------------------------------
+# Router: top-k selection and softmax
+# --------------------------------------------------------------------------
+
+def test_router_hand_cases():
+    ids, w = oracle.router_topk(np.array([[1, 3, 3, 2]], np.float32), 2)
+    assert ids.tolist() == [[1, 2]] and w.tolist() == [[0.5, 0.5]]  # tie: smaller index first
+    ids, w = oracle.router_topk(np.array([[1, 3, 3, 2]], np.float32), 4)
+    assert ids.tolist() == [[1, 2, 3, 0]]
+    ids, w = oracle.router_topk(np.array([[-5, -1, -2, -1]], np.float32), 3)
+    assert ids.tolist() == [[1, 3, 2]]
+    ids, w = oracle.router_topk(np.array([[0.25, 7.0]], np.float32), 1)
+    assert ids.tolist() == [[1]] and w.tolist() == [[1.0]]
+    # +0 and -0 compare equal: index order decides
+    ids, _ = oracle.router_topk(np.array([[-0.0, 0.0, -1.0]], np.float32), 2)
+    assert ids.tolist() == [[0, 1]]
+
+
+def test_router_closed_form_ramp():
+    """l_e = e / 4 (exact in fp32): the top 8 of 128 are 127 .. 120 and
+    w_s = exp(-s/4) / sum_j exp(-j/4)."""
+    E, k = 128, 8
+    logits = (np.arange(E, dtype=np.float32) / 4)[None]
+    ids, w = oracle.router_topk(logits, k)
+    assert ids[0].tolist() == list(range(127, 119, -1))
+    z = sum(math.exp(-j / 4) for j in range(k))
+    for s in range(k):
+        assert abs(w[0, s] - math.exp(-s / 4) / z) <= 1e-15
+
+
+def test_router_large_logits_no_overflow():
+    """Softmax is shift-invariant, and taking the largest selected logit as the
+    reference keeps exp() finite: logits 3000 + e/4 give the same weights as
+    the ramp from 0."""
+    E, k = 128, 8
+    logits = (3000 + np.arange(E, dtype=np.float32) / 4)[None]
+    ids, w = oracle.router_topk(logits, k)
+    assert ids[0].tolist() == list(range(127, 119, -1))
+    z = sum(math.exp(-j / 4) for j in range(k))
+    for s in range(k):
+        assert abs(w[0, s] - math.exp(-s / 4) / z) <= 1e-15
+
+
+def test_router_matches_stable_argsort_with_ties():
+    """Logits drawn from 6 values (many ties): the ids equal numpy's stable
+    argsort of -logits (equal keys keep index order), first k."""
+    rng = np.random.default_rng(61)
+    for E, k in [(128, 8), (64, 6), (1000, 16), (9, 9)]:
+        logits = rng.integers(-3, 3, size=(40, E)).astype(np.float32) * 0.5
+        ids, _ = oracle.router_topk(logits, k)
+        ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        np.testing.assert_array_equal(ids, ref)
+
+
+def test_router_softmax_invariants():
+    rng = np.random.default_rng(62)
+    logits = synth.router_logits(rng, 200, 128)
+    ids, w = oracle.router_topk(logits, 8)
+    for t in range(200):
+        sel = logits[t, ids[t]].astype(np.float64)
+        assert len(set(ids[t].tolist())) == 8
+        assert np.all(np.diff(sel) <= 0)
+        rest = np.delete(logits[t], ids[t])
+        assert rest.max() <= sel.min()
+        assert abs(w[t].sum() - 1.0) <= 1e-15
+        for i in range(1, 8):
+            assert abs(w[t, i] / w[t, 0] - math.exp(sel[i] - sel[0])) <= 1e-14
+    with pytest.raises(RuntimeError):
+        oracle.router_topk(logits[:2, :4], 5)
