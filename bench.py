@@ -300,42 +300,104 @@ def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
             "rel_err_sampled": err}
 
 
-def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4):
+def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=False):
+    """One MoE layer call (E=128, H=2048, F=768, top-8). from_logits: the call
+    also runs the router on N(0, 1) router logits [T][128]."""
     E, H, F = 128, 2048, 768
     d = synth.moe(T, down_qtype=down_qtype)
-    run = qdm.moe_q4k_grouped_gemm if down_qtype == 4 else qdm.moe_q4k_q5k_grouped_gemm
     x, w13, w2 = to_dev_bf16(torch, d["x"]), to_dev(torch, d["w13"]), to_dev(torch, d["w2"])
-    ids = torch.from_numpy(d["ids"]).to("cuda")
-    gw = torch.from_numpy(d["gw"]).to("cuda")
     sets = [(w13, w2), (w13.clone(), w2.clone())]
-    ws = torch.zeros(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8, device="cuda")
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    run(x, w13, w2, ids, gw, E, H, F, y=y, workspace=ws)
+    if from_logits:
+        logits = synth.moe_router(T)
+        ids_np, gw_np = oracle.router_topk(logits, 8)
+        lg = torch.from_numpy(logits).to("cuda")
+        ws = torch.zeros(qdm.moe_from_logits_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8,
+                         device="cuda")
+
+        def run(a, b):
+            qdm.moe_grouped_gemm_from_logits(x, lg, a, b, 8, E, H, F, down_qtype=down_qtype,
+                                             y=y, workspace=ws)
+    else:
+        ids_np, gw_np = d["ids"], d["gw"]
+        step = qdm.moe_q4k_grouped_gemm if down_qtype == 4 else qdm.moe_q4k_q5k_grouped_gemm
+        ids = torch.from_numpy(ids_np).to("cuda")
+        gw = torch.from_numpy(gw_np).to("cuda")
+        ws = torch.zeros(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8,
+                         device="cuda")
+
+        def run(a, b):
+            step(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+    run(w13, w2)
     torch.cuda.synchronize()
     toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 16).astype(int)
-    ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], d["ids"][toks], d["gw"][toks], E, H, F,
+    ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], ids_np[toks], gw_np[toks], E, H, F,
                      down_qtype)
     err = rel(y.cpu().numpy()[toks], ref)
     for i in range(3):
-        a, b = sets[i % 2]
-        run(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+        run(*sets[i % 2])
     tm = Timer(torch)
     evs = [tm.event()]
     for i in range(reps):
-        a, b = sets[i % 2]
-        run(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
+        run(*sets[i % 2])
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
     ms = float(np.mean(times))
-    distinct = len(np.unique(d["ids"]))
+    graph_ms = None
+    if T <= 8:
+        # Decode-sized calls are near the host's launch rate: also time them
+        # replayed from a graph (one call per weight copy), as a decode loop
+        # would run them. The replayed output must equal the eager one.
+        eager_y = y.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run(*sets[0])
+            run(*sets[1])
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, eager_y):
+            raise RuntimeError("MoE graph replay differs from the eager result (T=%d)" % T)
+        gt = Timer(torch)
+        g0 = gt.event()
+        for _ in range(reps):
+            graph.replay()
+        g1 = gt.event()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (2 * reps)
+    distinct = len(np.unique(ids_np))
     per_expert = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
                                                                    else Q5K_BPB)
-    touched = distinct * per_expert + T * H * 2 + T * H * 4
+    touched = distinct * per_expert + T * H * 2 + T * H * 4 + (T * E * 4 if from_logits else 0)
     flops = 2.0 * T * 8 * (2 * F * H + H * F)
-    return {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
-            "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
-            "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
+    r = {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
+         "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
+         "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
+    if graph_ms is not None:
+        r.update(graph_ms=graph_ms, graph_GBps=touched / graph_ms / 1e6)
+    return r
+
+
+def bench_router(torch, qdm, synth, oracle, T, reps):
+    """moe_router_topk alone on N(0, 1) logits [T][128], top-8."""
+    logits = synth.moe_router(T)
+    lg = torch.from_numpy(logits).to("cuda")
+    ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+    qdm.moe_router_topk(lg, 8, ids=ids, weights=gw)
+    torch.cuda.synchronize()
+    rid, _ = oracle.router_topk(logits, 8)
+    exact = bool(np.array_equal(ids.cpu().numpy(), rid))
+    for _ in range(3):
+        qdm.moe_router_topk(lg, 8, ids=ids, weights=gw)
+    tm = Timer(torch)
+    evs = [tm.event()]
+    for _ in range(reps):
+        qdm.moe_router_topk(lg, 8, ids=ids, weights=gw)
+        evs.append(tm.event())
+    torch.cuda.synchronize()
+    ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+    return {"T": T, "avg_ms": ms, "ids_bit_exact": exact}
 
 
 def cpu_baseline(oracle, synth, budget_s=10.0):
@@ -363,7 +425,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,moe,cpu",
+    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,moe,router,cpu",
                     help="comma list of: probe, decode, graph, gemm, q6k, q5k, moe, cpu "
                          "(decode always runs: it is the headline)")
     args = ap.parse_args()
@@ -413,6 +475,16 @@ def main():
                 key = "moe_q5kdown_t%d" % T
                 extra[key] = bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=5)
                 log("moe (Q5_K down) T=%d:" % T, extra[key])
+        if "router" in sections:
+            for T, reps in ((1, 50), (8, 50), (512, 50)):
+                key = "router_t%d" % T
+                extra[key] = bench_router(torch, qdm, synth, oracle, T, reps)
+                log("router T=%d:" % T, extra[key])
+            for T, reps in ((1, 50), (8, 50), (512, 10)):
+                key = "moe_logits_q5kdown_t%d" % T
+                extra[key] = bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=5,
+                                       from_logits=True)
+                log("moe from logits (Q5_K down) T=%d:" % T, extra[key])
 
     gu = dec["kernels"]["gate_up"]
     digest = src_digest("q4k_gemv.hip", "common.h")

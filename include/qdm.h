@@ -58,12 +58,16 @@ extern "C" {
 #define QDM_F32 0
 #define QDM_BF16 1
 
+/* weight types (moe_grouped_gemm_from_logits down experts) */
+#define QDM_Q4_K 4
+#define QDM_Q5_K 5
+
 /* status codes */
 #define QDM_OK 0
 #define QDM_ERR_NULL (-1)      /* a required pointer is NULL */
 #define QDM_ERR_SHAPE (-2)     /* bad size (K % 256, non-positive, limits) */
 #define QDM_ERR_ALIGN (-3)     /* a pointer is not 16-byte aligned */
-#define QDM_ERR_DTYPE (-4)     /* unknown or unsupported activation dtype */
+#define QDM_ERR_DTYPE (-4)     /* unknown or unsupported activation dtype or weight type */
 #define QDM_ERR_WORKSPACE (-5) /* workspace missing or too small */
 #define QDM_ERR_HIP (-6)       /* the HIP runtime reported an error */
 
@@ -163,6 +167,39 @@ int moe_q4k_q5k_grouped_gemm(const void *x, const void *w_gate_up, const void *w
                              const int32_t *topk_ids, const float *topk_w, float *y,
                              int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_router_topk: the router in front of the MoE grouped matmul (hipEngine
+ * README, "Status", names a routed MoE model, Qwen3.6-35B-A3B, but not its
+ * router; this is the plainest reading of one). For each token t of the
+ * logits [T][E] (fp32, finite): topk_ids[t] = the top_k experts with the
+ * largest logits, largest first, the smaller index first among equal logits;
+ * topk_w[t][s] = exp(l_s - l_0) / sum_j exp(l_j - l_0) over the selected
+ * logits (the softmax of the selection), fp32. Integer results are exact;
+ * the weights are within a few fp32 ulps of the float64 softmax.
+ * 1 <= T <= 2^24, 1 <= E <= 1024, 1 <= top_k <= min(16, E). topk_ids int32
+ * [T][top_k] and topk_w fp32 [T][top_k] are overwritten. The three arrays
+ * need only 4-byte alignment.
+ */
+int moe_router_topk(const float *logits, int64_t T, int64_t E, int64_t top_k,
+                    int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
+ * moe_grouped_gemm_from_logits: moe_router_topk followed by the routed MoE
+ * FFN in one call (gate+up experts Q4_K; down experts QDM_Q4_K or QDM_Q5_K
+ * by down_qtype). The ids and gate weights live in the workspace:
+ * moe_from_logits_workspace_bytes(T, E, top_k, H, F) bytes (scratch, no
+ * initial contents). router_logits: fp32 [T][E], 4-byte aligned. Arguments
+ * and limits otherwise as moe_q4k_grouped_gemm; top_k <= E. A down_qtype
+ * other than the two returns QDM_ERR_DTYPE.
+ */
+size_t moe_from_logits_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H,
+                                       int64_t F);
+int moe_grouped_gemm_from_logits(const void *x, const float *router_logits,
+                                 const void *w_gate_up, const void *w_down, int down_qtype,
+                                 float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
+                                 int64_t F, void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /*
  * qdm_probe_copy: streaming copy of n_bytes from src to dst (n_bytes % 16 ==

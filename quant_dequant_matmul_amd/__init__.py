@@ -59,6 +59,13 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p, sz, p]
             f.restype = i32
+        L.moe_router_topk.argtypes = [p, i64, i64, i64, p, p, p]
+        L.moe_router_topk.restype = i32
+        L.moe_from_logits_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.moe_from_logits_workspace_bytes.restype = sz
+        L.moe_grouped_gemm_from_logits.argtypes = [p, p, p, p, i32, p, i64, i64, i64, i64, i64,
+                                                   p, sz, p]
+        L.moe_grouped_gemm_from_logits.restype = i32
         L.qdm_probe_copy.argtypes = [p, p, i64, p]
         L.qdm_probe_copy.restype = i32
         _lib = L
@@ -203,6 +210,10 @@ def moe_q4k_workspace_bytes(T: int, E: int, top_k: int, H: int, F: int) -> int:
     return int(lib().moe_q4k_workspace_bytes(T, E, top_k, H, F))
 
 
+def moe_from_logits_workspace_bytes(T: int, E: int, top_k: int, H: int, F: int) -> int:
+    return int(lib().moe_from_logits_workspace_bytes(T, E, top_k, H, F))
+
+
 def _moe(fn: str, x, w_gate_up, w_down, topk_ids, topk_w, E, H, F, y, workspace, stream):
     T, top_k = topk_ids.shape
     y = _out(y, (T, H), x.device)
@@ -230,6 +241,39 @@ def moe_q4k_q5k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: 
     """The same routed MoE FFN with Q4_K gate+up experts and Q5_K down experts."""
     return _moe("moe_q4k_q5k_grouped_gemm", x, w_gate_up, w_down, topk_ids, topk_w, E, H, F, y,
                 workspace, stream)
+
+
+def moe_router_topk(logits, top_k: int, ids=None, weights=None, stream=None):
+    """Top-k experts per token and their softmax gate weights from fp32 router
+    logits [T][E]: (ids int32 [T][top_k], weights fp32 [T][top_k])."""
+    torch = _torch()
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    weights = _out(weights, (T, top_k), logits.device)
+    _check("moe_router_topk", lib().moe_router_topk(
+        _dev_ptr(logits, "logits"), T, E, top_k, _dev_ptr(ids, "ids"),
+        _dev_ptr(weights, "weights"), _stream(stream)))
+    return ids, weights
+
+
+def moe_grouped_gemm_from_logits(x, router_logits, w_gate_up, w_down, top_k: int, E: int,
+                                 H: int, F: int, down_qtype: int = 4, y=None, workspace=None,
+                                 stream=None):
+    """Router (top-k + softmax from router_logits [T][E]) then the routed MoE
+    FFN, in one call; down experts Q4_K (4) or Q5_K (5)."""
+    torch = _torch()
+    T = router_logits.shape[0]
+    y = _out(y, (T, H), x.device)
+    need = int(lib().moe_from_logits_workspace_bytes(T, E, top_k, H, F))
+    if workspace is None:
+        workspace = _cached_workspace("moe_logits", need, x.device)
+    _check("moe_grouped_gemm_from_logits", lib().moe_grouped_gemm_from_logits(
+        _dev_ptr(x, "x"), _dev_ptr(router_logits, "router_logits"),
+        _dev_ptr(w_gate_up, "w_gate_up"), _dev_ptr(w_down, "w_down"), down_qtype,
+        _dev_ptr(y, "y"), T, E, top_k, H, F, _dev_ptr(workspace, "workspace"),
+        workspace.numel(), _stream(stream)))
+    return y
 
 
 def probe_copy(src, dst, n_bytes: int, stream=None):

@@ -18,6 +18,7 @@ constexpr int64_t kMaxK = 65536;      // bf16 activations (x staged in LDS)
 constexpr int64_t kMaxKF32 = 32768;   // fp32 activations
 
 inline bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+inline bool misaligned4(const void *p) { return ((uintptr_t)p & 3u) != 0; }
 
 inline int finish_launch() {
   return hipGetLastError() == hipSuccess ? QDM_OK : QDM_ERR_HIP;
@@ -33,7 +34,7 @@ QDM_EXPORT const char *qdm_status_string(int status) {
     case QDM_ERR_NULL: return "a required pointer is NULL";
     case QDM_ERR_SHAPE: return "invalid size argument";
     case QDM_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case QDM_ERR_DTYPE: return "unsupported activation dtype";
+    case QDM_ERR_DTYPE: return "unsupported activation dtype or weight type";
     case QDM_ERR_WORKSPACE: return "workspace missing or too small";
     case QDM_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
@@ -163,6 +164,44 @@ QDM_EXPORT int moe_q4k_q5k_grouped_gemm(const void *x, const void *w_gate_up,
   if (rc) return rc;
   qdm::launch_moe_q4k_q5k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
                           workspace, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int moe_router_topk(const float *logits, int64_t T, int64_t E, int64_t top_k,
+                               int32_t *topk_ids, float *topk_w, void *stream) {
+  if (!logits || !topk_ids || !topk_w) return QDM_ERR_NULL;
+  if (T < 1 || T > (1 << 24) || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || top_k > E)
+    return QDM_ERR_SHAPE;
+  if (misaligned4(logits) || misaligned4(topk_ids) || misaligned4(topk_w)) return QDM_ERR_ALIGN;
+  qdm::launch_router_topk(logits, T, E, top_k, topk_ids, topk_w, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT size_t moe_from_logits_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H,
+                                                  int64_t F) {
+  if (T < 1 || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || top_k > E || bad_k(H) ||
+      bad_k(F))
+    return 0;
+  return qdm::moe_logits_workspace(T, E, top_k, H, F);
+}
+
+QDM_EXPORT int moe_grouped_gemm_from_logits(const void *x, const float *router_logits,
+                                            const void *w_gate_up, const void *w_down,
+                                            int down_qtype, float *y, int64_t T, int64_t E,
+                                            int64_t top_k, int64_t H, int64_t F,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream) {
+  if (!router_logits) return QDM_ERR_NULL;
+  if (down_qtype != QDM_Q4_K && down_qtype != QDM_Q5_K) return QDM_ERR_DTYPE;
+  // the MoE checks with a dummy ids/weights pointer (they are produced here)
+  const int rc = check_moe(x, w_gate_up, w_down, (const int32_t *)router_logits, router_logits,
+                           y, T, E, top_k, H, F, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (top_k > E) return QDM_ERR_SHAPE;
+  if (misaligned4(router_logits)) return QDM_ERR_ALIGN;
+  if (workspace_bytes < qdm::moe_logits_workspace(T, E, top_k, H, F)) return QDM_ERR_WORKSPACE;
+  qdm::launch_moe_from_logits(x, router_logits, w_gate_up, w_down, down_qtype == QDM_Q5_K, y, T,
+                              E, top_k, H, F, workspace, (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -31,6 +31,13 @@ void launch_moe_q4k_q5k(const void *x, const void *w13, const void *w2, const in
                         const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
                         int64_t H, int64_t F, void *workspace, hipStream_t s);
 
+void launch_router_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *ids,
+                        float *gw, hipStream_t s);
+size_t moe_logits_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
+void launch_moe_from_logits(const void *x, const float *logits, const void *w13, const void *w2,
+                            bool down_q5, float *y, int64_t T, int64_t E, int64_t top_k,
+                            int64_t H, int64_t F, void *workspace, hipStream_t s);
+
 void launch_probe_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
 
 }  // namespace qdm

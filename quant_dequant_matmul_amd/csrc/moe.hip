@@ -437,6 +437,107 @@ __global__ __launch_bounds__(256) void moe_combine_entries_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Router: top-k experts and their softmax gate weights from router logits.
+// ---------------------------------------------------------------------------
+// One wave per token; lane l holds logits l, l+64, ... (E <= 64 * PER). Each
+// logit becomes a 64-bit key: the logit's bits mapped to an unsigned integer
+// of the same order (-0 taken as +0, so equal logits give equal high words),
+// and ~e in the low word, so that the largest key is the largest logit and,
+// among equal logits, the smallest index. Each of the k rounds takes the
+// wave's largest key (lane-local maximum, DPP maxima within each row of 16
+// lanes, then the four row results read out), and the lane holding it clears
+// that key. Lane s keeps winner s; the gate weights are the softmax of the k
+// winners, exp(l_s - l_0) / sum_j exp(l_j - l_0) with l_0 the largest (no
+// overflow for large logits).
+constexpr int RT_THREADS = 256;
+constexpr int RT_MAX_E = 1024, RT_MAX_K = 16;
+static_assert(RT_MAX_K <= 16, "the winners are gathered in the 16 lanes of row 0");
+
+// DPP controls (row = 16 lanes): swap neighbours, swap pairs, mirror within
+// each half row, mirror within the row.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t a) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)a, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > a ? o : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_f32(float a) {
+  return a + __int_as_float(
+                 __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint64_t rd_lane_u64(uint64_t a, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)a, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_inv(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+template <int PER>
+__global__ __launch_bounds__(RT_THREADS) void moe_router_topk_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
+    float *__restrict__ gw) {
+  const int lane = threadIdx.x & 63;
+  const int t = (int)blockIdx.x * (RT_THREADS / WAVE) + (int)(threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave: the DPP steps below see all 64 lanes
+  const float *lt = logits + (int64_t)t * E;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; j++) v[j] = lt[min(lane + WAVE * j, E - 1)];  // all loads in flight
+  uint64_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; j++) {
+    const int e = lane + WAVE * j;
+    key[j] = e < E ? ((uint64_t)order_bits(v[j]) << 32) | (uint32_t)~(uint32_t)e : 0;
+  }
+  uint64_t mine = 0;  // lane s: the key of winner s
+  for (int s = 0; s < k; s++) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int j = 1; j < PER; j++) m = key[j] > m ? key[j] : m;
+    m = dpp_max_u64<DPP_XOR1>(m);
+    m = dpp_max_u64<DPP_XOR2>(m);
+    m = dpp_max_u64<DPP_HALF_MIRROR>(m);
+    m = dpp_max_u64<DPP_MIRROR>(m);
+    uint64_t best = rd_lane_u64(m, 0);
+#pragma unroll
+    for (int r = 1; r < 4; r++) {
+      const uint64_t o = rd_lane_u64(m, 16 * r);
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; j++)
+      if (key[j] == best) key[j] = 0;  // the winner's key exists once (the index is in it)
+    if (lane == s) mine = best;
+  }
+  // k <= 16: the winners sit in lanes 0..k-1 of row 0.
+  const float l0 = order_bits_inv((uint32_t)(rd_lane_u64(mine, 0) >> 32));
+  float ex = lane < k ? expf(order_bits_inv((uint32_t)(mine >> 32)) - l0) : 0.f;
+  float sum = dpp_add_f32<DPP_XOR1>(ex);
+  sum = dpp_add_f32<DPP_XOR2>(sum);
+  sum = dpp_add_f32<DPP_HALF_MIRROR>(sum);
+  sum = dpp_add_f32<DPP_MIRROR>(sum);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = (int32_t)~(uint32_t)mine;
+    gw[(int64_t)t * k + lane] = ex / sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core regime (n > 64).
 // ---------------------------------------------------------------------------
 constexpr int ROUTE_THREADS = 1024;
@@ -869,6 +970,43 @@ void launch_moe_q4k_q5k(const void *x, const void *w13, const void *w2, const in
                         const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
                         int64_t H, int64_t F, void *workspace, hipStream_t s) {
   launch_moe<true>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
+}
+
+void launch_router_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *ids,
+                        float *gw, hipStream_t s) {
+  constexpr int per_wg = RT_THREADS / WAVE;
+  const dim3 grid((unsigned)((T + per_wg - 1) / per_wg)), block(RT_THREADS);
+  if (E <= 2 * WAVE)
+    hipLaunchKernelGGL(moe_router_topk_kernel<2>, grid, block, 0, s, logits, (int)T, (int)E,
+                       (int)k, ids, gw);
+  else if (E <= 4 * WAVE)
+    hipLaunchKernelGGL(moe_router_topk_kernel<4>, grid, block, 0, s, logits, (int)T, (int)E,
+                       (int)k, ids, gw);
+  else if (E <= 8 * WAVE)
+    hipLaunchKernelGGL(moe_router_topk_kernel<8>, grid, block, 0, s, logits, (int)T, (int)E,
+                       (int)k, ids, gw);
+  else
+    hipLaunchKernelGGL(moe_router_topk_kernel<RT_MAX_E / WAVE>, grid, block, 0, s, logits,
+                       (int)T, (int)E, (int)k, ids, gw);
+}
+
+// Router then MoE in one call: the ids and gate weights go to the space after
+// the MoE workspace.
+size_t moe_logits_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F) {
+  return moe_workspace(T, E, top_k, H, F) + 2 * align256((size_t)(T * top_k) * 4);
+}
+
+void launch_moe_from_logits(const void *x, const float *logits, const void *w13, const void *w2,
+                            bool down_q5, float *y, int64_t T, int64_t E, int64_t top_k,
+                            int64_t H, int64_t F, void *workspace, hipStream_t s) {
+  char *extra = (char *)workspace + moe_workspace(T, E, top_k, H, F);
+  int32_t *ids = (int32_t *)extra;
+  float *gw = (float *)(extra + align256((size_t)(T * top_k) * 4));
+  launch_router_topk(logits, T, E, top_k, ids, gw, s);
+  if (down_q5)
+    launch_moe<true>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
+  else
+    launch_moe<false>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
 }
 
 }  // namespace qdm

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(qdm.LIB_PATH)
     names = declared_functions()
-    assert len(names) >= 14
+    assert len(names) >= 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +103,45 @@ def test_moe_validation(fn):
     assert moe(*args, T, E, k, H, F, NUL, need, NUL) == EWS
     assert moe(*args, T, E, k, H, F, A, need - 1, NUL) == EWS
     assert moe(*args, T, E, k, H, F, MIS, need, NUL) == EALIGN
+
+
+MIS4 = ctypes.c_void_p((1 << 20) + 2)  # not even 4-byte aligned
+
+
+def test_router_validation():
+    L = qdm.lib()
+    r = L.moe_router_topk
+    assert r(NUL, 4, 128, 8, A, A2, NUL) == ENULL
+    assert r(A, 4, 128, 8, NUL, A2, NUL) == ENULL
+    assert r(A, 0, 128, 8, A, A2, NUL) == ESHAPE
+    assert r(A, 4, 0, 1, A, A2, NUL) == ESHAPE
+    assert r(A, 4, 1025, 8, A, A2, NUL) == ESHAPE
+    assert r(A, 4, 128, 0, A, A2, NUL) == ESHAPE
+    assert r(A, 4, 128, 17, A, A2, NUL) == ESHAPE
+    assert r(A, 4, 6, 7, A, A2, NUL) == ESHAPE      # top_k > E
+    assert r(MIS4, 4, 128, 8, A, A2, NUL) == EALIGN
+    assert r(A, 4, 128, 8, A, MIS4, NUL) == EALIGN
+
+
+def test_moe_from_logits_validation():
+    L = qdm.lib()
+    moe = L.moe_grouped_gemm_from_logits
+    T, E, k, H, F = 8, 128, 8, 2048, 768
+    need = L.moe_from_logits_workspace_bytes(T, E, k, H, F)
+    assert need >= L.moe_q4k_workspace_bytes(T, E, k, H, F) + 2 * T * k * 4
+    assert L.moe_from_logits_workspace_bytes(T, 6, 7, H, F) == 0
+    assert L.moe_from_logits_workspace_bytes(T, E, k, 300, F) == 0
+    for dq in (4, 5):
+        args = [A, A, A, A, dq, A2]
+        assert moe(A, NUL, A, A, dq, A2, T, E, k, H, F, A, need, NUL) == ENULL
+        assert moe(NUL, A, A, A, dq, A2, T, E, k, H, F, A, need, NUL) == ENULL
+        assert moe(*args, 0, E, k, H, F, A, need, NUL) == ESHAPE
+        assert moe(*args, T, 6, 7, H, F, A, need, NUL) == ESHAPE
+        assert moe(*args, T, E, 17, H, F, A, need, NUL) == ESHAPE
+        assert moe(A, MIS4, A, A, dq, A2, T, E, k, H, F, A, need, NUL) == EALIGN
+        assert moe(*args, T, E, k, H, F, A, need - 1, NUL) == EWS
+        assert moe(*args, T, E, k, H, F, NUL, need, NUL) == EWS
+    assert moe(A, A, A, A, 6, A2, T, E, k, H, F, A, need, NUL) == EDTYPE
 
 
 def test_probe_validation():

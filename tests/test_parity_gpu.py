@@ -493,6 +493,100 @@ def test_moe_skips_out_of_range_ids():
 # --------------------------------------------------------------------------
 # determinism (race detector): identical calls give identical bits
 # --------------------------------------------------------------------------
+# Router (top-k + softmax of the selection) and MoE from router logits
+# --------------------------------------------------------------------------
+
+# fp32 weights vs the float64 softmax: expf (a few ulps), the fp32 difference
+# of two logits (relative error below |l_s - l_0| * 2^-24), a sum of at most 16
+# terms and one division stay below 4e-6 relative for logits spread over a
+# few units.
+TOL_ROUTER_W = 4e-6
+
+
+def _check_router(logits, k):
+    T, E = logits.shape
+    ids, w = qdm.moe_router_topk(torch.from_numpy(logits).to("cuda"), k)
+    ids, w = host(ids), host(w)
+    rid, rw = oracle.router_topk(logits, k)
+    assert np.array_equal(ids, rid)
+    e = np.max(np.abs(w.astype(np.float64) - rw) / rw)
+    say("  router weight rel err", e)
+    assert e <= TOL_ROUTER_W
+    return ids, w
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (513, 128, 8), (7, 100, 5), (3, 1024, 16),
+                                   (5, 1, 1), (9, 64, 16), (2, 16, 16), (33, 1000, 3)])
+def test_router_topk_matches_oracle(T, E, k):
+    say("router", T, E, k)
+    (g,) = synth.streams(T * 1000 + E + k, 1)
+    _check_router(synth.router_logits(g, T, E), k)
+
+
+def test_router_topk_ties_and_shift():
+    """Equal logits (ids must follow the smaller-index rule), rows of one
+    value (weights 1/k), and logits near 1000 (the softmax is shifted by the
+    largest)."""
+    (g,) = synth.streams(77, 1)
+    lg = synth.router_logits(g, 40, 200)
+    ties = (np.round(lg * 2) / 2).astype(np.float32)  # few distinct values
+    ties[3] = 0.25
+    ties[4] = -7.0
+    ties[5, ::3] = 9.0
+    say("router ties")
+    ids, w = _check_router(ties, 8)
+    assert np.array_equal(ids[3], np.arange(8))
+    assert np.allclose(w[3], 1 / 8, rtol=1e-6)
+    say("router shifted logits")
+    _check_router((lg + 1000).astype(np.float32), 8)
+
+
+def _moe_logits_dev(d, logits):
+    return (dev_x(d["x"]), torch.from_numpy(logits).to("cuda"), dev_bytes(d["w13"]),
+            dev_bytes(d["w2"]))
+
+
+@pytest.mark.parametrize("dq", [4, 5])
+@pytest.mark.parametrize("T,E,H,F,top_k", [(5, 6, 256, 256, 3), (33, 16, 256, 512, 4),
+                                           (64, 8, 768, 256, 8), (70, 100, 256, 256, 6),
+                                           (9, 8, 256, 256, 7)])
+def test_moe_from_logits_small_full(T, E, H, F, top_k, dq):
+    """Router and MoE in one call against the oracle's router feeding the
+    oracle's MoE; also bit-identical to the router entry followed by the MoE
+    entry with the same ids and weights."""
+    say("moe from logits", T, E, H, F, top_k, dq)
+    d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T + E + 2, down_qtype=dq)
+    logits = synth.moe_router(T, E=E, seed=T + E + 20)
+    xd, ld, w13, w2 = _moe_logits_dev(d, logits)
+    y = host(qdm.moe_grouped_gemm_from_logits(xd, ld, w13, w2, top_k, E, H, F, down_qtype=dq))
+    rid, rw = oracle.router_topk(logits, top_k)
+    ref = oracle.moe(d["x"], d["w13"], d["w2"], rid, rw, E, H, F, dq)
+    e = rel_err(y, ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+    ids, gw = qdm.moe_router_topk(ld, top_k)
+    step = qdm.moe_q4k_q5k_grouped_gemm if dq == 5 else qdm.moe_q4k_grouped_gemm
+    assert np.array_equal(host(step(xd, w13, w2, ids, gw, E, H, F)), y)
+
+
+@pytest.mark.parametrize("T", [1, 8, 512])
+def test_moe_from_logits_full_shape(T):
+    """128 experts, H=2048, F=768, top-8, Q5_K down experts, router logits
+    N(0, 1). All tokens checked for T <= 8, 24 sampled tokens at T = 512."""
+    E, H, F = 128, 2048, 768
+    say("moe from logits full T", T)
+    d = synth.moe(T, down_qtype=5)
+    logits = synth.moe_router(T)
+    y = host(qdm.moe_grouped_gemm_from_logits(*_moe_logits_dev(d, logits), 8, E, H, F,
+                                              down_qtype=5))
+    toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 24).astype(int)
+    rid, rw = oracle.router_topk(logits[toks], 8)
+    ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], rid, rw, E, H, F, 5)
+    e = rel_err(y[toks], ref)
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+# --------------------------------------------------------------------------
 
 def test_determinism_all_entry_points():
     rng = np.random.default_rng(99)
@@ -527,6 +621,15 @@ def test_determinism_all_entry_points():
         say("determinism moe q5k-down T", T)
         a = host(qdm.moe_q4k_q5k_grouped_gemm(*args5, 128, 2048, 768))
         b = host(qdm.moe_q4k_q5k_grouped_gemm(*args5, 128, 2048, 768))
+        assert np.array_equal(a, b)
+        lg = torch.from_numpy(synth.moe_router(T)).to("cuda")
+        say("determinism router + moe from logits T", T)
+        r1, r2 = qdm.moe_router_topk(lg, 8), qdm.moe_router_topk(lg, 8)
+        assert all(np.array_equal(host(p), host(q)) for p, q in zip(r1, r2))
+        a = host(qdm.moe_grouped_gemm_from_logits(args5[0], lg, args5[1], args5[2], 8, 128,
+                                                  2048, 768, down_qtype=5))
+        b = host(qdm.moe_grouped_gemm_from_logits(args5[0], lg, args5[1], args5[2], 8, 128,
+                                                  2048, 768, down_qtype=5))
         assert np.array_equal(a, b)
 
 
