@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
-BLOCK_BYTES = {4: 144, 5: 176, 6: 210}  # bytes per 256-weight super-block
+BLOCK_BYTES = {4: 144, 5: 176, 6: 210, 8: 34}  # bytes per block
+BLOCK_WEIGHTS = {4: 256, 5: 256, 6: 256, 8: 32}  # weights per block
 
 
 def build(force: bool = True) -> str:
@@ -46,6 +47,8 @@ def _load():
         lib.oracle_q5k_dequantize.restype = None
         lib.oracle_q6k_dequantize.argtypes = [p, i64, i64, p]
         lib.oracle_q6k_dequantize.restype = None
+        lib.oracle_q80_dequantize.argtypes = [p, i64, i64, p]
+        lib.oracle_q80_dequantize.restype = None
         lib.oracle_qmatmul.argtypes = [i32, p, p, i32, i64, i64, i64, p]
         lib.oracle_qmatmul.restype = i32
         lib.oracle_moe_q4k.argtypes = [p, i32, p, p, p, p, i64, i64, i64, i64, i64, p]
@@ -62,9 +65,9 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _blocks(blocks: np.ndarray, N: int, K: int, nbytes: int) -> np.ndarray:
+def _blocks(blocks: np.ndarray, N: int, K: int, nbytes: int, qk: int = 256) -> np.ndarray:
     b = np.ascontiguousarray(blocks, dtype=np.uint8)
-    if b.size != N * (K // 256) * nbytes or K % 256:
+    if b.size != N * (K // qk) * nbytes or K % qk:
         raise ValueError("block array does not match N=%d K=%d" % (N, K))
     return b
 
@@ -83,6 +86,14 @@ def q5k_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
     return out
 
 
+def q80_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Q8_0 (34-byte blocks of 32 weights, K % 32 == 0) -> fp32 [N][K]."""
+    b = _blocks(blocks, N, K, 34, 32)
+    out = np.empty((N, K), dtype=np.float32)
+    _load().oracle_q80_dequantize(_ptr(b), N, K, _ptr(out))
+    return out
+
+
 def q6k_dequantize(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
     b = _blocks(blocks, N, K, 210)
     out = np.empty((N, K), dtype=np.float32)
@@ -98,12 +109,13 @@ def _x(x: np.ndarray):
 
 
 def qmatmul(qtype: int, blocks: np.ndarray, x: np.ndarray, N: int, K: int) -> np.ndarray:
-    """float64 Y [M][N] = X [M][K] * dequant(W)^T; qtype 4 (Q4_K), 5 (Q5_K) or 6 (Q6_K)."""
+    """float64 Y [M][N] = X [M][K] * dequant(W)^T; qtype 4 (Q4_K), 5 (Q5_K),
+    6 (Q6_K) or 8 (Q8_0)."""
     xx, is_bf16 = _x(x)
     M = xx.shape[0]
     if xx.shape != (M, K):
         raise ValueError("x must be [M][K]")
-    b = _blocks(blocks, N, K, BLOCK_BYTES[qtype])
+    b = _blocks(blocks, N, K, BLOCK_BYTES[qtype], BLOCK_WEIGHTS[qtype])
     y = np.empty((M, N), dtype=np.float64)
     rc = _load().oracle_qmatmul(qtype, _ptr(b), _ptr(xx), is_bf16, M, N, K, _ptr(y))
     if rc:
@@ -121,6 +133,10 @@ def q5k_matmul(blocks, x, N, K):
 
 def q6k_matmul(blocks, x, N, K):
     return qmatmul(6, blocks, x, N, K)
+
+
+def q80_matmul(blocks, x, N, K):
+    return qmatmul(8, blocks, x, N, K)
 
 
 def moe(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, ids: np.ndarray,

@@ -1,6 +1,7 @@
 /*
- * CPU oracle for the GGUF k-quant (Q4_K, Q5_K, Q6_K) dequantize-fused matmul
- * and the top-k router in front of its MoE grouped matmul.
+ * CPU oracle for the GGUF k-quant (Q4_K, Q5_K, Q6_K) and Q8_0
+ * dequantize-fused matmul and the top-k router in front of its MoE grouped
+ * matmul.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this library. It shares no code, header or table
@@ -43,12 +44,17 @@
  *   high nibble otherwise) and its high 2 bits from bits 2g..2g+1 of
  *   QH[32h + l]. q = lo | hi << 4 in 0..63;  w = d*scale[i/16]*(q - 32).
  *
+ * Q8_0, 34 bytes per 32 weights (a reading: the pages name the type and its
+ *   share of a Q4_K_M file only): fp16 d @0, then 32 int8 codes q[i] @2+i
+ *   (two's complement); w = d*q[i]. A tensor row is K/32 consecutive blocks.
+ *
  * fp32 exactness of the dequant (why one fp32 formula is the reference):
  *   every product here is exact in fp32 (Q4_K d*sc*q has at most 11+6+4 = 21
  *   significant bits, Q5_K d*sc*q at most 11+6+5 = 22, dmin*m at most 17;
- *   Q6_K d*scale*(q-32) at most 11+7+5), so a Q4_K or Q5_K weight is the
+ *   Q6_K d*scale*(q-32) at most 11+7+5, Q8_0 d*q at most 11+7), so a Q4_K or Q5_K weight is the
  *   single correctly rounded value of the exact d*sc*q - dmin*m, whatever the
- *   evaluation order or FMA contraction, and the Q6_K weight is exact. Any
+ *   evaluation order or FMA contraction, and the Q6_K and Q8_0 weights are
+ *   exact. Any
  *   correct fp32 implementation is bit-identical.
  */
 #include <math.h>
@@ -60,6 +66,8 @@
 #define Q4K_BYTES 144
 #define Q5K_BYTES 176
 #define Q6K_BYTES 210
+#define Q80_WEIGHTS 32
+#define Q80_BYTES 34
 
 /* IEEE 754 binary16 -> float, from the definition:
  *   e in 1..30: (-1)^s 2^(e-15) (1 + m/1024);  e = 0: (-1)^s 2^-14 (m/1024). */
@@ -172,6 +180,24 @@ void oracle_q5k_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *o
             q5k_block_dequant(blocks + (n * nb + b) * Q5K_BYTES, out + n * K + b * QK);
 }
 
+/* Q8_0: w[i] = d * q[i], q[i] the int8 at byte 2 + i. */
+static void q80_block_dequant(const uint8_t *B, float *w)
+{
+    const float d = fp16_value((uint16_t)(B[0] | B[1] << 8));
+    for (int i = 0; i < Q80_WEIGHTS; i++)
+        w[i] = d * (float)(int8_t)B[2 + i]; /* exact */
+}
+
+void oracle_q80_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *out)
+{
+    const int64_t nb = K / Q80_WEIGHTS;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t b = 0; b < nb; b++)
+            q80_block_dequant(blocks + (n * nb + b) * Q80_BYTES,
+                              out + n * K + b * Q80_WEIGHTS);
+}
+
 void oracle_q6k_dequantize(const uint8_t *blocks, int64_t N, int64_t K, float *out)
 {
     const int64_t nb = K / QK;
@@ -190,15 +216,22 @@ static void widen_x(const void *x, int x_is_bf16, int64_t M, int64_t K, double *
 }
 
 /* Y [M][N] float64 = X [M][K] * W^T for a quantized W [N][K].
- * qtype 4 = Q4_K, 5 = Q5_K, 6 = Q6_K. Each row of W is dequantized once into
- * fp32, then Y[m][n] = sum_k X[m][k] * W[n][k] in float64, k increasing. */
+ * qtype 4 = Q4_K, 5 = Q5_K, 6 = Q6_K (K % 256 == 0), 8 = Q8_0 (K % 32 == 0).
+ * Each row of W is dequantized once into fp32, then
+ * Y[m][n] = sum_k X[m][k] * W[n][k] in float64, k increasing. */
 int oracle_qmatmul(int qtype, const uint8_t *blocks, const void *x, int x_is_bf16,
                    int64_t M, int64_t N, int64_t K, double *y)
 {
-    if (K % QK || M < 0 || N < 0 || (qtype != 4 && qtype != 5 && qtype != 6))
+    if (qtype != 4 && qtype != 5 && qtype != 6 && qtype != 8)
         return -1;
-    const int64_t nb = K / QK;
-    const int64_t bb = qtype == 4 ? Q4K_BYTES : qtype == 5 ? Q5K_BYTES : Q6K_BYTES;
+    const int64_t qk = qtype == 8 ? Q80_WEIGHTS : QK;
+    if (K % qk || M < 0 || N < 0)
+        return -1;
+    const int64_t nb = K / qk;
+    const int64_t bb = qtype == 4   ? Q4K_BYTES
+                       : qtype == 5 ? Q5K_BYTES
+                       : qtype == 6 ? Q6K_BYTES
+                                    : Q80_BYTES;
     double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!xd)
         return -2;
@@ -211,11 +244,13 @@ int oracle_qmatmul(int qtype, const uint8_t *blocks, const void *x, int x_is_bf1
             for (int64_t b = 0; b < nb; b++) {
                 const uint8_t *blk = blocks + (n * nb + b) * bb;
                 if (qtype == 4)
-                    q4k_block_dequant(blk, w + b * QK);
+                    q4k_block_dequant(blk, w + b * qk);
                 else if (qtype == 5)
-                    q5k_block_dequant(blk, w + b * QK);
+                    q5k_block_dequant(blk, w + b * qk);
+                else if (qtype == 6)
+                    q6k_block_dequant(blk, w + b * qk);
                 else
-                    q6k_block_dequant(blk, w + b * QK);
+                    q80_block_dequant(blk, w + b * qk);
             }
             for (int64_t m = 0; m < M; m++) {
                 double acc = 0.0;

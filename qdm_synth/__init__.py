@@ -43,6 +43,8 @@ import numpy as np
 Q4K_BLOCK_BYTES = 144
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
+Q80_BLOCK_BYTES = 34
+Q80_WEIGHTS = 32
 QK = 256  # weights per super-block
 
 
@@ -81,6 +83,18 @@ def q5k_blocks(rng: np.random.Generator, N: int, K: int,
     out[:, :, 0:2] = _fp16_bytes(rng.uniform(*d_range, size=(N, nb)))
     out[:, :, 2:4] = _fp16_bytes(rng.uniform(*dmin_range, size=(N, nb)))
     out[:, :, 4:] = rng.integers(0, 256, size=(N, nb, 172), dtype=np.uint8)
+    return out
+
+
+def q80_blocks(rng: np.random.Generator, N: int, K: int, d_range=(1e-3, 1e-2)) -> np.ndarray:
+    """Random Q8_0 tensor: uint8 array [N, K/32, 34] (fp16 d, then 32 uniform
+    int8 codes), rows contiguous."""
+    if K % Q80_WEIGHTS:
+        raise ValueError("K must be a multiple of 32")
+    nb = K // Q80_WEIGHTS
+    out = np.empty((N, nb, Q80_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = _fp16_bytes(rng.uniform(*d_range, size=(N, nb)))
+    out[:, :, 2:] = rng.integers(0, 256, size=(N, nb, 32), dtype=np.uint8)
     return out
 
 
@@ -150,6 +164,9 @@ Q6K_MIX = dict(name="q6k_gemv", seed=4,
 # takes the decode set's down shape (K=17408, N=5120); the MoE workload is the
 # Q4_K one with its down experts drawn as Q5_K.
 Q5K_GEMV = dict(name="q5k_gemv", seed=5, K=17408, N=5120, Ms=(1, 8))
+# Q8_0 (named with its share of a Q4_K_M file, no shape): a separately
+# generated tensor with the decode set's QKV shape (K=5120, N=7168).
+Q80_GEMV = dict(name="q80_gemv", seed=6, K=5120, N=7168, Ms=(1, 8))
 
 
 def tiny_gemv():
@@ -205,6 +222,13 @@ def q5k_gemv(M: int):
     g_w, g_x = streams(Q5K_GEMV["seed"], 2)
     w = q5k_blocks(g_w, Q5K_GEMV["N"], Q5K_GEMV["K"])
     x = normal_bf16(g_x, (M, Q5K_GEMV["K"]))
+    return w, x
+
+
+def q80_gemv(M: int):
+    g_w, g_x = streams(Q80_GEMV["seed"], 2)
+    w = q80_blocks(g_w, Q80_GEMV["N"], Q80_GEMV["K"])
+    x = normal_bf16(g_x, (M, Q80_GEMV["K"]))
     return w, x
 
 

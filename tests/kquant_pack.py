@@ -14,6 +14,7 @@ Q5_K (176 B): the Q4_K header @0..15, a high-bit plane @16 (32 B: bit j of
   byte l is the fifth bit of weight l of sub-block j), the Q4_K code bytes @48.
 Q6_K (210 B): low-nibble plane @0 (128 B), high-2-bit plane @128 (64 B),
   16 int8 scales @192, fp16 d @208; bit placement as read in the oracle.
+Q8_0 (34 B per 32 weights): fp16 d @0, 32 two's-complement int8 codes @2.
 """
 from __future__ import annotations
 
@@ -129,3 +130,19 @@ def grid_quantize_q4k(w: list[Fraction], d: Fraction, dmin: Fraction, qmax: int 
             assert qq.denominator == 1
             q.append(int(qq))
     return sc, mn, q
+
+
+def pack_q80(d_bits: int, q) -> np.ndarray:
+    """Q8_0 block (34 B) from the fp16 bits of d and 32 codes in -128..127."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and min(q) >= -128 and max(q) <= 127
+    b = np.zeros(34, dtype=np.uint8)
+    b[0], b[1] = d_bits & 255, d_bits >> 8
+    for i, v in enumerate(q):
+        b[2 + i] = v + 256 if v < 0 else v
+    return b
+
+
+def q80_exact_weights(d_bits: int, q):
+    d = Fraction(fp16_value(d_bits))
+    return [d * int(v) for v in q]

@@ -9,6 +9,9 @@ mathematics fix, never against the oracle itself.
 * Q5_K against Q4_K: with an empty high-bit plane a Q5_K block decodes
   exactly like the Q4_K block with the same header and code bytes.
 * fp16 decoding of d over every finite fp16 pattern vs numpy's conversion.
+* Q8_0: every code byte and both d bytes set directly, two's complement at
+  the ends of the range, every finite fp16 d, exact products, and a K that is
+  not a multiple of 256.
 * Round trip through an independent grid quantizer.
 * Matmul: exact rationals on tiny shapes within the fp64 summation bound,
   one-hot activations, bf16 widening, numpy cross-check.
@@ -28,8 +31,8 @@ import pytest
 import oracle
 import qdm_synth as synth
 from kquant_pack import (fp16_bits, fp16_value, grid_quantize_q4k, pack_q4k, pack_q5k,
-                         pack_q6k, q4k_exact_weights, q5k_exact_weights, q6k_exact_weights,
-                         rn32)
+                         pack_q6k, pack_q80, q4k_exact_weights, q5k_exact_weights,
+                         q6k_exact_weights, q80_exact_weights, rn32)
 
 ONE = 0x3C00  # fp16 1.0
 
@@ -392,6 +395,99 @@ def test_q5k_synthetic_fields_in_range():
 
 
 # --------------------------------------------------------------------------
+# Q8_0 (34-byte blocks of 32 weights)
+# --------------------------------------------------------------------------
+
+def _blank_q80(nb, d=ONE):
+    b = np.zeros((nb, 34), dtype=np.uint8)
+    b[:, 0], b[:, 1] = d & 255, d >> 8
+    return b
+
+
+def test_q80_code_placement_from_bytes():
+    """With d = 1, the code byte at offset 2+i of block b is weight 32b+i, as a
+    two's-complement int8; every position of every block of a 3-block row."""
+    nb, K = 3, 96
+    for b in range(nb):
+        for i in range(32):
+            for byte, val in ((0x01, 1), (0x7F, 127), (0x80, -128), (0xFF, -1), (0x9C, -100)):
+                blk = _blank_q80(nb)
+                blk[b, 2 + i] = byte
+                W = oracle.q80_dequantize(blk, 1, K)[0]
+                expect = np.zeros(K, dtype=np.float32)
+                expect[32 * b + i] = val
+                np.testing.assert_array_equal(W, expect)
+
+
+def test_q80_d_bytes_little_endian_every_fp16():
+    """All codes 1: every weight of the block is d. Byte 0 is the low byte of
+    the fp16 pattern; every finite pattern decodes as numpy's fp16."""
+    pats = np.arange(0x10000, dtype=np.uint32)
+    pats = pats[(pats & 0x7C00) != 0x7C00]  # finite only
+    blk = np.zeros((pats.size, 34), dtype=np.uint8)
+    blk[:, 0], blk[:, 1] = pats & 255, pats >> 8
+    blk[:, 2:] = 1
+    W = oracle.q80_dequantize(blk, pats.size, 32)
+    ref = pats.astype("<u2").view("<f2").astype(np.float32)
+    np.testing.assert_array_equal(W, np.repeat(ref[:, None], 32, axis=1))
+
+
+def test_q80_closed_form_and_exact_products():
+    """Random d and codes: every weight equals the exact rational d*q (the
+    product has at most 11 + 7 significant bits, so fp32 holds it exactly)."""
+    rng = np.random.default_rng(81)
+    for _ in range(40):
+        d_bits = int(rng.integers(0x0001, 0x7BFF))
+        q = rng.integers(-128, 128, size=32)
+        w = oracle.q80_dequantize(pack_q80(d_bits, q), 1, 32)[0]
+        exact = q80_exact_weights(d_bits, q)
+        assert all(Fraction(float(a)) == e for a, e in zip(w, exact))
+    w = oracle.q80_dequantize(pack_q80(fp16_bits(0.5), [-3] * 32), 1, 32)[0]
+    np.testing.assert_array_equal(w, np.full(32, -1.5, dtype=np.float32))
+
+
+def test_q80_grid_round_trip():
+    """Weights on the grid w = d*q recover every code as w/d, and the packed
+    bytes of those codes are the original block."""
+    rng = np.random.default_rng(82)
+    for _ in range(20):
+        d_bits = fp16_bits(float(rng.uniform(1e-3, 1e-1)))
+        q = rng.integers(-128, 128, size=32)
+        blk = pack_q80(d_bits, q)
+        w = oracle.q80_dequantize(blk, 1, 32)[0]
+        d = Fraction(fp16_value(d_bits))
+        rq = [Fraction(float(v)) / d for v in w]
+        assert all(r.denominator == 1 for r in rq)
+        np.testing.assert_array_equal(pack_q80(d_bits, [int(r) for r in rq]), blk)
+
+
+def test_q80_matmul_k_not_multiple_of_256():
+    """K = 96 (three blocks): the matmul equals the float64 product of the
+    exact weights, and block b covers k = 32b .. 32b+31 of its row."""
+    rng = np.random.default_rng(83)
+    N, K, M = 4, 96, 2
+    w = synth.q80_blocks(rng, N, K)
+    x = synth.normal_f32(rng, (M, K))
+    W = np.zeros((N, K))
+    for n in range(N):
+        for b in range(K // 32):
+            blk = w[n, b]
+            d = fp16_value(int(blk[0]) | int(blk[1]) << 8)
+            W[n, 32 * b:32 * b + 32] = d * blk[2:].view(np.int8).astype(np.float64)
+    Y = oracle.q80_matmul(w, x, N, K)
+    np.testing.assert_allclose(Y, x.astype(np.float64) @ W.T, rtol=1e-13, atol=1e-13)
+
+
+def test_q80_synthetic_fields_in_range():
+    rng = np.random.default_rng(84)
+    w = synth.q80_blocks(rng, 64, 512)
+    d = w[:, :, 0:2].copy().view("<f2").astype(np.float64)
+    assert d.min() >= 1e-3 * (1 - 2 ** -10) and d.max() <= 1e-2 * (1 + 2 ** -10)
+    codes = w[:, :, 2:].view(np.int8)
+    assert codes.min() == -128 and codes.max() == 127
+
+
+# --------------------------------------------------------------------------
 # Matmul (fp64 accumulation)
 # --------------------------------------------------------------------------
 
@@ -399,11 +495,12 @@ def _bf16_to_f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-_GEN = {4: synth.q4k_blocks, 5: synth.q5k_blocks, 6: synth.q6k_blocks}
-_DEQ = {4: oracle.q4k_dequantize, 5: oracle.q5k_dequantize, 6: oracle.q6k_dequantize}
+_GEN = {4: synth.q4k_blocks, 5: synth.q5k_blocks, 6: synth.q6k_blocks, 8: synth.q80_blocks}
+_DEQ = {4: oracle.q4k_dequantize, 5: oracle.q5k_dequantize, 6: oracle.q6k_dequantize,
+        8: oracle.q80_dequantize}
 
 
-@pytest.mark.parametrize("qtype", [4, 5, 6])
+@pytest.mark.parametrize("qtype", [4, 5, 6, 8])
 @pytest.mark.parametrize("xbf16", [False, True])
 def test_matmul_exact_rationals(qtype, xbf16):
     """Oracle fp64 result vs the exact rational sum: within the fp64
