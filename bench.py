@@ -39,6 +39,7 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 MALL_BYTES = 256 << 20
 DECODE = [("qkv", 5120, 7168), ("gate_up", 5120, 34816), ("down", 17408, 5120)]
 Q4K_BPB, Q5K_BPB, Q6K_BPB = 144, 176, 210
+Q80_BPB = 8 * 34  # bytes per 256 weights (eight 34-byte blocks)
 
 
 def log(*a):
@@ -270,6 +271,12 @@ def bench_q5k(torch, qdm, synth, oracle, M, reps):
     return bench_kgemv(torch, qdm.q5k_gemv, oracle.q5k_matmul, w, x, M, N, K, Q5K_BPB, reps)
 
 
+def bench_q80(torch, qdm, synth, oracle, M, reps):
+    K, N = synth.Q80_GEMV["K"], synth.Q80_GEMV["N"]
+    w, x = synth.q80_gemv(M)
+    return bench_kgemv(torch, qdm.q80_gemv, oracle.q80_matmul, w, x, M, N, K, Q80_BPB, reps)
+
+
 def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
     """A k-quant GEMV timed over rotating weight copies (larger than the
     last-level cache together), checked on sampled rows against the oracle."""
@@ -425,7 +432,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,moe,router,cpu",
+    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,q80,moe,router,cpu",
                     help="comma list of: probe, decode, graph, gemm, q6k, q5k, moe, cpu "
                          "(decode always runs: it is the headline)")
     args = ap.parse_args()
@@ -465,6 +472,11 @@ def main():
         for M, reps in ((1, 50), (8, 50)):
             key = "q5k_down_m%d" % M
             extra[key] = bench_q5k(torch, qdm, synth, oracle, M, reps)
+            log(key, extra[key])
+    if "q80" in sections:
+        for M, reps in ((1, 50), (8, 50)):
+            key = "q80_qkv_m%d" % M
+            extra[key] = bench_q80(torch, qdm, synth, oracle, M, reps)
             log(key, extra[key])
     if "moe" in sections:
         for T, reps in ((1, 50), (8, 50), (512, 10)):

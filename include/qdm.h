@@ -89,6 +89,16 @@ int q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream
 int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
 
 /*
+ * q80_dequantize: as above for Q8_0 (the type is named in the hipEngine
+ * README, "GGUF Support", payload table; the layout is a reading): 34-byte
+ * blocks of 32 weights, fp16 d @0 then 32 two's-complement int8 codes q @2,
+ * w = d * q (exact in fp32). A row of W is K/32 consecutive blocks.
+ * N >= 1, K >= 256, K % 256 == 0 (a row is then a whole number of 16-byte
+ * chunks).
+ */
+int q80_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
+
+/*
  * q4k_gemv / q5k_gemv / q6k_gemv: decode-regime matmul,
  * y[m][n] = sum_k x[m][k] * w(n,k)
  * for 1 <= M <= 16. x_dtype is QDM_F32 or QDM_BF16. Accumulation is fp32.
@@ -104,6 +114,16 @@ int q4k_gemv(const void *w, const void *x, int x_dtype, float *y,
 int q5k_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);
 int q6k_gemv(const void *w, const void *x, int x_dtype, float *y,
+             int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * q80_gemv: the same decode-regime matmul with Q8_0 weights (w: [N][K/32]
+ * 34-byte blocks, layout as in q80_dequantize). Arguments, limits and status
+ * codes as q4k_gemv; x is staged per column chunk, so K up to 65536 holds for
+ * fp32 x too within the q4k_gemv limits. Weights are applied in fp32 (exact),
+ * accumulation is fp32. Results are deterministic.
+ */
+int q80_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);
 
 /*

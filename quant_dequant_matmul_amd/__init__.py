@@ -41,11 +41,11 @@ def lib() -> ctypes.CDLL:
         L.qdm_status_string.argtypes = [i32]
         L.qdm_status_string.restype = ctypes.c_char_p
         L.qdm_version.restype = i32
-        for name in ("q4k_dequantize", "q5k_dequantize", "q6k_dequantize"):
+        for name in ("q4k_dequantize", "q5k_dequantize", "q6k_dequantize", "q80_dequantize"):
             f = getattr(L, name)
             f.argtypes = [p, p, i64, i64, p]
             f.restype = i32
-        for name in ("q4k_gemv", "q5k_gemv", "q6k_gemv"):
+        for name in ("q4k_gemv", "q5k_gemv", "q6k_gemv", "q80_gemv"):
             f = getattr(L, name)
             f.argtypes = [p, p, i32, p, i64, i64, i64, p]
             f.restype = i32
@@ -139,6 +139,13 @@ def q6k_dequantize(w, N: int, K: int, out=None, stream=None):
     return out
 
 
+def q80_dequantize(w, N: int, K: int, out=None, stream=None):
+    out = _out(out, (N, K), w.device)
+    _check("q80_dequantize", lib().q80_dequantize(_dev_ptr(w, "w"), _dev_ptr(out, "out"),
+                                                  N, K, _stream(stream)))
+    return out
+
+
 def q4k_gemv(w, x, N: int, K: int, y=None, stream=None):
     """y [M][N] fp32 = x [M][K] (fp32 or bf16) * W^T, W packed Q4_K [N][K/256]."""
     M = x.shape[0]
@@ -162,6 +169,15 @@ def q6k_gemv(w, x, N: int, K: int, y=None, stream=None):
     M = x.shape[0]
     y = _out(y, (M, N), x.device)
     _check("q6k_gemv", lib().q6k_gemv(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _x_dtype(x),
+                                      _dev_ptr(y, "y"), M, N, K, _stream(stream)))
+    return y
+
+
+def q80_gemv(w, x, N: int, K: int, y=None, stream=None):
+    """y [M][N] fp32 = x [M][K] (fp32 or bf16) * W^T, W packed Q8_0 [N][K/32]."""
+    M = x.shape[0]
+    y = _out(y, (M, N), x.device)
+    _check("q80_gemv", lib().q80_gemv(_dev_ptr(w, "w"), _dev_ptr(x, "x"), _x_dtype(x),
                                       _dev_ptr(y, "y"), M, N, K, _stream(stream)))
     return y
 

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "dequant.hip", "q4k_gemv.hip", "q6k_gemv.hip", "q4k_gemm.hip",
-           "moe.hip", "probe.hip"]
+SOURCES = ["api.hip", "dequant.hip", "q4k_gemv.hip", "q6k_gemv.hip", "q80_gemv.hip",
+           "q4k_gemm.hip", "moe.hip", "probe.hip"]
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          # keep the compiler from forming packed fp32 instructions

@@ -67,6 +67,14 @@ QDM_EXPORT int q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, v
   return finish_launch();
 }
 
+QDM_EXPORT int q80_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream) {
+  if (!w || !out) return QDM_ERR_NULL;
+  if (N < 1 || bad_k(K)) return QDM_ERR_SHAPE;
+  if (misaligned(w) || misaligned(out)) return QDM_ERR_ALIGN;
+  qdm::launch_q80_dequantize(w, out, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
 static int check_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
                       int64_t N, int64_t K) {
   if (!w || !x || !y) return QDM_ERR_NULL;
@@ -98,6 +106,15 @@ QDM_EXPORT int q6k_gemv(const void *w, const void *x, int x_dtype, float *y, int
   const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
   if (rc) return rc;
   qdm::launch_q6k_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int q80_gemv(const void *w, const void *x, int x_dtype, float *y, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+  const int rc = check_gemv(w, x, x_dtype, y, M, N, K);
+  if (rc) return rc;
+  if (!qdm::q80_gemv_fits(N, K)) return QDM_ERR_SHAPE;
+  qdm::launch_q80_gemv(w, x, x_dtype == QDM_BF16, y, M, N, K, (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -10,6 +10,7 @@ constexpr int QK = 256;          // weights per super-block
 constexpr int Q4K_BYTES = 144;   // Q4_K super-block
 constexpr int Q5K_BYTES = 176;   // Q5_K super-block: Q4_K header, 32 high-bit bytes, 128 code bytes
 constexpr int Q6K_BYTES = 210;   // Q6_K super-block
+constexpr int Q80_BYTES = 34;    // Q8_0 block: fp16 d, 32 int8 codes
 constexpr int WAVE = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -11,12 +11,16 @@ namespace qdm {
 void launch_q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
 void launch_q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
 void launch_q6k_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
+void launch_q80_dequantize(const void *w, float *out, int64_t N, int64_t K, hipStream_t s);
 
 void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s);
 void launch_q5k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s);
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s);
+bool q80_gemv_fits(int64_t N, int64_t K);
+void launch_q80_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s);
 
 size_t q4k_gemm_workspace(int64_t M, int64_t N, int64_t K);

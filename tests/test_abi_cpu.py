@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(qdm.LIB_PATH)
     names = declared_functions()
-    assert len(names) >= 17
+    assert len(names) >= 19
     for n in names:
         assert hasattr(lib, n), n
 
@@ -42,7 +42,7 @@ def test_status_strings():
     assert qdm.lib().qdm_version() >= 100
 
 
-@pytest.mark.parametrize("fn", ["q4k_gemv", "q5k_gemv", "q6k_gemv"])
+@pytest.mark.parametrize("fn", ["q4k_gemv", "q5k_gemv", "q6k_gemv", "q80_gemv"])
 def test_gemv_validation(fn):
     f = getattr(qdm.lib(), fn)
     assert f(NUL, A, 0, A2, 1, 8, 256, NUL) == ENULL
@@ -59,7 +59,8 @@ def test_gemv_validation(fn):
     assert f(A, A, 1, MIS, 1, 8, 256, NUL) == EALIGN
 
 
-@pytest.mark.parametrize("fn", ["q4k_dequantize", "q5k_dequantize", "q6k_dequantize"])
+@pytest.mark.parametrize("fn", ["q4k_dequantize", "q5k_dequantize", "q6k_dequantize",
+                                "q80_dequantize"])
 def test_dequant_validation(fn):
     f = getattr(qdm.lib(), fn)
     assert f(NUL, A, 4, 256, NUL) == ENULL

@@ -181,6 +181,79 @@ def test_q5k_gemv_down_full(M):
 
 
 # --------------------------------------------------------------------------
+# Q8_0 dequant and GEMV
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (37, 768, 5), (5, 17408, 6), (129, 1280, 7)])
+def test_q80_dequant_bit_exact(N, K, seed):
+    say("q80_dequantize", N, K, seed)
+    w = synth.q80_blocks(np.random.default_rng(seed), N, K)
+    out = host(qdm.q80_dequantize(dev_bytes(w), N, K))
+    ref = oracle.q80_dequantize(w, N, K)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# Ragged N, every token-chunk width (M = 16 -> 8 + 8, 5 -> 4 + 1, 3 -> 2 + 1),
+# rows shorter than a span (K = 256, 768), several spans per row, and K split
+# into column chunks (32768 with fp32 x, 65536 with bf16 x: 2 and 3 chunks).
+Q8_CASES = [(1, 1, 256), (1, 37, 768), (3, 1000, 1280), (5, 129, 2304), (16, 64, 4096),
+            (8, 333, 512), (2, 17, 8192), (1, 4099, 256), (1, 31, 32768), (4, 300, 5120),
+            (1, 257, 17408)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", Q8_CASES)
+def test_q80_gemv_ragged(M, N, K, dt):
+    say("q80_gemv", M, N, K, dt)
+    rng = np.random.default_rng(M * 1000 + N + K + 8)
+    w = synth.q80_blocks(rng, N, K)
+    x = synth.normal_f32(rng, (M, K)) if dt == "f32" else synth.normal_bf16(rng, (M, K))
+    y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
+    ref = oracle.q80_matmul(w, x, N, K)
+    e = rel_err(y, ref)
+    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+
+
+def test_q80_gemv_longest_k_bf16():
+    """K = 65536 with bf16 x: three column chunks, each adding into y."""
+    M, N, K = 2, 40, 65536
+    rng = np.random.default_rng(88)
+    w = synth.q80_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    say("q80_gemv longest K", M, N, K)
+    y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, oracle.q80_matmul(w, x, N, K))
+    assert e <= min(TOL_BF16, GUARD_VALU), e
+
+
+def test_q80_gemv_one_hot_rows_bit_exact():
+    """x = e_k (fp32) gives y[n] = W[n, k] exactly: every code position of the
+    four blocks of a quad (aligned and realigned code words)."""
+    N, K = 300, 1280
+    w = synth.q80_blocks(np.random.default_rng(9), N, K)
+    W = oracle.q80_dequantize(w, N, K)
+    wd = dev_bytes(w)
+    for k in [0, 1, 2, 3, 4, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 255, 256, 700, 1279]:
+        say("q80_gemv one-hot k", k)
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        y = host(qdm.q80_gemv(wd, dev_x(x), N, K))[0]
+        assert np.array_equal(y, W[:, k]), k
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_q80_gemv_qkv_full(M):
+    """The Q8_0 GEMV workload: the decode QKV shape (K=5120, N=7168), bf16 x."""
+    w, x = synth.q80_gemv(M)
+    N, K = synth.Q80_GEMV["N"], synth.Q80_GEMV["K"]
+    say("q80_gemv qkv full M", M)
+    y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, oracle.q80_matmul(w, x, N, K))
+    say("  rel err", e)
+    assert e <= min(TOL_BF16, GUARD_VALU)
+
+
+# --------------------------------------------------------------------------
 # Q6_K GEMV
 # --------------------------------------------------------------------------
 
@@ -605,6 +678,11 @@ def test_determinism_all_entry_points():
     say("determinism q6k M=8 (matrix cores, tiles split across waves)")
     a, b = host(qdm.q6k_gemv(w6, x6, 1000, K)), host(qdm.q6k_gemv(w6, x6, 1000, K))
     assert np.array_equal(a, b)
+    w8 = dev_bytes(synth.q80_blocks(rng, 1000, K))
+    say("determinism q80 M=1 and M=8")
+    for xx in (x, x6):
+        a, b = host(qdm.q80_gemv(w8, xx, 1000, K)), host(qdm.q80_gemv(w8, xx, 1000, K))
+        assert np.array_equal(a, b)
     w5 = dev_bytes(synth.q5k_blocks(rng, 1000, K))
     say("determinism q5k M=8")
     a, b = host(qdm.q5k_gemv(w5, x6, 1000, K)), host(qdm.q5k_gemv(w5, x6, 1000, K))
