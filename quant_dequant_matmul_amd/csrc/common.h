@@ -56,6 +56,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Sum over aligned groups of N = 2, 4 or 8 lanes, in every lane, with DPP
+// lane swaps (no LDS permute): neighbours, then pairs within a quad, then the
+// mirrored half row (lane i with 7 - i, which holds the other quad's sum).
+// Each step adds a lane's value and its partner's, as the xor butterfly
+// does, so the bits equal those of s += __shfl_xor(s, 1), (s, 2), (s, 4).
+// Every lane of the wave must be active.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8, "groups of 2, 4 or 8 lanes");
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 // Sum over the 64 lanes of a wave (result valid in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

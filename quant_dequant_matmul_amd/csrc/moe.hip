@@ -160,8 +160,7 @@ __device__ __forceinline__ void stage_rows(SrcRow src_row, int mt, int K, uint8_
         s = (f.x + f.y) + (f.z + f.w);
       }
     }
-#pragma unroll
-    for (int o = 1; o < CH_PER_SUM; o <<= 1) s += __shfl_xor(s, o, WAVE);
+    s = lane_group_sum<CH_PER_SUM>(s);
     if (cidx < nchunk && (cidx % CH_PER_SUM) == 0) lds_sum[cidx / CH_PER_SUM] = s;
   }
 }
@@ -298,8 +297,7 @@ struct RowsDot {
                 r = fmaf(a1, s1, r);
                 r = fmaf(-b1, xs.y, r);
               }
-              r += __shfl_xor(r, 1, WAVE);
-              r += __shfl_xor(r, 2, WAVE);
+              r = lane_group_sum<4>(r);
               if (valid && c == 0) part[m * nblk + b] = r;
             }
           }

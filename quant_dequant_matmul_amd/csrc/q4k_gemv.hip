@@ -66,8 +66,7 @@ __device__ __forceinline__ void stage_x(const void *__restrict__ x, int K, uint3
             bf16_bits_to_float(v.z) + bf16_bits_to_float(v.z >> 16) +
             bf16_bits_to_float(v.w) + bf16_bits_to_float(v.w >> 16);
       }
-      s += __shfl_xor(s, 1, WAVE);
-      s += __shfl_xor(s, 2, WAVE);
+      s = lane_group_sum<4>(s);
       if (c < nchunk && (c & 3) == 0) lds_sum[c >> 2] = s;
     }
   } else {
@@ -81,9 +80,7 @@ __device__ __forceinline__ void stage_x(const void *__restrict__ x, int K, uint3
         ((f32x4 *)lds_x)[c] = v;
         s = (v.x + v.y) + (v.z + v.w);
       }
-      s += __shfl_xor(s, 1, WAVE);
-      s += __shfl_xor(s, 2, WAVE);
-      s += __shfl_xor(s, 4, WAVE);
+      s = lane_group_sum<8>(s);
       if (c < nchunk && (c & 7) == 0) lds_sum[c >> 3] = s;
     }
   }
@@ -300,8 +297,7 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 #pragma unroll
         for (int m = 0; m < MT; m++) {
           float v = contrib[m];
-          v += __shfl_xor(v, 1, WAVE);
-          v += __shfl_xor(v, 2, WAVE);
+          v = lane_group_sum<4>(v);
           if (valid && c == 0) lds_part[m * max_wg_blocks + cb] = v;
         }
         cb += 16;
@@ -424,8 +420,7 @@ struct XStage {
                   bf16_bits_to_float(e.y) + bf16_bits_to_float(e.y >> 16) +
                   bf16_bits_to_float(e.z) + bf16_bits_to_float(e.z >> 16) +
                   bf16_bits_to_float(e.w) + bf16_bits_to_float(e.w >> 16);
-        s += __shfl_xor(s, 1, WAVE);
-        s += __shfl_xor(s, 2, WAVE);
+        s = lane_group_sum<4>(s);
         if (c < nchunk) {
           *(u32x4 *)(xrec + (c >> 5) * DN_XREC + (c & 31) * 16) = p;
           if ((c & 3) == 0) *(float *)(xrec + (c >> 5) * DN_XREC + 512 + 4 * ((c & 31) >> 2)) = s;

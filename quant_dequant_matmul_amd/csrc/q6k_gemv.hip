@@ -53,7 +53,7 @@ __device__ __forceinline__ void q6_stage_x(const void *__restrict__ x, int K, ui
             bf16_bits_to_float(v.z) + bf16_bits_to_float(v.z >> 16) +
             bf16_bits_to_float(v.w) + bf16_bits_to_float(v.w >> 16);
       }
-      s += __shfl_xor(s, 1, WAVE);
+      s = lane_group_sum<2>(s);
       if (c < nchunk && (c & 1) == 0) lds_sum[c >> 1] = s;
     }
   } else {
@@ -67,8 +67,7 @@ __device__ __forceinline__ void q6_stage_x(const void *__restrict__ x, int K, ui
         ((f32x4 *)lds_x)[c] = v;
         s = (v.x + v.y) + (v.z + v.w);
       }
-      s += __shfl_xor(s, 1, WAVE);
-      s += __shfl_xor(s, 2, WAVE);
+      s = lane_group_sum<4>(s);
       if (c < nchunk && (c & 3) == 0) lds_sum[c >> 2] = s;
     }
   }

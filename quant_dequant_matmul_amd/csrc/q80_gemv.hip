@@ -77,9 +77,7 @@ struct Q8XTask {
     else
       f = __builtin_bit_cast(f32x4, v);
     float s = valid ? (f.x + f.y) + (f.z + f.w) : 0.f;
-    s += __shfl_xor(s, 1, WAVE);
-    s += __shfl_xor(s, 2, WAVE);
-    s += __shfl_xor(s, 4, WAVE);
+    s = lane_group_sum<8>(s);
     if (valid) {
       const int m = task / tpt, c4 = task - m * tpt;
       uint8_t *rec = xrec + m * xstr + (c4 >> 5) * Q8_XREC;
