@@ -749,3 +749,55 @@ def test_graph_replay_matches_eager():
         # eager work between replays
         qdm.q4k_gemv(w4, x * 2, N, K, y=y4)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 40])
+def test_graph_replay_decode_layer(T):
+    """A decode layer's call sequence in one captured graph: Q8_0 QKV GEMV,
+    Q4_K and Q5_K GEMVs (min(T, 8) tokens), the router with the MoE behind it
+    (Q5_K down experts; T = 1 runs the decode kernels, T = 40 the matrix-core
+    path), and the Q6_K head. Replayed four times with eager calls and synchronizations in
+    between; every replay equals the eager result bit for bit."""
+    rng = np.random.default_rng(321 + T)
+    K, N = 2048, 1536
+    E, H, F, k = 8, 512, 256, 2
+    w8 = dev_bytes(synth.q80_blocks(rng, N, K))
+    w4 = dev_bytes(synth.q4k_blocks(rng, N, K))
+    w5 = dev_bytes(synth.q5k_blocks(rng, N, K))
+    w6 = dev_bytes(synth.q6k_blocks(rng, N, K))
+    M = min(T, 8)  # the GEMVs take up to 16 tokens
+    x = dev_x(synth.normal_bf16(rng, (M, K)))
+    d = synth.moe(T, E=E, H=H, F=F, top_k=k, seed=T + 7, down_qtype=5)
+    xm, w13, w2 = dev_x(d["x"]), dev_bytes(d["w13"]), dev_bytes(d["w2"])
+    lg = torch.from_numpy(synth.moe_router(T, E=E, seed=T + 70)).to("cuda")
+    ws = torch.zeros(qdm.moe_from_logits_workspace_bytes(T, E, k, H, F), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(4)]
+    ym = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def layer():
+        qdm.q80_gemv(w8, x, N, K, y=outs[0])
+        qdm.q4k_gemv(w4, x, N, K, y=outs[1])
+        qdm.q5k_gemv(w5, x, N, K, y=outs[2])
+        qdm.moe_grouped_gemm_from_logits(xm, lg, w13, w2, k, E, H, F, down_qtype=5, y=ym,
+                                         workspace=ws)
+        qdm.q6k_gemv(w6, x, N, K, y=outs[3])
+
+    say("graph layer: eager reference T", T)
+    layer()
+    ref = [host(o).copy() for o in outs + [ym]]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for rep in range(4):
+        say("graph layer: replay", rep)
+        for o in outs + [ym]:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = [host(o) for o in outs + [ym]]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert np.array_equal(a, b), (rep, i)
+        qdm.moe_grouped_gemm_from_logits(xm, lg * 2, w13, w2, k, E, H, F, down_qtype=5, y=ym,
+                                         workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
