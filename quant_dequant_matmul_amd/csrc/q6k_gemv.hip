@@ -118,6 +118,40 @@ __device__ __forceinline__ Q6Lane q6_load(const uint8_t *__restrict__ w, int64_t
   return L;
 }
 
+// d * scale for the four 16-weight groups gq of lane (h, l0): group gq is
+// sub-block 8h + 2gq + l0/16, byte 2gq + l0/16 of the 8 scale bytes s0|s1.
+__device__ __forceinline__ void q6_dsc(const Q6Lane &L, int l0, float (&dsc)[4]) {
+  const float d = half_bits_to_float(L.dbits);
+  const int sb = l0 >> 4;
+#pragma unroll
+  for (int gq = 0; gq < 4; gq++) {
+    const int bi = 2 * gq + sb;
+    const uint32_t word = bi < 4 ? L.s0 : L.s1;
+    dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+  }
+}
+
+// The 64 codes of lane (h, l0) as bf16 pairs 128 + q (exact: q < 64 fits the
+// 7-bit mantissa at exponent 7): pr[gq][2k + e] for group gq, code dword k,
+// e = 0 -> (l, l+2), 1 -> (l+1, l+3).
+__device__ __forceinline__ void q6_pairs(const Q6Lane &L, uint32_t (&pr)[4][8]) {
+  const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+  const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+  const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint32_t a = qa[k], b = qb[k], hh = qh[k];
+    pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
+    pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
+    pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
+    pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
+    pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
+    pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
+    pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
+    pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
+  }
+}
+
 // One block's contribution for every row m of x: lane (h, l0)'s 64 weights
 // against x staged in LDS, added to acc[m] (4 dot-product groups of 16, each
 // scaled by its sub-block scale).
@@ -125,35 +159,14 @@ template <bool XBF16, int MT>
 __device__ __forceinline__ void q6_block(const Q6Lane &L, const uint32_t *lds_x,
                                          const float *lds_sum, int K, int kb, int h, int l0,
                                          float (&acc)[MT]) {
-  const float d = half_bits_to_float(L.dbits);
-  // scale of group g' (sub-block 8h + 2g' + l0/16): byte (2g' + l0/16)
-  // of the 8 scale bytes s0|s1.
-  const int sb = l0 >> 4;
   float dsc[4];
-#pragma unroll
-  for (int gq = 0; gq < 4; gq++) {
-    const int bi = 2 * gq + sb;
-    const uint32_t word = bi < 4 ? L.s0 : L.s1;
-    dsc[gq] = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
-  }
+  q6_dsc(L, l0, dsc);
   const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
   const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
   const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
   if constexpr (XBF16) {
-    // pairs[gq][2k + e]: group gq, dword k, e = 0 -> (l, l+2), 1 -> (l+1, l+3)
     uint32_t pr[4][8];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const uint32_t a = qa[k], b = qb[k], hh = qh[k];
-      pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
-      pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
-      pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
-      pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
-      pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
-      pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
-      pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
-      pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
-    }
+    q6_pairs(L, pr);
 #pragma unroll
     for (int m = 0; m < MT; m++) {
       float r = acc[m];
@@ -607,10 +620,264 @@ void launch_q6k_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int6
   }
 }
 
+// ---------------------------------------------------------------------------
+// M = 1, bf16 x: dense-span kernel. A workgroup (one per compute unit) owns
+// a balanced range of whole rows whose bytes start on a 16-byte boundary
+// (rows are handed out in units of u = 8 / gcd(K/256, 8), so r0 * K/256 * 210
+// is a multiple of 16). Its waves take spans of 64 consecutive blocks (13440
+// bytes: thirteen 1-KiB loads per lane plus 128 bytes) from a workgroup
+// counter, keep two spans in flight in registers while computing a third from
+// their own LDS buffer, where lane l takes whole block l: four (half, 16-lane
+// offset) quarters, each read as aligned dwords shifted by v_alignbyte, with
+// the same pair arithmetic as the VALU path. x is staged once per workgroup as
+// 592-byte records per 256 columns: 512 bytes of bf16 in (x0, x2, x1, x3)
+// groups, the sixteen 16-column sums, and 16 bytes of padding (a stride of
+// 148 dwords, so consecutive records start 20 banks apart).
+// ---------------------------------------------------------------------------
+constexpr int Q6D_SPAN = 64;                                    // blocks per span
+constexpr int Q6D_SPAN_BYTES = Q6D_SPAN * Q6K_BYTES;            // 13440
+constexpr int Q6D_NCH = (Q6D_SPAN_BYTES + 1023) / 1024;         // 14 loads per lane
+constexpr int Q6D_XREC = 592;
+constexpr int Q6D_WAVES = 4;
+constexpr int Q6D_THREADS = Q6D_WAVES * WAVE;
+constexpr int Q6D_TARGET_WGS = 256;
+constexpr size_t Q6D_LDS_LIMIT = 160 * 1024;
+
+struct Q6Span {
+  u32x4 r[Q6D_NCH];
+};
+
+// x staging: XC 8-element chunks per thread, all loaded before the first
+// weight load and stored after it (storing waits for the x loads only).
+template <int XC>
+struct Q6XStage {
+  u32x4 v[XC];
+
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int K) {
+    const int nchunk = K / 8;
+#pragma unroll
+    for (int i = 0; i < XC; i++)
+      v[i] = ((const u32x4 *)x)[min(i * Q6D_THREADS + (int)threadIdx.x, nchunk - 1)];
+  }
+
+  __device__ __forceinline__ void store(int K, uint8_t *xrec) const {
+    const int nchunk = K / 8;  // 32 chunks per record, 2 per 16-column sum
+#pragma unroll
+    for (int i = 0; i < XC; i++) {
+      if (i * Q6D_THREADS < nchunk) {  // uniform
+        const int c = i * Q6D_THREADS + threadIdx.x;
+        const u32x4 e = v[i];
+        u32x4 p;
+        p.x = (e.x & 0xFFFFu) | (e.y << 16);
+        p.y = (e.x >> 16) | (e.y & 0xFFFF0000u);
+        p.z = (e.z & 0xFFFFu) | (e.w << 16);
+        p.w = (e.z >> 16) | (e.w & 0xFFFF0000u);
+        float s = bf16_bits_to_float(e.x) + bf16_bits_to_float(e.x >> 16) +
+                  bf16_bits_to_float(e.y) + bf16_bits_to_float(e.y >> 16) +
+                  bf16_bits_to_float(e.z) + bf16_bits_to_float(e.z >> 16) +
+                  bf16_bits_to_float(e.w) + bf16_bits_to_float(e.w >> 16);
+        s = lane_group_sum<2>(s);
+        if (c < nchunk) {
+          uint8_t *rec = xrec + (c >> 5) * Q6D_XREC;
+          *(u32x4 *)(rec + 16 * (c & 31)) = p;
+          if ((c & 1) == 0) *(float *)(rec + 512 + 4 * ((c & 31) >> 1)) = s;
+        }
+      }
+    }
+  }
+};
+
+// Quarter (h, l0) of a block against its x record xr (bf16 pairs).
+__device__ __forceinline__ float q6_quarter_rec(const Q6Lane &L, const uint8_t *xr, int h,
+                                                int l0) {
+  float dsc[4];
+  q6_dsc(L, l0, dsc);
+  uint32_t pr[4][8];
+  q6_pairs(L, pr);
+  float r = 0.f;
+#pragma unroll
+  for (int gq = 0; gq < 4; gq++) {
+    const int j0 = 128 * h + 32 * gq + l0;  // first column of the group in the record
+    const u32x4 x0 = *(const u32x4 *)(xr + 2 * j0), x1 = *(const u32x4 *)(xr + 2 * j0 + 16);
+    const float xs = *(const float *)(xr + 512 + 4 * (j0 >> 4));
+    float sd = 0.f;
+    sd = dot2_bf16(pr[gq][0], x0.x, sd);
+    sd = dot2_bf16(pr[gq][1], x0.y, sd);
+    sd = dot2_bf16(pr[gq][2], x0.z, sd);
+    sd = dot2_bf16(pr[gq][3], x0.w, sd);
+    sd = dot2_bf16(pr[gq][4], x1.x, sd);
+    sd = dot2_bf16(pr[gq][5], x1.y, sd);
+    sd = dot2_bf16(pr[gq][6], x1.z, sd);
+    sd = dot2_bf16(pr[gq][7], x1.w, sd);
+    r = fmaf(dsc[gq], fmaf(-160.f, xs, sd), r);
+  }
+  return r;
+}
+
+// floor(v / d) for 0 <= v < 2^16, 2 <= d < 2^16, magic = ceil(2^32 / d)
+// (d = 1 has no 32-bit magic; callers handle it).
+__device__ __forceinline__ int q6_div(int v, uint32_t magic) {
+  return (int)__umulhi((uint32_t)v, magic);
+}
+
+template <int XC>
+__global__ __launch_bounds__(Q6D_THREADS) void q6k_gemv_m1_kernel(
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int K,
+    int unit, int units_q, int units_rem, int N, uint32_t nb_magic) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int next_span;
+  const int nb = K / QK;
+  uint8_t *spanbuf = smem;                                    // [waves][span bytes]
+  uint8_t *xrec = smem + Q6D_WAVES * Q6D_SPAN_BYTES;          // [nb][592]
+  float *part = (float *)(xrec + nb * Q6D_XREC);              // [blocks of this workgroup]
+
+  const int bid = blockIdx.x;
+  const int r0 = unit * (bid * units_q + min(bid, units_rem));
+  const int r1 = min(N, r0 + unit * (units_q + (bid < units_rem ? 1 : 0)));
+  const int nblk = (r1 - r0) * nb;
+  const int nspan = (nblk + Q6D_SPAN - 1) / Q6D_SPAN;
+  const uint8_t *wbase = w + (int64_t)r0 * nb * Q6K_BYTES;   // 16-byte aligned
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Span si past the end reloads the last span; a chunk past the end of a
+  // partial span re-reads its last 16 bytes (every span size is a multiple of
+  // 16 bytes). Loads are unconditional so the waits count exactly.
+  auto issue = [&](Q6Span &sp, int sidx) {
+    const int si = __builtin_amdgcn_readfirstlane(min(sidx, nspan - 1));
+    const int nbytes = min(Q6D_SPAN, nblk - Q6D_SPAN * si) * Q6K_BYTES;
+    const uint8_t *base = wbase + (int64_t)si * Q6D_SPAN_BYTES;
+#pragma unroll
+    for (int j = 0; j < Q6D_NCH; j++) {
+      const int off = min(1024 * j + 16 * lane, nbytes - 16);
+      sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
+    }
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_span, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+
+  Q6XStage<XC> xst;
+  xst.load(x, K);
+  if (threadIdx.x == 0) next_span = 2 * Q6D_WAVES;
+  int sidx[2] = {wave, Q6D_WAVES + wave};
+  Q6Span R[2];
+  issue(R[0], sidx[0]);
+  xst.store(K, xrec);
+  issue(R[1], sidx[1]);
+  __syncthreads();
+
+  uint8_t *mybuf = spanbuf + wave * Q6D_SPAN_BYTES;
+  while (sidx[0] < nspan || sidx[1] < nspan) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int cur = sidx[p];
+      const int nbytes = cur < nspan ? min(Q6D_SPAN, nblk - Q6D_SPAN * cur) * Q6K_BYTES : 0;
+#pragma unroll
+      for (int j = 0; j < Q6D_NCH; j++) {
+        const int off = 1024 * j + 16 * lane;
+        if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
+      }
+      // refill this slot right away: two spans stay in flight during the math
+      const int nxt = cur < nspan ? grab() : nspan;
+      issue(R[p], nxt);
+      sidx[p] = nxt;
+      const int b = Q6D_SPAN * cur + lane;
+      if (cur < nspan && b < nblk) {
+        const int kb = nb == 1 ? 0 : b - q6_div(b, nb_magic) * nb;
+        const uint8_t *xr = xrec + kb * Q6D_XREC;
+        const int off = Q6K_BYTES * lane;
+        float r = 0.f;
+#pragma unroll
+        for (int qd = 0; qd < 4; qd++) {
+          const int h = qd >> 1, l0 = 16 * (qd & 1);
+          r += q6_quarter_rec(q6_load(mybuf, off, h, l0), xr, h, l0);
+        }
+        part[b] = r;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nrows = r1 - r0;
+  for (int t = threadIdx.x; t < nrows; t += Q6D_THREADS) {
+    const float *pp = part + t * nb;
+    float sacc = 0.f;
+    for (int k = 0; k < nb; k++) sacc += pp[k];
+    y[r0 + t] = sacc;
+  }
+}
+
+// Launch geometry of the dense kernel, or false if it does not apply: rows
+// whose bytes start 16-byte aligned need N * K/256 to be a multiple of 8, and
+// the spans, x records and one float per block of a workgroup must fit LDS.
+bool q6_dense_plan(int64_t N, int64_t K, int &unit, int &units_q, int &units_rem,
+                   int64_t &nwg, size_t &lds) {
+  const int64_t nb = K / QK;
+  int g = 8;
+  while (nb % g) g >>= 1;  // gcd(nb, 8)
+  unit = 8 / g;
+  if (N % unit || N > INT32_MAX) return false;
+  const int64_t units = N / unit;
+  const size_t fixed = (size_t)Q6D_WAVES * Q6D_SPAN_BYTES + (size_t)nb * Q6D_XREC;
+  if (fixed + (size_t)unit * nb * 4 * 2 > Q6D_LDS_LIMIT) return false;
+  const int64_t cap_units = (int64_t)((Q6D_LDS_LIMIT - fixed) / ((size_t)unit * nb * 4)) - 1;
+  nwg = Q6D_TARGET_WGS;
+  const int64_t need = (units + cap_units - 1) / cap_units;
+  if (need > nwg) nwg = need;
+  if (nwg > units) nwg = units;
+  units_q = (int)(units / nwg);
+  units_rem = (int)(units % nwg);
+  const int64_t max_blocks = (int64_t)(units_q + (units_rem ? 1 : 0)) * unit * nb;
+  lds = fixed + (size_t)max_blocks * 4;
+  return lds <= Q6D_LDS_LIMIT && max_blocks < 65536 && K / 8 <= 32 * Q6D_THREADS;
+}
+
+template <int XC>
+void q6_launch_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, int unit,
+                     int units_q, int units_rem, int64_t nwg, size_t lds, hipStream_t s) {
+  auto kern = q6k_gemv_m1_kernel<XC>;
+  (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+  const uint32_t nb = (uint32_t)(K / QK);
+  const uint32_t magic = nb > 1 ? (uint32_t)((((uint64_t)1 << 32) + nb - 1) / nb) : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(Q6D_THREADS), lds, s, (const uint8_t *)w,
+                     (const uint16_t *)x, y, (int)K, unit, units_q, units_rem, (int)N, magic);
+}
+
+// The dense kernel for M = 1 with bf16 x, or false if its plan does not fit.
+bool q6_try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, hipStream_t s) {
+  int unit, units_q, units_rem;
+  int64_t nwg;
+  size_t lds;
+  if (!q6_dense_plan(N, K, unit, units_q, units_rem, nwg, lds)) return false;
+  const int64_t xc = (K / 8 + Q6D_THREADS - 1) / Q6D_THREADS;
+  if (xc <= 4)
+    q6_launch_dense<4>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
+  else if (xc <= 8)
+    q6_launch_dense<8>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
+  else if (xc <= 16)
+    q6_launch_dense<16>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
+  else
+    q6_launch_dense<32>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
+  return true;
+}
+
 }  // namespace
 
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
+  // M = 1, bf16 x: the dense-span kernel when the VALU kernel would have fewer
+  // than 8 row groups per compute unit (it hands out whole row groups, so few
+  // of them leave some units with twice the work: 320 for the down shape K =
+  // 17408, N = 5120, 35.6 -> 29.7 us); with many row groups (the output head,
+  // 9496) the VALU kernel is balanced and faster (151 against 170 us).
+  if (M == 1 && x_bf16 && ((uintptr_t)w & 15) == 0) {
+    const int64_t rows_rg = (256 / WAVE) * (16 / gcd16((int)(K / QK)));
+    if ((N + rows_rg - 1) / rows_rg < 8 * 256 && q6_try_dense(w, x, y, N, K, s)) return;
+  }
   if (x_bf16 && M >= QDM_Q6_MFMA_MIN_M) {
     launch_q6k_mfma(w, (const uint16_t *)x, y, M, N, K, s);
     return;

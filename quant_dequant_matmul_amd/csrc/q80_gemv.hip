@@ -163,7 +163,8 @@ __device__ __forceinline__ void q8_quad(const uint8_t *q, const uint8_t *xr, int
 // bytes of "virtual" span space, segment r holding row r0 + r's chunk; a span
 // crosses at most one segment boundary (segb >= span bytes, or the segments
 // are whole, consecutive rows).
-// floor(v / d) for 0 <= v < 2^16 and 1 <= d < 2^16 with magic = ceil(2^32 / d):
+// floor(v / d) for 0 <= v < 2^16 and 2 <= d < 2^16 with magic = ceil(2^32 / d)
+// (here d = K/128 quads per row is at least 2):
 // the error of magic * v / 2^32 against v / d is below v / 2^32 < 1 / d.
 __device__ __forceinline__ int q8_div(int v, uint32_t magic) {
   return (int)__umulhi((uint32_t)v, magic);

@@ -297,6 +297,39 @@ def test_q6k_gemv_longest_k_bf16(M):
     assert e <= q6k_bf16_tol(M)
 
 
+# M = 1 with bf16 x takes the dense-span kernel when N * K/256 is a multiple of
+# 8 and its LDS plan fits: fewer workgroups than compute units (N = 16), row
+# counts that leave partial spans, 2-, 4- and 8-row units, and long rows.
+Q6_DENSE = [(16, 256), (512, 768), (4096, 5120), (1000, 17408), (136, 1280), (2048, 22528),
+            (258, 4096)]
+
+
+@pytest.mark.parametrize("N,K", Q6_DENSE)
+def test_q6k_gemv_dense_m1(N, K):
+    say("q6k_gemv dense M=1", N, K)
+    rng = np.random.default_rng(N + K + 66)
+    w = synth.q6k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (1, K))
+    y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, oracle.q6k_matmul(w, x, N, K))
+    assert e <= min(TOL_BF16, GUARD_VALU), e
+
+
+def test_q6k_gemv_dense_one_hot_bf16_bit_exact():
+    """x = e_k in bf16 on the dense path: every product and sum is exact, so
+    y[n] = W[n, k] bit for bit (each quarter and group of a block)."""
+    N, K = 512, 1280
+    w = synth.q6k_blocks(np.random.default_rng(14), N, K)
+    W = oracle.q6k_dequantize(w, N, K)
+    wd = dev_bytes(w)
+    for k in [0, 1, 2, 3, 15, 16, 17, 31, 32, 63, 64, 127, 128, 129, 191, 255, 256, 640, 1279]:
+        say("q6k dense one-hot k", k)
+        x = np.zeros((1, K), dtype=np.uint16)
+        x[0, k] = 0x3F80  # bf16 1.0
+        y = host(qdm.q6k_gemv(wd, dev_x(x), N, K))[0]
+        assert np.array_equal(y, W[:, k]), k
+
+
 def test_q6k_gemv_one_hot_rows_bit_exact():
     N, K = 100, 768
     w = synth.q6k_blocks(np.random.default_rng(4), N, K)
