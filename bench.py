@@ -432,7 +432,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,q80,moe,router,cpu",
+    ap.add_argument("--sections", default="probe,decode,graph,gemm,q6k,q5k,q80,gemv_m8,moe,router,cpu",
                     help="comma list of: probe, decode, graph, gemm, q6k, q5k, moe, cpu "
                          "(decode always runs: it is the headline)")
     args = ap.parse_args()
@@ -473,6 +473,13 @@ def main():
             key = "q5k_down_m%d" % M
             extra[key] = bench_q5k(torch, qdm, synth, oracle, M, reps)
             log(key, extra[key])
+    if "gemv_m8" in sections:
+        k, n = 5120, 34816
+        w4 = synth.q4k_blocks(np.random.default_rng(8), n, k)
+        x8 = synth.normal_bf16(np.random.default_rng(9), (8, k))
+        extra["q4k_gate_up_m8"] = bench_kgemv(torch, qdm.q4k_gemv, oracle.q4k_matmul, w4, x8, 8,
+                                              n, k, Q4K_BPB, 50)
+        log("q4k_gate_up_m8", extra["q4k_gate_up_m8"])
     if "q80" in sections:
         for M, reps in ((1, 50), (8, 50)):
             key = "q80_qkv_m%d" % M

@@ -104,8 +104,9 @@ int q80_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream
  * for 1 <= M <= 16. x_dtype is QDM_F32 or QDM_BF16. Accumulation is fp32.
  * N >= 1, K >= 256, K % 256 == 0, K <= 65536 (bf16 x) or K <= 32768 (fp32 x):
  * one activation row is staged in the 160 KiB LDS of a compute unit.
- * q6k_gemv with bf16 x and M >= 2 runs on the matrix cores: each weight is
- * decoded in fp32 (exact) and rounded to bf16 (nearest even) before the
+ * q4k_gemv, q5k_gemv and q6k_gemv with bf16 x and M >= 2 run on the matrix
+ * cores: each weight is decoded in fp32 (exact, or the single rounding of
+ * d*sc*q - dmin*m) and rounded to bf16 (nearest even) before the
  * bf16 x bf16 -> fp32 contraction, as in q4k_gemm. Every other case keeps the
  * weights in fp32. Results are deterministic.
  */

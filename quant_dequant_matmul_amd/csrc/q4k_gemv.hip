@@ -717,16 +717,27 @@ bool try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, hip
   return true;
 }
 
+// With bf16 x and M >= 2 the matrix-core GEMV (weights rounded to bf16 once,
+// every x row on the matrix cores): the general kernel spends M dot products
+// per weight and at M = 8 took 182 us for the gate+up shape.
 void launch_q4k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
   if (M == 1 && x_bf16 && try_dense<false>(w, x, y, N, K, s)) return;
+  if (M >= 2 && x_bf16 && ((uintptr_t)w & 15) == 0) {
+    launch_q4k_mfma_gemv(w, (const uint16_t *)x, y, M, N, K, false, s);
+    return;
+  }
   launch_general<false>(w, x, x_bf16, y, M, N, K, s);
 }
 
-// Q5_K: the same choice between the dense-span and the general kernel.
+// Q5_K: the same choice between the dense-span, matrix-core and general kernels.
 void launch_q5k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
   if (M == 1 && x_bf16 && try_dense<true>(w, x, y, N, K, s)) return;
+  if (M >= 2 && x_bf16 && ((uintptr_t)w & 15) == 0) {
+    launch_q4k_mfma_gemv(w, (const uint16_t *)x, y, M, N, K, true, s);
+    return;
+  }
   launch_general<true>(w, x, x_bf16, y, M, N, K, s);
 }
 

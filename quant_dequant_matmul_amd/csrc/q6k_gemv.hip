@@ -418,11 +418,119 @@ __device__ __forceinline__ Q6Lane q6_finish(const Q6Raw &R) {
   return L;
 }
 
-template <int THREADS>
-__global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__restrict__ w,
-                                                           const uint16_t *__restrict__ x,
-                                                           float *__restrict__ y, int M, int N,
-                                                           int K, int xs) {
+// Format policies of the matrix-core GEMV. Lane group s = lane / 16 owns a
+// 64-weight slice of every super-block; step t = 0..7 of an item gives the
+// lane's A operand, 8 weights decoded to bf16, and the B operand is x at the
+// same 8 positions of the super-block (any order shared by A and B gives the
+// same contraction). Weights are exact in fp32 and rounded to bf16 (nearest
+// even) once.
+//
+// Q6_K: slice (h, l0) = (s / 2, 16 (s % 2)); step t = 2g + e covers positions
+// 128h + 32g + l0 + 8e + j, group g's scale.
+struct MfQ6 {
+  static constexpr int BYTES = Q6K_BYTES;
+  typedef Q6Raw Raw;
+  __device__ static Raw load(const uint8_t *__restrict__ w, int64_t blk_off, int s) {
+    return q6_load_raw(w, blk_off, s >> 1, 16 * (s & 1));
+  }
+  __device__ static void mfma(const Raw &R, int s, const uint16_t *xk, f32x4 (&acc2)[2]) {
+    const int h = s >> 1, l0 = 16 * (s & 1);
+    const Q6Lane L = q6_finish(R);
+    const float d = half_bits_to_float(L.dbits);
+    const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
+    const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+    const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+    const uint16_t *xs = xk + 128 * h + l0;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      // scale of sub-block 8h + 2g + l0/16: byte 2g + l0/16 of s0|s1
+      const int bi = 2 * g + (l0 >> 4);
+      const uint32_t word = bi < 4 ? L.s0 : L.s1;
+      const float ds = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
+      const float nds = -32.f * ds;
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++) {
+          const int k = 2 * e + k2;
+          const uint32_t c4 = q6m_codes((g & 1) ? qb[k] : qa[k], qh[k], g);
+          pk[2 * k2] = pack_bf16(fmaf((float)(c4 & 255u), ds, nds),
+                                 fmaf((float)((c4 >> 8) & 255u), ds, nds));
+          pk[2 * k2 + 1] = pack_bf16(fmaf((float)((c4 >> 16) & 255u), ds, nds),
+                                     fmaf((float)(c4 >> 24), ds, nds));
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const bf16x8 bv = *(const bf16x8 *)(xs + 32 * g + 8 * e);
+        acc2[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc2[e], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// Q4_K / Q5_K (Q5): slice s is code chunk s, i.e. sub-blocks 2s (low nibbles)
+// and 2s + 1 (high nibbles); step t covers positions 64s + 8t + j, sub-block
+// 2s + t / 4. w = q * (d sc) - dmin m with one rounding (fma: the product is
+// exact). Q5_K adds bit 2s (or 2s + 1) of high-plane byte l as bit 4 of q.
+template <bool Q5>
+struct MfQ4 {
+  static constexpr int BYTES = Q5 ? Q5K_BYTES : Q4K_BYTES;
+  static constexpr int QOFF = Q5 ? 48 : 16;
+  struct Raw {
+    u32x4 hdr, qa, qb;
+    u32x4 ha[Q5 ? 1 : 0], hb[Q5 ? 1 : 0];
+  };
+  __device__ static Raw load(const uint8_t *__restrict__ w, int64_t blk_off, int s) {
+    Raw R;
+    const uint8_t *b = w + blk_off;  // 16-byte aligned
+    R.hdr = *(const u32x4 *)b;
+    R.qa = *(const u32x4 *)(b + QOFF + 32 * s);
+    R.qb = *(const u32x4 *)(b + QOFF + 32 * s + 16);
+    if constexpr (Q5) {
+      R.ha[0] = *(const u32x4 *)(b + 16);
+      R.hb[0] = *(const u32x4 *)(b + 32);
+    }
+    return R;
+  }
+  __device__ static void mfma(const Raw &R, int s, const uint16_t *xk, f32x4 (&acc2)[2]) {
+    const float d = half_bits_to_float(R.hdr.x), dmin = half_bits_to_float(R.hdr.x >> 16);
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(R.hdr.y, R.hdr.z, R.hdr.w, 2 * s, sc0, m0);
+    q4k_scale_min(R.hdr.y, R.hdr.z, R.hdr.w, 2 * s + 1, sc1, m1);
+    const float a0 = d * (float)sc0, nb0 = -(dmin * (float)m0);  // exact products
+    const float a1 = d * (float)sc1, nb1 = -(dmin * (float)m1);
+    const uint32_t q[8] = {R.qa.x, R.qa.y, R.qa.z, R.qa.w, R.qb.x, R.qb.y, R.qb.z, R.qb.w};
+    const uint16_t *xs = xk + 64 * s;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const bool hi = t >= 4;
+      const float a = hi ? a1 : a0, nb = hi ? nb1 : nb0;
+      uint32_t pk[4];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int k = 2 * (t & 3) + u;  // code dword: weights 4k .. 4k+3 of the sub-block
+        uint32_t c = (hi ? q[k] >> 4 : q[k]) & 0x0F0F0F0Fu;
+        if constexpr (Q5) {
+          const uint32_t hp[8] = {R.ha[0].x, R.ha[0].y, R.ha[0].z, R.ha[0].w,
+                                  R.hb[0].x, R.hb[0].y, R.hb[0].z, R.hb[0].w};
+          c |= ((hp[k] >> (2 * s + (hi ? 1 : 0))) << 4) & 0x10101010u;
+        }
+        pk[2 * u] = pack_bf16(fmaf((float)(c & 255u), a, nb), fmaf((float)((c >> 8) & 255u), a, nb));
+        pk[2 * u + 1] = pack_bf16(fmaf((float)((c >> 16) & 255u), a, nb),
+                                  fmaf((float)(c >> 24), a, nb));
+      }
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      const bf16x8 bv = *(const bf16x8 *)(xs + 8 * t);
+      acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc2[t & 1], 0, 0, 0);
+    }
+  }
+};
+
+template <int THREADS, class Fmt>
+__global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restrict__ w,
+                                                          const uint16_t *__restrict__ x,
+                                                          float *__restrict__ y, int M, int N,
+                                                          int K, int xs) {
   constexpr int WAVES = THREADS / WAVE;
   extern __shared__ __attribute__((aligned(16))) uint8_t q6m_smem[];
   f32x4 *part = (f32x4 *)q6m_smem;                                   // [WAVES][64]
@@ -439,14 +547,13 @@ __global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__rest
   auto start_of = [&](int v) { return (int)((int64_t)items * v / WAVES); };
   const int i0 = start_of(wave), i1 = start_of(wave + 1);
   const int s = lane >> 4, r = lane & 15;
-  const int h = s >> 1, l0 = 16 * (s & 1);
 
   if (tid < WAVES) flag[tid] = 0;
   auto load = [&](int i) {
     const int ic = max(min(i, i1 - 1), 0);  // past the range: a valid dummy
     const int tl = ic / nb;
     const int row = min((t0 + tl) * 16 + r, N - 1);
-    return q6_load_raw(w, ((int64_t)row * nb + (ic - tl * nb)) * Q6K_BYTES, h, l0);
+    return Fmt::load(w, ((int64_t)row * nb + (ic - tl * nb)) * Fmt::BYTES, s);
   };
   // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
   // apart), eight 16-byte loads in flight per thread; the first batch of x
@@ -471,7 +578,7 @@ __global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__rest
     }
   };
   x_load(0);
-  Q6Raw buf[Q6M_PF];
+  typename Fmt::Raw buf[Q6M_PF];
 #pragma unroll
   for (int p = 0; p < Q6M_PF; p++) buf[p] = load(i0 + p);
   x_store(0);
@@ -481,44 +588,14 @@ __global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__rest
   }
   __syncthreads();
 
-  const uint16_t *xb = xl + min(r, M - 1) * xs + 128 * h + l0;
+  const uint16_t *xb = xl + min(r, M - 1) * xs;
   // two accumulators (steps e = 0 and e = 1) halve the MFMA dependency chain
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // one item: decode the slice, 8 MFMAs; at the end of this wave's portion of
   // a tile, publish it or complete and store the tile
-  auto item = [&](int ii, Q6Raw &slot, bool reload) {
-    const Q6Lane L = q6_finish(slot);
+  auto item = [&](int ii, typename Fmt::Raw &slot, bool reload) {
     const int tl = ii / nb, b = ii - tl * nb;
-
-    const float d = half_bits_to_float(L.dbits);
-    const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
-    const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-    const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
-    const uint16_t *xk = xb + b * QK;
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      // scale of sub-block 8h + 2g + l0/16: byte 2g + l0/16 of s0|s1
-      const int bi = 2 * g + (l0 >> 4);
-      const uint32_t word = bi < 4 ? L.s0 : L.s1;
-      const float ds = d * (float)(int8_t)(uint8_t)(word >> (8 * (bi & 3)));
-      const float nds = -32.f * ds;
-#pragma unroll
-      for (int e = 0; e < 2; e++) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++) {
-          const int k = 2 * e + k2;
-          const uint32_t c4 = q6m_codes((g & 1) ? qb[k] : qa[k], qh[k], g);
-          pk[2 * k2] = pack_bf16(fmaf((float)(c4 & 255u), ds, nds),
-                                 fmaf((float)((c4 >> 8) & 255u), ds, nds));
-          pk[2 * k2 + 1] = pack_bf16(fmaf((float)((c4 >> 16) & 255u), ds, nds),
-                                     fmaf((float)(c4 >> 24), ds, nds));
-        }
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-        const bf16x8 bv = *(const bf16x8 *)(xk + 32 * g + 8 * e);
-        acc2[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc2[e], 0, 0, 0);
-      }
-    }
+    Fmt::mfma(slot, s, xb + b * QK, acc2);
     if (reload) slot = load(ii + Q6M_PF);
 
     if (b == nb - 1 || ii == i1 - 1) {  // end of this wave's portion of a tile
@@ -571,13 +648,13 @@ __global__ __launch_bounds__(THREADS) void q6k_mfma_kernel(const uint8_t *__rest
     if (i + p < i1) item(i + p, buf[p], false);
 }
 
-template <int THREADS>
+template <int THREADS, class Fmt>
 void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t N, int64_t K,
                     size_t lds, int per_cu, hipStream_t s) {
   const int64_t tiles = (N + 15) / 16;
   int64_t grid = 256 * per_cu;
   if (grid > tiles) grid = tiles;  // every workgroup owns at least one tile
-  auto kern = q6k_mfma_kernel<THREADS>;
+  auto kern = kq_mfma_kernel<THREADS, Fmt>;
   (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), lds, s, (const uint8_t *)w, x,
@@ -587,8 +664,9 @@ void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t 
 // Rows of x in chunks whose padded LDS copy fits; each chunk streams all
 // weights. 12 waves per compute unit (3 per SIMD, as many as the registers
 // allow): 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
-void launch_q6k_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
-                     int64_t K, hipStream_t s) {
+template <class Fmt>
+void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                    int64_t K, hipStream_t s) {
   constexpr size_t LDS_CU = 160 * 1024, SLACK = 512;  // SLACK: static LDS, rounding
   const size_t row_bytes = (size_t)(K + 8) * 2;
   const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
@@ -603,18 +681,18 @@ void launch_q6k_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int6
     float *ym = y + m0 * N;
 #if QDM_Q6M_WAVES_CU == 16
     if (4 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 4, s);
+      launch_q6_mfma<256, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 4, s);
     else if (2 * (xb + q6m_head_bytes(8) + SLACK) <= LDS_CU)
-      launch_q6_mfma<512>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(8), 2, s);
+      launch_q6_mfma<512, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(8), 2, s);
     else
-      launch_q6_mfma<1024>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(16), 1, s);
+      launch_q6_mfma<1024, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(16), 1, s);
 #else
     if (3 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 3, s);
+      launch_q6_mfma<256, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 3, s);
     else if (2 * (xb + q6m_head_bytes(6) + SLACK) <= LDS_CU)
-      launch_q6_mfma<384>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(6), 2, s);
+      launch_q6_mfma<384, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(6), 2, s);
     else
-      launch_q6_mfma<768>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(12), 1, s);
+      launch_q6_mfma<768, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(12), 1, s);
 #endif
     m0 += mc;
   }
@@ -867,6 +945,14 @@ bool q6_try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 
 }  // namespace
 
+void launch_q4k_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                          int64_t K, bool q5, hipStream_t s) {
+  if (q5)
+    launch_kq_mfma<MfQ4<true>>(w, x, y, M, N, K, s);
+  else
+    launch_kq_mfma<MfQ4<false>>(w, x, y, M, N, K, s);
+}
+
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
   // M = 1, bf16 x: the dense-span kernel when the VALU kernel would have fewer
@@ -879,7 +965,7 @@ void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
     if ((N + rows_rg - 1) / rows_rg < 8 * 256 && q6_try_dense(w, x, y, N, K, s)) return;
   }
   if (x_bf16 && M >= QDM_Q6_MFMA_MIN_M) {
-    launch_q6k_mfma(w, (const uint16_t *)x, y, M, N, K, s);
+    launch_kq_mfma<MfQ6>(w, (const uint16_t *)x, y, M, N, K, s);
     return;
   }
   const size_t per_row = (size_t)K * (x_bf16 ? 2 : 4) + (size_t)(K / 16) * 4;

@@ -24,6 +24,13 @@ if not torch.cuda.is_available():
 import quant_dequant_matmul_amd as qdm  # noqa: E402
 
 
+def bf16_tol(M):
+    """bf16 x with Q4_K, Q5_K and Q6_K weights: M = 1 runs an fp32-accumulating
+    VALU kernel, far inside the bf16 bar; M >= 2 runs the matrix-core GEMV
+    (weights rounded to bf16), held to the bf16 bar itself."""
+    return min(TOL_BF16, GUARD_VALU) if M == 1 else TOL_BF16
+
+
 # --------------------------------------------------------------------------
 # dequant exports: bit-exact
 # --------------------------------------------------------------------------
@@ -84,7 +91,7 @@ def test_q4k_gemv_ragged(M, N, K, dt):
     y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), N, K))
     ref = oracle.q4k_matmul(w, x, N, K)
     e = rel_err(y, ref)
-    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+    assert e <= (TOL_F32 if dt == "f32" else bf16_tol(M)), e
 
 
 def test_q4k_gemv_longest_k_bf16():
@@ -124,6 +131,44 @@ def test_q4k_gemv_power_of_two_scaling(dt):
     assert np.array_equal(y2, y1 * 8)
 
 
+@pytest.mark.parametrize("qtype", [4, 5])
+def test_mfma_gemv_one_hot_bf16_weights(qtype):
+    """bf16 x, M = 2 (matrix-core GEMV): rows e_k1 and e_k2 give the weights
+    W[:, k] rounded to bf16 (nearest even), bit for bit, for positions in
+    every sub-block, both nibbles and (Q5_K) both high-plane bits."""
+    N, K = 64, 512
+    rng = np.random.default_rng(40 + qtype)
+    gen, deq, gemv = ((synth.q4k_blocks, oracle.q4k_dequantize, qdm.q4k_gemv) if qtype == 4
+                      else (synth.q5k_blocks, oracle.q5k_dequantize, qdm.q5k_gemv))
+    w = gen(rng, N, K)
+    Wb = f32_to_bf16_f32(deq(w, N, K))
+    wd = dev_bytes(w)
+    ks = [0, 7, 8, 31, 32, 33, 63, 64, 100, 127, 128, 191, 192, 255, 256, 300, 383, 447, 448, 511]
+    for i in range(0, len(ks), 2):
+        k1, k2 = ks[i], ks[i + 1]
+        say("mfma one-hot", qtype, k1, k2)
+        x = np.zeros((2, K), dtype=np.uint16)
+        x[0, k1] = x[1, k2] = 0x3F80  # bf16 1.0
+        y = host(gemv(wd, dev_x(x), N, K))
+        assert np.array_equal(y[0], Wb[:, k1]), k1
+        assert np.array_equal(y[1], Wb[:, k2]), k2
+
+
+def test_q4k_gemv_gate_up_m8_sampled():
+    """Q4_K gate+up shape (K=5120, N=34816) at M = 8 with bf16 x: the
+    matrix-core GEMV against the oracle on every 97th row."""
+    K, N, M = 5120, 34816, 8
+    rng = np.random.default_rng(48)
+    w = synth.q4k_blocks(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    say("q4k_gemv gate+up M=8")
+    y = host(qdm.q4k_gemv(dev_bytes(w), dev_x(x), N, K))
+    rows = np.arange(0, N, 97)
+    e = rel_err(y[:, rows], oracle.q4k_matmul(w[rows], x, len(rows), K))
+    say("  rel err", e)
+    assert e <= TOL_BF16
+
+
 # --------------------------------------------------------------------------
 # Q5_K dequant and GEMV
 # --------------------------------------------------------------------------
@@ -151,7 +196,7 @@ def test_q5k_gemv_ragged(M, N, K, dt):
     y = host(qdm.q5k_gemv(dev_bytes(w), dev_x(x), N, K))
     ref = oracle.q5k_matmul(w, x, N, K)
     e = rel_err(y, ref)
-    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+    assert e <= (TOL_F32 if dt == "f32" else bf16_tol(M)), e
 
 
 def test_q5k_gemv_one_hot_rows_bit_exact():
@@ -177,7 +222,7 @@ def test_q5k_gemv_down_full(M):
     y = host(qdm.q5k_gemv(dev_bytes(w), dev_x(x), N, K))
     e = rel_err(y, oracle.q5k_matmul(w, x, N, K))
     say("  rel err", e)
-    assert e <= min(TOL_BF16, GUARD_VALU)
+    assert e <= bf16_tol(M)
 
 
 # --------------------------------------------------------------------------
@@ -272,14 +317,9 @@ def test_q6k_gemv_ragged(M, N, K, dt):
     y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
     ref = oracle.q6k_matmul(w, x, N, K)
     e = rel_err(y, ref)
-    assert e <= (TOL_F32 if dt == "f32" else q6k_bf16_tol(M)), e
+    assert e <= (TOL_F32 if dt == "f32" else bf16_tol(M)), e
 
 
-def q6k_bf16_tol(M):
-    """bf16 x: M = 1 runs the fp32-accumulating VALU kernel, far inside the bf16
-    bar; M >= 2 runs the matrix-core kernel (weights rounded to bf16), held to
-    the bf16 bar itself."""
-    return min(TOL_BF16, GUARD_VALU) if M == 1 else TOL_BF16
 
 
 @pytest.mark.parametrize("M", [1, 3])
@@ -294,7 +334,7 @@ def test_q6k_gemv_longest_k_bf16(M):
     y = host(qdm.q6k_gemv(dev_bytes(w), dev_x(x), N, K))
     e = rel_err(y, oracle.q6k_matmul(w, x, N, K))
     say("  rel err", e)
-    assert e <= q6k_bf16_tol(M)
+    assert e <= bf16_tol(M)
 
 
 # M = 1 with bf16 x takes the dense-span kernel when N * K/256 is a multiple of
@@ -355,7 +395,7 @@ def test_q6k_gemv_head_full_sampled(M):
     ref = oracle.q6k_matmul(w[rows], x, len(rows), K)
     e = rel_err(y[:, rows], ref)
     say("  rel err", e)
-    assert e <= q6k_bf16_tol(M)
+    assert e <= bf16_tol(M)
 
 
 def test_q6k_gemv_down_full():
