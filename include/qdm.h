@@ -120,9 +120,10 @@ int q6k_gemv(const void *w, const void *x, int x_dtype, float *y,
 /*
  * q80_gemv: the same decode-regime matmul with Q8_0 weights (w: [N][K/32]
  * 34-byte blocks, layout as in q80_dequantize). Arguments, limits and status
- * codes as q4k_gemv; x is staged per column chunk, so K up to 65536 holds for
- * fp32 x too within the q4k_gemv limits. Weights are applied in fp32 (exact),
- * accumulation is fp32. Results are deterministic.
+ * codes as q4k_gemv; x is staged per column chunk. With fp32 x, or M = 1,
+ * weights are applied in fp32 (exact); with bf16 x and M >= 2 the call runs
+ * on the matrix cores with the weights rounded to bf16 (nearest even), as
+ * q4k_gemv does. Accumulation is fp32. Results are deterministic.
  */
 int q80_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);

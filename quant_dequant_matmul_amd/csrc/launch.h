@@ -22,6 +22,9 @@ void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
 // Q4_K (or Q5_K when q5) GEMV on the matrix cores, bf16 x, any M >= 1.
 void launch_q4k_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, bool q5, hipStream_t s);
+// Q8_0 GEMV on the matrix cores, bf16 x, any M >= 1 (K % 256 == 0).
+void launch_q80_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                          int64_t K, hipStream_t s);
 bool q80_gemv_fits(int64_t N, int64_t K);
 void launch_q80_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s);

@@ -526,6 +526,65 @@ struct MfQ4 {
   }
 };
 
+// Q8_0: a "super-block" is 8 blocks of 34 bytes (272 B, 256 weights; rows
+// start 16-byte aligned when K % 256 == 0). Lane group s takes blocks 2s and
+// 2s + 1 (68 bytes from a 4-byte aligned offset); step t covers positions
+// 64s + 8t + j, block 2s + t/4, codes 8 (t % 4) .. +7 of it. w = d * q, exact
+// in fp32, then rounded to bf16.
+struct MfQ8 {
+  static constexpr int BYTES = 8 * Q80_BYTES;
+  struct Raw {
+    u32x4 v[4];
+    uint32_t t;
+  };
+  __device__ static Raw load(const uint8_t *__restrict__ w, int64_t blk_off, int s) {
+    typedef uint32_t u32x4_a4l __attribute__((ext_vector_type(4), aligned(4)));
+    Raw R;
+    const uint8_t *b = w + blk_off + 68 * s;
+#pragma unroll
+    for (int i = 0; i < 4; i++) R.v[i] = *(const u32x4_a4l *)(b + 16 * i);
+    R.t = *(const uint32_t *)(b + 64);
+    return R;
+  }
+  __device__ static void mfma(const Raw &R, int s, const uint16_t *xk, f32x4 (&acc2)[2]) {
+    uint32_t D[17];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      D[4 * i] = R.v[i].x;
+      D[4 * i + 1] = R.v[i].y;
+      D[4 * i + 2] = R.v[i].z;
+      D[4 * i + 3] = R.v[i].w;
+    }
+    D[16] = R.t;
+    // block 2s: d in bytes 0-1, codes from byte 2 (2 bytes into a dword);
+    // block 2s + 1: d in bytes 34-35 (dword 8, upper half), codes from byte 36
+    const float d0 = half_bits_to_float(D[0]), d1 = half_bits_to_float(D[8] >> 16);
+    const uint16_t *xs = xk + 64 * s;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const bool hi = t >= 4;
+      const float d = hi ? d1 : d0;
+      uint32_t c[2];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int k = 2 * (t & 3) + u;  // code dword k of the block
+        c[u] = hi ? D[9 + k] : __builtin_amdgcn_alignbyte(D[k + 1], D[k], 2);
+      }
+      uint32_t pk[4];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        pk[2 * u] = pack_bf16(d * (float)(int8_t)(c[u] & 255u),
+                              d * (float)(int8_t)((c[u] >> 8) & 255u));
+        pk[2 * u + 1] = pack_bf16(d * (float)(int8_t)((c[u] >> 16) & 255u),
+                                  d * (float)(int8_t)(c[u] >> 24));
+      }
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      const bf16x8 bv = *(const bf16x8 *)(xs + 8 * t);
+      acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc2[t & 1], 0, 0, 0);
+    }
+  }
+};
+
 template <int THREADS, class Fmt>
 __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restrict__ w,
                                                           const uint16_t *__restrict__ x,
@@ -944,6 +1003,11 @@ bool q6_try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 }
 
 }  // namespace
+
+void launch_q80_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                          int64_t K, hipStream_t s) {
+  launch_kq_mfma<MfQ8>(w, x, y, M, N, K, s);
+}
 
 void launch_q4k_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, bool q5, hipStream_t s) {

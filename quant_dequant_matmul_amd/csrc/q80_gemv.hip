@@ -480,8 +480,14 @@ __global__ __launch_bounds__(256) void q80_dequant_kernel(const uint8_t *__restr
 
 bool q80_gemv_fits(int64_t N, int64_t K) { return q8_nchunks(1, N, K) > 0; }
 
+// bf16 x with M >= 2: the matrix-core GEMV (weights rounded to bf16 once);
+// the kernel here spends M FMAs per code (59.8 us at M = 8 for the QKV shape).
 void launch_q80_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M, int64_t N,
                      int64_t K, hipStream_t s) {
+  if (x_bf16 && M >= 2 && ((uintptr_t)w & 15) == 0) {
+    launch_q80_mfma_gemv(w, (const uint16_t *)x, y, M, N, K, s);
+    return;
+  }
   if (x_bf16)
     q8_gemv<true>(w, x, y, M, N, K, s);
   else

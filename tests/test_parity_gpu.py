@@ -25,7 +25,7 @@ import quant_dequant_matmul_amd as qdm  # noqa: E402
 
 
 def bf16_tol(M):
-    """bf16 x with Q4_K, Q5_K and Q6_K weights: M = 1 runs an fp32-accumulating
+    """bf16 x with Q4_K, Q5_K, Q6_K and Q8_0 weights: M = 1 runs an fp32-accumulating
     VALU kernel, far inside the bf16 bar; M >= 2 runs the matrix-core GEMV
     (weights rounded to bf16), held to the bf16 bar itself."""
     return min(TOL_BF16, GUARD_VALU) if M == 1 else TOL_BF16
@@ -131,15 +131,17 @@ def test_q4k_gemv_power_of_two_scaling(dt):
     assert np.array_equal(y2, y1 * 8)
 
 
-@pytest.mark.parametrize("qtype", [4, 5])
+@pytest.mark.parametrize("qtype", [4, 5, 8])
 def test_mfma_gemv_one_hot_bf16_weights(qtype):
     """bf16 x, M = 2 (matrix-core GEMV): rows e_k1 and e_k2 give the weights
     W[:, k] rounded to bf16 (nearest even), bit for bit, for positions in
-    every sub-block, both nibbles and (Q5_K) both high-plane bits."""
+    every sub-block (Q8_0: every block of a super-block, aligned and
+    realigned code words), both nibbles and (Q5_K) both high-plane bits."""
     N, K = 64, 512
     rng = np.random.default_rng(40 + qtype)
-    gen, deq, gemv = ((synth.q4k_blocks, oracle.q4k_dequantize, qdm.q4k_gemv) if qtype == 4
-                      else (synth.q5k_blocks, oracle.q5k_dequantize, qdm.q5k_gemv))
+    gen, deq, gemv = {4: (synth.q4k_blocks, oracle.q4k_dequantize, qdm.q4k_gemv),
+                      5: (synth.q5k_blocks, oracle.q5k_dequantize, qdm.q5k_gemv),
+                      8: (synth.q80_blocks, oracle.q80_dequantize, qdm.q80_gemv)}[qtype]
     w = gen(rng, N, K)
     Wb = f32_to_bf16_f32(deq(w, N, K))
     wd = dev_bytes(w)
@@ -256,7 +258,7 @@ def test_q80_gemv_ragged(M, N, K, dt):
     y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
     ref = oracle.q80_matmul(w, x, N, K)
     e = rel_err(y, ref)
-    assert e <= (TOL_F32 if dt == "f32" else min(TOL_BF16, GUARD_VALU)), e
+    assert e <= (TOL_F32 if dt == "f32" else bf16_tol(M)), e
 
 
 def test_q80_gemv_longest_k_bf16():
@@ -268,7 +270,7 @@ def test_q80_gemv_longest_k_bf16():
     say("q80_gemv longest K", M, N, K)
     y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
     e = rel_err(y, oracle.q80_matmul(w, x, N, K))
-    assert e <= min(TOL_BF16, GUARD_VALU), e
+    assert e <= bf16_tol(M), e
 
 
 def test_q80_gemv_one_hot_rows_bit_exact():
@@ -295,7 +297,7 @@ def test_q80_gemv_qkv_full(M):
     y = host(qdm.q80_gemv(dev_bytes(w), dev_x(x), N, K))
     e = rel_err(y, oracle.q80_matmul(w, x, N, K))
     say("  rel err", e)
-    assert e <= min(TOL_BF16, GUARD_VALU)
+    assert e <= bf16_tol(M)
 
 
 # --------------------------------------------------------------------------
