@@ -585,11 +585,15 @@ struct MfQ8 {
   }
 };
 
+// One launch covers the K columns [256 kb0, 256 kb0 + K) of rows that are
+// ldk columns long (x rows too: x points at column 256 kb0 of row 0); with
+// accumulate set it adds its sums to y (column chunks of a long K).
 template <int THREADS, class Fmt>
 __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restrict__ w,
                                                           const uint16_t *__restrict__ x,
                                                           float *__restrict__ y, int M, int N,
-                                                          int K, int xs) {
+                                                          int K, int xs, int ldk, int kb0,
+                                                          int accumulate) {
   constexpr int WAVES = THREADS / WAVE;
   extern __shared__ __attribute__((aligned(16))) uint8_t q6m_smem[];
   f32x4 *part = (f32x4 *)q6m_smem;                                   // [WAVES][64]
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
   uint16_t *xl = (uint16_t *)(q6m_smem + q6m_head_bytes(WAVES));    // [M][xs] bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform ranges
-  const int nb = K / QK;
+  const int nb = K / QK, nbt = ldk / QK;
   const int tiles = (N + 15) / 16;
   const int tq = tiles / (int)gridDim.x, tr = tiles % (int)gridDim.x;
   const int bid = blockIdx.x;
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     const int ic = max(min(i, i1 - 1), 0);  // past the range: a valid dummy
     const int tl = ic / nb;
     const int row = min((t0 + tl) * 16 + r, N - 1);
-    return Fmt::load(w, ((int64_t)row * nb + (ic - tl * nb)) * Fmt::BYTES, s);
+    return Fmt::load(w, ((int64_t)row * nbt + kb0 + (ic - tl * nb)) * Fmt::BYTES, s);
   };
   // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
   // apart), eight 16-byte loads in flight per thread; the first batch of x
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     for (int j = 0; j < 8; j++) {
       const int c = min(base + j * THREADS + tid, total - 1);
       const int m = c / cpr;
-      xv[j] = *(const u32x4 *)(x + (int64_t)m * K + 8 * (c - m * cpr));
+      xv[j] = *(const u32x4 *)(x + (int64_t)m * ldk + 8 * (c - m * cpr));
     }
   };
   auto x_store = [&](int base) {
@@ -687,7 +691,10 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
 #pragma unroll
           for (int q = 0; q < 4; q++) {
             const int n = (t0 + tl) * 16 + 4 * s + q;
-            if (n < N) y[(int64_t)m * N + n] = acc[q];
+            if (n < N) {
+              float *yo = y + (int64_t)m * N + n;
+              *yo = accumulate ? *yo + acc[q] : acc[q];
+            }
           }
         }
       }
@@ -709,7 +716,8 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
 
 template <int THREADS, class Fmt>
 void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t N, int64_t K,
-                    size_t lds, int per_cu, hipStream_t s) {
+                    int64_t ldk, int64_t kb0, bool accumulate, size_t lds, int per_cu,
+                    hipStream_t s) {
   const int64_t tiles = (N + 15) / 16;
   int64_t grid = 256 * per_cu;
   if (grid > tiles) grid = tiles;  // every workgroup owns at least one tile
@@ -717,7 +725,7 @@ void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t 
   (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), lds, s, (const uint8_t *)w, x,
-                     y, mc, (int)N, (int)K, (int)(K + 8));
+                     y, mc, (int)N, (int)K, (int)(K + 8), (int)ldk, (int)kb0, accumulate ? 1 : 0);
 }
 
 // Rows of x in chunks whose padded LDS copy fits; each chunk streams all
@@ -726,34 +734,40 @@ void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t 
 template <class Fmt>
 void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
                     int64_t K, hipStream_t s) {
+  // All M rows of x in every launch; when their padded LDS copy would not fit,
+  // K is split into equal chunks of whole super-blocks, each launch streaming
+  // only its columns of the weights and adding into y after the first (the
+  // weights are read once; splitting M instead would read them per split).
+  // 12 waves per compute unit (3 per SIMD, as many as the registers allow):
+  // 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
   constexpr size_t LDS_CU = 160 * 1024, SLACK = 512;  // SLACK: static LDS, rounding
-  const size_t row_bytes = (size_t)(K + 8) * 2;
   const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
-  const int64_t cap = (int64_t)(x_cap / row_bytes);  // >= 2 for K <= 65536
-  const int64_t chunks = (M + cap - 1) / cap;
-  const int64_t base = M / chunks, extra = M % chunks;
-  int64_t m0 = 0;
-  for (int64_t c = 0; c < chunks; c++) {
-    const int mc = (int)(base + (c < extra ? 1 : 0));
-    const size_t xb = (size_t)mc * row_bytes;
-    const uint16_t *xm = x + m0 * K;
-    float *ym = y + m0 * N;
+  const int64_t units = K / QK;
+  int64_t nch = 1;
+  while ((size_t)M * ((units + nch - 1) / nch * QK + 8) * 2 > x_cap) nch++;
+  int64_t kb0 = 0;
+  for (int64_t c = 0; c < nch; c++) {
+    const int64_t kc = (units / nch + (c < units % nch ? 1 : 0)) * QK;
+    const size_t xb = (size_t)M * (kc + 8) * 2;
+    const uint16_t *xm = x + kb0 * QK;
+    const int mc = (int)M;
+    const bool acc = c > 0;
 #if QDM_Q6M_WAVES_CU == 16
     if (4 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 4, s);
+      launch_q6_mfma<256, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(4), 4, s);
     else if (2 * (xb + q6m_head_bytes(8) + SLACK) <= LDS_CU)
-      launch_q6_mfma<512, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(8), 2, s);
+      launch_q6_mfma<512, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(8), 2, s);
     else
-      launch_q6_mfma<1024, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(16), 1, s);
+      launch_q6_mfma<1024, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(16), 1, s);
 #else
     if (3 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(4), 3, s);
+      launch_q6_mfma<256, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(4), 3, s);
     else if (2 * (xb + q6m_head_bytes(6) + SLACK) <= LDS_CU)
-      launch_q6_mfma<384, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(6), 2, s);
+      launch_q6_mfma<384, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(6), 2, s);
     else
-      launch_q6_mfma<768, Fmt>(w, xm, ym, mc, N, K, xb + q6m_head_bytes(12), 1, s);
+      launch_q6_mfma<768, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(12), 1, s);
 #endif
-    m0 += mc;
+    kb0 += kc / QK;
   }
 }
 
