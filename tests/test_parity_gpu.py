@@ -301,6 +301,42 @@ def test_q80_gemv_qkv_full(M):
 
 
 # --------------------------------------------------------------------------
+# Random shapes across the GEMV paths of every format
+# --------------------------------------------------------------------------
+
+def _random_gemv_cases(n_cases=10, seed=2024):
+    """Seeded (qtype, M, N, K, dtype) draws: M in 1..16, N in 1..3000, K a
+    multiple of 256 up to 24576 (dense, matrix-core with and without K
+    chunks, and VALU paths all occur)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for qtype in (4, 5, 6, 8):
+        for i in range(n_cases):
+            M = int(rng.choice([1, 1, 2, 3, 5, 8, 16]))
+            N = int(rng.integers(1, 3001))
+            K = 256 * int(rng.choice([1, 2, 3, 5, 9, 20, 33, 68, 96]))
+            dt = "bf16" if i % 3 else "f32"
+            cases.append((qtype, M, N, K, dt))
+    return cases
+
+
+_GEMV = {4: ("q4k_blocks", "q4k_matmul", "q4k_gemv"), 5: ("q5k_blocks", "q5k_matmul", "q5k_gemv"),
+         6: ("q6k_blocks", "q6k_matmul", "q6k_gemv"), 8: ("q80_blocks", "q80_matmul", "q80_gemv")}
+
+
+@pytest.mark.parametrize("qtype,M,N,K,dt", _random_gemv_cases())
+def test_gemv_random_shapes(qtype, M, N, K, dt):
+    gen, ref_mm, fn = _GEMV[qtype]
+    say("random gemv", qtype, M, N, K, dt)
+    rng = np.random.default_rng(qtype * 100003 + M * 1009 + N * 7 + K)
+    w = getattr(synth, gen)(rng, N, K)
+    x = synth.normal_f32(rng, (M, K)) if dt == "f32" else synth.normal_bf16(rng, (M, K))
+    y = host(getattr(qdm, fn)(dev_bytes(w), dev_x(x), N, K))
+    e = rel_err(y, getattr(oracle, ref_mm)(w, x, N, K))
+    assert e <= (TOL_F32 if dt == "f32" else bf16_tol(M)), e
+
+
+# --------------------------------------------------------------------------
 # Q6_K GEMV
 # --------------------------------------------------------------------------
 
@@ -715,6 +751,33 @@ def test_moe_from_logits_small_full(T, E, H, F, top_k, dq):
     ids, gw = qdm.moe_router_topk(ld, top_k)
     step = qdm.moe_q4k_q5k_grouped_gemm if dq == 5 else qdm.moe_q4k_grouped_gemm
     assert np.array_equal(host(step(xd, w13, w2, ids, gw, E, H, F)), y)
+
+
+def _random_moe_cases(n_cases=10, seed=77):
+    """Seeded (T, E, H, F, top_k, down_qtype): T 1..96, E 1..160, top_k up to
+    min(8, E), H and F multiples of 256 up to 1536; both regimes occur."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n_cases):
+        E = int(rng.integers(1, 161))
+        k = int(rng.integers(1, min(8, E) + 1))
+        T = int(rng.choice([1, 2, 3, 7, 8, 16, 33, 96]))
+        H = 256 * int(rng.integers(1, 7))
+        F = 256 * int(rng.integers(1, 7))
+        out.append((T, E, H, F, k, 4 + (i & 1)))
+    return out
+
+
+@pytest.mark.parametrize("T,E,H,F,top_k,dq", _random_moe_cases())
+def test_moe_from_logits_random_shapes(T, E, H, F, top_k, dq):
+    say("random moe from logits", T, E, H, F, top_k, dq)
+    d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T * 31 + E, down_qtype=dq)
+    logits = synth.moe_router(T, E=E, seed=T * 37 + E)
+    y = host(qdm.moe_grouped_gemm_from_logits(*_moe_logits_dev(d, logits), top_k, E, H, F,
+                                              down_qtype=dq))
+    rid, rw = oracle.router_topk(logits, top_k)
+    e = rel_err(y, oracle.moe(d["x"], d["w13"], d["w2"], rid, rw, E, H, F, dq))
+    assert e <= TOL_BF16, e
 
 
 @pytest.mark.parametrize("T", [1, 8, 512])
