@@ -143,11 +143,12 @@ QDM_EXPORT size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, i
   return qdm::moe_workspace(T, E, top_k, H, F);
 }
 
-static int check_moe(const void *x, const void *w_gate_up, const void *w_down,
-                     const int32_t *topk_ids, const float *topk_w, float *y, int64_t T,
-                     int64_t E, int64_t top_k, int64_t H, int64_t F, void *workspace,
-                     size_t workspace_bytes) {
-  if (!x || !w_gate_up || !w_down || !topk_ids || !topk_w || !y) return QDM_ERR_NULL;
+// Arguments of the MoE FFN shared by the entry points (the routing inputs,
+// ids and gate weights or router logits, are checked by each caller).
+static int check_moe(const void *x, const void *w_gate_up, const void *w_down, float *y,
+                     int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                     void *workspace, size_t workspace_bytes) {
+  if (!x || !w_gate_up || !w_down || !y) return QDM_ERR_NULL;
   if (T < 1 || T > (1 << 24) || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || bad_k(H) ||
       bad_k(F) || H > kMaxK || F > kMaxK)
     return QDM_ERR_SHAPE;
@@ -163,8 +164,9 @@ QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const 
                                     const int32_t *topk_ids, const float *topk_w, float *y,
                                     int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
                                     void *workspace, size_t workspace_bytes, void *stream) {
-  const int rc = check_moe(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
-                           workspace, workspace_bytes);
+  if (!topk_ids || !topk_w) return QDM_ERR_NULL;
+  const int rc = check_moe(x, w_gate_up, w_down, y, T, E, top_k, H, F, workspace,
+                           workspace_bytes);
   if (rc) return rc;
   qdm::launch_moe_q4k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F, workspace,
                       (hipStream_t)stream);
@@ -176,8 +178,9 @@ QDM_EXPORT int moe_q4k_q5k_grouped_gemm(const void *x, const void *w_gate_up,
                                         const float *topk_w, float *y, int64_t T, int64_t E,
                                         int64_t top_k, int64_t H, int64_t F, void *workspace,
                                         size_t workspace_bytes, void *stream) {
-  const int rc = check_moe(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
-                           workspace, workspace_bytes);
+  if (!topk_ids || !topk_w) return QDM_ERR_NULL;
+  const int rc = check_moe(x, w_gate_up, w_down, y, T, E, top_k, H, F, workspace,
+                           workspace_bytes);
   if (rc) return rc;
   qdm::launch_moe_q4k_q5k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F,
                           workspace, (hipStream_t)stream);
@@ -210,9 +213,9 @@ QDM_EXPORT int moe_grouped_gemm_from_logits(const void *x, const float *router_l
                                             void *stream) {
   if (!router_logits) return QDM_ERR_NULL;
   if (down_qtype != QDM_Q4_K && down_qtype != QDM_Q5_K) return QDM_ERR_DTYPE;
-  // the MoE checks with a dummy ids/weights pointer (they are produced here)
-  const int rc = check_moe(x, w_gate_up, w_down, (const int32_t *)router_logits, router_logits,
-                           y, T, E, top_k, H, F, workspace, workspace_bytes);
+  // ids and gate weights are produced here, into the workspace
+  const int rc = check_moe(x, w_gate_up, w_down, y, T, E, top_k, H, F, workspace,
+                           workspace_bytes);
   if (rc) return rc;
   if (top_k > E) return QDM_ERR_SHAPE;
   if (misaligned4(router_logits)) return QDM_ERR_ALIGN;
