@@ -733,11 +733,13 @@ def _moe_logits_dev(d, logits):
 @pytest.mark.parametrize("dq", [4, 5])
 @pytest.mark.parametrize("T,E,H,F,top_k", [(5, 6, 256, 256, 3), (33, 16, 256, 512, 4),
                                            (64, 8, 768, 256, 8), (70, 100, 256, 256, 6),
-                                           (9, 8, 256, 256, 7)])
+                                           (9, 8, 256, 256, 7), (3, 16, 256, 256, 4),
+                                           (1, 128, 512, 256, 8)])
 def test_moe_from_logits_small_full(T, E, H, F, top_k, dq):
     """Router and MoE in one call against the oracle's router feeding the
     oracle's MoE; also bit-identical to the router entry followed by the MoE
-    entry with the same ids and weights."""
+    entry with the same ids and weights (T <= 4 with E <= 128 runs the router
+    inside the gate+up kernel, the other cases the router kernel first)."""
     say("moe from logits", T, E, H, F, top_k, dq)
     d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T + E + 2, down_qtype=dq)
     logits = synth.moe_router(T, E=E, seed=T + E + 20)
