@@ -338,10 +338,11 @@ def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    ms = float(np.mean(times))
+    ms = float(np.median(times))  # one host stall must not move the figure
     b = gemv_bytes(N, K, M, bpb)
     del ws
     return {"M": M, "N": N, "K": K, "copies": ncopy, "bytes": b, "avg_ms": ms,
+            "mean_ms": float(np.mean(times)),
             "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
             "rel_err_sampled": err}
 
@@ -389,7 +390,8 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    ms = float(np.mean(times))
+    ms = float(np.median(times))  # one host stall must not move the figure
+    mean_ms = float(np.mean(times))
     graph_ms = None
     if T <= 8:
         # Decode-sized calls are near the host's launch rate: also time them
@@ -417,6 +419,7 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
     touched = distinct * per_expert + T * H * 2 + T * H * 4 + (T * E * 4 if from_logits else 0)
     flops = 2.0 * T * 8 * (2 * F * H + H * F)
     r = {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
+         "mean_ms": mean_ms,
          "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
          "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
     if graph_ms is not None:
