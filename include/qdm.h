@@ -1,6 +1,7 @@
 /*
- * qdm.h — C ABI of the Q4_K / Q5_K / Q6_K dequantize-fused matmul library for
- * MI355X (gfx950). Shared library: libqdm.so.
+ * qdm.h — C ABI of the Q4_K / Q5_K / Q6_K / Q8_0 dequantize-fused matmul
+ * library for MI355X (gfx950), with the top-k router in front of its MoE
+ * grouped matmul. Shared library: libqdm.so.
  *
  * What it computes. GGUF k-quant weights stay packed in HBM and are decoded on
  * the fly inside the matmul: a GEMV for decode and a matrix-core GEMM for
@@ -11,8 +12,9 @@
  * micro-benchmark).
  *
  * Weight layout. A weight tensor W has N output rows of K weights; each row is
- * K/256 consecutive super-blocks and rows are contiguous (row n starts at byte
- * n * (K/256) * block_bytes). The value of weight (n, k) is:
+ * K/256 consecutive super-blocks (Q8_0: K/32 blocks of 32 weights) and rows
+ * are contiguous (row n starts at byte n * (K/256) * block_bytes; Q8_0:
+ * n * (K/32) * 34). The value of weight (n, k) is:
  *   Q4_K (144-byte block): fp16 d @0, fp16 dmin @2, 12 bytes of packed 6-bit
  *     scales/mins @4, 128 bytes of 4-bit codes @16 (chunk c of 32 bytes holds
  *     sub-block 2c in its low nibbles and 2c+1 in its high nibbles);
@@ -27,6 +29,9 @@
  *   Q6_K (210-byte block): 128 bytes of low 4 bits @0, 64 bytes of high 2 bits
  *     @128, 16 int8 scales @192 (one per 16 weights), fp16 d @208;
  *     w = d * scale * (q - 32), q in 0..63.
+ *   Q8_0 (34-byte block of 32 weights): fp16 d @0, 32 two's-complement int8
+ *     codes @2; w = d * q. Named in the same payload table without a layout;
+ *     this is the reading the library and its tests share.
  *
  * Matmul convention. X is [M][K] row-major (fp32 or bf16), Y = X * W^T is
  * [M][N] fp32 row-major and is overwritten (no accumulation into Y).
@@ -40,7 +45,8 @@
  *    failed check the call returns a negative status and enqueues nothing
  *    (outputs are untouched). A launch error reported by the HIP runtime maps
  *    to QDM_ERR_HIP. There is no fallback path of any kind.
- *  - Alignment: w, x, y, out and workspace must be 16-byte aligned.
+ *  - Alignment: w, x, y, out and workspace must be 16-byte aligned (the
+ *    router's logits, ids and weights: 4-byte aligned).
  *  - Calls are stateless and may overlap on different streams as long as
  *    their outputs and workspaces do not overlap.
  */
