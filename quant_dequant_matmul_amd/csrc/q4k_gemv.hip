@@ -589,11 +589,28 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   __syncthreads();
 
   const int nrows = r1 - r0;
-  for (int t = threadIdx.x; t < nrows; t += DN_THREADS) {
-    const float *pp = part + t * nb;
-    float sacc = 0.f;
-    for (int k = 0; k < nb; k++) sacc += pp[k];
-    y[r0 + t] = sacc;
+  if ((nb & 3) == 0) {
+    // A row's partials start 16-byte aligned: four running sums over 16-byte
+    // reads keep the LDS reads independent (one latency, not one per block).
+    for (int t = threadIdx.x; t < nrows; t += DN_THREADS) {
+      const f32x4 *pp = (const f32x4 *)(part + t * nb);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int k = 0; k < nb / 4; k++) {
+        const f32x4 v = pp[k];
+        a0 += v.x;
+        a1 += v.y;
+        a2 += v.z;
+        a3 += v.w;
+      }
+      y[r0 + t] = (a0 + a1) + (a2 + a3);
+    }
+  } else {
+    for (int t = threadIdx.x; t < nrows; t += DN_THREADS) {
+      const float *pp = part + t * nb;
+      float sacc = 0.f;
+      for (int k = 0; k < nb; k++) sacc += pp[k];
+      y[r0 + t] = sacc;
+    }
   }
 }
 
