@@ -4,8 +4,9 @@ Headline (`value`): the Q4_K decode GEMV set at M = 1 with bf16 activations —
 fused QKV (K=5120, N=7168), fused gate+up (K=5120, N=34816) and down
 (K=17408, N=5120) — as effective GB/s: the algorithmic bytes of one step
 (packed weights + x + y of the three GEMVs) over the time of one step. A step
-is the three calls launched back to back through the Python binding (the rate
-of the same step replayed from a captured HIP graph is reported beside it);
+is the three calls launched back to back through the C ABI with arguments
+marshalled once (the rate of the same step replayed from a captured HIP graph
+is reported beside it);
 the timed region is `--steps` steps after `--warmup` untimed ones. Weight
 sets rotate over copies whose total exceeds twice the 256 MB MALL, so the
 rate is an HBM rate.
@@ -212,7 +213,7 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
         graph_ms_per_step = g0.elapsed_time(g1) / (reps * ncopy)
         graph_steps = reps * ncopy
 
-    # eager steps through the Python binding
+    # eager steps through the C ABI
     tm = Timer(torch)
     t0 = tm.event()
     for i in range(steps):

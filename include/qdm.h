@@ -88,7 +88,12 @@ int qdm_version(void);
  * row-major) = the value of weight (n, k), bit-identical to the format formula
  * evaluated in fp32 (every product in it is exact in fp32, so the result is
  * the single correctly rounded value; Q6_K values are exact). Test-facing.
- * N >= 1, K >= 256, K % 256 == 0.
+ * Source: hipEngine README, "GGUF Support" (payload table: the Q4_K, Q5_K and
+ * Q6_K tensor families of a Q4_K_M file, read by GGUF-specific quant readers);
+ * the formulas are those of the layout preamble above.
+ * w: the packed tensor (read only); out: caller-owned, fully overwritten.
+ * N >= 1, K >= 256, K % 256 == 0, else QDM_ERR_SHAPE; NULL pointers give
+ * QDM_ERR_NULL, pointers not 16-byte aligned QDM_ERR_ALIGN.
  */
 int q4k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
 int q5k_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream);
@@ -107,7 +112,12 @@ int q80_dequantize(const void *w, float *out, int64_t N, int64_t K, void *stream
 /*
  * q4k_gemv / q5k_gemv / q6k_gemv: decode-regime matmul,
  * y[m][n] = sum_k x[m][k] * w(n,k)
- * for 1 <= M <= 16. x_dtype is QDM_F32 or QDM_BF16. Accumulation is fp32.
+ * for 1 <= M <= 16. Source: hipEngine README, "Quickstart" (decode runs a
+ * GEMV over the quantized weights) and hipster README, "Verify the claims"
+ * (the GEMV micro-benchmark, reported in GB/s).
+ * w: packed [N][K/256] blocks (read only); x: [M][K] row-major, fp32 or bf16
+ * (read only); y: [M][N] fp32, caller-owned, fully overwritten.
+ * x_dtype is QDM_F32 or QDM_BF16 (else QDM_ERR_DTYPE). Accumulation is fp32.
  * N >= 1, K >= 256, K % 256 == 0, K <= 65536 (bf16 x) or K <= 32768 (fp32 x):
  * one activation row is staged in the 160 KiB LDS of a compute unit.
  * q4k_gemv, q5k_gemv and q6k_gemv with bf16 x and M >= 2 run on the matrix
@@ -135,28 +145,53 @@ int q80_gemv(const void *w, const void *x, int x_dtype, float *y,
              int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
- * q4k_gemm: prefill-regime matmul on the matrix cores. x is bf16 [M][K]; the
- * Q4_K weights are decoded in fp32 and rounded to bf16 (nearest even) before
- * the bf16 x bf16 -> fp32 MFMA contraction; y is fp32 [M][N].
- * M >= 1, N >= 1, K >= 256, K % 256 == 0.
- * The tile x K iteration space is split evenly over one workgroup per
- * compute unit; a tile computed by several workgroups is summed in a fixed
- * order (results are deterministic).
+ * q4k_gemm: prefill-regime matmul on the matrix cores. Source: hipEngine
+ * README, "Quickstart" (prefill runs on the matrix cores, decode on a GEMV)
+ * and "GGUF Support" (a bulk-prefill path over the GGUF quant readers).
+ * x is bf16 [M][K] (read only); the Q4_K weights w [N][K/256] (read only) are
+ * decoded in fp32 and rounded to bf16 (nearest even) before the
+ * bf16 x bf16 -> fp32 MFMA contraction; y is fp32 [M][N], fully overwritten.
+ * M >= 1, N >= 1, K >= 256, K % 256 == 0 (else QDM_ERR_SHAPE).
+ * With at least as many 256 x 256 tiles as compute units, the tile x K
+ * iteration space is split evenly over one workgroup per compute unit, and a
+ * tile computed by several workgroups is summed in a fixed order (results are
+ * deterministic); with fewer tiles each tile is one workgroup.
  * workspace: q4k_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, on the
- * device of the call: a flag word per workgroup, then one fp32 256 x 256
- * partial tile per workgroup. It must be zero-filled before its first use;
- * every call leaves the flag words zero again, so one buffer serves any
- * number of calls in stream order. Two calls that overlap in time (different
- * streams) need different workspaces. The size depends on the current
- * device's compute-unit count (256 if no device is visible).
+ * device of the call; 0 bytes (workspace may be NULL) when no tile is split.
+ * Otherwise: a 256-byte status block, a flag word per workgroup, then one fp32
+ * 256 x 256 partial tile per workgroup (a too-small or NULL workspace gives
+ * QDM_ERR_WORKSPACE). It must be zero-filled before its first use; every call
+ * leaves the flag words zero again, so one buffer serves any number of calls
+ * in stream order. Two calls that overlap in time (different streams) need
+ * different workspaces. The size depends on the current device's
+ * compute-unit count (256 if no device is visible).
+ * Status word (32-bit word 0 of the workspace): the number of split-tile
+ * waits that gave up (a partial tile that did not arrive within about a
+ * second of polling), counted across calls and never cleared by the library.
+ * Such a tile of y is written as NaN. The caller reads the word after the
+ * stream has synchronized; it stays 0 in normal operation.
  */
 size_t q4k_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * qdm_set_gemm_spin_limit: polls a q4k_gemm owner makes before giving up on a
+ * split-tile partial (0 restores the default, about a second). A test hook of
+ * the give-up path of the workspace status word: with a tiny limit the
+ * kernels still end normally, some tiles are written as NaN and counted, and
+ * the flags are left zero. Process-wide; set it only while no q4k_gemm call is
+ * being enqueued on another thread. Returns QDM_OK.
+ */
+int qdm_set_gemm_spin_limit(uint32_t polls);
+
+/*
  * moe_q4k_grouped_gemm: routed MoE FFN with Q4_K experts, one call for the
- * whole layer:
+ * whole layer. Source: hipster README, "Verify the claims" (the MoE grouped
+ * GEMM micro-benchmark over an expert tensor) and hipEngine README, "Status"
+ * (a routed MoE model, Qwen3.6-35B-A3B); the activation between the two
+ * expert matmuls (SwiGLU, gate rows before up rows) is a reading, the pages
+ * do not state it:
  *   for every token t and slot s, e = topk_ids[t][s]:
  *     u = W13[e] * x_t                  (2F values; W13[e] is [2F][H])
  *     h = silu(u[0:F]) * u[F:2F]        (gate rows first, then up rows)
@@ -164,14 +199,22 @@ int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64
  *   x: bf16 [T][H]; w_gate_up: E tensors of [2F][H/256] Q4_K blocks back to
  *   back; w_down: E tensors of [H][F/256]; topk_ids int32 [T][top_k] (each in
  *   [0, E), distinct within a row); topk_w fp32 [T][top_k]; y fp32 [T][H]
- *   (overwritten). Tokens are grouped by expert on the device (histogram,
- *   scan, scatter) so every expert's weights are streamed once per call.
- *   Ids outside [0, E) are skipped (they contribute nothing).
+ *   (overwritten). x, the weights, ids and gate weights are read only. Tokens
+ *   are grouped by expert on the device (histogram, scan, scatter) so every
+ *   expert's weights are streamed once per call.
+ *   Ids outside [0, E) are skipped (they contribute nothing) and counted:
+ *   32-bit word 0 of the workspace holds, after the call, the number of
+ *   (t, s) entries of this call whose id was outside [0, E) (stored by the
+ *   call's routing step; the caller reads it after the stream synchronizes).
+ *   Ids repeated within a row are a precondition violation (not detected).
  *   1 <= T <= 2^24, 1 <= E <= 1024, 1 <= top_k <= 16, H and F multiples of
- *   256 and at most 65536.
+ *   256 and at most 65536, and each expert's tensors below 2 GiB
+ *   (2F * H/256 * 176 and H * F/256 * 176 bytes under 2^31); else
+ *   QDM_ERR_SHAPE.
  *   workspace: moe_q4k_workspace_bytes(T, E, top_k, H, F) bytes, 16-byte
  *   aligned, on the device of the call (scratch; no initial contents
- *   needed). Calls that overlap in time need different workspaces.
+ *   needed; too small or NULL gives QDM_ERR_WORKSPACE). Calls that overlap in
+ *   time need different workspaces.
  *   With T * top_k <= 64 (decode) the call is three kernels: gate+up+SwiGLU
  *   and down, each of which routes the few entries itself, and the combine.
  *   Above that: a routing kernel, two grouped matrix-core kernels and the
@@ -232,7 +275,9 @@ int moe_grouped_gemm_from_logits(const void *x, const float *router_logits,
 /*
  * qdm_probe_copy: streaming copy of n_bytes from src to dst (n_bytes % 16 ==
  * 0). A plain, known-size kernel used to calibrate memory-traffic counters
- * and to measure the achievable HBM bandwidth of the device.
+ * and to measure the achievable HBM bandwidth of the device (hipster README,
+ * "Hardware and software this was measured on": measured roofs beside the
+ * nominal ones).
  */
 int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void *stream);
 

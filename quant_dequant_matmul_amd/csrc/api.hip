@@ -137,6 +137,11 @@ QDM_EXPORT int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64
   return finish_launch();
 }
 
+QDM_EXPORT int qdm_set_gemm_spin_limit(uint32_t polls) {
+  qdm::set_gemm_spin_limit(polls);
+  return QDM_OK;
+}
+
 QDM_EXPORT size_t moe_q4k_workspace_bytes(int64_t T, int64_t E, int64_t top_k, int64_t H,
                                           int64_t F) {
   if (T < 1 || E < 1 || top_k < 1 || top_k > 16 || bad_k(H) || bad_k(F)) return 0;
@@ -151,6 +156,10 @@ static int check_moe(const void *x, const void *w_gate_up, const void *w_down, f
   if (!x || !w_gate_up || !w_down || !y) return QDM_ERR_NULL;
   if (T < 1 || T > (1 << 24) || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || bad_k(H) ||
       bad_k(F) || H > kMaxK || F > kMaxK)
+    return QDM_ERR_SHAPE;
+  // one expert's tensor must stay below 2 GiB (the kernels address it with
+  // 32-bit offsets); 176 bytes per 256 weights covers Q4_K and Q5_K
+  if (2 * F * (H / 256) * 176 >= ((int64_t)1 << 31) || H * (F / 256) * 176 >= ((int64_t)1 << 31))
     return QDM_ERR_SHAPE;
   if (misaligned(x) || misaligned(w_gate_up) || misaligned(w_down) || misaligned(y))
     return QDM_ERR_ALIGN;

@@ -30,6 +30,7 @@ void launch_q80_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
                      int64_t N, int64_t K, hipStream_t s);
 
 size_t q4k_gemm_workspace(int64_t M, int64_t N, int64_t K);
+void set_gemm_spin_limit(uint32_t limit);
 void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
                      void *workspace, hipStream_t s);
 

@@ -47,10 +47,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = DEC_THREADS / WAVE;
 constexpr int DEC_MAX_N = 64;
-#ifndef QDM_DEC_PF
-#define QDM_DEC_PF 3
-#endif
-constexpr int DEC_PF = QDM_DEC_PF;  // wave iterations of weight loads in flight
+constexpr int DEC_PF = 3;  // wave iterations of weight loads in flight
 // Rows per decode workgroup: gate/up row pairs (FR) and W2 rows (RW). Few
 // tokens touch few experts, and small workgroups spread them over more compute
 // units; from 4 tokens on, larger workgroups spend less on their fixed costs
@@ -68,9 +65,10 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
 
 // Routing of at most 64 entries, derived by every workgroup from the ids:
 // the number of distinct valid experts, the a-th of them in increasing id
-// order (-1 past the end) and its entries in increasing (t, s) order.
+// order (-1 past the end), its entries in increasing (t, s) order, and the
+// number of entries whose id is outside [0, E).
 struct SmallRoute {
-  int nact, e, cnt;
+  int nact, e, cnt, bad;
   int ent[DEC_MAX_N];
 };
 
@@ -107,11 +105,13 @@ __device__ void small_route(const int32_t *__restrict__ ids, int n, int E, int a
     }
     const bool mine = e >= 0 && tid < n && myid == e;
     const uint64_t mm = __ballot(mine);
+    const uint64_t bad = __ballot(tid < n && (myid < 0 || myid >= E));
     if (mine) sr.ent[__popcll(mm & ((1ull << tid) - 1ull))] = tid;
     if (tid == 0) {
       sr.nact = total;
       sr.e = e;
       sr.cnt = __popcll(mm);
+      sr.bad = __popcll(bad);
     }
   }
   __syncthreads();
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w13,
     const int32_t *__restrict__ ids, int n, int top_k, int E, int H, int F,
     float *__restrict__ h, const float *__restrict__ logits, int32_t *__restrict__ ids_out,
-    float *__restrict__ gw_out) {
+    float *__restrict__ gw_out, uint32_t *__restrict__ status) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ SmallRoute sr;
   __shared__ uint32_t bitmap[32];
@@ -442,6 +442,8 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_gateup_kernel(
     rid = lg_ids;
   }
   small_route(rid, n, E, blockIdx.y, sr, bitmap);
+  // the call's count of skipped ids (every workgroup derives the same value)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) status[0] = (uint32_t)sr.bad;
   if (sr.e < 0) return;
   const int e = sr.e, cnt = sr.cnt;
   const int nb = H / QK;
@@ -577,7 +579,7 @@ constexpr int ROUTE_IDS = 4;  // ids per thread and batch
 // is the expert's running offset + the counts of earlier waves + its rank.
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
     const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ perm) {
+    int32_t *__restrict__ perm, uint32_t *__restrict__ status) {
   extern __shared__ int32_t rsm[];
   int32_t *run = rsm;       // [E] running offsets
   int32_t *cntw = rsm + E;  // [ROUTE_WAVES][E] per-wave counts of a chunk
@@ -622,7 +624,10 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
     offsets[tid] = wpre + incl - v;
     run[tid] = wpre + incl - v;
   }
-  if (tid == 0) offsets[E] = total;
+  if (tid == 0) {
+    offsets[E] = total;
+    status[0] = (uint32_t)(n - total);  // entries skipped: id outside [0, E)
+  }
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
   for (int base = 0; base < n; base += BATCH) {
@@ -731,6 +736,7 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
   const uint8_t *wexp = wq + (int64_t)e * NR * nbk * BB;
   // raw chunk i of this thread: chunk c = tid + 256 i of the column, which is
   // piece c % NCH of the block of tile row c / NCH
+  // (32-bit offsets: the host admits only experts whose tensor is below 2 GiB)
   int choff[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; i++) {
@@ -866,10 +872,12 @@ __global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
 
 }  // namespace
 
-// Workspace: o [n][H] fp32 by entry (both regimes), then h [n][F] fp32 by
-// entry (decode) and offsets [E+1], perm [n], hb [n][F] bf16 by entry
-// (matrix cores).
+// Workspace: a 256-byte status block (word 0: entries of the last call whose
+// id was outside [0, E), stored by the routing step of either regime), o
+// [n][H] fp32 by entry (both regimes), then h [n][F] fp32 by entry (decode)
+// and offsets [E+1], perm [n], hb [n][F] bf16 by entry (matrix cores).
 struct MoeWs {
+  uint32_t *status;
   float *o, *h;
   int32_t *offsets, *perm;
   uint16_t *hb;
@@ -885,6 +893,7 @@ MoeWs carve(void *base, int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t 
     return (char *)base + at;
   };
   MoeWs ws;
+  ws.status = (uint32_t *)take(256);
   ws.o = (float *)take(sizeof(float) * n * H);
   ws.h = (float *)take(sizeof(float) * n * F);
   ws.offsets = (int32_t *)take(sizeof(int32_t) * (E + 1));
@@ -921,8 +930,9 @@ int dec_mt(int64_t T, int64_t n, int64_t H, int64_t F, int fr, int rw, size_t &l
 template <int MT, int FR, int RW, bool Q5>
 void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *ids,
                 const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
-                int64_t F, float *hbuf, float *obuf, size_t lds1, size_t lds2, hipStream_t s,
+                int64_t F, const MoeWs &ws, size_t lds1, size_t lds2, hipStream_t s,
                 const float *logits) {
+  float *hbuf = ws.h, *obuf = ws.o;
   const int n = (int)(T * top_k);
   const unsigned slots = (unsigned)(E < n ? E : n);
   auto k1 = logits ? moe_dec_gateup_kernel<MT, FR, true> : moe_dec_gateup_kernel<MT, FR, false>;
@@ -932,7 +942,7 @@ void launch_dec(const void *x, const void *w13, const void *w2, const int32_t *i
   hipLaunchKernelGGL(k1, dim3((unsigned)((F + FR - 1) / FR), slots), dim3(DEC_THREADS), lds1, s,
                      (const uint16_t *)x, (const uint8_t *)w13, logits ? nullptr : ids, n,
                      (int)top_k, (int)E, (int)H, (int)F, hbuf, logits, (int32_t *)ids,
-                     (float *)gw);
+                     (float *)gw, ws.status);
   hipLaunchKernelGGL(k2, dim3((unsigned)((H + RW - 1) / RW), slots), dim3(DEC_THREADS), lds2, s,
                      hbuf, (const uint8_t *)w2, ids, obuf, n, (int)top_k, (int)E, (int)H, (int)F);
   const int64_t total = T * H / 4;
@@ -948,9 +958,9 @@ bool try_dec(const void *x, const void *w13, const void *w2, const int32_t *ids,
              const MoeWs &ws, hipStream_t s, const float *logits = nullptr) {
   size_t lds1 = 0, lds2 = 0;
   switch (dec_mt(T, T * top_k, H, F, FR, RW, lds1, lds2)) {
-    case 4: launch_dec<4, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s, logits); return true;
-    case 2: launch_dec<2, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s, logits); return true;
-    case 1: launch_dec<1, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws.h, ws.o, lds1, lds2, s, logits); return true;
+    case 4: launch_dec<4, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, lds1, lds2, s, logits); return true;
+    case 2: launch_dec<2, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, lds1, lds2, s, logits); return true;
+    case 1: launch_dec<1, FR, RW, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, lds1, lds2, s, logits); return true;
     default: return false;
   }
 }
@@ -970,7 +980,7 @@ void launch_moe(const void *x, const void *w13, const void *w2, const int32_t *i
   (void)hipFuncSetAttribute((const void *)moe_route_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, s, ids, n,
-                     (int)E, ws.offsets, ws.perm);
+                     (int)E, ws.offsets, ws.perm, ws.status);
   auto k1 = moe_mfma_kernel<true, false>;
   auto k2 = moe_mfma_kernel<false, Q5>;
   constexpr size_t lds1 = mx_lds(false), lds2 = mx_lds(Q5);

@@ -56,6 +56,12 @@
 // index order and a unit only waits on units with a smaller index, which have
 // started before it; each unit computes the segment others wait for before
 // the one that waits: the waits cannot deadlock and do not form chains.
+// If a wait runs out of its bound anyway, the handshake stays two-sided: the
+// owner marks the flag abandoned (compare-and-swap 0 -> 2; if the swap finds
+// 1 the partial did arrive and is used), writes the tile as NaN and counts the
+// event in the workspace status word; a contributor raises its flag with an
+// exchange and, finding the abandoned mark, lowers it to 0. Every flag is
+// then zero when the kernel ends, whatever the timing.
 //
 // MFMA operand layout (32x32x16 bf16, wave64): lane l holds, for A, row l%32
 // and 8 consecutive k; for B, column l%32 and the same 8 k (lane halves take
@@ -268,6 +274,17 @@ __device__ __forceinline__ void gemm_stage(f32x16 (&acc)[8][2], bf16x8 (&bf)[2][
   __syncthreads();  // x of stage s+1 complete in nsx; sx free for stage s+2
 }
 
+// Flag states: 0 idle, 1 partial published, 2 abandoned by an owner whose
+// wait ran out (the contributor then resets it).
+constexpr uint32_t FLAG_PUBLISHED = 1u, FLAG_ABANDONED = 2u;
+
+__device__ __forceinline__ void raise_flag(uint32_t *flag) {
+  const uint32_t old =
+      __hip_atomic_exchange(flag, FLAG_PUBLISHED, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (old == FLAG_ABANDONED)  // nobody will read this partial: leave the flag idle
+    __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Multiplies stage range [s0, s1) (s1 - s0 even, >= 2) of tile (m0, n0) into acc.
 __device__ __forceinline__ void run_segment(f32x16 (&acc)[8][2], uint16_t *smem,
                                             const uint8_t *__restrict__ w,
@@ -321,13 +338,14 @@ __device__ __forceinline__ void run_segment(f32x16 (&acc)[8][2], uint16_t *smem,
       // make it visible device-wide and raise its flag
       __threadfence();
       __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_store(publish, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) raise_flag(publish);
     }
   }
 }
 
-constexpr uint32_t SPIN_LIMIT = 1u << 24;  // ~1 s of polling before giving up
+// Polls of a flag before an owner gives up (about 1 s of polling); the host
+// can lower it (qdm_set_gemm_spin_limit) to exercise the give-up path.
+constexpr uint32_t SPIN_LIMIT = 1u << 24;
 
 // A partial tile in the accumulators' own layout: accumulator group
 // g = (i*2 + j)*4 + v/4 (64 groups of 4 floats per thread) of thread t sits at
@@ -442,7 +460,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[8][2], float *yt,
 
 __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int M,
-    int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags, int units) {
+    int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags,
+    uint32_t *__restrict__ status, int units, uint32_t spin_limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // x stage buffer p at smem + p*XTILE; the LDS store of a split tile reuses it
   __shared__ uint32_t timed_out;
@@ -491,13 +510,23 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     while (lowest > 0 && total * lowest / units > (int64_t)tile * P) lowest--;
     if (threadIdx.x == 0) {
       uint32_t spins = 0;
+      bool lost = false;
       for (int u = unit - 1; u >= lowest; u--) {
         while (__hip_atomic_load(&flags[u], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-               ++spins < SPIN_LIMIT)
+               ++spins < spin_limit)
           __builtin_amdgcn_s_sleep(2);
+        uint32_t seen = 0u;
+        if (spins >= spin_limit &&
+            __hip_atomic_compare_exchange_strong(&flags[u], &seen, FLAG_ABANDONED,
+                                                 __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          lost = true;  // the contributor resets the abandoned flag when it publishes
+          continue;
+        }
         __hip_atomic_store(&flags[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      timed_out = spins >= SPIN_LIMIT;
+      timed_out = lost;
+      if (lost) atomicAdd(status, 1u);
     }
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -508,8 +537,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
   if (pending != nullptr) {  // the last segment left a partial: publish it now
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(pending, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) raise_flag(pending);
   }
 }
 
@@ -550,25 +578,41 @@ int gemm_units(int64_t M, int64_t N, int64_t K) {
   return (int)(total < cus ? total : cus);
 }
 
+// Whether a call splits tiles between workgroups (then it needs the flags and
+// partial tiles of the workspace).
+bool gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return gemm_units(M, N, K) != tiles;
+}
+
+uint32_t g_spin_limit = SPIN_LIMIT;
+
 }  // namespace
 
-// Workspace: one flag word per unit (256-byte aligned block), then one fp32
-// partial tile per unit.
+void set_gemm_spin_limit(uint32_t limit) { g_spin_limit = limit ? limit : SPIN_LIMIT; }
+
+// Workspace of a call that splits tiles (none otherwise): a 256-byte status
+// block (word 0: split-tile waits that gave up, counted across calls), one
+// flag word per unit (256-byte aligned block) and one fp32 partial tile per
+// unit.
 size_t q4k_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  if (!gemm_splits(M, N, K)) return 0;  // whole tiles: no flags, partials or waits
   const size_t units = (size_t)gemm_units(M, N, K);
-  return align256(units * sizeof(uint32_t)) + units * BM * BN * sizeof(float);
+  return 256 + align256(units * sizeof(uint32_t)) + units * BM * BN * sizeof(float);
 }
 
 void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N, int64_t K,
                      void *workspace, hipStream_t s) {
   const int units = gemm_units(M, N, K);
-  uint32_t *flags = (uint32_t *)workspace;
-  float *partials = (float *)((char *)workspace + align256((size_t)units * sizeof(uint32_t)));
+  uint32_t *status = (uint32_t *)workspace;
+  uint32_t *flags = (uint32_t *)((char *)workspace + 256);
+  float *partials =
+      (float *)((char *)workspace + 256 + align256((size_t)units * sizeof(uint32_t)));
   (void)hipFuncSetAttribute((const void *)q4k_gemm_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
   hipLaunchKernelGGL(q4k_gemm_kernel, dim3((unsigned)units), dim3(GEMM_THREADS), GEMM_LDS, s,
                      (const uint8_t *)w, (const uint16_t *)x, y, (int)M, (int)N, (int)K, partials,
-                     flags, units);
+                     flags, status, units, g_spin_limit);
 }
 
 }  // namespace qdm

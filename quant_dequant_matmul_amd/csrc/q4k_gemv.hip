@@ -345,18 +345,10 @@ constexpr int dn_span_bytes() { return DN_SPAN * dn_block_bytes<Q5>(); }
 template <bool Q5>
 constexpr int dn_span_chunks() { return dn_span_bytes<Q5>() / 1024; }
 constexpr int DN_XREC = 560;                          // LDS bytes per x column block
-#ifndef QDM_DN_TARGET_WGS
-#define QDM_DN_TARGET_WGS 256
-#endif
-constexpr int DN_TARGET_WGS = QDM_DN_TARGET_WGS;      // workgroups per launch (one per CU)
+constexpr int DN_TARGET_WGS = 256;      // workgroups per launch (one per CU)
 constexpr int DN_MAX_WG_BLOCKS = 8192;
 constexpr size_t DN_LDS_LIMIT = 160 * 1024;
-#ifndef QDM_DN_WAVES
-#define QDM_DN_WAVES 4  // waves per workgroup of the dense kernel
-#endif
-#ifndef QDM_DN_PHASED
-#define QDM_DN_PHASED 1  // keep each sub-block pair's LDS reads next to its math
-#endif
+constexpr int DN_WAVES = 4;  // waves per workgroup of the dense kernel
 
 template <int NCH>
 struct Span {
@@ -493,9 +485,8 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
     r = fmaf(-fmaf(128.f, a0, b0), xs[j0], r);
     r = fmaf(a1, s1, r);
     r = fmaf(-fmaf(128.f, a1, b1), xs[j0 + 1], r);
-#if QDM_DN_PHASED
+    // keep each sub-block pair's LDS reads next to its math
     __builtin_amdgcn_sched_barrier(0);
-#endif
   }
   return r;
 }
@@ -719,18 +710,18 @@ bool try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, hip
   int64_t nwg;
   int rows_q, rows_rem;
   size_t lds;
-  if (!dense_plan<QDM_DN_WAVES, Q5>(N, K, nwg, rows_q, rows_rem, lds)) return false;
-  const int64_t per_thread = (K / 8 + QDM_DN_WAVES * WAVE - 1) / (QDM_DN_WAVES * WAVE);
+  if (!dense_plan<DN_WAVES, Q5>(N, K, nwg, rows_q, rows_rem, lds)) return false;
+  const int64_t per_thread = (K / 8 + DN_WAVES * WAVE - 1) / (DN_WAVES * WAVE);
   if (per_thread <= 2)
-    launch_dense<QDM_DN_WAVES, 2, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+    launch_dense<DN_WAVES, 2, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
   else if (per_thread <= 3)
-    launch_dense<QDM_DN_WAVES, 3, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+    launch_dense<DN_WAVES, 3, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
   else if (per_thread <= 5)
-    launch_dense<QDM_DN_WAVES, 5, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+    launch_dense<DN_WAVES, 5, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
   else if (per_thread <= 8)
-    launch_dense<QDM_DN_WAVES, 8, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+    launch_dense<DN_WAVES, 8, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
   else
-    launch_dense<QDM_DN_WAVES, 16, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
+    launch_dense<DN_WAVES, 16, Q5>(w, x, y, K, nwg, rows_q, rows_rem, lds, s);
   return true;
 }
 

@@ -342,16 +342,8 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 // portion of their range) in LDS, and the first wave adds those portions in
 // wave order before it stores. Loads run Q6M_PF items ahead.
 // ---------------------------------------------------------------------------
-#ifndef QDM_Q6_MFMA_MIN_M
-#define QDM_Q6_MFMA_MIN_M 2  // smallest M (bf16 x) that takes the matrix-core kernel
-#endif
-#ifndef QDM_Q6M_WAVES_CU
-#define QDM_Q6M_WAVES_CU 12  // waves per compute unit
-#endif
-#ifndef QDM_Q6M_PF
-#define QDM_Q6M_PF 2  // super-blocks in flight per wave
-#endif
-constexpr int Q6M_PF = QDM_Q6M_PF;
+constexpr int Q6_MFMA_MIN_M = 2;  // smallest M (bf16 x) that takes the matrix-core kernel
+constexpr int Q6M_PF = 2;         // super-blocks in flight per wave
 constexpr size_t Q6M_FLAGS = 256;  // flag words, padded
 constexpr int Q6M_SPIN_LIMIT = 1 << 24;
 
@@ -752,21 +744,12 @@ void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64
     const uint16_t *xm = x + kb0 * QK;
     const int mc = (int)M;
     const bool acc = c > 0;
-#if QDM_Q6M_WAVES_CU == 16
-    if (4 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(4), 4, s);
-    else if (2 * (xb + q6m_head_bytes(8) + SLACK) <= LDS_CU)
-      launch_q6_mfma<512, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(8), 2, s);
-    else
-      launch_q6_mfma<1024, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(16), 1, s);
-#else
     if (3 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
       launch_q6_mfma<256, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(4), 3, s);
     else if (2 * (xb + q6m_head_bytes(6) + SLACK) <= LDS_CU)
       launch_q6_mfma<384, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(6), 2, s);
     else
       launch_q6_mfma<768, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(12), 1, s);
-#endif
     kb0 += kc / QK;
   }
 }
@@ -1042,7 +1025,7 @@ void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_
     const int64_t rows_rg = (256 / WAVE) * (16 / gcd16((int)(K / QK)));
     if ((N + rows_rg - 1) / rows_rg < 8 * 256 && q6_try_dense(w, x, y, N, K, s)) return;
   }
-  if (x_bf16 && M >= QDM_Q6_MFMA_MIN_M) {
+  if (x_bf16 && M >= Q6_MFMA_MIN_M) {
     launch_kq_mfma<MfQ6>(w, (const uint16_t *)x, y, M, N, K, s);
     return;
   }

@@ -158,3 +158,114 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 256, dtype=torch.float32)
     with pytest.raises(ValueError):
         qdm.q4k_gemv(w, x, 1, 256, y=torch.empty(1, 1))
+
+
+def test_gemm_workspace_only_when_tiles_split():
+    """Whole-tile calls (fewer 256 x 256 tiles than compute units) need no
+    workspace; split calls need the status block, flags and partial tiles."""
+    L = qdm.lib()
+    assert L.q4k_gemm_workspace_bytes(512, 17408, 5120) == 0  # 136 tiles
+    need = L.q4k_gemm_workspace_bytes(4096, 17408, 5120)       # 1088 tiles
+    assert need >= 256 + 256 * 256 * 256 * 4
+    assert L.q4k_gemm(A, A, A2, 4096, 17408, 5120, NUL, 0, NUL) == EWS
+    assert L.qdm_set_gemm_spin_limit(0) == OK
+
+
+def test_moe_rejects_experts_over_2gib():
+    L = qdm.lib()
+    moe = L.moe_q4k_grouped_gemm
+    need = L.moe_q4k_workspace_bytes(1, 4, 2, 65536, 65536)
+    args = [A, A, A, A, A, A2]
+    assert moe(*args, 1, 4, 2, 65536, 65536, A, need, NUL) == ESHAPE  # 4.9 GB per expert
+    assert moe(*args, 1, 4, 2, 65536, 29696, A, need, NUL) == ESHAPE  # just over 2 GiB
+
+
+# --------------------------------------------------------------------------
+# The Python binding refuses wrong dtypes, shapes and sizes before any call
+# reaches the library (CPU tensors: the checks run before the device check).
+# --------------------------------------------------------------------------
+
+def _refuses(match, fn, *a, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_binding_gemv_checks():
+    import torch
+    K, N = 512, 4
+    w = torch.zeros(qdm.packed_bytes("q4k", N, K), dtype=torch.uint8)
+    _refuses("x must be", qdm.q4k_gemv, w, torch.zeros(1, K, dtype=torch.float16), N, K)
+    _refuses("x must be", qdm.q4k_gemv, w, torch.zeros(1, K, dtype=torch.int32), N, K)
+    _refuses(r"x must be \[M\]", qdm.q4k_gemv, w, torch.zeros(1, K - 256), N, K)
+    _refuses(r"x must be \[M\]", qdm.q4k_gemv, w, torch.zeros(K), N, K)
+    _refuses("w holds", qdm.q4k_gemv, w[:-1], torch.zeros(1, K), N, K)
+    for fmt, fn in (("q5k", qdm.q5k_gemv), ("q6k", qdm.q6k_gemv), ("q80", qdm.q80_gemv)):
+        need = qdm.packed_bytes(fmt, N, K)
+        _refuses("w holds", fn, torch.zeros(need - 1, dtype=torch.uint8), torch.zeros(1, K), N, K)
+        # the right size passes the checks and stops at the device check
+        _refuses("GPU tensor", fn, torch.zeros(need, dtype=torch.uint8), torch.zeros(1, K), N, K)
+    _refuses("y must be", qdm.q4k_gemv, w, torch.zeros(1, K), N, K,
+             y=torch.empty(1, N, dtype=torch.float64))
+    assert qdm.packed_bytes("q4k", 7168, 5120) == 7168 * 20 * 144
+    assert qdm.packed_bytes("q80", 7, 512) == 7 * 16 * 34
+
+
+def test_binding_dequant_checks():
+    import torch
+    for fmt in ("q4k", "q5k", "q6k", "q80"):
+        fn = getattr(qdm, fmt + "_dequantize")
+        need = qdm.packed_bytes(fmt, 3, 256)
+        _refuses("w holds", fn, torch.zeros(need - 2, dtype=torch.uint8), 3, 256)
+
+
+def test_binding_gemm_checks():
+    import torch
+    K, N = 256, 8
+    w = torch.zeros(qdm.packed_bytes("q4k", N, K), dtype=torch.uint8)
+    _refuses("x must be", qdm.q4k_gemm, w, torch.zeros(4, K, dtype=torch.float32), N, K)
+    _refuses(r"x must be \[M\]", qdm.q4k_gemm, w, torch.zeros(4, 2 * K, dtype=torch.bfloat16),
+             N, K)
+    _refuses("w holds", qdm.q4k_gemm, w[:100], torch.zeros(4, K, dtype=torch.bfloat16), N, K)
+
+
+def test_binding_moe_checks():
+    import torch
+    T, E, k, H, F = 2, 4, 2, 256, 256
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    w13 = torch.zeros(qdm.packed_bytes("q4k", E * 2 * F, H), dtype=torch.uint8)
+    w2 = torch.zeros(qdm.packed_bytes("q4k", E * H, F), dtype=torch.uint8)
+    w2q5 = torch.zeros(qdm.packed_bytes("q5k", E * H, F), dtype=torch.uint8)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    gw = torch.zeros(T, k, dtype=torch.float32)
+    f = qdm.moe_q4k_grouped_gemm
+    # int64 ids (torch.topk's default) would be read as interleaved int32 halves
+    _refuses("topk_ids must be", f, x, w13, w2, ids.long(), gw, E, H, F)
+    _refuses("topk_w must be", f, x, w13, w2, ids, gw.half(), E, H, F)
+    _refuses("topk_w must have shape", f, x, w13, w2, ids, gw[:1], E, H, F)
+    _refuses("x must be", f, x.float(), w13, w2, ids, gw, E, H, F)
+    _refuses("x must have shape", f, x[:1], w13, w2, ids, gw, E, H, F)
+    _refuses("w_gate_up holds", f, x, w13[:-16], w2, ids, gw, E, H, F)
+    _refuses("w_down holds", f, x, w13, w2[:-16], ids, gw, E, H, F)
+    # Q5_K down experts are 176 bytes per block: a Q4_K-sized tensor is short
+    _refuses("w_down holds", qdm.moe_q4k_q5k_grouped_gemm, x, w13, w2, ids, gw, E, H, F)
+    _refuses("GPU tensor", qdm.moe_q4k_q5k_grouped_gemm, x, w13, w2q5, ids, gw, E, H, F)
+
+
+def test_binding_router_checks():
+    import torch
+    lg = torch.zeros(3, 16, dtype=torch.float32)
+    _refuses("logits must be", qdm.moe_router_topk, lg.double(), 4)
+    _refuses(r"logits must be \[T\]\[E\]", qdm.moe_router_topk, lg[0], 4)
+    _refuses("ids must be", qdm.moe_router_topk, lg, 4, ids=torch.zeros(3, 4, dtype=torch.int64))
+    _refuses("ids must have shape", qdm.moe_router_topk, lg, 4,
+             ids=torch.zeros(3, 5, dtype=torch.int32))
+    T, E, k, H, F = 3, 16, 2, 256, 256
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    w13 = torch.zeros(qdm.packed_bytes("q4k", E * 2 * F, H), dtype=torch.uint8)
+    w2 = torch.zeros(qdm.packed_bytes("q4k", E * H, F), dtype=torch.uint8)
+    g = qdm.moe_grouped_gemm_from_logits
+    _refuses("router_logits must have shape", g, x, lg[:, :8], w13, w2, k, E, H, F)
+    _refuses("router_logits must be", g, x, lg.double(), w13, w2, k, E, H, F)
+    _refuses("x must have shape", g, x[:2], lg, w13, w2, k, E, H, F)
+    _refuses("down_qtype", g, x, lg, w13, w2, k, E, H, F, down_qtype=6)
+    _refuses("w_down holds", g, x, lg, w13, w2, k, E, H, F, down_qtype=5)
