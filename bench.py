@@ -130,6 +130,61 @@ def bench_probe(torch, qdm):
     return {"copy_bytes": nbytes, "ms": ms, "read_plus_write_GBps": 2 * nbytes / ms / 1e6}
 
 
+def _time_launches(torch, fn, reps):
+    """Mean per launch (ms) of reps back-to-back launches between two events."""
+    tm = Timer(torch)
+    fn(0)
+    torch.cuda.synchronize()
+    e0 = tm.event()
+    for i in range(reps):
+        fn(i)
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_roofs(torch, qdm):
+    """Measured roofs beside the nominal ones: a read-only stream from HBM
+    (1 GiB buffers, three of them in turn: 3 GiB between re-reads) and from the
+    last-level cache (one 64 MiB buffer re-read), back-to-back bf16 MFMAs on
+    every compute unit with the shader clock during the loop, and the cost of
+    an empty launch."""
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    big = 1 << 30
+    bufs = [torch.ones(big, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    ms_hbm = _time_launches(torch, lambda i: qdm.probe_read(bufs[i % 3], big, sink), 30)
+    del bufs
+    small = 64 << 20
+    buf = torch.ones(small, dtype=torch.uint8, device="cuda")
+    ms_mall = _time_launches(torch, lambda i: qdm.probe_read(buf, small, sink), 200)
+    reads = {}
+    for nb in (20 << 20, 100 << 20):  # the decode QKV and gate+up byte counts, HBM-cold
+        k = -(-(2 * MALL_BYTES) // nb) + 1
+        bs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(k)]
+        reads["%d_MiB" % (nb >> 20)] = _time_launches(
+            torch, lambda i: qdm.probe_read(bs[i % k], nb, sink), 10 * k) * 1e3
+        del bs
+    del buf
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 8192
+    clocks = torch.zeros(2 * wgs, dtype=torch.int64, device="cuda")
+    fsink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ms_mfma = _time_launches(torch, lambda i: qdm.probe_mfma(iters, wgs, fsink, clocks), 5)
+    ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    mhz = float(np.median(ck[:, 0] / ck[:, 1] * 100.0))
+    flops = wgs * 4 * iters * 8 * 32768.0
+    ms_empty = _time_launches(torch, lambda i: qdm.probe_empty(wgs), 2000)
+    return {"hbm_read_GBps": big / ms_hbm / 1e6, "mall_read_GBps": small / ms_mall / 1e6,
+            "read_us_by_size_hbm": reads,
+            "mfma_bf16_TFLOPs": flops / ms_mfma / 1e9,
+            "mfma_shader_clock_MHz": mhz,
+            "empty_launch_us": ms_empty * 1e3,
+            "notes": "read: qdm_probe_read; mfma: qdm_probe_mfma (%d workgroups x 4 waves x %d x 8 "
+                     "v_mfma_f32_32x32x16_bf16); clock = s_memtime / s_memrealtime ticks x "
+                     "100 MHz; empty: back-to-back launches of %d idle workgroups"
+                     % (wgs, iters, wgs)}
+
+
 def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
     """The headline: QKV, gate+up, down per step, rotating weight copies."""
     host_w, host_x, dev_x = {}, {}, {}
@@ -236,28 +291,36 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
 
     # Per-kernel launch duration: a batch of back-to-back launches of one
     # kernel through the C ABI with pre-marshalled arguments (the queue stays
-    # ahead of the GPU), bracketed by two events on the launch stream.
+    # ahead of the GPU), bracketed by two events on the launch stream. Each
+    # shape rotates over its own copies, at least twice the 256 MB last-level
+    # cache in total (25 for QKV, 6 for gate+up, 11 for down).
     stream = eager_stream
     kernels = {}
     nb = max(20, steps)
+    del graph
     for name, K, N in DECODE:
-        args = [(ctypes.c_void_p(dev_w[c][name].data_ptr()), ctypes.c_void_p(dev_x[name].data_ptr()),
+        shape_copies = copies_for(host_w[name].nbytes)
+        ws = [dev_w[c][name] for c in range(ncopy)]
+        ws += [ws[0].clone() for _ in range(max(0, shape_copies - ncopy))]
+        args = [(ctypes.c_void_p(wc.data_ptr()), ctypes.c_void_p(dev_x[name].data_ptr()),
                  qdm.QDM_BF16, ctypes.c_void_p(ys[name].data_ptr()), 1, N, K, stream)
-                for c in range(ncopy)]
+                for wc in ws]
+        nb_shape = max(nb, 2 * len(args))
         for a in args:
             lib.q4k_gemv(*a)
         k0 = tm.event()
-        for i in range(nb):
-            lib.q4k_gemv(*args[i % ncopy])
+        for i in range(nb_shape):
+            lib.q4k_gemv(*args[i % len(args)])
         k1 = tm.event()
         torch.cuda.synchronize()
-        ms = k0.elapsed_time(k1) / nb
+        ms = k0.elapsed_time(k1) / nb_shape
         b = gemv_bytes(N, K)
-        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb,
-                         "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
-                         "rel_err": errs[name]}
+        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb_shape,
+                         "copies": len(args), "GBps": b / ms / 1e6,
+                         "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS, "rel_err": errs[name]}
+        del ws, args
     step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
-    del graph, dev_w
+    del dev_w
     return {"ms_per_step": total_ms / steps, "step_bytes": step_bytes, "copies": ncopy,
             "GBps": step_bytes / (total_ms / steps) / 1e6,
             "median5_ms_per_step": median5_ms, "median5_GBps": step_bytes / median5_ms / 1e6,
@@ -354,7 +417,14 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
     E, H, F = 128, 2048, 768
     d = synth.moe(T, down_qtype=down_qtype)
     x, w13, w2 = to_dev_bf16(torch, d["x"]), to_dev(torch, d["w13"]), to_dev(torch, d["w2"])
-    sets = [(w13, w2), (w13.clone(), w2.clone())]
+    ids0 = d["ids"] if not from_logits else oracle.router_topk(synth.moe_router(T), 8)[0]
+    per_expert0 = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
+                                                                    else Q5K_BPB)
+    # Weight sets called in turn: the experts one call touches, times the
+    # number of sets, exceed 512 MB (twice the last-level cache), so every
+    # call reads its experts from HBM (T = 1: 25 sets, T = 8: 4, T = 512: 2).
+    nsets = max(2, -(-(2 * MALL_BYTES) // (len(np.unique(ids0)) * per_expert0)))
+    sets = [(w13, w2)] + [(w13.clone(), w2.clone()) for _ in range(nsets - 1)]
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     if from_logits:
         logits = synth.moe_router(T)
@@ -382,12 +452,14 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
     ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], ids_np[toks], gw_np[toks], E, H, F,
                      down_qtype)
     err = rel(y.cpu().numpy()[toks], ref)
-    for i in range(3):
-        run(*sets[i % 2])
+    del d
+    for i in range(len(sets)):
+        run(*sets[i])
+    reps = max(reps, 2 * len(sets))
     tm = Timer(torch)
     evs = [tm.event()]
     for i in range(reps):
-        run(*sets[i % 2])
+        run(*sets[i % len(sets)])
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
@@ -396,31 +468,34 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
     graph_ms = None
     if T <= 8:
         # Decode-sized calls are near the host's launch rate: also time them
-        # replayed from a graph (one call per weight copy), as a decode loop
+        # replayed from a graph (one call per weight set), as a decode loop
         # would run them. The replayed output must equal the eager one.
         eager_y = y.clone()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            run(*sets[0])
-            run(*sets[1])
+            for st in sets:
+                run(*st)
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(y, eager_y):
             raise RuntimeError("MoE graph replay differs from the eager result (T=%d)" % T)
+        greps = max(2, reps // len(sets))
         gt = Timer(torch)
         g0 = gt.event()
-        for _ in range(reps):
+        for _ in range(greps):
             graph.replay()
         g1 = gt.event()
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / (2 * reps)
+        graph_ms = g0.elapsed_time(g1) / (greps * len(sets))
+        del graph
     distinct = len(np.unique(ids_np))
     per_expert = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
                                                                    else Q5K_BPB)
     touched = distinct * per_expert + T * H * 2 + T * H * 4 + (T * E * 4 if from_logits else 0)
     flops = 2.0 * T * 8 * (2 * F * H + H * F)
     r = {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
-         "mean_ms": mean_ms,
+         "mean_ms": mean_ms, "weight_sets": len(sets),
+         "bytes_per_cycle": len(sets) * distinct * per_expert,
          "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
          "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
     if graph_ms is not None:
@@ -470,6 +545,82 @@ def cpu_baseline(oracle, synth, budget_s=10.0):
                       % (nsteps, dt)}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_per_config(oracle, synth):
+    """The oracle on one host core, per workload: direct where a call is short
+    (tiny, decode set, MoE T <= 8, Q6_K down), else from a timed 1/16 of the
+    output rows (tokens for the MoE) scaled by 16 (labelled extrapolated)."""
+    import ctypes.util
+    gomp = None
+    name = ctypes.util.find_library("gomp")
+    if name:
+        try:
+            gomp = ctypes.CDLL(name)
+        except OSError:
+            gomp = None
+    if gomp is not None:
+        gomp.omp_set_num_threads(1)
+
+    def timed(fn, min_s=0.2):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                return dt / n * 1e3
+
+    out = {}
+    w, x = synth.tiny_gemv()
+    out["tiny_q4k_gemv"] = {"ms": timed(lambda: oracle.q4k_matmul(w, x, 256, 256)),
+                            "how": "direct"}
+    dec = [(synth.decode_gemv(n), K, N) for n, K, N in DECODE]
+    out["decode_set_step"] = {"ms": timed(lambda: [oracle.q4k_matmul(a, b, N, K)
+                                                   for (a, b), K, N in dec]), "how": "direct"}
+    del dec
+    wg, xg = synth.prefill_gemm(512)
+    rows = 512 // 16
+    ms = timed(lambda: oracle.q4k_matmul(wg, xg[:rows], 17408, 5120), 0.0)
+    out["prefill_gemm_m512"] = {"ms": ms * 16, "how": "extrapolated: %d of 512 rows x 16" % rows}
+    out["prefill_gemm_m4096"] = {"ms": ms * 128,
+                                 "how": "extrapolated: %d rows x 128 (same per-row cost)" % rows}
+    del wg, xg
+    for T in (1, 8):
+        d = synth.moe(T)
+        out["moe_t%d" % T] = {"ms": timed(lambda: oracle.moe(d["x"], d["w13"], d["w2"], d["ids"],
+                                                             d["gw"], 128, 2048, 768, 4)),
+                              "how": "direct"}
+    d = synth.moe(512)
+    sel = np.arange(0, 512, 16)
+    ms = timed(lambda: oracle.moe(d["x"][sel], d["w13"], d["w2"], d["ids"][sel], d["gw"][sel],
+                                  128, 2048, 768, 4), 0.0)
+    out["moe_t512"] = {"ms": ms * 16, "how": "extrapolated: 32 of 512 tokens x 16"}
+    del d
+    for M in (1, 8):
+        w6, x6 = synth.q6k_gemv("head", M)
+        n16 = 151936 // 16
+        ms = timed(lambda: oracle.q6k_matmul(w6[:n16], x6, n16, 5120), 0.0)
+        out["q6k_head_m%d" % M] = {"ms": ms * 16, "how": "extrapolated: 1/16 of the rows x 16"}
+    del w6, x6
+    w6, x6 = synth.q6k_gemv("down", 1)
+    out["q6k_down_m1"] = {"ms": timed(lambda: oracle.q6k_matmul(w6, x6, 5120, 17408)),
+                          "how": "direct"}
+    if gomp is not None:
+        gomp.omp_set_num_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    return {"threads": 1 if gomp is not None else None, "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(), "kind": "oracle", "configs": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,9 +649,12 @@ def main():
     log("device:", dev_name)
 
     extra = {}
+    measured_roofs = None
     if "probe" in sections:
         extra["probe_copy"] = bench_probe(torch, qdm)
         log("probe copy:", extra["probe_copy"])
+        measured_roofs = bench_roofs(torch, qdm)
+        log("measured roofs:", measured_roofs)
     dec = bench_decode(torch, qdm, synth, oracle, args.steps, args.warmup, "graph" in sections)
     log("decode: %.1f GB/s per step (eager), graph replay: %s GB/s" % (dec["GBps"], dec["graph_GBps"]))
     if "gemm" in sections:
@@ -560,6 +714,8 @@ def main():
     if "cpu" in sections:
         cpu = cpu_baseline(oracle, synth)
         log("cpu baseline:", cpu)
+        extra["cpu_oracle_per_config"] = cpu_oracle_per_config(oracle, synth)
+        log("cpu oracle per config:", extra["cpu_oracle_per_config"])
     else:
         cpu = None
     rec = {"metric": METRIC, "value": dec["GBps"], "unit": "GB/s", "n_gpus": 1,
@@ -571,7 +727,8 @@ def main():
                                   "(one step = the three calls launched back to back; %d "
                                   "rotating weight copies)" % dec["copies"],
                       "frac_hbm_peak": dec["GBps"] / HBM_PEAK_GBS, "device": dev_name},
-           "roofline": roofline, "cpu_baseline": cpu, "decode_kernels": dec["kernels"],
+           "roofline": roofline, "cpu_baseline": cpu, "measured_roofs": measured_roofs,
+           "decode_kernels": dec["kernels"],
            "decode_median_of_5": {"ms_per_step": dec["median5_ms_per_step"],
                                   "GBps": dec["median5_GBps"],
                                   "protocol": "7 repetitions of 20 steps, 2 discarded"},

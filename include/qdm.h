@@ -281,6 +281,27 @@ int moe_grouped_gemm_from_logits(const void *x, const float *router_logits,
  */
 int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void *stream);
 
+/*
+ * Roofline probes (the same source: measured roofs beside the nominal ones).
+ * qdm_probe_read: reads the n_bytes of src once (n_bytes % 16 == 0, src
+ *   16-byte aligned), a read-only HBM (or, for a buffer re-read while it fits
+ *   the 256 MB last-level cache, cache) stream; sink is a 4-byte device word
+ *   the kernel may write (so no load can be dropped).
+ * qdm_probe_mfma: `workgroups` workgroups of four waves, each wave issuing
+ *   iters x 8 back-to-back bf16 MFMAs of 32 x 32 x 16 (32768 flops each);
+ *   1 <= iters <= 2^24, 1 <= workgroups <= 65536. clocks (8-byte aligned,
+ *   2 * workgroups uint64) receives per workgroup the shader-clock and the
+ *   100 MHz reference-clock ticks of its first wave's loop (their ratio is the
+ *   shader clock under MFMA load); sink is a 4-byte device word as above.
+ * qdm_probe_empty: a launch of `workgroups` workgroups that do nothing (the
+ *   per-launch cost), 1 <= workgroups <= 65536.
+ * Status codes as elsewhere (NULL, size, alignment checked first).
+ */
+int qdm_probe_read(const void *src, int64_t n_bytes, void *sink, void *stream);
+int qdm_probe_mfma(int64_t iters, int64_t workgroups, float *sink, uint64_t *clocks,
+                   void *stream);
+int qdm_probe_empty(int64_t workgroups, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,14 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm_from_logits.restype = i32
         L.qdm_probe_copy.argtypes = [p, p, i64, p]
         L.qdm_probe_copy.restype = i32
+        L.qdm_probe_read.argtypes = [p, i64, p, p]
+        L.qdm_probe_read.restype = i32
+        L.qdm_probe_mfma.argtypes = [i64, i64, p, p, p]
+        L.qdm_probe_mfma.restype = i32
+        L.qdm_probe_empty.argtypes = [i64, p]
+        L.qdm_probe_empty.restype = i32
+        L.qdm_set_gemm_spin_limit.argtypes = [ctypes.c_uint32]
+        L.qdm_set_gemm_spin_limit.restype = i32
         _lib = L
     return _lib
 
@@ -428,3 +436,23 @@ def probe_copy(src, dst, n_bytes: int, stream=None):
         raise ValueError("src and dst must hold n_bytes")
     _check("qdm_probe_copy", lib().qdm_probe_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"),
                                                   n_bytes, _stream(stream)))
+
+
+def probe_read(src, n_bytes: int, sink, stream=None):
+    if _nbytes(src) < n_bytes or _nbytes(sink) < 4:
+        raise ValueError("src must hold n_bytes and sink 4 bytes")
+    _check("qdm_probe_read", lib().qdm_probe_read(_dev_ptr(src, "src"), n_bytes,
+                                                  _dev_ptr(sink, "sink"), _stream(stream)))
+
+
+def probe_mfma(iters: int, workgroups: int, sink, clocks, stream=None):
+    torch = _torch()
+    _need_dtype(clocks, "clocks", torch.int64)
+    if clocks.numel() < 2 * workgroups or _nbytes(sink) < 4:
+        raise ValueError("clocks must hold 2 * workgroups values and sink 4 bytes")
+    _check("qdm_probe_mfma", lib().qdm_probe_mfma(iters, workgroups, _dev_ptr(sink, "sink"),
+                                                  _dev_ptr(clocks, "clocks"), _stream(stream)))
+
+
+def probe_empty(workgroups: int, stream=None):
+    _check("qdm_probe_empty", lib().qdm_probe_empty(workgroups, _stream(stream)))

@@ -241,3 +241,27 @@ QDM_EXPORT int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void 
   qdm::launch_probe_copy(src, dst, n_bytes, (hipStream_t)stream);
   return finish_launch();
 }
+
+QDM_EXPORT int qdm_probe_read(const void *src, int64_t n_bytes, void *sink, void *stream) {
+  if (!src || !sink) return QDM_ERR_NULL;
+  if (n_bytes < 16 || n_bytes % 16) return QDM_ERR_SHAPE;
+  if (misaligned(src) || misaligned4(sink)) return QDM_ERR_ALIGN;
+  qdm::launch_probe_read(src, n_bytes, (uint32_t *)sink, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int qdm_probe_mfma(int64_t iters, int64_t workgroups, float *sink, uint64_t *clocks,
+                              void *stream) {
+  if (!sink || !clocks) return QDM_ERR_NULL;
+  if (iters < 1 || iters > (1 << 24) || workgroups < 1 || workgroups > (1 << 16))
+    return QDM_ERR_SHAPE;
+  if (misaligned4(sink) || ((uintptr_t)clocks & 7u)) return QDM_ERR_ALIGN;
+  qdm::launch_probe_mfma(iters, workgroups, sink, clocks, (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int qdm_probe_empty(int64_t workgroups, void *stream) {
+  if (workgroups < 1 || workgroups > (1 << 16)) return QDM_ERR_SHAPE;
+  qdm::launch_probe_empty(workgroups, (hipStream_t)stream);
+  return finish_launch();
+}

@@ -50,5 +50,9 @@ void launch_moe_from_logits(const void *x, const float *logits, const void *w13,
                             int64_t H, int64_t F, void *workspace, hipStream_t s);
 
 void launch_probe_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t s);
+void launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, hipStream_t s);
+void launch_probe_mfma(int64_t iters, int64_t workgroups, float *sink, uint64_t *clocks,
+                       hipStream_t s);
+void launch_probe_empty(int64_t workgroups, hipStream_t s);
 
 }  // namespace qdm

@@ -152,6 +152,18 @@ def test_probe_validation():
     assert L.qdm_probe_copy(MIS, A2, 1024, NUL) == EALIGN
 
 
+def test_probe_roof_validation():
+    L = qdm.lib()
+    assert L.qdm_probe_read(NUL, 1024, A2, NUL) == ENULL
+    assert L.qdm_probe_read(A, 1000, A2, NUL) == ESHAPE
+    assert L.qdm_probe_read(MIS, 1024, A2, NUL) == EALIGN
+    assert L.qdm_probe_mfma(10, 4, NUL, A2, NUL) == ENULL
+    assert L.qdm_probe_mfma(0, 4, A, A2, NUL) == ESHAPE
+    assert L.qdm_probe_mfma(10, 0, A, A2, NUL) == ESHAPE
+    assert L.qdm_probe_mfma(10, 4, A, ctypes.c_void_p((1 << 20) + 4), NUL) == EALIGN
+    assert L.qdm_probe_empty(0, NUL) == ESHAPE
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     w = torch.zeros(144, dtype=torch.uint8)

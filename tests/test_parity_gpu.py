@@ -971,6 +971,27 @@ def test_determinism_all_entry_points():
 
 
 # --------------------------------------------------------------------------
+# roofline probes: they run, and report plausible clocks
+# --------------------------------------------------------------------------
+
+def test_probes_run():
+    say("probe read / mfma / empty")
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    qdm.probe_read(buf, 1 << 20, sink)
+    clocks = torch.zeros(2 * 8, dtype=torch.int64, device="cuda")
+    fsink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    qdm.probe_mfma(64, 8, fsink, clocks)
+    qdm.probe_empty(8)
+    ck = host(clocks).reshape(8, 2).astype(np.float64)
+    assert (ck > 0).all()
+    mhz = ck[:, 0] / ck[:, 1] * 100.0
+    say("  shader clock under MFMA, MHz:", mhz)
+    assert ((mhz > 100) & (mhz < 5000)).all()
+    assert host(fsink)[0] == 0.0
+
+
+# --------------------------------------------------------------------------
 # HIP graph capture and replay of a decode step
 # --------------------------------------------------------------------------
 
