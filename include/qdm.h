@@ -76,6 +76,10 @@ extern "C" {
 #define QDM_ERR_DTYPE (-4)     /* unknown or unsupported activation dtype or weight type */
 #define QDM_ERR_WORKSPACE (-5) /* workspace missing or too small */
 #define QDM_ERR_HIP (-6)       /* the HIP runtime reported an error */
+#define QDM_ERR_SCRATCH (-7)   /* more scratch than moe_q4k_grouped_gemm_noalloc holds */
+
+/* Bytes of the static scratch array behind moe_q4k_grouped_gemm_noalloc. */
+#define QDM_MOE_SCRATCH_BYTES (16u << 20)
 
 /* Human-readable text for a status code (static storage). */
 const char *qdm_status_string(int status);
@@ -225,6 +229,25 @@ int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const void *w_dow
                          const int32_t *topk_ids, const float *topk_w, float *y,
                          int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_q4k_grouped_gemm_noalloc: moe_q4k_grouped_gemm for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments and results without the workspace: the
+ * call's workspace lives in a static device array of QDM_MOE_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends. A
+ * call whose moe_q4k_workspace_bytes(T, E, top_k, H, F) exceeds it returns
+ * QDM_ERR_SCRATCH and enqueues nothing (at H = 2048, F = 768, top-8 that is
+ * above 160 tokens). The call allocates and frees nothing. All calls on one
+ * GPU share its array: two calls that overlap in time on one GPU (different
+ * streams) race and give wrong results; calls in stream order are safe. The
+ * stream must belong to the current device. The skipped-id count is kept in
+ * the array and not exposed.
+ */
+int moe_q4k_grouped_gemm_noalloc(const void *x, const void *w_gate_up, const void *w_down,
+                                 const int32_t *topk_ids, const float *topk_w, float *y,
+                                 int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F,
+                                 void *stream);
 
 /*
  * moe_q4k_q5k_grouped_gemm: the same routed MoE FFN with Q4_K gate+up experts

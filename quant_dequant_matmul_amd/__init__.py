@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p, sz, p]
             f.restype = i32
+        L.moe_q4k_grouped_gemm_noalloc.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p]
+        L.moe_q4k_grouped_gemm_noalloc.restype = i32
         L.moe_router_topk.argtypes = [p, i64, i64, i64, p, p, p]
         L.moe_router_topk.restype = i32
         L.moe_from_logits_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -381,6 +383,29 @@ def moe_q4k_q5k_grouped_gemm(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: 
     """The same routed MoE FFN with Q4_K gate+up experts and Q5_K down experts."""
     return _moe("moe_q4k_q5k_grouped_gemm", "q5k", x, w_gate_up, w_down, topk_ids, topk_w, E, H,
                 F, y, workspace, stream)
+
+
+def moe_q4k_grouped_gemm_noalloc(x, w_gate_up, w_down, topk_ids, topk_w, E: int, H: int,
+                                 F: int, y=None, stream=None):
+    """moe_q4k_grouped_gemm with its workspace in the library's static device
+    scratch (no allocation by the library; calls overlapping on one GPU race)."""
+    torch = _torch()
+    _need_dtype(topk_ids, "topk_ids", torch.int32)
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T][top_k], got %s" % (tuple(topk_ids.shape),))
+    T, top_k = topk_ids.shape
+    _need_dtype(topk_w, "topk_w", torch.float32)
+    _need_shape(topk_w, "topk_w", (T, top_k))
+    _need_dtype(x, "x", torch.bfloat16)
+    _need_shape(x, "x", (T, H))
+    _moe_weights(w_gate_up, w_down, E, H, F, "q4k")
+    _need_gpu(x=x, w_gate_up=w_gate_up, w_down=w_down, topk_ids=topk_ids, topk_w=topk_w)
+    y = _out(y, (T, H), x.device)
+    _check("moe_q4k_grouped_gemm_noalloc", lib().moe_q4k_grouped_gemm_noalloc(
+        _dev_ptr(x, "x"), _dev_ptr(w_gate_up, "w_gate_up"), _dev_ptr(w_down, "w_down"),
+        _dev_ptr(topk_ids, "topk_ids"), _dev_ptr(topk_w, "topk_w"), _dev_ptr(y, "y"),
+        T, E, top_k, H, F, _stream(stream)))
+    return y
 
 
 def moe_router_topk(logits, top_k: int, ids=None, weights=None, stream=None):

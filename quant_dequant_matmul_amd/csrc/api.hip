@@ -37,6 +37,7 @@ QDM_EXPORT const char *qdm_status_string(int status) {
     case QDM_ERR_DTYPE: return "unsupported activation dtype or weight type";
     case QDM_ERR_WORKSPACE: return "workspace missing or too small";
     case QDM_ERR_HIP: return "HIP runtime error at launch";
+    case QDM_ERR_SCRATCH: return "the call needs more scratch than the static array holds";
     default: return "unknown status";
   }
 }
@@ -179,6 +180,24 @@ QDM_EXPORT int moe_q4k_grouped_gemm(const void *x, const void *w_gate_up, const 
   if (rc) return rc;
   qdm::launch_moe_q4k(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F, workspace,
                       (hipStream_t)stream);
+  return finish_launch();
+}
+
+QDM_EXPORT int moe_q4k_grouped_gemm_noalloc(const void *x, const void *w_gate_up,
+                                            const void *w_down, const int32_t *topk_ids,
+                                            const float *topk_w, float *y, int64_t T, int64_t E,
+                                            int64_t top_k, int64_t H, int64_t F, void *stream) {
+  if (!topk_ids || !topk_w) return QDM_ERR_NULL;
+  // the argument checks of moe_q4k_grouped_gemm, with a stand-in for the
+  // workspace (its size is checked against the scratch array just below)
+  const int rc = check_moe(x, w_gate_up, w_down, y, T, E, top_k, H, F, (void *)x,
+                           qdm::moe_workspace(T, E, top_k, H, F));
+  if (rc) return rc;
+  if (qdm::moe_workspace(T, E, top_k, H, F) > qdm::MOE_SCRATCH_BYTES) return QDM_ERR_SCRATCH;
+  void *ptr = qdm::moe_scratch_ptr();
+  if (!ptr) return QDM_ERR_HIP;
+  qdm::launch_moe_q4k_scratch(x, w_gate_up, w_down, topk_ids, topk_w, y, T, E, top_k, H, F, ptr,
+                              (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -35,6 +35,14 @@ void launch_q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t 
                      void *workspace, hipStream_t s);
 
 size_t moe_workspace(int64_t T, int64_t E, int64_t top_k, int64_t H, int64_t F);
+// Bytes of the static scratch array behind moe_q4k_grouped_gemm_noalloc.
+constexpr size_t MOE_SCRATCH_BYTES = (size_t)16 << 20;
+// The current device's copy of that array (looked up once per device), or
+// nullptr if the runtime could not provide it.
+void *moe_scratch_ptr();
+void launch_moe_q4k_scratch(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                            const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
+                            int64_t H, int64_t F, void *scratch_ptr, hipStream_t s);
 void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_t *ids,
                     const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                     int64_t F, void *workspace, hipStream_t s);

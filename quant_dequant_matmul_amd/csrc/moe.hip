@@ -30,9 +30,17 @@
 //  3. down: workgroup (row tile of 256, e): W2[e] rows times the h rows of
 //     e's entries -> o[entry][r], fp32.
 //  4. combine as above.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "q4k_tile.h"
+
+// Scratch of the no-allocation MoE entry point: the workspace of one call
+// lives in this device array (every GPU the library runs on holds its own copy
+// until the process ends). Host code never uses the array's name as an
+// address: it takes each device's copy through hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[qdm::MOE_SCRATCH_BYTES];
 
 namespace qdm {
 
@@ -1002,6 +1010,28 @@ void launch_moe_q4k(const void *x, const void *w13, const void *w2, const int32_
                     const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                     int64_t F, void *workspace, hipStream_t s) {
   launch_moe<false>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, workspace, s);
+}
+
+// This device's copy of the scratch array, looked up once per device (with
+// that device current) and kept; nullptr if the lookup failed.
+void *moe_scratch_ptr() {
+  static std::mutex mu;
+  static void *ptr[64] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+void launch_moe_q4k_scratch(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                            const float *gw, float *y, int64_t T, int64_t E, int64_t top_k,
+                            int64_t H, int64_t F, void *scratch_ptr, hipStream_t s) {
+  launch_moe<false>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, scratch_ptr, s);
 }
 
 void launch_moe_q4k_q5k(const void *x, const void *w13, const void *w2, const int32_t *ids,
