@@ -155,13 +155,15 @@ int q80_gemv(const void *w, const void *x, int x_dtype, float *y,
  * x is bf16 [M][K] (read only); the Q4_K weights w [N][K/256] (read only) are
  * decoded in fp32 and rounded to bf16 (nearest even) before the
  * bf16 x bf16 -> fp32 MFMA contraction; y is fp32 [M][N], fully overwritten.
- * M >= 1, N >= 1, K >= 256, K % 256 == 0 (else QDM_ERR_SHAPE).
- * With at least as many 256 x 256 tiles as compute units, the tile x K
- * iteration space is split evenly over one workgroup per compute unit, and a
- * tile computed by several workgroups is summed in a fixed order (results are
- * deterministic); with fewer tiles each tile is one workgroup.
+ * M >= 1, 1 <= N <= 2^20, K >= 256, K % 256 == 0 (else QDM_ERR_SHAPE).
+ * When that gives every compute unit at least two of the K/128 stage pairs,
+ * the 256 x 256 tiles x K iteration space is split evenly over one workgroup
+ * per compute unit, and a tile computed by several workgroups is summed in a
+ * fixed order (results are deterministic); otherwise each tile is one
+ * workgroup.
  * workspace: q4k_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, on the
- * device of the call; 0 bytes (workspace may be NULL) when no tile is split.
+ * device of the call; 0 bytes (workspace may be NULL) when no tile is split
+ * (few tiles and short K).
  * Otherwise: a 256-byte status block, a flag word per workgroup, then one fp32
  * 256 x 256 partial tile per workgroup (a too-small or NULL workspace gives
  * QDM_ERR_WORKSPACE). It must be zero-filled before its first use; every call

@@ -127,7 +127,8 @@ QDM_EXPORT size_t q4k_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 QDM_EXPORT int q4k_gemm(const void *w, const void *x, float *y, int64_t M, int64_t N,
                         int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
   if (!w || !x || !y) return QDM_ERR_NULL;
-  if (M < 1 || M > INT32_MAX || N < 1 || N > INT32_MAX || bad_k(K) || K > INT32_MAX ||
+  // N <= 2^20: 256 rows of y are addressed with 32-bit offsets
+  if (M < 1 || M > INT32_MAX || N < 1 || N > (1 << 20) || bad_k(K) || K > INT32_MAX ||
       ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX)
     return QDM_ERR_SHAPE;
   if (misaligned(w) || misaligned(x) || misaligned(y)) return QDM_ERR_ALIGN;

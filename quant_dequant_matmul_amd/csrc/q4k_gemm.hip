@@ -45,11 +45,10 @@
 // computes the last stage pair of a tile owns it. A contributor (a unit that
 // computed earlier pairs of the tile) leaves its fp32 partial tile in the
 // workspace in the accumulators' own register order, so its stores and the
-// owner's loads are whole 4 KiB lines per instruction. The owner writes its
-// accumulators into LDS, half a tile at a time, adds there the partials of the
-// contributors (always units with a smaller index, in decreasing index order,
-// so the sum is deterministic), and stores y from LDS in 16-byte pieces of
-// rows; a tile with no contributor goes from the accumulators straight to y. A
+// owner's loads are whole 4 KiB lines per instruction. The owner adds the
+// partials of the contributors (always units with a smaller index, in
+// decreasing index order, so the sum is deterministic) to its accumulators a
+// quarter tile at a time in registers and stores y as a whole tile is stored. A
 // contributor writes its partial, fences at device scope and raises its flag;
 // the owner waits on the flag (bounded), reads the partial and lowers the flag
 // again, so the workspace flags are zero between calls. Workgroups start in
@@ -285,6 +284,18 @@ __device__ __forceinline__ void raise_flag(uint32_t *flag) {
     __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Makes this workgroup's partial tile visible to the other XCDs and raises
+// its flag: every thread waits for its own stores to reach the L2, then one
+// release (an L2 write-back, no invalidate) precedes the flag. A device-wide
+// fence in every thread would also invalidate the L2 that the other compute
+// units of the XCD read x and the weights through (measured: M = 512 split over
+// 256 units 152 -> 126 us without it).
+__device__ __forceinline__ void publish_partial(uint32_t *flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) raise_flag(flag);
+}
+
 // Multiplies stage range [s0, s1) (s1 - s0 even, >= 2) of tile (m0, n0) into acc.
 __device__ __forceinline__ void run_segment(f32x16 (&acc)[8][2], uint16_t *smem,
                                             const uint8_t *__restrict__ w,
@@ -333,13 +344,7 @@ __device__ __forceinline__ void run_segment(f32x16 (&acc)[8][2], uint16_t *smem,
     // odd stage s+1: codes wb, x in sx1; x of s+2 (xa) into sx0; loads of s+3 into xb, wb
     gemm_stage(acc, bf, scb, sca, wb, wa, min(s + 2, last), min(s + 3, last), xa, xb, sx1, sx0,
                lo, live, xtile, wtile, M, m0, lane);
-    if (publish != nullptr && s == s0) {
-      // the partial tile stored before this segment has long been written:
-      // make it visible device-wide and raise its flag
-      __threadfence();
-      __syncthreads();
-      if (threadIdx.x == 0) raise_flag(publish);
-    }
+    if (publish != nullptr && s == s0) publish_partial(publish);
   }
 }
 
@@ -366,94 +371,95 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[8][2], float *
                   acc[i][j][4 * q + 3]};
 }
 
-// y tile store straight from the accumulators (a tile no other unit worked
-// on): each lane writes its 32-column runs of rows; rows and columns past M, N
-// skipped.
+// y stores go through a buffer resource over the tile's rows: the lane's
+// column (and lane-half row offset) is the vector offset and each row's
+// offset is a scalar, so a store costs no vector address arithmetic; bytes
+// past the tile's last valid row (rows past M) are dropped by the hardware's
+// range check, and lanes whose column is past N are masked. The host limits
+// N to 2^20, so 256 rows of y stay within 2^31 bytes.
+constexpr int BUF_DWORD3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+
+struct YOut {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff;     // (lane-half row offset * ldy + column) * 4 for this lane, column tile 0
+  int ldy4;     // ldy * 4
+  bool live0, live1;  // column tile 0 / 1 of this lane inside N
+};
+
+__device__ __forceinline__ YOut y_out(float *yt, int ldy, int rows, int cols) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = WAVE_ROWS * wave + (lane & 31), rq = 4 * (lane >> 5);
+  YOut o;
+  o.rsrc = __builtin_amdgcn_make_buffer_rsrc(yt, (short)0, min(rows, BM) * ldy * 4, BUF_DWORD3);
+  o.voff = (rq * ldy + col) * 4;
+  o.ldy4 = ldy * 4;
+  o.live0 = col < cols;
+  o.live1 = col + 32 < cols;
+  return o;
+}
+
+// Value v (accumulator index 0..15) of MFMA tile (i, j): row
+// i*32 + 8*(v/4) + (lane-half offset) + v%4, column j*32 + (lane column).
+__device__ __forceinline__ void y_put(const YOut &o, float val, int i, int j, int v) {
+  if (j == 0 ? o.live0 : o.live1)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), o.rsrc,
+                                          o.voff + j * 128,
+                                          (i * 32 + 8 * (v >> 2) + (v & 3)) * o.ldy4, 0);
+}
+
+// A tile no other unit worked on: straight from the accumulators.
 __device__ __forceinline__ void store_direct(const f32x16 (&acc)[8][2], float *yt, int ldy,
                                              int rows, int cols) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // lane coordinates pass through an opaque move, so the per-element address
-  // arithmetic is not hoisted out of the tile loop (where it would hold a
-  // register per element for the whole kernel)
-  int col = WAVE_ROWS * wave + (lane & 31), rq = 4 * (lane >> 5);
-  asm volatile("" : "+v"(col), "+v"(rq));
+  const YOut o = y_out(yt, ldy, rows, cols);
 #pragma unroll
   for (int i = 0; i < 8; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = j * 32 + col;
+    for (int j = 0; j < 2; j++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int r = i * 32 + 8 * (v >> 2) + rq + (v & 3);
-        if (r < rows && c < cols) yt[(int64_t)r * ldy + c] = acc[i][j][v];
-      }
-    }
+      for (int v = 0; v < 16; v++) y_put(o, acc[i][j][v], i, j, v);
 }
 
-// y tile store through LDS (a tile with contributors): the two 128-row halves
-// of the tile in turn are written into LDS by every wave (row tiles 4h..4h+3),
-// plus the partial tiles of the contributors (each thread adds the values at
-// its own accumulator positions, contributor by contributor in a fixed order),
-// then every thread writes whole 16-byte pieces of rows to y (rows and columns
-// past M, N skipped).
-constexpr int EPI_LD = BN + 4;  // floats per LDS row (16 bytes of bank padding)
-
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[8][2], float *yt, int ldy,
-                                           int rows, int cols, uint16_t *smem, bool vec,
-                                           bool bad, const float *__restrict__ part0,
-                                           int nparts) {
-  float *st = (float *)smem;  // [128][EPI_LD]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// A tile with contributors: its y values are the owner's accumulators plus
+// the contributors' partial tiles (stored in accumulator order, so thread t
+// finds its own values as whole 16-byte pieces), added in a fixed order (the
+// owner's, then unit - 1, unit - 2, ...: deterministic). A quarter of the tile
+// (two row tiles, 64 values per thread) at a time: the sums live in registers
+// beside the accumulators, which are only read, and the quarter goes out as
+// store_direct writes a whole tile. A tile whose partial never arrived is
+// written as NaN.
+__device__ __forceinline__ void store_summed(const f32x16 (&acc)[8][2], float *yt, int ldy,
+                                             int rows, int cols, const float *__restrict__ part0,
+                                             int nparts, bool poison) {
+  const YOut o = y_out(yt, ldy, rows, cols);
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
-    __syncthreads();  // the LDS is free (MFMAs done / previous half written out)
-    {
-      // lane coordinates pass through an opaque move so the per-element
-      // address arithmetic is not hoisted (it would pin a register per element)
-      int col = WAVE_ROWS * wave + (lane & 31), rq = 4 * (lane >> 5);
-      asm volatile("" : "+v"(col), "+v"(rq));
+  for (int qt = 0; qt < 4; qt++) {
+    f32x4 sum[16];
 #pragma unroll
-      for (int ii = 0; ii < 4; ii++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-          for (int v = 0; v < 16; v++)
-            st[(ii * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] =
-                acc[4 * h + ii][j][v];
-      for (int k = 0; k < nparts; k++) {
-        const f32x4 *src = (const f32x4 *)(part0 - (size_t)k * BM * BN);
-#pragma unroll
-        for (int ii = 0; ii < 4; ii++)
-#pragma unroll
-          for (int j = 0; j < 2; j++) {
-            int off = ((4 * h + ii) * 2 + j) * 4 * GEMM_THREADS + (int)threadIdx.x;
-            asm volatile("" : "+v"(off));
-            f32x4 t[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) t[q] = src[off + q * GEMM_THREADS];
-#pragma unroll
-            for (int v = 0; v < 16; v++)
-              st[(ii * 32 + 8 * (v >> 2) + rq + (v & 3)) * EPI_LD + j * 32 + col] +=
-                  t[v >> 2][v & 3];
-          }
-      }
+    for (int gg = 0; gg < 16; gg++) {
+      const int i = 2 * qt + (gg >> 3), j = (gg >> 2) & 1, v0 = 4 * (gg & 3);
+      sum[gg] = f32x4{acc[i][j][v0], acc[i][j][v0 + 1], acc[i][j][v0 + 2], acc[i][j][v0 + 3]};
     }
-    __syncthreads();
-    // 128 rows x 64 pieces of 16 bytes, 32 per thread
-    for (int e = threadIdx.x; e < 128 * (BN / 4); e += GEMM_THREADS) {
-      const int r = e / (BN / 4), c = 4 * (e % (BN / 4));
-      const int gr = 128 * h + r;
-      if (gr >= rows) continue;
-      f32x4 v = *(const f32x4 *)(st + r * EPI_LD + c);
-      if (bad) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      float *py = yt + (int64_t)gr * ldy + c;
-      if (vec && c + 3 < cols) {
-        *(f32x4 *)py = v;
-      } else {
+    for (int k = 0; k < nparts; k++) {
+      const f32x4 *src = (const f32x4 *)(part0 - (size_t)k * BM * BN) + t;
+      f32x4 p[16];
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-          if (c + q < cols) py[q] = v[q];
-      }
+      for (int gg = 0; gg < 16; gg++) p[gg] = src[(16 * qt + gg) * GEMM_THREADS];
+#pragma unroll
+      for (int gg = 0; gg < 16; gg++) sum[gg] += p[gg];
+    }
+    if (poison) {
+#pragma unroll
+      for (int gg = 0; gg < 16; gg++)
+        sum[gg] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                        __builtin_nanf("")};
+    }
+#pragma unroll
+    for (int gg = 0; gg < 16; gg++) {
+      const int i = 2 * qt + (gg >> 3), j = (gg >> 2) & 1, q = gg & 3;
+#pragma unroll
+      for (int e = 0; e < 4; e++) y_put(o, sum[gg][e], i, j, 4 * q + e);
     }
   }
 }
@@ -462,8 +468,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, int M,
     int N, int K, float *__restrict__ partials, uint32_t *__restrict__ flags,
     uint32_t *__restrict__ status, int units, uint32_t spin_limit) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // x stage buffer p at smem + p*XTILE; the LDS store of a split tile reuses it
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];  // x stage buffer p at smem + p*XTILE
   __shared__ uint32_t timed_out;
 
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -512,7 +517,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
       uint32_t spins = 0;
       bool lost = false;
       for (int u = unit - 1; u >= lowest; u--) {
-        while (__hip_atomic_load(&flags[u], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+        // relaxed polls (an acquire load would invalidate the L2 on every poll)
+        while (__hip_atomic_load(&flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
                ++spins < spin_limit)
           __builtin_amdgcn_s_sleep(2);
         uint32_t seen = 0u;
@@ -527,25 +533,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
       }
       timed_out = lost;
       if (lost) atomicAdd(status, 1u);
+      // one acquire for the partials seen (drops stale cached copies of them)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const bool bad = timed_out != 0u;  // a partial that never arrived poisons the tile
-    store_tile(acc, yt, N, M - m0, N - n0, smem, (N & 3) == 0, bad,
-               partials + (size_t)(unit - 1) * BM * BN, unit - lowest);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    store_summed(acc, yt, N, M - m0, N - n0, partials + (size_t)(unit - 1) * BM * BN,
+                 unit - lowest, timed_out != 0u);
   }
-  if (pending != nullptr) {  // the last segment left a partial: publish it now
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) raise_flag(pending);
-  }
+  if (pending != nullptr) publish_partial(pending);  // the last segment left a partial
 }
 
-// Dynamic LDS: two x stage buffers (73728 bytes), or the 128-row fp32 staging
-// of a split tile's store (133120 bytes), whichever is larger.
-constexpr size_t GEMM_LDS_MAIN = 2 * XTILE * sizeof(uint16_t);
-constexpr size_t GEMM_LDS_EPI = 128 * EPI_LD * sizeof(float);
-constexpr size_t GEMM_LDS = GEMM_LDS_MAIN > GEMM_LDS_EPI ? GEMM_LDS_MAIN : GEMM_LDS_EPI;
+// Dynamic LDS: two x stage buffers (73728 bytes).
+constexpr size_t GEMM_LDS = 2 * XTILE * sizeof(uint16_t);
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -564,18 +564,20 @@ int device_units() {
   return cached[dev];
 }
 
-// Workgroups of a call. With fewer tiles than compute units, one workgroup
-// per tile: splitting them costs more in partial-tile traffic and in clock
-// (every unit busy) than the idle units leave on the table (measured at
-// M = 512, N = 17408, K = 5120: 136 tiles, 166 us whole versus 190 us split).
-// With at least as many tiles as units, the stream-K split evens out the
-// last wave of tiles.
+// Workgroups of a call: the stream-K split over one workgroup per compute
+// unit when there are at least as many tiles as units, or when the split
+// gives every unit at least two stage pairs and no tile more than 16 units
+// (an owner adds its contributors' partial tiles one after another). With
+// fewer tiles than units this puts the idle units to work (M = 512,
+// N = 17408, K = 5120: 136 tiles, 140 -> 122 us). Otherwise one workgroup per
+// tile.
 int gemm_units(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t cus = device_units();
-  if (tiles < cus) return (int)tiles;
   const int64_t total = tiles * (K / (2 * BK));
-  return (int)(total < cus ? total : cus);
+  if (tiles >= cus || (total >= 2 * cus && 16 * tiles >= cus))
+    return (int)(total < cus ? total : cus);
+  return (int)tiles;
 }
 
 // Whether a call splits tiles between workgroups (then it needs the flags and

@@ -176,10 +176,13 @@ def test_gemm_workspace_only_when_tiles_split():
     """Whole-tile calls (fewer 256 x 256 tiles than compute units) need no
     workspace; split calls need the status block, flags and partial tiles."""
     L = qdm.lib()
-    assert L.q4k_gemm_workspace_bytes(512, 17408, 5120) == 0  # 136 tiles
-    need = L.q4k_gemm_workspace_bytes(4096, 17408, 5120)       # 1088 tiles
-    assert need >= 256 + 256 * 256 * 256 * 4
-    assert L.q4k_gemm(A, A, A2, 4096, 17408, 5120, NUL, 0, NUL) == EWS
+    assert L.q4k_gemm_workspace_bytes(64, 1000, 2304) == 0     # 4 tiles of 9 stage pairs
+    assert L.q4k_gemm_workspace_bytes(64, 64, 65536) == 0      # one tile
+    for M in (512, 4096):                                      # 136 / 1088 tiles: split
+        need = L.q4k_gemm_workspace_bytes(M, 17408, 5120)
+        assert need >= 256 + 256 * 256 * 256 * 4
+        assert L.q4k_gemm(A, A, A2, M, 17408, 5120, NUL, 0, NUL) == EWS
+    assert L.q4k_gemm(A, A, A2, 64, (1 << 20) + 1, 256, NUL, 0, NUL) == ESHAPE  # N <= 2^20
     assert L.qdm_set_gemm_spin_limit(0) == OK
 
 

@@ -516,18 +516,28 @@ def test_q4k_gemm_ragged(M, N, K):
 
 
 def _gemm_units(M, N, K):
+    """Workgroups of a q4k_gemm call (the library's rule: stream-K over one
+    per compute unit with >= as many tiles as units, or >= 2 stage pairs per
+    unit and <= 16 units per tile; else one per tile)."""
     tiles = ((M + 255) // 256) * ((N + 255) // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return tiles if tiles < cus else min(cus, tiles * (K // 128))
+    total = tiles * (K // 128)
+    if tiles >= cus or (total >= 2 * cus and 16 * tiles >= cus):
+        return min(cus, total)
+    return tiles
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 65536), (4352, 4096, 512), (4097, 4100, 768)])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 65536), (4352, 4096, 512), (4097, 4100, 768),
+                                   (300, 4000, 2048), (40, 5000, 5120)])
 def test_q4k_gemm_split_tiles(M, N, K):
-    """Long K in one tile, and tile counts above the unit count, where tiles
-    are split between workgroups (272 tiles of 4 stage pairs over 256 units;
-    289 ragged tiles of 6): sampled outputs against the oracle, every output
-    against the bf16-weight reference, every flag word of the workspace zero
-    after the call and its status word (waits that gave up) zero."""
+    """Long K in one tile; tile counts above the unit count, where tiles are
+    split between workgroups (272 tiles of 4 stage pairs over 256 units; 289
+    ragged tiles of 6); fewer tiles than units split over all of them (32
+    ragged tiles of 16 pairs: 2 pairs per unit, up to 8 units per tile; 20
+    tiles of 40 pairs, ragged M). Sampled outputs against the oracle, every
+    output against the bf16-weight reference, every flag word of the
+    workspace zero after the call and its status word (waits that gave up)
+    zero."""
     say("q4k_gemm split", M, N, K, "units", _gemm_units(M, N, K))
     rng = np.random.default_rng(K + N)
     w = synth.q4k_blocks(rng, N, K)
