@@ -173,7 +173,8 @@ def bench_roofs(torch, qdm):
     ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
     mhz = float(np.median(ck[:, 0] / ck[:, 1] * 100.0))
     flops = wgs * 4 * iters * 8 * 32768.0
-    ms_empty = _time_launches(torch, lambda i: qdm.probe_empty(wgs), 2000)
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ms_empty = _time_launches(torch, lambda i: lib.qdm_probe_empty(wgs, st), 2000)
     return {"hbm_read_GBps": big / ms_hbm / 1e6, "mall_read_GBps": small / ms_mall / 1e6,
             "read_us_by_size_hbm": reads,
             "mfma_bf16_TFLOPs": flops / ms_mfma / 1e9,
@@ -181,7 +182,7 @@ def bench_roofs(torch, qdm):
             "empty_launch_us": ms_empty * 1e3,
             "notes": "read: qdm_probe_read; mfma: qdm_probe_mfma (%d workgroups x 4 waves x %d x 8 "
                      "v_mfma_f32_32x32x16_bf16); clock = s_memtime / s_memrealtime ticks x "
-                     "100 MHz; empty: back-to-back launches of %d idle workgroups"
+                     "100 MHz; empty: back-to-back C ABI launches of %d idle workgroups"
                      % (wgs, iters, wgs)}
 
 
@@ -340,22 +341,30 @@ def bench_gemm(torch, qdm, synth, oracle, M, reps):
     cols = np.arange(0, N, 211)
     rows = np.arange(0, M, max(1, M // 128))
     err = rel(y.cpu().numpy()[np.ix_(rows, cols)], oracle.q4k_matmul(w[cols], x[rows], len(cols), K))
-    # untimed warm-up of about 30 ms of launches: the shader clock settles
-    # only after a sustained run (a cold 5-launch timing reads up to 20 % slow)
+    # C ABI calls with pre-marshalled arguments; untimed warm-up of about
+    # 30 ms of launches first: the shader clock settles only after a
+    # sustained run (a cold 5-launch timing reads up to 20 % slow)
+    need = qdm.q4k_gemm_workspace_bytes(M, N, K)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (ctypes.c_void_p(wd.data_ptr()), ctypes.c_void_p(xd.data_ptr()),
+         ctypes.c_void_p(y.data_ptr()), M, N, K, ctypes.c_void_p(ws.data_ptr()), need, st)
     t0 = time.perf_counter()
-    qdm.q4k_gemm(wd, xd, N, K, y=y)
+    lib.q4k_gemm(*a)
     torch.cuda.synchronize()
     one_ms = (time.perf_counter() - t0) * 1e3
     for _ in range(max(3, int(30.0 / max(one_ms, 1e-3)))):
-        qdm.q4k_gemm(wd, xd, N, K, y=y)
+        lib.q4k_gemm(*a)
     tm = Timer(torch)
     evs = [tm.event()]
     for _ in range(reps):
-        qdm.q4k_gemm(wd, xd, N, K, y=y)
+        lib.q4k_gemm(*a)
         evs.append(tm.event())
     torch.cuda.synchronize()
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
     ms = float(np.mean(times))
+    if qdm.q4k_gemm_timeouts(ws) if need else 0:
+        raise RuntimeError("q4k_gemm: a split-tile wait gave up during the benchmark")
     flops = 2.0 * M * N * K
     return {"M": M, "N": N, "K": K, "avg_ms": ms, "median_ms": float(np.median(times)),
             "TFLOPs": flops / ms / 1e9, "frac_mfma_peak": flops / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS,
@@ -365,22 +374,37 @@ def bench_gemm(torch, qdm, synth, oracle, M, reps):
 def bench_q6k(torch, qdm, synth, oracle, which, M, reps):
     K, N = {"head": (5120, 151936), "down": (17408, 5120)}[which]
     w, x = synth.q6k_gemv(which, M)
-    return bench_kgemv(torch, qdm.q6k_gemv, oracle.q6k_matmul, w, x, M, N, K, Q6K_BPB, reps)
+    return bench_kgemv(torch, qdm, "q6k_gemv", oracle.q6k_matmul, w, x, M, N, K, Q6K_BPB, reps)
 
 
 def bench_q5k(torch, qdm, synth, oracle, M, reps):
     K, N = synth.Q5K_GEMV["K"], synth.Q5K_GEMV["N"]
     w, x = synth.q5k_gemv(M)
-    return bench_kgemv(torch, qdm.q5k_gemv, oracle.q5k_matmul, w, x, M, N, K, Q5K_BPB, reps)
+    return bench_kgemv(torch, qdm, "q5k_gemv", oracle.q5k_matmul, w, x, M, N, K, Q5K_BPB, reps)
 
 
 def bench_q80(torch, qdm, synth, oracle, M, reps):
     K, N = synth.Q80_GEMV["K"], synth.Q80_GEMV["N"]
     w, x = synth.q80_gemv(M)
-    return bench_kgemv(torch, qdm.q80_gemv, oracle.q80_matmul, w, x, M, N, K, Q80_BPB, reps)
+    return bench_kgemv(torch, qdm, "q80_gemv", oracle.q80_matmul, w, x, M, N, K, Q80_BPB, reps)
 
 
-def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
+def time_batch(torch, call, nargs, reps):
+    """Mean per call (ms) of `reps` back-to-back calls through the C ABI with
+    pre-marshalled arguments (call(i) enqueues call i; the host stays ahead of
+    the GPU), bracketed by two events on the launch stream."""
+    for i in range(nargs):
+        call(i)
+    tm = Timer(torch)
+    e0 = tm.event()
+    for i in range(reps):
+        call(i % nargs)
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_kgemv(torch, qdm, fn, ref_matmul, w, x, M, N, K, bpb, reps):
     """A k-quant GEMV timed over rotating weight copies (larger than the
     last-level cache together), checked on sampled rows against the oracle."""
     nbytes = w.nbytes
@@ -389,92 +413,88 @@ def bench_kgemv(torch, gemv, ref_matmul, w, x, M, N, K, bpb, reps):
     ws = [base] + [base.clone() for _ in range(ncopy - 1)]
     xd = to_dev_bf16(torch, x)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    gemv(ws[0], xd, N, K, y=y)
+    getattr(qdm, fn)(ws[0], xd, N, K, y=y)
     torch.cuda.synchronize()
     rows = np.arange(0, N, 97 if N > 20000 else 1)
     err = rel(y.cpu().numpy()[:, rows], ref_matmul(w[rows], x, len(rows), K))
-    for i in range(3):
-        gemv(ws[i % ncopy], xd, N, K, y=y)
-    tm = Timer(torch)
-    evs = [tm.event()]
-    for i in range(reps):
-        gemv(ws[i % ncopy], xd, N, K, y=y)
-        evs.append(tm.event())
-    torch.cuda.synchronize()
-    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    ms = float(np.median(times))  # one host stall must not move the figure
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = getattr(lib, fn)
+    args = [(ctypes.c_void_p(wc.data_ptr()), ctypes.c_void_p(xd.data_ptr()), qdm.QDM_BF16,
+             ctypes.c_void_p(y.data_ptr()), M, N, K, st) for wc in ws]
+    reps = max(reps, 2 * ncopy)
+    ms = time_batch(torch, lambda i: f(*args[i]), ncopy, reps)
     b = gemv_bytes(N, K, M, bpb)
     del ws
-    return {"M": M, "N": N, "K": K, "copies": ncopy, "bytes": b, "avg_ms": ms,
-            "mean_ms": float(np.mean(times)),
+    return {"M": M, "N": N, "K": K, "copies": ncopy, "bytes": b, "avg_ms": ms, "launches": reps,
             "GBps": b / ms / 1e6, "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS,
             "rel_err_sampled": err}
 
 
 def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=False):
     """One MoE layer call (E=128, H=2048, F=768, top-8). from_logits: the call
-    also runs the router on N(0, 1) router logits [T][128]."""
+    also runs the router on N(0, 1) router logits [T][128]. Calls go through
+    the C ABI with pre-marshalled arguments, back to back (the mean per call
+    is avg_ms); T <= 8 is also timed replayed from a captured graph."""
     E, H, F = 128, 2048, 768
     d = synth.moe(T, down_qtype=down_qtype)
     x, w13, w2 = to_dev_bf16(torch, d["x"]), to_dev(torch, d["w13"]), to_dev(torch, d["w2"])
-    ids0 = d["ids"] if not from_logits else oracle.router_topk(synth.moe_router(T), 8)[0]
-    per_expert0 = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
-                                                                    else Q5K_BPB)
-    # Weight sets called in turn: the experts one call touches, times the
-    # number of sets, exceed 512 MB (twice the last-level cache), so every
-    # call reads its experts from HBM (T = 1: 25 sets, T = 8: 4, T = 512: 2).
-    nsets = max(2, -(-(2 * MALL_BYTES) // (len(np.unique(ids0)) * per_expert0)))
-    sets = [(w13, w2)] + [(w13.clone(), w2.clone()) for _ in range(nsets - 1)]
-    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     if from_logits:
         logits = synth.moe_router(T)
         ids_np, gw_np = oracle.router_topk(logits, 8)
-        lg = torch.from_numpy(logits).to("cuda")
-        ws = torch.zeros(qdm.moe_from_logits_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8,
-                         device="cuda")
-
-        def run(a, b):
-            qdm.moe_grouped_gemm_from_logits(x, lg, a, b, 8, E, H, F, down_qtype=down_qtype,
-                                             y=y, workspace=ws)
     else:
         ids_np, gw_np = d["ids"], d["gw"]
-        step = qdm.moe_q4k_grouped_gemm if down_qtype == 4 else qdm.moe_q4k_q5k_grouped_gemm
+    per_expert = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
+                                                                   else Q5K_BPB)
+    distinct = len(np.unique(ids_np))
+    # Weight sets called in turn: the experts one call touches, times the
+    # number of sets, exceed 512 MB (twice the last-level cache), so every
+    # call reads its experts from HBM (T = 1: 25 sets, T = 8: 4, T = 512: 2).
+    nsets = max(2, -(-(2 * MALL_BYTES) // (distinct * per_expert)))
+    sets = [(w13, w2)] + [(w13.clone(), w2.clone()) for _ in range(nsets - 1)]
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    if from_logits:
+        lg = torch.from_numpy(logits).to("cuda")
+        wsb = qdm.moe_from_logits_workspace_bytes(T, E, 8, H, F)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        args = [(P(x.data_ptr()), P(lg.data_ptr()), P(a.data_ptr()), P(b.data_ptr()), down_qtype,
+                 P(y.data_ptr()), T, E, 8, H, F, P(ws.data_ptr()), wsb, st) for a, b in sets]
+        fn = lib.moe_grouped_gemm_from_logits
+    else:
         ids = torch.from_numpy(ids_np).to("cuda")
         gw = torch.from_numpy(gw_np).to("cuda")
-        ws = torch.zeros(qdm.moe_q4k_workspace_bytes(T, E, 8, H, F), dtype=torch.uint8,
-                         device="cuda")
+        wsb = qdm.moe_q4k_workspace_bytes(T, E, 8, H, F)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        args = [(P(x.data_ptr()), P(a.data_ptr()), P(b.data_ptr()), P(ids.data_ptr()),
+                 P(gw.data_ptr()), P(y.data_ptr()), T, E, 8, H, F, P(ws.data_ptr()), wsb, st)
+                for a, b in sets]
+        fn = lib.moe_q4k_grouped_gemm if down_qtype == 4 else lib.moe_q4k_q5k_grouped_gemm
 
-        def run(a, b):
-            step(x, a, b, ids, gw, E, H, F, y=y, workspace=ws)
-    run(w13, w2)
+    def run(i):
+        if fn(*args[i]):
+            raise RuntimeError("MoE call failed in the benchmark")
+    run(0)
     torch.cuda.synchronize()
     toks = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 16).astype(int)
     ref = oracle.moe(d["x"][toks], d["w13"], d["w2"], ids_np[toks], gw_np[toks], E, H, F,
                      down_qtype)
     err = rel(y.cpu().numpy()[toks], ref)
     del d
-    for i in range(len(sets)):
-        run(*sets[i])
-    reps = max(reps, 2 * len(sets))
-    tm = Timer(torch)
-    evs = [tm.event()]
-    for i in range(reps):
-        run(*sets[i % len(sets)])
-        evs.append(tm.event())
-    torch.cuda.synchronize()
-    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    ms = float(np.median(times))  # one host stall must not move the figure
-    mean_ms = float(np.mean(times))
+    reps = max(reps, 4 * len(sets))
+    ms = time_batch(torch, run, len(sets), reps)
     graph_ms = None
     if T <= 8:
-        # Decode-sized calls are near the host's launch rate: also time them
-        # replayed from a graph (one call per weight set), as a decode loop
-        # would run them. The replayed output must equal the eager one.
+        # Decode-sized calls replayed from a captured graph (one call per
+        # weight set), as a decode loop would run them; the replayed output
+        # must equal the eager one.
         eager_y = y.clone()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for st in sets:
-                run(*st)
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for a in args:
+                if fn(*a[:-1], cap):
+                    raise RuntimeError("MoE call failed under capture")
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(y, eager_y):
@@ -488,13 +508,10 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / (greps * len(sets))
         del graph
-    distinct = len(np.unique(ids_np))
-    per_expert = 2 * F * (H // 256) * Q4K_BPB + H * (F // 256) * (Q4K_BPB if down_qtype == 4
-                                                                   else Q5K_BPB)
     touched = distinct * per_expert + T * H * 2 + T * H * 4 + (T * E * 4 if from_logits else 0)
     flops = 2.0 * T * 8 * (2 * F * H + H * F)
     r = {"T": T, "distinct_experts": distinct, "touched_bytes": touched, "avg_ms": ms,
-         "mean_ms": mean_ms, "weight_sets": len(sets),
+         "calls": reps, "weight_sets": len(sets),
          "bytes_per_cycle": len(sets) * distinct * per_expert,
          "GBps": touched / ms / 1e6, "frac_hbm_peak": touched / ms / 1e6 / HBM_PEAK_GBS,
          "TFLOPs": flops / ms / 1e9, "rel_err_sampled": err}
@@ -504,7 +521,8 @@ def bench_moe(torch, qdm, synth, oracle, T, reps, down_qtype=4, from_logits=Fals
 
 
 def bench_router(torch, qdm, synth, oracle, T, reps):
-    """moe_router_topk alone on N(0, 1) logits [T][128], top-8."""
+    """moe_router_topk alone on N(0, 1) logits [T][128], top-8 (C ABI calls,
+    back to back)."""
     logits = synth.moe_router(T)
     lg = torch.from_numpy(logits).to("cuda")
     ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
@@ -513,15 +531,10 @@ def bench_router(torch, qdm, synth, oracle, T, reps):
     torch.cuda.synchronize()
     rid, _ = oracle.router_topk(logits, 8)
     exact = bool(np.array_equal(ids.cpu().numpy(), rid))
-    for _ in range(3):
-        qdm.moe_router_topk(lg, 8, ids=ids, weights=gw)
-    tm = Timer(torch)
-    evs = [tm.event()]
-    for _ in range(reps):
-        qdm.moe_router_topk(lg, 8, ids=ids, weights=gw)
-        evs.append(tm.event())
-    torch.cuda.synchronize()
-    ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (ctypes.c_void_p(lg.data_ptr()), T, 128, 8, ctypes.c_void_p(ids.data_ptr()),
+         ctypes.c_void_p(gw.data_ptr()), st)
+    ms = time_batch(torch, lambda i: lib.moe_router_topk(*a), 1, reps)
     return {"T": T, "avg_ms": ms, "ids_bit_exact": exact}
 
 
@@ -675,7 +688,7 @@ def main():
         k, n = 5120, 34816
         w4 = synth.q4k_blocks(np.random.default_rng(8), n, k)
         x8 = synth.normal_bf16(np.random.default_rng(9), (8, k))
-        extra["q4k_gate_up_m8"] = bench_kgemv(torch, qdm.q4k_gemv, oracle.q4k_matmul, w4, x8, 8,
+        extra["q4k_gate_up_m8"] = bench_kgemv(torch, qdm, "q4k_gemv", oracle.q4k_matmul, w4, x8, 8,
                                               n, k, Q4K_BPB, 50)
         log("q4k_gate_up_m8", extra["q4k_gate_up_m8"])
     if "q80" in sections:
