@@ -36,6 +36,8 @@
 #include "launch.h"
 #include "q4k_tile.h"
 
+#include <type_traits>
+
 // Scratch of the no-allocation MoE entry point: the workspace of one call
 // lives in this device array (every GPU the library runs on holds its own copy
 // until the process ends). Host code never uses the array's name as an
@@ -673,208 +675,280 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
   }
 }
 
-constexpr int MX_THREADS = 256;
-constexpr int MX_MS = 2;                    // 32-row entry subtiles per pass
-constexpr int MX_ROWS = 32 * MX_MS;         // entries per pass
-constexpr int MX_AJ = MX_ROWS * 8 / MX_THREADS;  // 16-byte A chunks per thread and stage
-// LDS of the matrix-core kernel: the weight region holds either the bf16
-// weight tile (256 rows x 144 B) or the raw block column it is decoded from
-// (256 x 144 B for Q4_K, 256 x 176 B for Q5_K), then the A rows and the
-// entries of a pass. 46,336 B (Q4_K) or 54,528 B (Q5_K): two workgroups per CU.
-constexpr int mx_w_elems(bool q5) {
-  return (256 * (q5 ? Q5K_BYTES : Q4K_BYTES) / 2) > 256 * TILE_LROW
-             ? 256 * (q5 ? Q5K_BYTES : Q4K_BYTES) / 2
-             : 256 * TILE_LROW;
-}
-constexpr size_t mx_lds(bool q5) {
-  return (size_t)(mx_w_elems(q5) + MX_ROWS * TILE_LROW) * sizeof(uint16_t) +
-         MX_ROWS * sizeof(int32_t);
-}
+constexpr int MX_THREADS = 512;  // eight waves: one workgroup per compute unit
+constexpr int MX_WROWS = 64;     // weight rows per wave pair: two 32-row MFMA tiles
+constexpr int MX_PASS = 64;      // entries per pass: one or two 32-row MFMA tiles
+constexpr int MX_ASLOTS = 33;    // 16-byte LDS slots per A row: a block's 32, one of padding
+constexpr int MX_ABYTES = MX_PASS * MX_ASLOTS * 16;  // one A buffer: 33,792 B
+constexpr int mx_wbytes(bool q5) { return 4 * MX_WROWS * (q5 ? Q5K_BYTES : Q4K_BYTES); }
 
-// Grouped matrix-core kernel. Workgroup (tile, e), for the entries
-// perm[offsets[e] ..] of expert e in passes of MX_ROWS:
-//   GATEUP: A = x rows (token = entry / top_k), K = H; weight tile = gate rows
-//           f0 .. f0+127 and up rows F+f0 .. of W13[e]; hb[entry][f] = bf16 of
-//           silu(g) * u.
-//   DOWN:   A = hb rows (by entry), K = F; weight tile = rows r0 .. r0+255 of
-//           W2[e]; o[entry][r] fp32.
-// Weights arrive one super-block column at a time: the tile's 256 blocks of
-// column b (144 B each, one per weight row) are read as consecutive 16-byte
-// chunks (9 per block, so a wave's loads cover whole blocks of a few rows)
-// into LDS, and each thread then takes its own row's block from there. The
-// column's four stages of 64 K follow: each thread decodes 64 weights of its
-// row into the bf16 LDS tile, which reuses the raw column's bytes, and stores
-// its share of the A tile; the next column and the A tiles of the next two
-// stages are in flight meanwhile, and two workgroups share a compute unit, so
-// one decodes while the other multiplies. Wave w owns weight columns (GATEUP)
-// gate 32w .. and up 32w .. (g and u of one (entry, f) then share a lane), or
-// (DOWN) 64w .. 64w+63; every wave covers all entry subtiles of the pass.
-// Q5 (DOWN only): W2 is Q5_K; a row's block is 11 chunks of 16 B (header,
-// two of the high-bit plane, eight of codes) instead of 9, and the decode
-// merges the plane's bits into the codes.
-template <bool GATEUP, bool Q5>
-__global__ __launch_bounds__(MX_THREADS, 2) void moe_mfma_kernel(
-    const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int K,
-    int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
-  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;  // bytes per block
-  constexpr int NCH = BB / 16;                    // 16-byte chunks per block
-  constexpr int QC = Q5 ? 3 : 1;                  // first code chunk
-  extern __shared__ __attribute__((aligned(16))) uint16_t msm[];
-  uint16_t *sw = msm;                       // [256][TILE_LROW] weight rows (bf16)
-  uint8_t *raw = (uint8_t *)msm;            // [256][BB] raw block column (same bytes as sw)
-  uint16_t *sa = msm + mx_w_elems(Q5);      // [MX_ROWS][TILE_LROW] A rows (bf16)
-  int32_t *sent = (int32_t *)(sa + MX_ROWS * TILE_LROW);  // [MX_ROWS] entries of the pass
-  // blockIdx.x = expert, blockIdx.y = tile: consecutive workgroup ids go to
-  // different XCDs, so the tiles of one expert share an XCD and its L2 holds
-  // that expert's A rows for all of them
-  const int e = blockIdx.x, tile = blockIdx.y;
-  const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-  if (cnt == 0) return;
-  const int nbk = K / QK, stages = K / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto tile_row = [&](int t) {
-    if constexpr (GATEUP) {
-      const int f0 = tile * 128;
-      return t < 128 ? f0 + t : F + f0 + (t - 128);
-    } else {
-      return tile * 256 + t;
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// One pass over up to MX_PASS entries (MS tiles of 32) of the workgroup's
+// 256 weight rows. Waves w and w+4 (one SIMD) own the same 64 rows: wave w
+// multiplies chunks 0 and 1 of every block, wave w+4 chunks 2 and 3, and at
+// the end of the pass wave w+4 hands its sums to wave w through LDS. Block by
+// block: at the top of block b every wave waits for its copies of block b, a
+// barrier makes all of them visible, the copies of block b+1 into the other
+// buffers are issued, and block b is multiplied.
+// Copies go from global memory straight into LDS (global_load_lds_dwordx4), a
+// wave's 64 lanes writing 1 KiB of consecutive LDS:
+//   weights: row group g's rows (64 per group), block b of each (BB bytes,
+//     BB/16 pieces), piece p = 64i + lane of copy i at LDS byte 16p of the
+//     group's area (row-major, BB per row); the group's two waves take the
+//     even and the odd copies;
+//   A: entry row r of the pass, its 256 k of block b (512 bytes) in slots
+//     33r .. 33r+31 (slot 33r+32 is padding: rows 528 bytes apart keep the
+//     16-byte reads below free of bank conflicts), slot s = 64(8i + wave) +
+//     lane of copy i. Rows past the pass's entries repeat its last entry.
+// Lane (n, h) = (lane % 32, lane / 32) reads its rows' code bytes and its A
+// pieces from LDS and multiplies as follows. The reduction order over K is
+// free, so K is permuted to suit the code layout: in chunk c of a block
+// (sub-blocks 2c and 2c+1), code byte l holds weight 64c + l in its low nibble
+// and 64c + 32 + l in its high nibble; lane half h takes bytes 16h .. 16h+15,
+// and the four MFMA steps of the chunk take, from those bytes, the low
+// nibbles of bytes 0..7, of 8..15, then the high nibbles of 0..7, of 8..15.
+// The A operand of step t then holds x at k = 64c + 32(t/2) + 16h + 8(t%2)
+// .. +7: one 16-byte LDS read. The weights are decoded in registers straight
+// into the B operand; nothing decoded goes through LDS.
+template <bool GATEUP, bool Q5, int MS>
+__device__ __forceinline__ void mx_pass(const uint16_t *__restrict__ a_src,
+                                        const uint8_t *const (&wsrc)[(Q5 ? 11 : 9) / 2 + 1],
+                                        const int32_t *__restrict__ pent, int rows, int top_k,
+                                        int K, int ldo, int col0, uint16_t *__restrict__ hb,
+                                        float *__restrict__ o, uint8_t *const (&sw)[2],
+                                        uint8_t *const (&sa)[2]) {
+  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;
+  constexpr int NP = BB / 16;         // 16-byte pieces per block
+  constexpr int QOFF = Q5 ? 48 : 16;  // first code byte of a block
+  constexpr int NA = (MS * 32 * MX_ASLOTS + 63) / 64;  // A copies per block (all waves)
+  constexpr int NAW = (NA + 7) / 8;                    // A copies per wave, at most
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int grp = wave & 3, kh = wave >> 2;
+  const int nbk = K / QK;
+  // A copy sources: slot s of copy i is piece s % 33 (the padding slot copies
+  // piece 31 again) of entry row s / 33
+  const uint16_t *asrc[NAW];
+#pragma unroll
+  for (int i = 0; i < NAW; i++) {
+    const int s = 64 * (8 * i + wave) + lane;
+    const int r = min(s / MX_ASLOTS, rows - 1);
+    const int ent = pent[r];
+    asrc[i] = a_src + (int64_t)(GATEUP ? ent / top_k : ent) * K + 8 * min(s % MX_ASLOTS, 31);
+  }
+  // A first: its sources depend on the entry loads, and waiting for those
+  // then waits for no weight copy
+  auto copy_block = [&](int b, uint8_t *w, uint8_t *a) {
+#pragma unroll
+    for (int i = 0; i < NAW; i++)
+      if (8 * i + wave < NA)  // uniform
+        __builtin_amdgcn_global_load_lds((const void *)(asrc[i] + QK * b),
+                                         (lds_ptr_t)(a + 1024 * (8 * i + wave)), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; 2 * i + kh < NP; i++)
+      __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + (int64_t)b * BB),
+                                       (lds_ptr_t)(w + MX_WROWS * BB * grp + 1024 * (2 * i + kh)),
+                                       16, 0, 0);
+  };
+  f32x16 acc[MS][2];
+#pragma unroll
+  for (int i = 0; i < MS; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+  // this wave's two chunks of a block from LDS: decode 8 weights per step and
+  // tile (w = d*sc*q - dmin*m in fp32, rounded to bf16 nearest-even, as in
+  // every matrix-core path) and multiply
+  auto multiply_kh = [&](const uint8_t *w, const uint8_t *a, auto khc) {
+    constexpr int KH = decltype(khc)::value;
+    const uint8_t *wr[2] = {w + BB * (MX_WROWS * grp + n), w + BB * (MX_WROWS * grp + 32 + n)};
+    u32x4 hd[2], qh[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      hd[j] = *(const u32x4 *)wr[j];
+      if constexpr (Q5) qh[j] = *(const u32x4 *)(wr[j] + 16 + 16 * h);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; cc++) {
+      const int c = 2 * KH + cc;
+      u32x4 q[2], av[MS][4];
+#pragma unroll
+      for (int j = 0; j < 2; j++) q[j] = *(const u32x4 *)(wr[j] + QOFF + 32 * c + 16 * h);
+#pragma unroll
+      for (int i = 0; i < MS; i++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+          av[i][t] = *(const u32x4 *)(a + 16 * MX_ASLOTS * (32 * i + n) +
+                                      2 * (64 * c + 32 * (t >> 1) + 16 * h + 8 * (t & 1)));
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        // Q4_K: a code byte q read as fp8 e4m3 is exactly q * 2^-9 (the small
+        // ones as subnormals), so v_cvt_pk_f32_fp8 turns two codes into
+        // floats in one instruction and the scale carries 2^9 (exact): the
+        // fma forms d*sc*q - dmin*m with the same single rounding as from an
+        // integer q. Q5_K codes reach 31, past e4m3's exact integers: one
+        // v_cvt_f32_ubyteN per code.
+        const RowScales sc = hdr_scales(hd[j], true, c);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const bool hi = t >= 2;
+          const float dm = hi ? sc.b1 : sc.b0;
+          uint32_t cw[2];
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            const uint32_t d = q[j][2 * (t & 1) + u];
+            cw[u] = (hi ? d >> 4 : d) & 0x0F0F0F0Fu;
+            if constexpr (Q5) {
+              const uint32_t hh = qh[j][2 * (t & 1) + u] >> (2 * c);
+              cw[u] |= (hi ? hh << 3 : hh << 4) & 0x10101010u;
+            }
+          }
+          u32x4 bw;
+          if constexpr (Q5) {
+            const float ds = hi ? sc.a1 : sc.a0;
+            bw = u32x4{pack_bf16(ds * (float)(cw[0] & 255u) - dm, ds * (float)((cw[0] >> 8) & 255u) - dm),
+                       pack_bf16(ds * (float)((cw[0] >> 16) & 255u) - dm, ds * (float)(cw[0] >> 24) - dm),
+                       pack_bf16(ds * (float)(cw[1] & 255u) - dm, ds * (float)((cw[1] >> 8) & 255u) - dm),
+                       pack_bf16(ds * (float)((cw[1] >> 16) & 255u) - dm, ds * (float)(cw[1] >> 24) - dm)};
+          } else {
+            const float ds = (hi ? sc.a1 : sc.a0) * 512.f;
+            const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[0], false);
+            const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[0], true);
+            const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[1], false);
+            const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[1], true);
+            bw = u32x4{pack_bf16(ds * p0[0] - dm, ds * p0[1] - dm), pack_bf16(ds * p1[0] - dm, ds * p1[1] - dm),
+                       pack_bf16(ds * p2[0] - dm, ds * p2[1] - dm), pack_bf16(ds * p3[0] - dm, ds * p3[1] - dm)};
+          }
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+          for (int i = 0; i < MS; i++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, av[i][t]), bop, acc[i][j], 0, 0, 0);
+        }
+      }
     }
   };
-  const uint8_t *wexp = wq + (int64_t)e * NR * nbk * BB;
-  // raw chunk i of this thread: chunk c = tid + 256 i of the column, which is
-  // piece c % NCH of the block of tile row c / NCH
-  // (32-bit offsets: the host admits only experts whose tensor is below 2 GiB)
-  int choff[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; i++) {
-    const int c = tid + MX_THREADS * i;
-    const int row = c / NCH;
-    choff[i] = tile_row(row) * nbk * BB + 16 * (c - NCH * row);
-  }
-  // B operand rows of this lane's two 32-column tiles, A operand k offset
-  const int brow0 = GATEUP ? 32 * wave + (lane & 31) : 64 * wave + (lane & 31);
-  const int brow1 = GATEUP ? 128 + 32 * wave + (lane & 31) : 64 * wave + 32 + (lane & 31);
-  const int koff = 8 * (lane >> 5);
-
-  for (int p0 = 0; p0 < cnt; p0 += MX_ROWS) {
-    const int rows = min(MX_ROWS, cnt - p0);
-    const int ms = (rows + 31) >> 5;
-    __syncthreads();  // the previous pass's epilogue is done with sent
-    if (tid < MX_ROWS) sent[tid] = perm[beg + p0 + min(tid, rows - 1)];
-    __syncthreads();
-    // A chunks of this thread: row q/8, 16-byte column q%8 for q = tid + 256j
-    const uint16_t *arow[MX_AJ];
-    bool alive[MX_AJ];
-#pragma unroll
-    for (int j = 0; j < MX_AJ; j++) {
-      const int q = tid + MX_THREADS * j;
-      alive[j] = (q >> 3) < rows;
-      const int ent = sent[q >> 3];
-      arow[j] = a_src + (int64_t)(GATEUP ? ent / top_k : ent) * K + 8 * (q & 7);
+  auto multiply = [&](const uint8_t *w, const uint8_t *a) {
+    if (kh == 0)
+      multiply_kh(w, a, std::integral_constant<int, 0>{});
+    else
+      multiply_kh(w, a, std::integral_constant<int, 1>{});
+  };
+  __syncthreads();  // every wave is done with buffer 0 (previous pass)
+  copy_block(0, sw[0], sa[0]);
+  for (int b = 0; b < nbk; b += 2) {
+    __syncthreads();  // block b is in buffer 0 for every wave; buffer 1 is free
+    if (b + 1 < nbk) copy_block(b + 1, sw[1], sa[1]);
+    multiply(sw[0], sa[0]);
+    if (b + 1 < nbk) {
+      __syncthreads();  // block b+1 is in buffer 1; buffer 0 is free
+      if (b + 2 < nbk) copy_block(b + 2, sw[0], sa[0]);
+      multiply(sw[1], sa[1]);
     }
-    f32x16 acc[MX_MS][2];
+  }
+  // wave w+4's sums to wave w through the weight buffers, entry tile i in
+  // buffer i at [group][j][v][lane] (32 KiB: no copy is in flight and every
+  // wave is past its last multiply after the barrier)
+  __syncthreads();
+  float *xch[MS];
 #pragma unroll
-    for (int i = 0; i < MX_MS; i++)
+  for (int i = 0; i < MS; i++) xch[i] = (float *)sw[i] + grp * 2 * 16 * WAVE + lane;
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < MS; i++)
 #pragma unroll
       for (int j = 0; j < 2; j++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+        for (int v = 0; v < 16; v++) xch[i][(j * 16 + v) * WAVE] = acc[i][j][v];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < MS; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] += xch[i][(j * 16 + v) * WAVE];
+  // lane holds column n of each 32-column tile and rows 32i + 8(v/4) + 4h + v%4
+#pragma unroll
+  for (int i = 0; i < MS; i++) {
+    const int ent_lane = pent[min(32 * i + n, rows - 1)];
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const int rr = 8 * (v >> 2) + 4 * h + (v & 3);
+      const int e_r = __shfl(ent_lane, rr, WAVE);
+      if (32 * i + rr < rows) {
+        if constexpr (GATEUP) {
+          const float g = acc[i][0][v], u = acc[i][1][v];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          hb[(int64_t)e_r * ldo + col0 + n] = (uint16_t)f32_to_bf16_rne(hv);
+        } else {
+          float *orow = o + (int64_t)e_r * ldo + col0 + n;
+          orow[0] = acc[i][0][v];
+          orow[32] = acc[i][1][v];
+        }
+      }
+    }
+  }
+}
 
-    struct AStage {
-      u32x4 a[MX_AJ];
-    };
-    u32x4 rawv[NCH];
-    auto load_raw = [&](int b) {
+// Grouped matrix-core kernel: workgroup (blockIdx.x, blockIdx.y) = (expert e,
+// tile) of eight waves, row group g = wave % 4 with 64 weight rows, over the
+// entries perm[offsets[e] ..] of expert e in passes of MX_PASS:
+//   GATEUP: A = x rows (token = entry / top_k), K = H; group g's weight tiles
+//           are gate rows f0+32g .. f0+32g+31 and up rows F+f0+32g .. of W13[e]
+//           (f0 = 128 tile), so g and u of one (entry, f) meet in one lane;
+//           hb[entry][f] = bf16 of silu(g) * u.
+//   DOWN:   A = hb rows (by entry), K = F; group g's weight tiles are rows
+//           r0+64g .. r0+64g+31 and r0+64g+32 .. of W2[e] (r0 = 256 tile);
+//           o[entry][r] fp32.
+// Consecutive workgroup ids go to different XCDs, so with E a multiple of 8
+// the tiles of one expert share an XCD and its L2 holds that expert's A rows.
+// Q5 (DOWN only): W2 is Q5_K (176-byte blocks: header, 32-byte high-bit plane,
+// 128 code bytes); the decode merges the plane's bits into the codes.
+template <bool GATEUP, bool Q5>
+__global__ __launch_bounds__(MX_THREADS, 1) void moe_mfma_kernel(
+    const uint16_t *__restrict__ a_src, const uint8_t *__restrict__ wq,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, int top_k, int K,
+    int F, int NR, uint16_t *__restrict__ hb, float *__restrict__ o, int H) {
+  constexpr int BB = Q5 ? Q5K_BYTES : Q4K_BYTES;
+  constexpr int NP = BB / 16;
+  // LDS, double-buffered by block: the raw blocks of the 256 weight rows
+  // (36,864 B per buffer, Q5_K 45,056 B) and the A rows of a pass (33,792 B
+  // per buffer); 141,312 B (Q5_K 157,696 B), one workgroup per compute unit.
+  // The buffers are separate variables, so the compiler can tell an LDS read
+  // of one buffer from the copy into the other still in flight.
+  __shared__ __attribute__((aligned(16))) uint8_t sw0[mx_wbytes(Q5)], sw1[mx_wbytes(Q5)];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[MX_ABYTES], sa1[MX_ABYTES];
+  const int e = blockIdx.x, tile = blockIdx.y;
+  const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+  if (cnt == 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row_bytes = (int64_t)(K / QK) * BB;
+  const uint8_t *wexp = wq + (int64_t)e * NR * row_bytes;
+  // weight copy sources of this wave: copy 2i + kh of row group grp = wave % 4;
+  // its piece p = 64(2i + kh) + lane is piece p % NP of group row p / NP
+  // (tile (p / NP) / 32, row (p / NP) % 32 of the tile)
+  const int grp = wave & 3, kh = wave >> 2;
+  const uint8_t *wsrc[NP / 2 + 1];
 #pragma unroll
-      for (int i = 0; i < NCH; i++)
-        rawv[i] = *(const u32x4 *)(wexp + choff[i] + (int64_t)b * BB);
-    };
-    auto load_a = [&](AStage &r, int st) {
-#pragma unroll
-      for (int j = 0; j < MX_AJ; j++) r.a[j] = *(const u32x4 *)(arow[j] + 64 * st);
-    };
-    // one stage of 64 K: decode this thread's row into sw, store the A tile,
-    // refill its A registers two stages ahead, then the MFMAs
-    auto stage = [&](const WRegs &wr, const u32x4 &qh0, const u32x4 &qh1, AStage &ar,
-                     int st) {
-      __syncthreads();  // every row is out of the raw column / the last MFMAs are done
-      const RowScales sc = row_scales(wr, true, st & 3);
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++) {
-        if constexpr (Q5)
-          store_w_part5(wr, qh0, qh1, sc, kk, st & 3, sw);
-        else
-          store_w_part(wr, sc, kk, sw);
-      }
-#pragma unroll
-      for (int j = 0; j < MX_AJ; j++) {
-        const int q = tid + MX_THREADS * j;
-        *(u32x4 *)(sa + (q >> 3) * TILE_LROW + 8 * (q & 7)) =
-            alive[j] ? ar.a[j] : u32x4{0u, 0u, 0u, 0u};
-      }
-      load_a(ar, min(st + 2, stages - 1));  // the tail reloads the last stage
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++) {
-        const bf16x8 b0 = *(const bf16x8 *)(sw + brow0 * TILE_LROW + 16 * kk + koff);
-        const bf16x8 b1 = *(const bf16x8 *)(sw + brow1 * TILE_LROW + 16 * kk + koff);
-#pragma unroll
-        for (int i = 0; i < MX_MS; i++) {
-          if (i < ms) {  // uniform
-            const bf16x8 a =
-                *(const bf16x8 *)(sa + (32 * i + (lane & 31)) * TILE_LROW + 16 * kk + koff);
-            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
-          }
-        }
-      }
-    };
-    AStage ra, rb;
-    load_raw(0);
-    load_a(ra, 0);
-    load_a(rb, min(1, stages - 1));
-    for (int b = 0; b < nbk; b++) {
-      __syncthreads();  // the last MFMAs are done with sw, which the raw column reuses
-#pragma unroll
-      for (int i = 0; i < NCH; i++) *(u32x4 *)(raw + 16 * (tid + MX_THREADS * i)) = rawv[i];
-      load_raw(min(b + 1, nbk - 1));  // the last column reloads itself
-      __syncthreads();
-      u32x4 blk[NCH];
-#pragma unroll
-      for (int j = 0; j < NCH; j++) blk[j] = *(const u32x4 *)(raw + BB * tid + 16 * j);
-      // stages 4b .. 4b+3 (code chunk c holds sub-blocks 2c and 2c+1); for
-      // Q5_K chunks 1 and 2 are the high-bit plane
-      const u32x4 qh0 = blk[Q5 ? 1 : 0], qh1 = blk[Q5 ? 2 : 0];
-      stage(WRegs{blk[0], blk[QC], blk[QC + 1]}, qh0, qh1, ra, 4 * b);
-      stage(WRegs{blk[0], blk[QC + 2], blk[QC + 3]}, qh0, qh1, rb, 4 * b + 1);
-      stage(WRegs{blk[0], blk[QC + 4], blk[QC + 5]}, qh0, qh1, ra, 4 * b + 2);
-      stage(WRegs{blk[0], blk[QC + 6], blk[QC + 7]}, qh0, qh1, rb, 4 * b + 3);
-    }
-    // epilogue: lane holds column (lane & 31) of each 32-column tile and rows
-    // 32i + 8(v/4) + 4(lane/32) + v%4
-#pragma unroll
-    for (int i = 0; i < MX_MS; i++) {
-      if (i < ms) {
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (r < rows) {
-            const int ent = sent[r];
-            if constexpr (GATEUP) {
-              const float g = acc[i][0][v], u = acc[i][1][v];
-              const float hv = g / (1.0f + expf(-g)) * u;
-              hb[(int64_t)ent * F + tile * 128 + 32 * wave + (lane & 31)] =
-                  (uint16_t)f32_to_bf16_rne(hv);
-            } else {
-              float *orow = o + (int64_t)ent * H + tile * 256 + 64 * wave + (lane & 31);
-              orow[0] = acc[i][0][v];
-              orow[32] = acc[i][1][v];
-            }
-          }
-        }
-      }
-    }
+  for (int i = 0; i < NP / 2 + 1; i++) {
+    const int p = min(64 * (2 * i + kh) + lane, 64 * NP - 1), wr = p / NP, j = wr >> 5, nn = wr & 31;
+    const int row = GATEUP ? (j == 0 ? 128 * tile + 32 * grp + nn : F + 128 * tile + 32 * grp + nn)
+                           : 256 * tile + 64 * grp + 32 * j + nn;
+    wsrc[i] = wexp + row * row_bytes + 16 * (p - NP * wr);
+  }
+  const int ldo = GATEUP ? F : H;
+  const int col0 = GATEUP ? 128 * tile + 32 * grp : 256 * tile + 64 * grp;
+  uint8_t *const sw[2] = {sw0, sw1}, *const sa[2] = {sa0, sa1};
+  for (int p0 = 0; p0 < cnt; p0 += MX_PASS) {
+    const int rows = min(MX_PASS, cnt - p0);
+    if (rows > 32)
+      mx_pass<GATEUP, Q5, 2>(a_src, wsrc, perm + beg + p0, rows, top_k, K, ldo, col0, hb, o, sw, sa);
+    else
+      mx_pass<GATEUP, Q5, 1>(a_src, wsrc, perm + beg + p0, rows, top_k, K, ldo, col0, hb, o, sw, sa);
   }
 }
 
@@ -991,13 +1065,10 @@ void launch_moe(const void *x, const void *w13, const void *w2, const int32_t *i
                      (int)E, ws.offsets, ws.perm, ws.status);
   auto k1 = moe_mfma_kernel<true, false>;
   auto k2 = moe_mfma_kernel<false, Q5>;
-  constexpr size_t lds1 = mx_lds(false), lds2 = mx_lds(Q5);
-  (void)hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-  (void)hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-  hipLaunchKernelGGL(k1, dim3((unsigned)E, (unsigned)(F / 128)), dim3(MX_THREADS), lds1, s,
+  hipLaunchKernelGGL(k1, dim3((unsigned)E, (unsigned)(F / 128)), dim3(MX_THREADS), 0, s,
                      (const uint16_t *)x, (const uint8_t *)w13, ws.offsets, ws.perm, (int)top_k,
                      (int)H, (int)F, (int)(2 * F), ws.hb, (float *)nullptr, (int)H);
-  hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), lds2, s,
+  hipLaunchKernelGGL(k2, dim3((unsigned)E, (unsigned)(H / 256)), dim3(MX_THREADS), 0, s,
                      (const uint16_t *)ws.hb, (const uint8_t *)w2, ws.offsets, ws.perm,
                      (int)top_k, (int)F, (int)F, (int)H, (uint16_t *)nullptr, ws.o, (int)H);
   const int64_t total = T * H / 4;

@@ -683,8 +683,11 @@ def check_moe(y, d, ids, gw, E, H, F, dq, toks=None, what="moe"):
 
 
 @pytest.mark.parametrize("T,E,H,F,top_k", [(5, 6, 256, 256, 3), (1, 4, 512, 256, 2),
-                                           (33, 16, 256, 512, 4), (64, 8, 768, 256, 8)])
+                                           (33, 16, 256, 512, 4), (64, 8, 768, 256, 8),
+                                           (160, 4, 512, 256, 2), (300, 6, 256, 512, 3)])
 def test_moe_small_full(T, E, H, F, top_k):
+    """Matrix-core regime from 65 entries on; the last two cases give experts
+    about 80 and 150 entries, so passes of 64 entries end with a one-tile pass."""
     say("moe small", T, E, H, F, top_k)
     d = synth.moe(T, E=E, H=H, F=F, top_k=top_k, seed=T + E)
     y = host(qdm.moe_q4k_grouped_gemm(*_moe_dev(d), E, H, F))
