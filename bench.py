@@ -290,11 +290,12 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
         reps_ms.append(a.elapsed_time(b) / 20)
     median5_ms = float(np.median(reps_ms[2:]))
 
-    # Per-kernel launch duration: a batch of back-to-back launches of one
-    # kernel through the C ABI with pre-marshalled arguments (the queue stays
-    # ahead of the GPU), bracketed by two events on the launch stream. Each
-    # shape rotates over its own copies, at least twice the 256 MB last-level
-    # cache in total (25 for QKV, 6 for gate+up, 11 for down).
+    # Per-kernel launch duration: back-to-back launches of one kernel through
+    # the C ABI with pre-marshalled arguments (the queue stays ahead of the
+    # GPU), in 5 batches each bracketed by two events on the launch stream;
+    # the median batch mean is reported. Each shape rotates over its own
+    # copies, at least twice the 256 MB last-level cache in total (25 for QKV,
+    # 6 for gate+up, 11 for down).
     stream = eager_stream
     kernels = {}
     nb = max(20, steps)
@@ -307,18 +308,13 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
                  qdm.QDM_BF16, ctypes.c_void_p(ys[name].data_ptr()), 1, N, K, stream)
                 for wc in ws]
         nb_shape = max(nb, 2 * len(args))
-        for a in args:
-            lib.q4k_gemv(*a)
-        k0 = tm.event()
-        for i in range(nb_shape):
-            lib.q4k_gemv(*args[i % len(args)])
-        k1 = tm.event()
-        torch.cuda.synchronize()
-        ms = k0.elapsed_time(k1) / nb_shape
+        bm = batch_means(torch, lambda i: lib.q4k_gemv(*args[i]), len(args), nb_shape)
+        ms = float(np.median(bm))
         b = gemv_bytes(N, K)
         kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb_shape,
                          "copies": len(args), "GBps": b / ms / 1e6,
-                         "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS, "rel_err": errs[name]}
+                         "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS, "rel_err": errs[name],
+                         "batch_ms": [round(v, 5) for v in bm]}
         del ws, args
     step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
     del dev_w
@@ -389,19 +385,31 @@ def bench_q80(torch, qdm, synth, oracle, M, reps):
     return bench_kgemv(torch, qdm, "q80_gemv", oracle.q80_matmul, w, x, M, N, K, Q80_BPB, reps)
 
 
-def time_batch(torch, call, nargs, reps):
-    """Mean per call (ms) of `reps` back-to-back calls through the C ABI with
-    pre-marshalled arguments (call(i) enqueues call i; the host stays ahead of
-    the GPU), bracketed by two events on the launch stream."""
+def batch_means(torch, call, nargs, reps, nbatch=5):
+    """Per-call means (ms) of `nbatch` batches of back-to-back calls through
+    the C ABI with pre-marshalled arguments (call(i) enqueues call i; the host
+    stays ahead of the GPU), each bracketed by two events on the launch
+    stream. A call rotates over nargs argument sets."""
     for i in range(nargs):
         call(i)
     tm = Timer(torch)
-    e0 = tm.event()
-    for i in range(reps):
-        call(i % nargs)
-    e1 = tm.event()
+    per = max(1, -(-reps // nbatch))
+    marks = [tm.event()]
+    i = 0
+    for _ in range(nbatch):
+        for _ in range(per):
+            call(i % nargs)
+            i += 1
+        marks.append(tm.event())
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return [marks[j].elapsed_time(marks[j + 1]) / per for j in range(nbatch)]
+
+
+def time_batch(torch, call, nargs, reps):
+    """Median over 5 batches of the mean time per call (ms): one disturbed
+    stretch of the run (a clock dip, another process) moves one batch, not the
+    figure."""
+    return float(np.median(batch_means(torch, call, nargs, reps)))
 
 
 def bench_kgemv(torch, qdm, fn, ref_matmul, w, x, M, N, K, bpb, reps):
