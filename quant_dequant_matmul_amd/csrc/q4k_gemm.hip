@@ -41,7 +41,10 @@
 // workgroup per unit; a range then covers the end of one tile, whole tiles,
 // and the start of another, so every unit gets the same number of MFMAs and
 // the last wave of tiles is not left to a few units. With fewer tiles than
-// units, each workgroup gets exactly one tile (no split). The unit that
+// units the space is still split over every unit when it holds at least two
+// stage pairs per unit and a tile per 16 units (M = 512, N = 17408: 136
+// tiles on 256 units); smaller calls take one whole tile per workgroup. The
+// unit that
 // computes the last stage pair of a tile owns it. A contributor (a unit that
 // computed earlier pairs of the tile) leaves its fp32 partial tile in the
 // workspace in the accumulators' own register order, so its stores and the
@@ -49,9 +52,11 @@
 // partials of the contributors (always units with a smaller index, in
 // decreasing index order, so the sum is deterministic) to its accumulators a
 // quarter tile at a time in registers and stores y as a whole tile is stored. A
-// contributor writes its partial, fences at device scope and raises its flag;
-// the owner waits on the flag (bounded), reads the partial and lowers the flag
-// again, so the workspace flags are zero between calls. Workgroups start in
+// contributor writes its partial and, once every store of the workgroup has
+// completed, one thread raises its flag with a device-scope release; the owner
+// polls the flag (bounded), acquires once, reads the partial and lowers the
+// flag again, so the workspace flags are zero between calls. (A device-scope
+// fence in every thread would invalidate the L2 of its XCD each time.) Workgroups start in
 // index order and a unit only waits on units with a smaller index, which have
 // started before it; each unit computes the segment others wait for before
 // the one that waits: the waits cannot deadlock and do not form chains.
