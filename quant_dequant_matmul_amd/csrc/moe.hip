@@ -536,11 +536,17 @@ __global__ __launch_bounds__(DEC_THREADS) void moe_dec_down_kernel(
 }
 
 // y[t][r] = sum over slots s in order of gw[t][s] * o[t*top_k+s][r], slots
-// with an id outside [0, E) skipped (o is indexed by entry).
+// with an id outside [0, E) skipped (o is indexed by entry). The loads of a
+// group of up to 8 slots (id, gate weight, 4 outputs) are all issued before
+// any is used: their addresses do not depend on the ids (every entry's o row
+// exists), so a call waits about one memory latency per group instead of
+// several in a row; an invalid slot is masked afterwards (its o row may hold
+// anything: it is never multiplied).
 __global__ __launch_bounds__(256) void moe_combine_entries_kernel(
     const float *__restrict__ o, const int32_t *__restrict__ ids, const float *__restrict__ gw,
     float *__restrict__ y, int T, int top_k, int E, int H) {
   // one thread per token t and 4 consecutive outputs (H % 4 == 0)
+  constexpr int G = 8;
   const int h4 = H / 4;
   const int64_t total = (int64_t)T * h4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -548,16 +554,25 @@ __global__ __launch_bounds__(256) void moe_combine_entries_kernel(
     const int64_t t = i / h4;
     const int c = (int)(i - t * h4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < top_k; s++) {
-      const int64_t en = t * top_k + s;
-      const int id = ids[en];
-      if (id >= 0 && id < E) {
-        const float g = gw[en];
-        const f32x4 v = *(const f32x4 *)(o + en * H + 4 * c);
-        acc.x = fmaf(g, v.x, acc.x);
-        acc.y = fmaf(g, v.y, acc.y);
-        acc.z = fmaf(g, v.z, acc.z);
-        acc.w = fmaf(g, v.w, acc.w);
+    for (int s0 = 0; s0 < top_k; s0 += G) {
+      int id[G];
+      float g[G];
+      f32x4 v[G];
+#pragma unroll
+      for (int j = 0; j < G; j++) {
+        const int64_t en = t * top_k + min(s0 + j, top_k - 1);
+        id[j] = ids[en];
+        g[j] = gw[en];
+        v[j] = *(const f32x4 *)(o + en * H + 4 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < G; j++) {
+        if (s0 + j < top_k && id[j] >= 0 && id[j] < E) {
+          acc.x = fmaf(g[j], v[j].x, acc.x);
+          acc.y = fmaf(g[j], v[j].y, acc.y);
+          acc.z = fmaf(g[j], v[j].z, acc.z);
+          acc.w = fmaf(g[j], v[j].w, acc.w);
+        }
       }
     }
     *(f32x4 *)(y + t * H + 4 * c) = acc;
