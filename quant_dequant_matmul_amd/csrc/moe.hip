@@ -597,17 +597,18 @@ constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
 constexpr int ROUTE_IDS = 4;  // ids per thread and batch
 
 // One workgroup: offsets[e] = first sorted position of expert e (exclusive
-// scan of the counts, offsets[E] = valid entries), perm[pos] = entry index,
-// entries of one expert in increasing (t, s) order. The scatter takes 1024
-// entries at a time: each wave ranks its lanes among equal ids (ballots of the
-// id bits), the per-wave counts of every id go to LDS, and an entry's position
-// is the expert's running offset + the counts of earlier waves + its rank.
+// scan of the counts, offsets[E] = valid entries), perm[pos] = entry index
+// for the entries of e at positions offsets[e] .. offsets[e+1]-1. Within an
+// expert the order is whatever order the LDS atomics hand out positions in:
+// an entry's outputs do not depend on where it sits among its expert's
+// entries (each output row of the matrix-core kernels is its own dot
+// product, and the combine sums an entry's slots in slot order), so the
+// results are the same bit for bit whatever that order.
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
     const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, uint32_t *__restrict__ status) {
   extern __shared__ int32_t rsm[];
-  int32_t *run = rsm;       // [E] running offsets
-  int32_t *cntw = rsm + E;  // [ROUTE_WAVES][E] per-wave counts of a chunk
+  int32_t *run = rsm;  // [E] counts, then running positions
   __shared__ int32_t wsum[ROUTE_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ids are read once per batch of ROUTE_IDS chunks (all loads in flight
@@ -654,38 +655,12 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(
     status[0] = (uint32_t)(n - total);  // entries skipped: id outside [0, E)
   }
   __syncthreads();
-  const uint64_t below = (1ull << lane) - 1ull;
   for (int base = 0; base < n; base += BATCH) {
     if (n > BATCH) load_batch(base);  // a single batch is still in registers
 #pragma unroll
     for (int j = 0; j < ROUTE_IDS; j++) {
-      if (base + ROUTE_THREADS * j >= n) break;  // uniform
-      for (int q = tid; q < ROUTE_WAVES * E; q += ROUTE_THREADS) cntw[q] = 0;
-      __syncthreads();
       const int i = base + ROUTE_THREADS * j + tid;
-      const int id = idr[j];
-      // entries of this wave with the same id: match the 10 id bits by ballot
-      uint64_t match = __ballot(id >= 0);
-#pragma unroll
-      for (int bit = 0; bit < 10; bit++) {  // E <= 1024
-        const uint64_t ones = __ballot(id >= 0 && ((id >> bit) & 1));
-        match &= ((id >> bit) & 1) ? ones : ~ones;
-      }
-      const int rank = __popcll(match & below);
-      if (id >= 0 && rank == 0) cntw[wave * E + id] = __popcll(match);
-      __syncthreads();
-      if (id >= 0) {
-        int pos = run[id] + rank;
-        for (int w = 0; w < wave; w++) pos += cntw[w * E + id];
-        perm[pos] = i;
-      }
-      __syncthreads();
-      for (int e = tid; e < E; e += ROUTE_THREADS) {
-        int add = 0;
-        for (int w = 0; w < ROUTE_WAVES; w++) add += cntw[w * E + e];
-        run[e] += add;
-      }
-      __syncthreads();
+      if (idr[j] >= 0) perm[atomicAdd(&run[idr[j]], 1)] = i;
     }
   }
 }
@@ -1073,7 +1048,7 @@ void launch_moe(const void *x, const void *w13, const void *w2, const int32_t *i
           : try_dec<DEC_FR_SMALL, DEC_RW_SMALL, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s))
     return;
   const int n = (int)n64;
-  const size_t route_lds = sizeof(int32_t) * (1 + ROUTE_WAVES) * E;
+  const size_t route_lds = sizeof(int32_t) * E;
   (void)hipFuncSetAttribute((const void *)moe_route_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, s, ids, n,
