@@ -150,19 +150,33 @@ def bench_roofs(torch, qdm):
     every compute unit with the shader clock during the loop, and the cost of
     an empty launch."""
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    sinkp = P(sink.data_ptr())
+
+    def read_ms(bufs, nb, reps):
+        # one launch through the binding's checks, then back-to-back launches
+        # through the C ABI (a Python call per launch would time the host at
+        # these sizes), rotating over the buffers
+        qdm.probe_read(bufs[0], nb, sink)
+        ptrs = [P(b.data_ptr()) for b in bufs]
+        return time_batch(torch, lambda i: lib.qdm_probe_read(ptrs[i], nb, sinkp, st),
+                          len(ptrs), reps)
+
     big = 1 << 30
     bufs = [torch.ones(big, dtype=torch.uint8, device="cuda") for _ in range(3)]
-    ms_hbm = _time_launches(torch, lambda i: qdm.probe_read(bufs[i % 3], big, sink), 30)
+    ms_hbm = read_ms(bufs, big, 30)
     del bufs
     small = 64 << 20
     buf = torch.ones(small, dtype=torch.uint8, device="cuda")
-    ms_mall = _time_launches(torch, lambda i: qdm.probe_read(buf, small, sink), 200)
+    ms_mall = read_ms([buf], small, 200)
     reads = {}
-    for nb in (20 << 20, 100 << 20):  # the decode QKV and gate+up byte counts, HBM-cold
+    # the decode byte counts (QKV, down, gate+up), HBM-cold: the buffers of one
+    # cycle exceed twice the last-level cache
+    for nb in (20 << 20, 48 << 20, 96 << 20):
         k = -(-(2 * MALL_BYTES) // nb) + 1
         bs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(k)]
-        reads["%d_MiB" % (nb >> 20)] = _time_launches(
-            torch, lambda i: qdm.probe_read(bs[i % k], nb, sink), 10 * k) * 1e3
+        reads["%d_MiB" % (nb >> 20)] = read_ms(bs, nb, 10 * k) * 1e3
         del bs
     del buf
     wgs = torch.cuda.get_device_properties(0).multi_processor_count
@@ -173,14 +187,13 @@ def bench_roofs(torch, qdm):
     ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
     mhz = float(np.median(ck[:, 0] / ck[:, 1] * 100.0))
     flops = wgs * 4 * iters * 8 * 32768.0
-    lib, st = qdm.lib(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    ms_empty = _time_launches(torch, lambda i: lib.qdm_probe_empty(wgs, st), 2000)
+    ms_empty = time_batch(torch, lambda i: lib.qdm_probe_empty(wgs, st), 1, 2000)
     return {"hbm_read_GBps": big / ms_hbm / 1e6, "mall_read_GBps": small / ms_mall / 1e6,
             "read_us_by_size_hbm": reads,
             "mfma_bf16_TFLOPs": flops / ms_mfma / 1e9,
             "mfma_shader_clock_MHz": mhz,
             "empty_launch_us": ms_empty * 1e3,
-            "notes": "read: qdm_probe_read; mfma: qdm_probe_mfma (%d workgroups x 4 waves x %d x 8 "
+            "notes": "read: qdm_probe_read (a contiguous slice per workgroup), C ABI launches back to back; mfma: qdm_probe_mfma (%d workgroups x 4 waves x %d x 8 "
                      "v_mfma_f32_32x32x16_bf16); clock = s_memtime / s_memrealtime ticks x "
                      "100 MHz; empty: back-to-back C ABI launches of %d idle workgroups"
                      % (wgs, iters, wgs)}

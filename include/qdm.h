@@ -310,7 +310,8 @@ int qdm_probe_copy(const void *src, void *dst, int64_t n_bytes, void *stream);
  * Roofline probes (the same source: measured roofs beside the nominal ones).
  * qdm_probe_read: reads the n_bytes of src once (n_bytes % 16 == 0, src
  *   16-byte aligned), a read-only HBM (or, for a buffer re-read while it fits
- *   the 256 MB last-level cache, cache) stream; sink is a 4-byte device word
+ *   the 256 MB last-level cache, cache) stream, each of up to 1024
+ *   workgroups reading one contiguous slice; sink is a 4-byte device word
  *   the kernel may write (so no load can be dropped).
  * qdm_probe_mfma: `workgroups` workgroups of four waves, each wave issuing
  *   iters x 8 back-to-back bf16 MFMAs of 32 x 32 x 16 (32768 flops each);

@@ -4,8 +4,8 @@
 // DRAM read, per-launch cost and bf16 GEMM).
 //  * probe_copy: streaming copy of a known byte count, also the calibration
 //    kernel of the memory-traffic counters;
-//  * probe_read: read-only stream (every byte read once, 16-byte
-//    non-temporal loads, four in flight per thread);
+//  * probe_read: read-only stream (every byte read once, a contiguous slice
+//    per workgroup, 16-byte non-temporal loads, four 4 KiB steps in flight);
 //  * probe_mfma: back-to-back bf16 MFMAs (v_mfma_f32_32x32x16_bf16, eight
 //    independent accumulators per wave) with the shader clock and the
 //    100 MHz reference clock read around the loop;
@@ -30,30 +30,38 @@ void launch_probe_copy(const void *src, void *dst, int64_t n_bytes, hipStream_t 
                      (const u32x4 *)src, (u32x4 *)dst, n16);
 }
 
-// The xor of everything read decides a store that practically never happens
-// (sink must be a valid 4-byte buffer all the same), so no load is dropped.
-__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4 *__restrict__ src,
-                                                         int64_t n16, uint32_t *__restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Workgroup b reads its own contiguous slice of the buffer front to back, a
+// 4 KiB step per iteration (256 threads x 16 bytes, non-temporal), four steps
+// in flight. Reading a contiguous slice per workgroup sustains about 7 TB/s
+// on MI355X; a grid-stride walk (every thread's loads spread over the whole
+// buffer) topped out near 5.6 TB/s at 2048 workgroups. The xor of everything
+// read decides a store that practically never happens (sink must be a valid
+// 4-byte buffer all the same), so no load is dropped.
+constexpr int PR_THREADS = 256, PR_STEPS = 4, PR_WGS = 1024;
+__global__ __launch_bounds__(PR_THREADS) void probe_read_kernel(const u32x4 *__restrict__ src,
+                                                                int64_t n16, uint32_t *__restrict__ sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= (a ^ b) ^ (c ^ d);
+  int64_t i = b0 + threadIdx.x;
+  for (; i + (PR_STEPS - 1) * PR_THREADS < b1; i += PR_STEPS * PR_THREADS) {
+    u32x4 v[PR_STEPS];
+#pragma unroll
+    for (int u = 0; u < PR_STEPS; u++) v[u] = __builtin_nontemporal_load(src + i + u * PR_THREADS);
+#pragma unroll
+    for (int u = 0; u < PR_STEPS; u++) acc ^= v[u];
   }
-  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  for (; i < b1; i += PR_THREADS) acc ^= __builtin_nontemporal_load(src + i);
   const uint32_t v = (acc.x ^ acc.y) ^ (acc.z ^ acc.w);
   if (v == 0x9E3779B9u) sink[0] = v;
 }
 
 void launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, hipStream_t s) {
   const int64_t n16 = n_bytes / 16;
-  int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 256 * 8) blocks = 256 * 8;  // eight workgroups per compute unit
-  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+  int64_t blocks = (n16 + PR_THREADS - 1) / PR_THREADS;  // at least one 4 KiB step each
+  if (blocks > PR_WGS) blocks = PR_WGS;
+  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(PR_THREADS), 0, s,
                      (const u32x4 *)src, n16, sink);
 }
 
