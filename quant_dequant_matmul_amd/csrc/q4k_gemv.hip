@@ -325,12 +325,15 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 //
 // Every wave instruction reads 1 KiB of consecutive bytes: a wave loads a
 // span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB; Q5_K 64 x 176 B
-// = 11 x 1 KiB) with
-// non-temporal 16-byte loads, keeps two spans in flight in registers while it
-// computes a third, and moves each span through its own LDS buffer so that
-// lane l receives whole block l. One lane then decodes a whole super-block: the header once
-// per 256 weights, the codes with one v_and_or_b32 per two codes and
-// v_dot2_f32_bf16 against x.
+// = 11 x 1 KiB) with non-temporal 16-byte loads from a wave-uniform base, keeps
+// the next span in flight in registers while it computes the current one, and
+// moves each span through its own LDS buffer so that lane l receives whole
+// block l. One lane then decodes a whole super-block: the header once per 256
+// weights, the codes with one v_and_or_b32 per two codes and v_dot2_f32_bf16
+// against x. Eight waves per workgroup, two per SIMD: once the memory queues
+// are full a wave stalls at its next load, and its SIMD then runs the other
+// wave's block math (one wave per SIMD with two spans in flight left the math
+// and the stalls in series).
 // x lives in LDS as 560-byte records per 256-element column block: 512 bytes
 // of bf16 (groups of four stored as x0, x2, x1, x3), the eight 32-element sums,
 // and 16 bytes of padding so that lanes reading consecutive column blocks hit
@@ -348,36 +351,16 @@ constexpr int DN_XREC = 560;                          // LDS bytes per x column 
 constexpr int DN_TARGET_WGS = 256;      // workgroups per launch (one per CU)
 constexpr int DN_MAX_WG_BLOCKS = 8192;
 constexpr size_t DN_LDS_LIMIT = 160 * 1024;
-constexpr int DN_WAVES = 4;  // waves per workgroup of the dense kernel
+constexpr int DN_WAVES = 8;  // waves per workgroup of the dense kernel
 
 template <int NCH>
 struct Span {
   u32x4 r[NCH];
 };
 
-// A full span: NCH KiB from one base, chunk j at byte 1024 j + 16 lane.
-template <int NCH>
-__device__ __forceinline__ void load_span_full(Span<NCH> &sp, const uint8_t *__restrict__ base,
-                                               int lane) {
-  const uint8_t *p = base + 16 * lane;
-#pragma unroll
-  for (int j = 0; j < NCH; j++)
-    sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(p + 1024 * j));
-}
-
 // Loads are unconditional so the compiler can count outstanding loads and
 // wait for exactly the span it needs (a load behind a branch forces it to wait
-// for every load in flight). Chunks past the end of a partial span re-read the
-// span's last chunk, which is already in flight.
-template <int NCH>
-__device__ __forceinline__ void load_span(Span<NCH> &sp, const uint8_t *__restrict__ base,
-                                          int nbytes, int lane) {
-#pragma unroll
-  for (int j = 0; j < NCH; j++) {
-    const int off = min(1024 * j + 16 * lane, nbytes - 16);
-    sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
-  }
-}
+// for every load in flight).
 
 // x staging in two phases: every x load is issued first (before any weight
 // load, so waiting for x never waits for weights), then the chunks are
@@ -423,6 +406,13 @@ struct XStage {
 };
 
 // sum_k x[k] * w(k) over one super-block held in LDS (blk), x record xr.
+// Per sub-block j (32 weights, 6-bit scale sc_j and min m_j):
+//   sum_l x_l w_l = d sc_j sum_l x_l q_l - dmin m_j xs_j,  xs_j = sum_l x_l,
+// so the block is d * sum_j sc_j t_j - dmin * sum_j m_j xs_j with integer-valued
+// sc_j, m_j and t_j = sum_l x_l q_l. The code pairs enter v_dot2 as the bf16
+// values 128 + q, so t_j's sum starts at -128 xs_j. The twelve scale bytes are
+// unpacked four at a time with word masks (j < 4: low 6 bits of bytes 0-3 and
+// 4-7; j >= 4: low/high nibble of bytes 8-11 and the top 2 bits of bytes 0-7).
 // Q5_K (Q5): codes at 48 and the high-bit plane at 16; the code bytes are
 // assembled (nibble | bit 2cc or 2cc+1 of the plane << 4) and picked with
 // MASK = 0x00FF00FF instead of 0x000F000F.
@@ -434,15 +424,24 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
   const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
   const f32x4 xsa = *(const f32x4 *)(xr + 512), xsb = *(const f32x4 *)(xr + 528);
   const float xs[8] = {xsa.x, xsa.y, xsa.z, xsa.w, xsb.x, xsb.y, xsb.z, xsb.w};
-  float r = 0.f;
+  const uint32_t S0 = hdr.y, S1 = hdr.z, S2 = hdr.w;
+  const uint32_t sc_lo = S0 & 0x3F3F3F3Fu, m_lo = S1 & 0x3F3F3F3Fu;
+  const uint32_t sc_hi = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+  const uint32_t m_hi = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+  const float sc[8] = {(float)(sc_lo & 255u), (float)((sc_lo >> 8) & 255u),
+                       (float)((sc_lo >> 16) & 255u), (float)(sc_lo >> 24),
+                       (float)(sc_hi & 255u), (float)((sc_hi >> 8) & 255u),
+                       (float)((sc_hi >> 16) & 255u), (float)(sc_hi >> 24)};
+  const float mn[8] = {(float)(m_lo & 255u), (float)((m_lo >> 8) & 255u),
+                       (float)((m_lo >> 16) & 255u), (float)(m_lo >> 24),
+                       (float)(m_hi & 255u), (float)((m_hi >> 8) & 255u),
+                       (float)((m_hi >> 16) & 255u), (float)(m_hi >> 24)};
+  float tsum = 0.f, msum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) msum = fmaf(mn[j], xs[j], msum);
 #pragma unroll
   for (int cc = 0; cc < 4; cc++) {
     const int j0 = 2 * cc;
-    uint32_t sc0, m0, sc1, m1;
-    q4k_scale_min(hdr.y, hdr.z, hdr.w, j0, sc0, m0);
-    q4k_scale_min(hdr.y, hdr.z, hdr.w, j0 + 1, sc1, m1);
-    const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
-    const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
     const u32x4 qa = *(const u32x4 *)(blk + QOFF + 32 * cc);
     const u32x4 qb = *(const u32x4 *)(blk + QOFF + 16 + 32 * cc);
     const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
@@ -466,7 +465,7 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
     }
     const u32x4 *xv0 = (const u32x4 *)(xr + 64 * j0);
     const u32x4 *xv1 = (const u32x4 *)(xr + 64 * (j0 + 1));
-    float s0 = 0.f, s1 = 0.f;
+    float s0 = -128.f * xs[j0], s1 = -128.f * xs[j0 + 1];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       const u32x4 x0 = xv0[t], x1 = xv1[t];
@@ -481,24 +480,24 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
       s1 = dot2_bf16((qd14 & MASK) | MAGIC, x1.z, s1);
       s1 = dot2_bf16(((qd14 >> 8) & MASK) | MAGIC, x1.w, s1);
     }
-    r = fmaf(a0, s0, r);
-    r = fmaf(-fmaf(128.f, a0, b0), xs[j0], r);
-    r = fmaf(a1, s1, r);
-    r = fmaf(-fmaf(128.f, a1, b1), xs[j0 + 1], r);
+    tsum = fmaf(sc[j0], s0, tsum);
+    tsum = fmaf(sc[j0 + 1], s1, tsum);
     // keep each sub-block pair's LDS reads next to its math
     __builtin_amdgcn_sched_barrier(0);
   }
-  return r;
+  return d * tsum - dmin * msum;
 }
 
-// WAVES waves per workgroup. Each wave holds two spans in registers: while it
-// computes one span (from its LDS buffer), the next two are in flight. Spans
-// are handed out in order from a workgroup counter, so a wave whose data
-// arrived late takes fewer spans and the waves finish together.
+// WAVES waves per workgroup. Each wave holds one span in registers while it
+// computes the previous one from its LDS buffer. Spans are handed out in order
+// from a workgroup counter, so a wave whose data arrived late takes fewer
+// spans and the waves finish together. nb_magic = ceil(2^32 / nb) gives the
+// column block of block b as b - nb * umulhi(b, nb_magic), exact while
+// b * nb < 2^32 (b < 8192 + nb here).
 template <int WAVES, int XC, bool Q5>
 __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int K, int rows_q, int rows_rem) {
+    int K, int rows_q, int rows_rem, uint32_t nb_magic) {
   constexpr int DN_THREADS = WAVES * WAVE;
   constexpr int BB = dn_block_bytes<Q5>();
   constexpr int DN_SPAN_BYTES = dn_span_bytes<Q5>();
@@ -521,16 +520,19 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   const int nfull = nblk / DN_SPAN;  // spans before nfull are full
 
   // A span index past the end loads the last span again (its bytes are
-  // already on their way), so every wave issues the same loads in every
-  // iteration and the compiler can wait for exactly the span it needs. Both
-  // branches issue the same NCH loads into the same registers.
+  // already on their way), so every wave issues the same NCH loads in every
+  // iteration and the compiler can wait for exactly the span it needs. The
+  // span base is wave-uniform; lane offsets past the end of a partial span
+  // are clamped to its last 16 bytes.
   auto issue = [&](Span<NCH> &r, int sidx) {
     const int si = min(sidx, nspan - 1);
     const uint8_t *base = wbase + (int64_t)si * DN_SPAN_BYTES;
-    if (si < nfull)
-      load_span_full<NCH>(r, base, lane);
-    else
-      load_span<NCH>(r, base, (nblk - DN_SPAN * si) * BB, lane);
+    const int lim = (si < nfull ? DN_SPAN_BYTES : (nblk - DN_SPAN * si) * BB) - 16;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+      const uint32_t off = (uint32_t)min(1024 * j + 16 * lane, lim);
+      r.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
+    }
   };
   auto grab = [&]() {
     int v = 0;
@@ -540,41 +542,37 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
 
   XStage<DN_THREADS, XC> xst;
   xst.load(x, K);
-  if (threadIdx.x == 0) next_span = 2 * WAVES;
-  int sidx[2] = {wave, WAVES + wave};
-  // x loads, the first span, the x records, then the second span: x does not
-  // wait behind the whole initial burst of weight loads (measured fastest)
-  Span<NCH> R[2];
-  issue(R[0], sidx[0]);
+  if (threadIdx.x == 0) next_span = WAVES;
+  int sidx = wave;
+  // x loads, the first span, then the x records: x does not wait behind the
+  // workgroup's whole initial burst of weight loads
+  Span<NCH> R;
+  issue(R, sidx);
   xst.store(K, xrec);
-  issue(R[1], sidx[1]);
   __syncthreads();
 
   const uint32_t MASK = opaque(Q5 ? 0x00FF00FFu : 0x000F000Fu), MAGIC = opaque(0x43004300u);
   uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
-  while (sidx[0] < nspan || sidx[1] < nspan) {
+  while (sidx < nspan) {
+    const int cur = sidx;
+    if (cur < nfull) {
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      const int cur = sidx[p];
-      if (cur < nfull) {
+      for (int j = 0; j < NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R.r[j];
+    } else {
+      const int nbytes = (nblk - DN_SPAN * cur) * BB;
 #pragma unroll
-        for (int j = 0; j < NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R[p].r[j];
-      } else {
-        const int nbytes = cur < nspan ? (nblk - DN_SPAN * cur) * BB : 0;
-#pragma unroll
-        for (int j = 0; j < NCH; j++) {
-          const int off = 1024 * j + 16 * lane;
-          if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
-        }
+      for (int j = 0; j < NCH; j++) {
+        const int off = 1024 * j + 16 * lane;
+        if (off < nbytes) *(u32x4 *)(mybuf + off) = R.r[j];
       }
-      // refill this slot right away: two spans stay in flight during the math
-      const int nxt = cur < nspan ? grab() : nspan;
-      issue(R[p], nxt);
-      sidx[p] = nxt;
-      const int b = DN_SPAN * cur + lane;
-      if (cur < nspan && b < nblk)
-        part[b] = q4k_block_dot_bf16<Q5>(mybuf + BB * lane, xrec + (b % nb) * DN_XREC, MASK,
-                                         MAGIC);
+    }
+    // refill right away: the next span is in flight during the math
+    sidx = grab();
+    issue(R, sidx);
+    const int b = DN_SPAN * cur + lane;
+    if (b < nblk) {
+      const uint32_t kb = nb == 1 ? 0u : (uint32_t)b - (uint32_t)nb * __umulhi((uint32_t)b, nb_magic);
+      part[b] = q4k_block_dot_bf16<Q5>(mybuf + BB * lane, xrec + kb * DN_XREC, MASK, MAGIC);
     }
   }
   __syncthreads();
@@ -628,8 +626,11 @@ void launch_dense(const void *w, const void *x, float *y, int64_t K, int64_t nwg
   auto kern = q4k_gemv_m1_kernel<DN_WAVES, XC, Q5>;
   (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
+  const uint64_t nb = (uint64_t)(K / QK);
+  const uint32_t nb_magic = (uint32_t)((((uint64_t)1 << 32) + nb - 1) / nb);  // unused for nb = 1
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(DN_WAVES * WAVE), lds, s,
-                     (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem);
+                     (const uint8_t *)w, (const uint16_t *)x, y, (int)K, rows_q, rows_rem,
+                     nb_magic);
 }
 
 template <bool XBF16, int MT, bool Q5>
