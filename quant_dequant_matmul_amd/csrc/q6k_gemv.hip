@@ -758,10 +758,12 @@ void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64
 // M = 1, bf16 x: dense-span kernel. A workgroup (one per compute unit) owns
 // a balanced range of whole rows whose bytes start on a 16-byte boundary
 // (rows are handed out in units of u = 8 / gcd(K/256, 8), so r0 * K/256 * 210
-// is a multiple of 16). Its waves take spans of 64 consecutive blocks (13440
-// bytes: thirteen 1-KiB loads per lane plus 128 bytes) from a workgroup
-// counter, keep two spans in flight in registers while computing a third from
-// their own LDS buffer, where lane l takes whole block l: four (half, 16-lane
+// is a multiple of 16). Its eight waves (two per SIMD: one wave's math runs
+// while the other stalls on a full memory queue) take spans of 64 consecutive
+// blocks (13440 bytes: thirteen 1-KiB loads per lane plus 128 bytes) from a
+// workgroup counter, keep the next span in flight in registers while
+// computing the current one from their own LDS buffer, where lane l takes
+// whole block l: four (half, 16-lane
 // offset) quarters, each read as aligned dwords shifted by v_alignbyte, with
 // the same pair arithmetic as the VALU path. x is staged once per workgroup as
 // 592-byte records per 256 columns: 512 bytes of bf16 in (x0, x2, x1, x3)
@@ -772,7 +774,7 @@ constexpr int Q6D_SPAN = 64;                                    // blocks per sp
 constexpr int Q6D_SPAN_BYTES = Q6D_SPAN * Q6K_BYTES;            // 13440
 constexpr int Q6D_NCH = (Q6D_SPAN_BYTES + 1023) / 1024;         // 14 loads per lane
 constexpr int Q6D_XREC = 592;
-constexpr int Q6D_WAVES = 4;
+constexpr int Q6D_WAVES = 8;
 constexpr int Q6D_THREADS = Q6D_WAVES * WAVE;
 constexpr int Q6D_TARGET_WGS = 256;
 constexpr size_t Q6D_LDS_LIMIT = 160 * 1024;
@@ -876,14 +878,15 @@ __global__ __launch_bounds__(Q6D_THREADS) void q6k_gemv_m1_kernel(
 
   // Span si past the end reloads the last span; a chunk past the end of a
   // partial span re-reads its last 16 bytes (every span size is a multiple of
-  // 16 bytes). Loads are unconditional so the waits count exactly.
+  // 16 bytes). Loads are unconditional so the waits count exactly; the span
+  // base is wave-uniform and the lane offsets 32-bit.
   auto issue = [&](Q6Span &sp, int sidx) {
     const int si = __builtin_amdgcn_readfirstlane(min(sidx, nspan - 1));
-    const int nbytes = min(Q6D_SPAN, nblk - Q6D_SPAN * si) * Q6K_BYTES;
+    const int lim = min(Q6D_SPAN, nblk - Q6D_SPAN * si) * Q6K_BYTES - 16;
     const uint8_t *base = wbase + (int64_t)si * Q6D_SPAN_BYTES;
 #pragma unroll
     for (int j = 0; j < Q6D_NCH; j++) {
-      const int off = min(1024 * j + 16 * lane, nbytes - 16);
+      const uint32_t off = (uint32_t)min(1024 * j + 16 * lane, lim);
       sp.r[j] = __builtin_nontemporal_load((const u32x4 *)(base + off));
     }
   };
@@ -895,42 +898,37 @@ __global__ __launch_bounds__(Q6D_THREADS) void q6k_gemv_m1_kernel(
 
   Q6XStage<XC> xst;
   xst.load(x, K);
-  if (threadIdx.x == 0) next_span = 2 * Q6D_WAVES;
-  int sidx[2] = {wave, Q6D_WAVES + wave};
-  Q6Span R[2];
-  issue(R[0], sidx[0]);
+  if (threadIdx.x == 0) next_span = Q6D_WAVES;
+  int sidx = wave;
+  Q6Span R;
+  issue(R, sidx);
   xst.store(K, xrec);
-  issue(R[1], sidx[1]);
   __syncthreads();
 
   uint8_t *mybuf = spanbuf + wave * Q6D_SPAN_BYTES;
-  while (sidx[0] < nspan || sidx[1] < nspan) {
+  while (sidx < nspan) {
+    const int cur = sidx;
+    const int nbytes = min(Q6D_SPAN, nblk - Q6D_SPAN * cur) * Q6K_BYTES;
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      const int cur = sidx[p];
-      const int nbytes = cur < nspan ? min(Q6D_SPAN, nblk - Q6D_SPAN * cur) * Q6K_BYTES : 0;
+    for (int j = 0; j < Q6D_NCH; j++) {
+      const int off = 1024 * j + 16 * lane;
+      if (off < nbytes) *(u32x4 *)(mybuf + off) = R.r[j];
+    }
+    // refill right away: the next span is in flight during the math
+    sidx = grab();
+    issue(R, sidx);
+    const int b = Q6D_SPAN * cur + lane;
+    if (b < nblk) {
+      const int kb = nb == 1 ? 0 : b - q6_div(b, nb_magic) * nb;
+      const uint8_t *xr = xrec + kb * Q6D_XREC;
+      const int off = Q6K_BYTES * lane;
+      float r = 0.f;
 #pragma unroll
-      for (int j = 0; j < Q6D_NCH; j++) {
-        const int off = 1024 * j + 16 * lane;
-        if (off < nbytes) *(u32x4 *)(mybuf + off) = R[p].r[j];
+      for (int qd = 0; qd < 4; qd++) {
+        const int h = qd >> 1, l0 = 16 * (qd & 1);
+        r += q6_quarter_rec(q6_load(mybuf, off, h, l0), xr, h, l0);
       }
-      // refill this slot right away: two spans stay in flight during the math
-      const int nxt = cur < nspan ? grab() : nspan;
-      issue(R[p], nxt);
-      sidx[p] = nxt;
-      const int b = Q6D_SPAN * cur + lane;
-      if (cur < nspan && b < nblk) {
-        const int kb = nb == 1 ? 0 : b - q6_div(b, nb_magic) * nb;
-        const uint8_t *xr = xrec + kb * Q6D_XREC;
-        const int off = Q6K_BYTES * lane;
-        float r = 0.f;
-#pragma unroll
-        for (int qd = 0; qd < 4; qd++) {
-          const int h = qd >> 1, l0 = 16 * (qd & 1);
-          r += q6_quarter_rec(q6_load(mybuf, off, h, l0), xr, h, l0);
-        }
-        part[b] = r;
-      }
+      part[b] = r;
     }
   }
   __syncthreads();
@@ -958,9 +956,11 @@ bool q6_dense_plan(int64_t N, int64_t K, int &unit, int &units_q, int &units_rem
   const size_t fixed = (size_t)Q6D_WAVES * Q6D_SPAN_BYTES + (size_t)nb * Q6D_XREC;
   if (fixed + (size_t)unit * nb * 4 * 2 > Q6D_LDS_LIMIT) return false;
   const int64_t cap_units = (int64_t)((Q6D_LDS_LIMIT - fixed) / ((size_t)unit * nb * 4)) - 1;
+  // one workgroup per compute unit, or a whole multiple of that when the
+  // block partials need more (the output head: 512, two rounds of equal size)
   nwg = Q6D_TARGET_WGS;
   const int64_t need = (units + cap_units - 1) / cap_units;
-  if (need > nwg) nwg = need;
+  if (need > nwg) nwg = (need + Q6D_TARGET_WGS - 1) / Q6D_TARGET_WGS * Q6D_TARGET_WGS;
   if (nwg > units) nwg = units;
   units_q = (int)(units / nwg);
   units_rem = (int)(units % nwg);
@@ -988,7 +988,9 @@ bool q6_try_dense(const void *w, const void *x, float *y, int64_t N, int64_t K, 
   size_t lds;
   if (!q6_dense_plan(N, K, unit, units_q, units_rem, nwg, lds)) return false;
   const int64_t xc = (K / 8 + Q6D_THREADS - 1) / Q6D_THREADS;
-  if (xc <= 4)
+  if (xc <= 2)
+    q6_launch_dense<2>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
+  else if (xc <= 4)
     q6_launch_dense<4>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
   else if (xc <= 8)
     q6_launch_dense<8>(w, x, y, N, K, unit, units_q, units_rem, nwg, lds, s);
@@ -1016,15 +1018,11 @@ void launch_q4k_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M,
 
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
-  // M = 1, bf16 x: the dense-span kernel when the VALU kernel would have fewer
-  // than 8 row groups per compute unit (it hands out whole row groups, so few
-  // of them leave some units with twice the work: 320 for the down shape K =
-  // 17408, N = 5120, 35.6 -> 29.7 us); with many row groups (the output head,
-  // 9496) the VALU kernel is balanced and faster (151 against 170 us).
-  if (M == 1 && x_bf16 && ((uintptr_t)w & 15) == 0) {
-    const int64_t rows_rg = (256 / WAVE) * (16 / gcd16((int)(K / QK)));
-    if ((N + rows_rg - 1) / rows_rg < 8 * 256 && q6_try_dense(w, x, y, N, K, s)) return;
-  }
+  // M = 1, bf16 x: the dense-span kernel whenever its plan fits (K up to about
+  // 24K). It runs the down shape K = 17408, N = 5120 in 21.8 us and the output
+  // head K = 5120, N = 151936 in 114.5 us, against 25.5 us (its 4-wave form)
+  // and 136-138 us (the VALU kernel, which hands out whole row groups).
+  if (M == 1 && x_bf16 && ((uintptr_t)w & 15) == 0 && q6_try_dense(w, x, y, N, K, s)) return;
   if (x_bf16 && M >= Q6_MFMA_MIN_M) {
     launch_kq_mfma<MfQ6>(w, (const uint16_t *)x, y, M, N, K, s);
     return;
