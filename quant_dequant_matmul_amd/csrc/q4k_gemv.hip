@@ -414,8 +414,8 @@ struct XStage {
 // unpacked four at a time with word masks (j < 4: low 6 bits of bytes 0-3 and
 // 4-7; j >= 4: low/high nibble of bytes 8-11 and the top 2 bits of bytes 0-7).
 // Q5_K (Q5): codes at 48 and the high-bit plane at 16; the code bytes are
-// assembled (nibble | bit 2cc or 2cc+1 of the plane << 4) and picked with
-// MASK = 0x00FF00FF instead of 0x000F000F.
+// assembled (nibble | bit 2cc or 2cc+1 of the plane << 4), and v_perm_b32
+// forms the bf16 pairs from them (MAGIC = 0x43434343 then).
 template <bool Q5>
 __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const uint8_t *xr,
                                                     uint32_t MASK, uint32_t MAGIC) {
@@ -471,14 +471,27 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
       const u32x4 x0 = xv0[t], x1 = xv1[t];
       const uint32_t qd0 = lo[2 * t], qd1 = lo[2 * t + 1];
       const uint32_t qd04 = hi[2 * t], qd14 = hi[2 * t + 1];
-      s0 = dot2_bf16((qd0 & MASK) | MAGIC, x0.x, s0);
-      s0 = dot2_bf16(((qd0 >> 8) & MASK) | MAGIC, x0.y, s0);
-      s0 = dot2_bf16((qd1 & MASK) | MAGIC, x0.z, s0);
-      s0 = dot2_bf16(((qd1 >> 8) & MASK) | MAGIC, x0.w, s0);
-      s1 = dot2_bf16((qd04 & MASK) | MAGIC, x1.x, s1);
-      s1 = dot2_bf16(((qd04 >> 8) & MASK) | MAGIC, x1.y, s1);
-      s1 = dot2_bf16((qd14 & MASK) | MAGIC, x1.z, s1);
-      s1 = dot2_bf16(((qd14 >> 8) & MASK) | MAGIC, x1.w, s1);
+      if constexpr (Q5) {
+        // whole code bytes: v_perm_b32 picks bytes (0, 2) or (1, 3) and sets
+        // the high byte of each half to 0x43 (MAGIC holds 0x43 in every byte)
+        s0 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd0, 0x04020400u), x0.x, s0);
+        s0 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd0, 0x04030401u), x0.y, s0);
+        s0 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd1, 0x04020400u), x0.z, s0);
+        s0 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd1, 0x04030401u), x0.w, s0);
+        s1 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd04, 0x04020400u), x1.x, s1);
+        s1 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd04, 0x04030401u), x1.y, s1);
+        s1 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd14, 0x04020400u), x1.z, s1);
+        s1 = dot2_bf16(__builtin_amdgcn_perm(MAGIC, qd14, 0x04030401u), x1.w, s1);
+      } else {
+        s0 = dot2_bf16((qd0 & MASK) | MAGIC, x0.x, s0);
+        s0 = dot2_bf16(((qd0 >> 8) & MASK) | MAGIC, x0.y, s0);
+        s0 = dot2_bf16((qd1 & MASK) | MAGIC, x0.z, s0);
+        s0 = dot2_bf16(((qd1 >> 8) & MASK) | MAGIC, x0.w, s0);
+        s1 = dot2_bf16((qd04 & MASK) | MAGIC, x1.x, s1);
+        s1 = dot2_bf16(((qd04 >> 8) & MASK) | MAGIC, x1.y, s1);
+        s1 = dot2_bf16((qd14 & MASK) | MAGIC, x1.z, s1);
+        s1 = dot2_bf16(((qd14 >> 8) & MASK) | MAGIC, x1.w, s1);
+      }
     }
     tsum = fmaf(sc[j0], s0, tsum);
     tsum = fmaf(sc[j0 + 1], s1, tsum);
@@ -551,7 +564,7 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   xst.store(K, xrec);
   __syncthreads();
 
-  const uint32_t MASK = opaque(Q5 ? 0x00FF00FFu : 0x000F000Fu), MAGIC = opaque(0x43004300u);
+  const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(Q5 ? 0x43434343u : 0x43004300u);
   uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
   while (sidx < nspan) {
     const int cur = sidx;

@@ -133,22 +133,26 @@ __device__ __forceinline__ void q6_dsc(const Q6Lane &L, int l0, float (&dsc)[4])
 
 // The 64 codes of lane (h, l0) as bf16 pairs 128 + q (exact: q < 64 fits the
 // 7-bit mantissa at exponent 7): pr[gq][2k + e] for group gq, code dword k,
-// e = 0 -> (l, l+2), 1 -> (l+1, l+3).
+// e = 0 -> (l, l+2), 1 -> (l+1, l+3). Four 6-bit codes are first assembled as
+// bytes (low nibble from ql | two bits of qh << 4); v_perm_b32 then picks
+// bytes (0, 2) or (1, 3) and sets the high byte of each half to 0x43.
 __device__ __forceinline__ void q6_pairs(const Q6Lane &L, uint32_t (&pr)[4][8]) {
   const uint32_t qa[4] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w};
   const uint32_t qb[4] = {L.qb.x, L.qb.y, L.qb.z, L.qb.w};
   const uint32_t qh[4] = {L.qh.x, L.qh.y, L.qh.z, L.qh.w};
+  const uint32_t EXP = 0x43434343u;
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     const uint32_t a = qa[k], b = qb[k], hh = qh[k];
-    pr[0][2 * k + 0] = (a & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | 0x43004300u;
-    pr[0][2 * k + 1] = ((a >> 8) & 0x000F000Fu) | ((hh >> 4) & 0x00300030u) | 0x43004300u;
-    pr[1][2 * k + 0] = (b & 0x000F000Fu) | ((hh << 2) & 0x00300030u) | 0x43004300u;
-    pr[1][2 * k + 1] = ((b >> 8) & 0x000F000Fu) | ((hh >> 6) & 0x00300030u) | 0x43004300u;
-    pr[2][2 * k + 0] = ((a >> 4) & 0x000F000Fu) | (hh & 0x00300030u) | 0x43004300u;
-    pr[2][2 * k + 1] = ((a >> 12) & 0x000F000Fu) | ((hh >> 8) & 0x00300030u) | 0x43004300u;
-    pr[3][2 * k + 0] = ((b >> 4) & 0x000F000Fu) | ((hh >> 2) & 0x00300030u) | 0x43004300u;
-    pr[3][2 * k + 1] = ((b >> 12) & 0x000F000Fu) | ((hh >> 10) & 0x00300030u) | 0x43004300u;
+    const uint32_t c[4] = {(a & 0x0F0F0F0Fu) | ((hh << 4) & 0x30303030u),
+                           (b & 0x0F0F0F0Fu) | ((hh << 2) & 0x30303030u),
+                           ((a >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u),
+                           ((b >> 4) & 0x0F0F0F0Fu) | ((hh >> 2) & 0x30303030u)};
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      pr[g][2 * k + 0] = __builtin_amdgcn_perm(EXP, c[g], 0x04020400u);
+      pr[g][2 * k + 1] = __builtin_amdgcn_perm(EXP, c[g], 0x04030401u);
+    }
   }
 }
 
