@@ -323,30 +323,35 @@ __global__ __launch_bounds__(GV_THREADS) void q4k_gemv_kernel(
 // ---------------------------------------------------------------------------
 // M = 1, bf16 x: dense-span kernel (the decode hot path).
 //
-// Every wave instruction reads 1 KiB of consecutive bytes: a wave loads a
-// span of 64 consecutive super-blocks (64 x 144 B = 9 x 1 KiB; Q5_K 64 x 176 B
-// = 11 x 1 KiB) with non-temporal 16-byte loads from a wave-uniform base, keeps
-// the next span in flight in registers while it computes the current one, and
-// moves each span through its own LDS buffer so that lane l receives whole
-// block l. One lane then decodes a whole super-block: the header once per 256
-// weights, the codes with one v_and_or_b32 per two codes and v_dot2_f32_bf16
-// against x. Eight waves per workgroup, two per SIMD: once the memory queues
-// are full a wave stalls at its next load, and its SIMD then runs the other
-// wave's block math (one wave per SIMD with two spans in flight left the math
-// and the stalls in series).
+// A wave loads a span of 32 consecutive super-blocks (32 x 144 B = 4.5 KiB;
+// Q5_K 32 x 176 B = 5.5 KiB) with 1-KiB wave loads of non-temporal 16-byte
+// lane loads from a wave-uniform base (the last load partly re-reads the
+// span's last 16 bytes), keeps the next span in flight in registers while it
+// computes the current one, and moves each span through its own LDS buffer.
+// Two lanes share a super-block there: lane 2i + h decodes code chunks 2h and
+// 2h + 1 of block i (sub-blocks 4h .. 4h+3: the header once per 128 weights,
+// the codes with one v_and_or_b32 per two codes, v_dot2_f32_bf16 against x),
+// and the pair's two halves are added in a fixed order. Half-size spans keep
+// the workgroup's first burst of weight loads small (x, loaded first, is ready
+// sooner) and the last span's math short. Eight waves per workgroup, two per
+// SIMD: once the memory queues are full a wave stalls at its next load, and
+// its SIMD then runs the other wave's block math (one wave per SIMD with two
+// spans in flight left the math and the stalls in series).
 // x lives in LDS as 560-byte records per 256-element column block: 512 bytes
 // of bf16 (groups of four stored as x0, x2, x1, x3), the eight 32-element sums,
 // and 16 bytes of padding so that lanes reading consecutive column blocks hit
 // distinct LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int DN_SPAN = 64;                           // blocks per span, one per lane
-// span bytes: 64 x 144 = 9 x 1 KiB (Q4_K) or 64 x 176 = 11 x 1 KiB (Q5_K)
+constexpr int DN_SPAN = 32;  // blocks per span, two lanes per block
 template <bool Q5>
 constexpr int dn_block_bytes() { return Q5 ? Q5K_BYTES : Q4K_BYTES; }
 template <bool Q5>
 constexpr int dn_span_bytes() { return DN_SPAN * dn_block_bytes<Q5>(); }
+// 1-KiB wave loads per span (5 for Q4_K, 6 for Q5_K) and the LDS buffer they fill
 template <bool Q5>
-constexpr int dn_span_chunks() { return dn_span_bytes<Q5>() / 1024; }
+constexpr int dn_span_chunks() { return (dn_span_bytes<Q5>() + 1023) / 1024; }
+template <bool Q5>
+constexpr int dn_span_buf() { return 1024 * dn_span_chunks<Q5>(); }
 constexpr int DN_XREC = 560;                          // LDS bytes per x column block
 constexpr int DN_TARGET_WGS = 256;      // workgroups per launch (one per CU)
 constexpr int DN_MAX_WG_BLOCKS = 8192;
@@ -405,43 +410,39 @@ struct XStage {
   }
 };
 
-// sum_k x[k] * w(k) over one super-block held in LDS (blk), x record xr.
-// Per sub-block j (32 weights, 6-bit scale sc_j and min m_j):
+// Half h of sum_k x[k] * w(k) over one super-block held in LDS (blk), x
+// record xr: code chunks 2h and 2h + 1, i.e. sub-blocks j = 4h .. 4h+3 (32
+// weights each, 6-bit scale sc_j and min m_j):
 //   sum_l x_l w_l = d sc_j sum_l x_l q_l - dmin m_j xs_j,  xs_j = sum_l x_l,
-// so the block is d * sum_j sc_j t_j - dmin * sum_j m_j xs_j with integer-valued
+// so the half is d * sum_j sc_j t_j - dmin * sum_j m_j xs_j with integer-valued
 // sc_j, m_j and t_j = sum_l x_l q_l. The code pairs enter v_dot2 as the bf16
-// values 128 + q, so t_j's sum starts at -128 xs_j. The twelve scale bytes are
-// unpacked four at a time with word masks (j < 4: low 6 bits of bytes 0-3 and
-// 4-7; j >= 4: low/high nibble of bytes 8-11 and the top 2 bits of bytes 0-7).
+// values 128 + q, so t_j's sum starts at -128 xs_j. The scale bytes are
+// unpacked four at a time with word masks (h = 0: low 6 bits of bytes 0-3 and
+// 4-7; h = 1: low/high nibble of bytes 8-11 and the top 2 bits of bytes 0-7).
 // Q5_K (Q5): codes at 48 and the high-bit plane at 16; the code bytes are
 // assembled (nibble | bit 2cc or 2cc+1 of the plane << 4), and v_perm_b32
 // forms the bf16 pairs from them (MAGIC = 0x43434343 then).
 template <bool Q5>
-__device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const uint8_t *xr,
-                                                    uint32_t MASK, uint32_t MAGIC) {
+__device__ __forceinline__ float q4k_half_dot_bf16(const uint8_t *blk, const uint8_t *xr, int h,
+                                                   uint32_t MASK, uint32_t MAGIC) {
   constexpr int QOFF = Q5 ? 48 : 16;
   const u32x4 hdr = *(const u32x4 *)blk;
   const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
-  const f32x4 xsa = *(const f32x4 *)(xr + 512), xsb = *(const f32x4 *)(xr + 528);
-  const float xs[8] = {xsa.x, xsa.y, xsa.z, xsa.w, xsb.x, xsb.y, xsb.z, xsb.w};
+  const f32x4 xs4 = *(const f32x4 *)(xr + 512 + 16 * h);
+  const float xs[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
   const uint32_t S0 = hdr.y, S1 = hdr.z, S2 = hdr.w;
-  const uint32_t sc_lo = S0 & 0x3F3F3F3Fu, m_lo = S1 & 0x3F3F3F3Fu;
-  const uint32_t sc_hi = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
-  const uint32_t m_hi = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
-  const float sc[8] = {(float)(sc_lo & 255u), (float)((sc_lo >> 8) & 255u),
-                       (float)((sc_lo >> 16) & 255u), (float)(sc_lo >> 24),
-                       (float)(sc_hi & 255u), (float)((sc_hi >> 8) & 255u),
-                       (float)((sc_hi >> 16) & 255u), (float)(sc_hi >> 24)};
-  const float mn[8] = {(float)(m_lo & 255u), (float)((m_lo >> 8) & 255u),
-                       (float)((m_lo >> 16) & 255u), (float)(m_lo >> 24),
-                       (float)(m_hi & 255u), (float)((m_hi >> 8) & 255u),
-                       (float)((m_hi >> 16) & 255u), (float)(m_hi >> 24)};
+  const uint32_t scw = h ? (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u) : S0 & 0x3F3F3F3Fu;
+  const uint32_t mw = h ? ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u) : S1 & 0x3F3F3F3Fu;
+  const float sc[4] = {(float)(scw & 255u), (float)((scw >> 8) & 255u),
+                       (float)((scw >> 16) & 255u), (float)(scw >> 24)};
+  const float mn[4] = {(float)(mw & 255u), (float)((mw >> 8) & 255u),
+                       (float)((mw >> 16) & 255u), (float)(mw >> 24)};
   float tsum = 0.f, msum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; j++) msum = fmaf(mn[j], xs[j], msum);
+  for (int j = 0; j < 4; j++) msum = fmaf(mn[j], xs[j], msum);
 #pragma unroll
-  for (int cc = 0; cc < 4; cc++) {
-    const int j0 = 2 * cc;
+  for (int c2 = 0; c2 < 2; c2++) {
+    const int cc = 2 * h + c2;
     const u32x4 qa = *(const u32x4 *)(blk + QOFF + 32 * cc);
     const u32x4 qb = *(const u32x4 *)(blk + QOFF + 16 + 32 * cc);
     const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
@@ -452,9 +453,9 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
       const uint32_t hbits[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const uint32_t hh = hbits[i] >> (2 * cc);
-        lo[i] = (q[i] & 0x0F0F0F0Fu) | ((hh << 4) & 0x10101010u);
-        hi[i] = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hh << 3) & 0x10101010u);
+        const uint32_t hhb = hbits[i] >> (2 * cc);
+        lo[i] = (q[i] & 0x0F0F0F0Fu) | ((hhb << 4) & 0x10101010u);
+        hi[i] = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hhb << 3) & 0x10101010u);
       }
     } else {
 #pragma unroll
@@ -463,9 +464,9 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
         hi[i] = q[i] >> 4;
       }
     }
-    const u32x4 *xv0 = (const u32x4 *)(xr + 64 * j0);
-    const u32x4 *xv1 = (const u32x4 *)(xr + 64 * (j0 + 1));
-    float s0 = -128.f * xs[j0], s1 = -128.f * xs[j0 + 1];
+    const u32x4 *xv0 = (const u32x4 *)(xr + 128 * cc);
+    const u32x4 *xv1 = (const u32x4 *)(xr + 128 * cc + 64);
+    float s0 = -128.f * xs[2 * c2], s1 = -128.f * xs[2 * c2 + 1];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       const u32x4 x0 = xv0[t], x1 = xv1[t];
@@ -493,8 +494,8 @@ __device__ __forceinline__ float q4k_block_dot_bf16(const uint8_t *blk, const ui
         s1 = dot2_bf16(((qd14 >> 8) & MASK) | MAGIC, x1.w, s1);
       }
     }
-    tsum = fmaf(sc[j0], s0, tsum);
-    tsum = fmaf(sc[j0 + 1], s1, tsum);
+    tsum = fmaf(sc[2 * c2], s0, tsum);
+    tsum = fmaf(sc[2 * c2 + 1], s1, tsum);
     // keep each sub-block pair's LDS reads next to its math
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -515,11 +516,12 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   constexpr int BB = dn_block_bytes<Q5>();
   constexpr int DN_SPAN_BYTES = dn_span_bytes<Q5>();
   constexpr int NCH = dn_span_chunks<Q5>();
+  constexpr int SPAN_BUF = dn_span_buf<Q5>();
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int next_span;
   const int nb = K / QK;
-  uint8_t *spanbuf = smem;                            // [waves][span bytes]
-  uint8_t *xrec = smem + WAVES * DN_SPAN_BYTES;       // [nb][560]
+  uint8_t *spanbuf = smem;                            // [waves][NCH KiB]
+  uint8_t *xrec = smem + WAVES * SPAN_BUF;            // [nb][560]
   float *part = (float *)(xrec + nb * DN_XREC);       // [blocks of this workgroup]
 
   const int bid = blockIdx.x;
@@ -535,8 +537,9 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   // A span index past the end loads the last span again (its bytes are
   // already on their way), so every wave issues the same NCH loads in every
   // iteration and the compiler can wait for exactly the span it needs. The
-  // span base is wave-uniform; lane offsets past the end of a partial span
-  // are clamped to its last 16 bytes.
+  // span base is wave-uniform; lane offsets past the end of a span (the last
+  // 1-KiB load of every span, and a partial span's tail) are clamped to its
+  // last 16 bytes.
   auto issue = [&](Span<NCH> &r, int sidx) {
     const int si = min(sidx, nspan - 1);
     const uint8_t *base = wbase + (int64_t)si * DN_SPAN_BYTES;
@@ -565,28 +568,25 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
   __syncthreads();
 
   const uint32_t MASK = opaque(0x000F000Fu), MAGIC = opaque(Q5 ? 0x43434343u : 0x43004300u);
-  uint8_t *mybuf = spanbuf + wave * DN_SPAN_BYTES;
+  uint8_t *mybuf = spanbuf + wave * SPAN_BUF;
+  const int h = lane & 1;
   while (sidx < nspan) {
     const int cur = sidx;
-    if (cur < nfull) {
+    // every chunk is stored: the buffer holds NCH KiB, and what lies past the
+    // span's bytes is never read
 #pragma unroll
-      for (int j = 0; j < NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R.r[j];
-    } else {
-      const int nbytes = (nblk - DN_SPAN * cur) * BB;
-#pragma unroll
-      for (int j = 0; j < NCH; j++) {
-        const int off = 1024 * j + 16 * lane;
-        if (off < nbytes) *(u32x4 *)(mybuf + off) = R.r[j];
-      }
-    }
+    for (int j = 0; j < NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R.r[j];
     // refill right away: the next span is in flight during the math
     sidx = grab();
     issue(R, sidx);
-    const int b = DN_SPAN * cur + lane;
+    const int b = DN_SPAN * cur + (lane >> 1);
+    float r = 0.f;
     if (b < nblk) {
       const uint32_t kb = nb == 1 ? 0u : (uint32_t)b - (uint32_t)nb * __umulhi((uint32_t)b, nb_magic);
-      part[b] = q4k_block_dot_bf16<Q5>(mybuf + BB * lane, xrec + kb * DN_XREC, MASK, MAGIC);
+      r = q4k_half_dot_bf16<Q5>(mybuf + BB * (lane >> 1), xrec + kb * DN_XREC, h, MASK, MAGIC);
     }
+    r += __shfl_xor(r, 1, WAVE);  // half 0 + half 1 (the same sum on both lanes)
+    if (b < nblk && h == 0) part[b] = r;
   }
   __syncthreads();
 
@@ -619,7 +619,6 @@ __global__ __launch_bounds__(WAVES * WAVE) void q4k_gemv_m1_kernel(
 // Launch geometry of the dense kernel, or false if its LDS does not fit.
 template <int DN_WAVES, bool Q5>
 bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, size_t &lds) {
-  constexpr int DN_SPAN_BYTES = dn_span_bytes<Q5>();
   const int64_t nb = K / QK;
   nwg = DN_TARGET_WGS;
   const int64_t need = (N * nb + DN_MAX_WG_BLOCKS - 1) / DN_MAX_WG_BLOCKS;
@@ -628,7 +627,7 @@ bool dense_plan(int64_t N, int64_t K, int64_t &nwg, int &rows_q, int &rows_rem, 
   rows_q = (int)(N / nwg);
   rows_rem = (int)(N % nwg);
   const int64_t max_blocks = (rows_q + (rows_rem ? 1 : 0)) * nb;
-  lds = (size_t)DN_WAVES * DN_SPAN_BYTES + (size_t)nb * DN_XREC + (size_t)max_blocks * 4;
+  lds = (size_t)DN_WAVES * dn_span_buf<Q5>() + (size_t)nb * DN_XREC + (size_t)max_blocks * 4;
   return lds <= DN_LDS_LIMIT && K / 8 <= (int64_t)16 * DN_WAVES * WAVE;
 }
 
