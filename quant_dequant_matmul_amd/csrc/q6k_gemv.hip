@@ -763,20 +763,22 @@ void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64
 // a balanced range of whole rows whose bytes start on a 16-byte boundary
 // (rows are handed out in units of u = 8 / gcd(K/256, 8), so r0 * K/256 * 210
 // is a multiple of 16). Its eight waves (two per SIMD: one wave's math runs
-// while the other stalls on a full memory queue) take spans of 64 consecutive
-// blocks (13440 bytes: thirteen 1-KiB loads per lane plus 128 bytes) from a
-// workgroup counter, keep the next span in flight in registers while
-// computing the current one from their own LDS buffer, where lane l takes
-// whole block l: four (half, 16-lane
+// while the other stalls on a full memory queue) take spans of 32 consecutive
+// blocks (6720 bytes: six 1-KiB wave loads plus 576 bytes) from a workgroup
+// counter, keep the next span in flight in registers while computing the
+// current one from their own LDS buffer, where lanes 2i and 2i + 1 share
+// block i (lane 2i + h takes its half h, 128 weights, and the two halves are
+// added in a fixed order): two (half, 16-lane
 // offset) quarters, each read as aligned dwords shifted by v_alignbyte, with
 // the same pair arithmetic as the VALU path. x is staged once per workgroup as
 // 592-byte records per 256 columns: 512 bytes of bf16 in (x0, x2, x1, x3)
 // groups, the sixteen 16-column sums, and 16 bytes of padding (a stride of
 // 148 dwords, so consecutive records start 20 banks apart).
 // ---------------------------------------------------------------------------
-constexpr int Q6D_SPAN = 64;                                    // blocks per span
-constexpr int Q6D_SPAN_BYTES = Q6D_SPAN * Q6K_BYTES;            // 13440
-constexpr int Q6D_NCH = (Q6D_SPAN_BYTES + 1023) / 1024;         // 14 loads per lane
+constexpr int Q6D_SPAN = 32;                                    // blocks per span, 2 lanes each
+constexpr int Q6D_SPAN_BYTES = Q6D_SPAN * Q6K_BYTES;            // 6720
+constexpr int Q6D_NCH = (Q6D_SPAN_BYTES + 1023) / 1024;         // 7 loads per lane
+constexpr int Q6D_SPAN_BUF = 1024 * Q6D_NCH;                    // LDS per wave
 constexpr int Q6D_XREC = 592;
 constexpr int Q6D_WAVES = 8;
 constexpr int Q6D_THREADS = Q6D_WAVES * WAVE;
@@ -868,7 +870,7 @@ __global__ __launch_bounds__(Q6D_THREADS) void q6k_gemv_m1_kernel(
   __shared__ int next_span;
   const int nb = K / QK;
   uint8_t *spanbuf = smem;                                    // [waves][span bytes]
-  uint8_t *xrec = smem + Q6D_WAVES * Q6D_SPAN_BYTES;          // [nb][592]
+  uint8_t *xrec = smem + Q6D_WAVES * Q6D_SPAN_BUF;            // [nb][592]
   float *part = (float *)(xrec + nb * Q6D_XREC);              // [blocks of this workgroup]
 
   const int bid = blockIdx.x;
@@ -909,31 +911,28 @@ __global__ __launch_bounds__(Q6D_THREADS) void q6k_gemv_m1_kernel(
   xst.store(K, xrec);
   __syncthreads();
 
-  uint8_t *mybuf = spanbuf + wave * Q6D_SPAN_BYTES;
+  uint8_t *mybuf = spanbuf + wave * Q6D_SPAN_BUF;
+  const int h = lane & 1;
   while (sidx < nspan) {
     const int cur = sidx;
-    const int nbytes = min(Q6D_SPAN, nblk - Q6D_SPAN * cur) * Q6K_BYTES;
+    // every chunk is stored: the buffer holds Q6D_NCH KiB, and what lies past
+    // the span's bytes is never read
 #pragma unroll
-    for (int j = 0; j < Q6D_NCH; j++) {
-      const int off = 1024 * j + 16 * lane;
-      if (off < nbytes) *(u32x4 *)(mybuf + off) = R.r[j];
-    }
+    for (int j = 0; j < Q6D_NCH; j++) *(u32x4 *)(mybuf + 1024 * j + 16 * lane) = R.r[j];
     // refill right away: the next span is in flight during the math
     sidx = grab();
     issue(R, sidx);
-    const int b = Q6D_SPAN * cur + lane;
+    const int b = Q6D_SPAN * cur + (lane >> 1);
+    float r = 0.f;
     if (b < nblk) {
       const int kb = nb == 1 ? 0 : b - q6_div(b, nb_magic) * nb;
       const uint8_t *xr = xrec + kb * Q6D_XREC;
-      const int off = Q6K_BYTES * lane;
-      float r = 0.f;
-#pragma unroll
-      for (int qd = 0; qd < 4; qd++) {
-        const int h = qd >> 1, l0 = 16 * (qd & 1);
-        r += q6_quarter_rec(q6_load(mybuf, off, h, l0), xr, h, l0);
-      }
-      part[b] = r;
+      const int off = Q6K_BYTES * (lane >> 1);
+      r = q6_quarter_rec(q6_load(mybuf, off, h, 0), xr, h, 0);
+      r += q6_quarter_rec(q6_load(mybuf, off, h, 16), xr, h, 16);
     }
+    r += __shfl_xor(r, 1, WAVE);  // half 0 + half 1 (the same sum on both lanes)
+    if (b < nblk && h == 0) part[b] = r;
   }
   __syncthreads();
 
@@ -957,7 +956,7 @@ bool q6_dense_plan(int64_t N, int64_t K, int &unit, int &units_q, int &units_rem
   unit = 8 / g;
   if (N % unit || N > INT32_MAX) return false;
   const int64_t units = N / unit;
-  const size_t fixed = (size_t)Q6D_WAVES * Q6D_SPAN_BYTES + (size_t)nb * Q6D_XREC;
+  const size_t fixed = (size_t)Q6D_WAVES * Q6D_SPAN_BUF + (size_t)nb * Q6D_XREC;
   if (fixed + (size_t)unit * nb * 4 * 2 > Q6D_LDS_LIMIT) return false;
   const int64_t cap_units = (int64_t)((Q6D_LDS_LIMIT - fixed) / ((size_t)unit * nb * 4)) - 1;
   // one workgroup per compute unit, or a whole multiple of that when the
