@@ -8,12 +8,15 @@
 // Mapping. A quad is 4 consecutive blocks of a row: 136 bytes, 128 columns.
 // A row holds an even number of quads, so quads never straddle rows. A
 // workgroup owns a contiguous range of rows, i.e. of quads. Its waves take
-// spans of 64 quads (8704 bytes) from a workgroup counter and load each span
-// with 16-byte non-temporal loads (1 KiB per wave instruction). Two spans stay
-// in flight in registers while the wave computes a third from its own LDS
-// buffer, where lane l reads whole quad l (8-byte aligned). Blocks 0 and 2 of
-// a quad have their codes 2 bytes into a dword and are realigned with
-// v_alignbyte; blocks 1 and 3 have them dword-aligned.
+// spans of 32 quads (4352 bytes) from a workgroup counter and load each span
+// with 16-byte non-temporal loads (1 KiB per wave instruction). The next span
+// stays in flight in registers while the wave computes the current one from
+// its own LDS buffer, where lanes 2i and 2i + 1 share quad i: lane 2i + h
+// reads blocks 2h and 2h + 1 (68 bytes, 4-byte aligned), and the two halves
+// are added in a fixed order. Blocks 0 and 2 of a quad have their codes 2
+// bytes into a dword and are realigned with v_alignbyte; blocks 1 and 3 have
+// them dword-aligned. Half-size spans keep the first burst of weight loads
+// small (x, loaded first, is ready sooner) and the last span's math short.
 //
 // Per code, q + 128 = byte ^ 0x80 is converted with v_cvt_f32_ubyte and
 // multiplied by fp32 x from LDS; per block sum_k x_k q_k = s - 128 sum_k x_k,
@@ -34,11 +37,12 @@ namespace qdm {
 namespace {
 
 constexpr int Q8_QUAD = 4 * Q80_BYTES;                 // 136 bytes, 128 columns
-constexpr int Q8_SPAN = 64;                            // quads per span, one per lane
-constexpr int Q8_SPAN_BYTES = Q8_SPAN * Q8_QUAD;       // 8704 = 8.5 KiB
-constexpr int Q8_NCH = (Q8_SPAN_BYTES + 1023) / 1024;  // 9 loads per lane, the last half used
+constexpr int Q8_SPAN = 32;                            // quads per span, two lanes each
+constexpr int Q8_SPAN_BYTES = Q8_SPAN * Q8_QUAD;       // 4352 = 4.25 KiB
+constexpr int Q8_NCH = (Q8_SPAN_BYTES + 1023) / 1024;  // 5 loads per lane, the last partly used
+constexpr int Q8_SPAN_BUF = 1024 * Q8_NCH;             // LDS per wave
 constexpr int Q8_XREC = 528;                           // LDS bytes per 128-column x record
-constexpr int Q8_NB = 2;                               // spans in flight per wave
+constexpr int Q8_NB = 1;                               // spans in flight per wave
 constexpr int Q8_TARGET_WGS = 256;                     // one workgroup per compute unit
 constexpr int Q8_MIN_CHUNK = 8192;                     // columns of a chunk when K is split
 constexpr size_t Q8_LDS_LIMIT = 160 * 1024;
@@ -117,30 +121,27 @@ __device__ __forceinline__ void q8_block(const uint32_t (&cw)[8], float d, const
   }
 }
 
-// Partial dot products of one quad (136 bytes at q, 8-byte aligned LDS)
-// against its x record xr, for MT tokens.
+// Partial dot products of half h of one quad (blocks 2h and 2h + 1: the 68
+// bytes at q, 4-byte aligned LDS) against the quad's x record xr, for MT
+// tokens.
 template <int MT>
-__device__ __forceinline__ void q8_quad(const uint8_t *q, const uint8_t *xr, int xstr,
-                                        float (&out)[MT]) {
-  uint32_t D[34];
+__device__ __forceinline__ void q8_half_quad(const uint8_t *q, const uint8_t *xr, int h, int xstr,
+                                             float (&out)[MT]) {
+  uint32_t D[17];
 #pragma unroll
-  for (int i = 0; i < 17; i++) {
-    const u32x2 t = *(const u32x2 *)(q + 8 * i);
-    D[2 * i] = t.x;
-    D[2 * i + 1] = t.y;
-  }
+  for (int i = 0; i < 17; i++) D[i] = *(const uint32_t *)(q + 4 * i);
   float acc[MT];
   float dsum[MT];  // sum over blocks of d_b * (32-column sum of x)
 #pragma unroll
   for (int m = 0; m < MT; m++) acc[m] = dsum[m] = 0.f;
 #pragma unroll
-  for (int b = 0; b < 4; b++) {
-    // block b starts at byte 34 b: dword 17 (b / 2) + 8 (b % 2), at byte 0 of it
-    // (b even) or byte 2 (b odd)
-    const int w0 = 17 * (b >> 1) + 8 * (b & 1);
+  for (int bb = 0; bb < 2; bb++) {
+    // block bb of the half starts at byte 34 bb: dword 8 bb, at byte 0 of it
+    // (bb = 0) or byte 2 (bb = 1)
+    const int w0 = 8 * bb, b = 2 * h + bb;
     uint32_t cw[8];
     float d;
-    if ((b & 1) == 0) {
+    if (bb == 0) {
       d = half_bits_to_float(D[w0]);
 #pragma unroll
       for (int c = 0; c < 8; c++) cw[c] = __builtin_amdgcn_alignbyte(D[w0 + c + 1], D[w0 + c], 2);
@@ -183,8 +184,8 @@ __global__ __launch_bounds__(WAVES * WAVE) void q80_gemv_kernel(
   const int qpr = kcn / 128;                                  // quads per row in the chunk
   const int xstr = qpr * Q8_XREC;                             // bytes per token's records
   constexpr int Q8_THREADS = WAVES * WAVE;
-  uint8_t *spanbuf = smem;                                    // [waves][span bytes]
-  uint8_t *xrec = smem + WAVES * Q8_SPAN_BYTES;               // [MT][qpr][528]
+  uint8_t *spanbuf = smem;                                    // [waves][Q8_NCH KiB]
+  uint8_t *xrec = smem + WAVES * Q8_SPAN_BUF;                 // [MT][qpr][528]
   float *part = (float *)(xrec + MT * xstr);                  // [MT][pq]
 
   const int bid = blockIdx.x;
@@ -263,7 +264,8 @@ __global__ __launch_bounds__(WAVES * WAVE) void q80_gemv_kernel(
   for (int b = 1; b < Q8_NB; b++) issue(R[b], sidx[b]);
   __syncthreads();
 
-  uint8_t *mybuf = spanbuf + wave * Q8_SPAN_BYTES;
+  uint8_t *mybuf = spanbuf + wave * Q8_SPAN_BUF;
+  const int h = lane & 1;
   auto more = [&]() {
     bool m = false;
 #pragma unroll
@@ -284,11 +286,20 @@ __global__ __launch_bounds__(WAVES * WAVE) void q80_gemv_kernel(
       const int nxt = cur < nspan ? grab() : nspan;
       issue(R[p], nxt);
       sidx[p] = nxt;
-      const int g = Q8_SPAN * cur + lane;
+      // lanes 2i and 2i + 1 share quad i: half h is blocks 2h and 2h + 1, and
+      // the halves are added in a fixed order
+      const int g = Q8_SPAN * cur + (lane >> 1);
+      float o[MT];
+#pragma unroll
+      for (int m = 0; m < MT; m++) o[m] = 0.f;
       if (cur < nspan && g < nquads) {
         const int qc = g - q8_div(g, qpr_magic) * qpr;
-        float o[MT];
-        q8_quad<MT>(mybuf + Q8_QUAD * lane, xrec + qc * Q8_XREC, xstr, o);
+        q8_half_quad<MT>(mybuf + Q8_QUAD * (lane >> 1) + 68 * h, xrec + qc * Q8_XREC, h, xstr,
+                         o);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; m++) o[m] += __shfl_xor(o[m], 1, WAVE);
+      if (cur < nspan && g < nquads && h == 0) {
 #pragma unroll
         for (int m = 0; m < MT; m++) part[m * pq + g] = o[m];
       }
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(WAVES * WAVE) void q80_gemv_kernel(
 }
 
 size_t q8_lds(int waves, int mt, int64_t kcn, int64_t pq) {
-  return (size_t)waves * Q8_SPAN_BYTES + (size_t)mt * (kcn / 128) * Q8_XREC +
+  return (size_t)waves * Q8_SPAN_BUF + (size_t)mt * (kcn / 128) * Q8_XREC +
          (size_t)mt * pq * 4;
 }
 
