@@ -63,6 +63,9 @@ constexpr int DEC_PF = 3;  // wave iterations of weight loads in flight
 // units; from 4 tokens on, larger workgroups spend less on their fixed costs
 // (measured at H = 2048, F = 768, 128 experts, top-8).
 constexpr int DEC_FR_SMALL = 16, DEC_RW_SMALL = 64;
+// A single token: 8 row pairs per gate+up workgroup (twice the workgroups;
+// 17.0 -> 16.4 us at T = 1, but 21.8 -> 24.3 us at T = 2)
+constexpr int DEC_FR_ONE = 8;
 constexpr int DEC_FR_LARGE = 32, DEC_RW_LARGE = 128;
 constexpr int DEC_LARGE_FROM_T = 4;
 constexpr int DEC_MT_MAX = 4;  // entries per pass (more entries of one expert take more passes)
@@ -1037,16 +1040,28 @@ bool try_dec(const void *x, const void *w13, const void *w2, const int32_t *ids,
   }
 }
 
+// The decode regime with the tile sizes for T tokens; false if it does not apply.
+template <bool Q5>
+bool try_dec_tiles(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                   const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
+                   int64_t F, const MoeWs &ws, hipStream_t s, const float *logits = nullptr) {
+  if (T >= DEC_LARGE_FROM_T)
+    return try_dec<DEC_FR_LARGE, DEC_RW_LARGE, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws,
+                                                   s, logits);
+  if (T == 1)
+    return try_dec<DEC_FR_ONE, DEC_RW_SMALL, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s,
+                                                 logits);
+  return try_dec<DEC_FR_SMALL, DEC_RW_SMALL, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s,
+                                                 logits);
+}
+
 template <bool Q5>
 void launch_moe(const void *x, const void *w13, const void *w2, const int32_t *ids,
                 const float *gw, float *y, int64_t T, int64_t E, int64_t top_k, int64_t H,
                 int64_t F, void *workspace, hipStream_t s) {
   const int64_t n64 = T * top_k;
   const MoeWs ws = carve(workspace, T, E, top_k, H, F);
-  if (T >= DEC_LARGE_FROM_T
-          ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s)
-          : try_dec<DEC_FR_SMALL, DEC_RW_SMALL, Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s))
-    return;
+  if (try_dec_tiles<Q5>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s)) return;
   const int n = (int)n64;
   const size_t route_lds = sizeof(int32_t) * E;
   (void)hipFuncSetAttribute((const void *)moe_route_kernel,
@@ -1138,16 +1153,8 @@ void launch_moe_from_logits(const void *x, const float *logits, const void *w13,
   if (E <= 2 * WAVE && T <= DEC_THREADS / WAVE) {
     const MoeWs ws = carve(workspace, T, E, top_k, H, F);
     const bool done =
-        down_q5 ? (T >= DEC_LARGE_FROM_T
-                       ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE, true>(x, w13, w2, ids, gw, y, T, E,
-                                                                   top_k, H, F, ws, s, logits)
-                       : try_dec<DEC_FR_SMALL, DEC_RW_SMALL, true>(x, w13, w2, ids, gw, y, T, E,
-                                                                   top_k, H, F, ws, s, logits))
-                : (T >= DEC_LARGE_FROM_T
-                       ? try_dec<DEC_FR_LARGE, DEC_RW_LARGE, false>(x, w13, w2, ids, gw, y, T, E,
-                                                                    top_k, H, F, ws, s, logits)
-                       : try_dec<DEC_FR_SMALL, DEC_RW_SMALL, false>(x, w13, w2, ids, gw, y, T, E,
-                                                                    top_k, H, F, ws, s, logits));
+        down_q5 ? try_dec_tiles<true>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s, logits)
+                : try_dec_tiles<false>(x, w13, w2, ids, gw, y, T, E, top_k, H, F, ws, s, logits);
     if (done) return;
   }
   launch_router_topk(logits, T, E, top_k, ids, gw, s);
