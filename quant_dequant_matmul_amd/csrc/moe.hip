@@ -230,6 +230,9 @@ struct RowsDot {
     // are assembled into bytes (nibble | high bit << 4) first
     const uint32_t MASK = opaque_u32(Q5 ? 0x00FF00FFu : 0x000F000Fu);
     const uint32_t MAGIC = opaque_u32(0x43004300u);
+    // column block of the lane's block, stepped by 16 blocks per iteration
+    const int s16 = 16 % nb;
+    int kb = (wb0 + g) % nb;
     for (int it0 = 0; it0 < iters; it0 += DEC_PF) {
 #pragma unroll
       for (int p = 0; p < DEC_PF; p++) {
@@ -262,7 +265,6 @@ struct RowsDot {
           q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, m1);
           const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
           const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-          const int kb = b % nb;
           const int e0 = kb * QK + 64 * c;  // first input column of sub-block 2c
 #pragma unroll
           for (int m = 0; m < MT; m++) {
@@ -314,6 +316,8 @@ struct RowsDot {
               if (valid && c == 0) part[m * nblk + b] = r;
             }
           }
+          kb += s16;
+          if (kb >= nb) kb -= nb;
         }
       }
     }
