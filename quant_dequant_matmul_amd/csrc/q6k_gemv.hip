@@ -960,7 +960,7 @@ bool q6_dense_plan(int64_t N, int64_t K, int &unit, int &units_q, int &units_rem
   if (fixed + (size_t)unit * nb * 4 * 2 > Q6D_LDS_LIMIT) return false;
   const int64_t cap_units = (int64_t)((Q6D_LDS_LIMIT - fixed) / ((size_t)unit * nb * 4)) - 1;
   // one workgroup per compute unit, or a whole multiple of that when the
-  // block partials need more (the output head: 512, two rounds of equal size)
+  // block partials need more (equal rounds; the output head fits in one)
   nwg = Q6D_TARGET_WGS;
   const int64_t need = (units + cap_units - 1) / cap_units;
   if (need > nwg) nwg = (need + Q6D_TARGET_WGS - 1) / Q6D_TARGET_WGS * Q6D_TARGET_WGS;
@@ -1022,9 +1022,9 @@ void launch_q4k_mfma_gemv(const void *w, const uint16_t *x, float *y, int64_t M,
 void launch_q6k_gemv(const void *w, const void *x, bool x_bf16, float *y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s) {
   // M = 1, bf16 x: the dense-span kernel whenever its plan fits (K up to about
-  // 24K). It runs the down shape K = 17408, N = 5120 in 21.8 us and the output
-  // head K = 5120, N = 151936 in 114.5 us, against 25.5 us (its 4-wave form)
-  // and 136-138 us (the VALU kernel, which hands out whole row groups).
+  // 30K). It runs the down shape K = 17408, N = 5120 in about 16 us and the
+  // output head K = 5120, N = 151936 in about 97-104 us, against 25.5 us and
+  // 136-138 us for the VALU kernel's forms (which hand out whole row groups).
   if (M == 1 && x_bf16 && ((uintptr_t)w & 15) == 0 && q6_try_dense(w, x, y, N, K, s)) return;
   if (x_bf16 && M >= Q6_MFMA_MIN_M) {
     launch_kq_mfma<MfQ6>(w, (const uint16_t *)x, y, M, N, K, s);
