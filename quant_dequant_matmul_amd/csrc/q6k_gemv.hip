@@ -495,6 +495,9 @@ struct MfQ4 {
     q4k_scale_min(R.hdr.y, R.hdr.z, R.hdr.w, 2 * s + 1, sc1, m1);
     const float a0 = d * (float)sc0, nb0 = -(dmin * (float)m0);  // exact products
     const float a1 = d * (float)sc1, nb1 = -(dmin * (float)m1);
+    // Q4_K: a code byte (0..15) read as fp8 e4m3 is exactly q * 2^-9, so
+    // v_cvt_pk_f32_fp8 converts two codes at once and the scale carries 2^9:
+    // fma(q * 2^-9, a * 2^9, -b) is the same single rounding as fma(q, a, -b)
     const uint32_t q[8] = {R.qa.x, R.qa.y, R.qa.z, R.qa.w, R.qb.x, R.qb.y, R.qb.z, R.qb.w};
     const uint16_t *xs = xk + 64 * s;
 #pragma unroll
@@ -511,9 +514,17 @@ struct MfQ4 {
                                   R.hb[0].x, R.hb[0].y, R.hb[0].z, R.hb[0].w};
           c |= ((hp[k] >> (2 * s + (hi ? 1 : 0))) << 4) & 0x10101010u;
         }
-        pk[2 * u] = pack_bf16(fmaf((float)(c & 255u), a, nb), fmaf((float)((c >> 8) & 255u), a, nb));
-        pk[2 * u + 1] = pack_bf16(fmaf((float)((c >> 16) & 255u), a, nb),
-                                  fmaf((float)(c >> 24), a, nb));
+        if constexpr (Q5) {
+          pk[2 * u] = pack_bf16(fmaf((float)(c & 255u), a, nb), fmaf((float)((c >> 8) & 255u), a, nb));
+          pk[2 * u + 1] = pack_bf16(fmaf((float)((c >> 16) & 255u), a, nb),
+                                    fmaf((float)(c >> 24), a, nb));
+        } else {
+          const float a9 = a * 512.f;
+          const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+          const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+          pk[2 * u] = pack_bf16(fmaf(f01[0], a9, nb), fmaf(f01[1], a9, nb));
+          pk[2 * u + 1] = pack_bf16(fmaf(f23[0], a9, nb), fmaf(f23[1], a9, nb));
+        }
       }
       const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
       const bf16x8 bv = *(const bf16x8 *)(xs + 8 * t);
