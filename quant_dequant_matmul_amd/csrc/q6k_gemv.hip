@@ -345,6 +345,12 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 // super-block: the waves that continue it publish their portion (the first
 // portion of their range) in LDS, and the first wave adds those portions in
 // wave order before it stores. Loads run Q6M_PF items ahead.
+// Staged loads: a lane's slice is scattered over one row (16 rows per load
+// instruction, several instructions per line), so an item's lines are fetched
+// again and again. When staging, the wave instead loads the item's 16 row
+// blocks as consecutive 16-byte chunks (consecutive lanes read consecutive
+// bytes of a row), writes them to its own LDS rows and reads the slices back
+// from there; the next item's loads go out as soon as the chunks are written.
 // ---------------------------------------------------------------------------
 constexpr int Q6_MFMA_MIN_M = 2;  // smallest M (bf16 x) that takes the matrix-core kernel
 constexpr int Q6M_PF = 2;         // super-blocks in flight per wave
@@ -425,6 +431,11 @@ __device__ __forceinline__ Q6Lane q6_finish(const Q6Raw &R) {
 // 128h + 32g + l0 + 8e + j, group g's scale.
 struct MfQ6 {
   static constexpr int BYTES = Q6K_BYTES;
+  // staged copy: a row's block is copied as the 14 aligned 16-byte chunks that
+  // cover it (it starts at an even offset), rows 240 bytes apart in LDS
+  static constexpr bool STAGE_OK = true;
+  static constexpr int STAGE_CPR = 14, STAGE_RS = 240;
+  static constexpr bool STAGE_SHIFT = true;
   typedef Q6Raw Raw;
   __device__ static Raw load(const uint8_t *__restrict__ w, int64_t blk_off, int s) {
     return q6_load_raw(w, blk_off, s >> 1, 16 * (s & 1));
@@ -472,6 +483,9 @@ template <bool Q5>
 struct MfQ4 {
   static constexpr int BYTES = Q5 ? Q5K_BYTES : Q4K_BYTES;
   static constexpr int QOFF = Q5 ? 48 : 16;
+  static constexpr bool STAGE_OK = true;
+  static constexpr int STAGE_CPR = BYTES / 16, STAGE_RS = BYTES;
+  static constexpr bool STAGE_SHIFT = false;
   struct Raw {
     u32x4 hdr, qa, qb;
     u32x4 ha[Q5 ? 1 : 0], hb[Q5 ? 1 : 0];
@@ -540,6 +554,11 @@ struct MfQ4 {
 // in fp32, then rounded to bf16.
 struct MfQ8 {
   static constexpr int BYTES = 8 * Q80_BYTES;
+  // direct loads: the staged copy (five chunks per lane) spills registers at
+  // 12 waves per compute unit and measured slower
+  static constexpr bool STAGE_OK = false;
+  static constexpr int STAGE_CPR = BYTES / 16, STAGE_RS = BYTES;
+  static constexpr bool STAGE_SHIFT = false;
   struct Raw {
     u32x4 v[4];
     uint32_t t;
@@ -595,17 +614,33 @@ struct MfQ8 {
 // One launch covers the K columns [256 kb0, 256 kb0 + K) of rows that are
 // ldk columns long (x rows too: x points at column 256 kb0 of row 0); with
 // accumulate set it adds its sums to y (column chunks of a long K).
-template <int THREADS, class Fmt>
+// Staged copy of one item: NCI 16-byte chunks per lane cover 16 rows of
+// STAGE_CPR chunks each (the last load instruction repeats the final chunk in
+// its spare lanes).
+template <class Fmt>
+struct KqStage {
+  static constexpr int CPR = Fmt::STAGE_CPR, RS = Fmt::STAGE_RS;
+  static constexpr int NCI = (16 * CPR + WAVE - 1) / WAVE;
+  static constexpr size_t WAVE_BYTES = (size_t)16 * RS;  // LDS per wave
+  struct Raw {
+    u32x4 c[NCI];
+  };
+};
+
+template <int THREADS, class Fmt, bool STAGE>
 __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restrict__ w,
                                                           const uint16_t *__restrict__ x,
                                                           float *__restrict__ y, int M, int N,
                                                           int K, int xs, int ldk, int kb0,
                                                           int accumulate) {
   constexpr int WAVES = THREADS / WAVE;
+  typedef KqStage<Fmt> St;
+  constexpr size_t STAGE_BYTES = STAGE ? WAVES * St::WAVE_BYTES : 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t q6m_smem[];
   f32x4 *part = (f32x4 *)q6m_smem;                                   // [WAVES][64]
   int *flag = (int *)(q6m_smem + (size_t)WAVES * WAVE * sizeof(f32x4));  // [WAVES]
-  uint16_t *xl = (uint16_t *)(q6m_smem + q6m_head_bytes(WAVES));    // [M][xs] bf16
+  uint8_t *stage = q6m_smem + q6m_head_bytes(WAVES);                // [WAVES][16][RS]
+  uint16_t *xl = (uint16_t *)(stage + STAGE_BYTES);                  // [M][xs] bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform ranges
   const int nb = K / QK, nbt = ldk / QK;
@@ -619,12 +654,41 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
   const int s = lane >> 4, r = lane & 15;
 
   if (tid < WAVES) flag[tid] = 0;
+  // staged copy, per lane: chunk k is chunk sj[k] of tile row srow[k], kept
+  // at byte sdst[k] of the wave's LDS rows
+  int srow[St::NCI], sj[St::NCI];
+  uint32_t sdst[St::NCI];
+#pragma unroll
+  for (int k = 0; k < St::NCI; k++) {
+    const int c = min(lane + WAVE * k, 16 * St::CPR - 1);
+    srow[k] = c / St::CPR;
+    sj[k] = c - srow[k] * St::CPR;
+    sdst[k] = (uint32_t)(srow[k] * St::RS + 16 * sj[k]);
+  }
+  uint8_t *sbuf = stage + (size_t)wave * St::WAVE_BYTES;
   auto load = [&](int i) {
     const int ic = max(min(i, i1 - 1), 0);  // past the range: a valid dummy
     const int tl = ic / nb;
-    const int row = min((t0 + tl) * 16 + r, N - 1);
-    return Fmt::load(w, ((int64_t)row * nbt + kb0 + (ic - tl * nb)) * Fmt::BYTES, s);
+    const int blk = kb0 + (ic - tl * nb);
+    if constexpr (STAGE) {
+      // a row's chunks start at its block rounded down to 16 bytes; for Q6_K
+      // the last chunk may run up to 14 bytes past the block, which stays
+      // inside the tensor when its size is a multiple of 16 bytes
+      typename St::Raw R;
+#pragma unroll
+      for (int k = 0; k < St::NCI; k++) {
+        const int row = min((t0 + tl) * 16 + srow[k], N - 1);
+        int64_t g = ((int64_t)row * nbt + blk) * Fmt::BYTES;
+        if constexpr (Fmt::STAGE_SHIFT) g &= ~(int64_t)15;
+        R.c[k] = *(const u32x4 *)(w + g + 16 * sj[k]);
+      }
+      return R;
+    } else {
+      const int row = min((t0 + tl) * 16 + r, N - 1);
+      return Fmt::load(w, ((int64_t)row * nbt + blk) * Fmt::BYTES, s);
+    }
   };
+  typedef decltype(load(0)) Buf;
   // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
   // apart), eight 16-byte loads in flight per thread; the first batch of x
   // loads goes out before the first weight loads, so its stores wait for x only
@@ -648,7 +712,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     }
   };
   x_load(0);
-  typename Fmt::Raw buf[Q6M_PF];
+  Buf buf[Q6M_PF];
 #pragma unroll
   for (int p = 0; p < Q6M_PF; p++) buf[p] = load(i0 + p);
   x_store(0);
@@ -663,10 +727,25 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // one item: decode the slice, 8 MFMAs; at the end of this wave's portion of
   // a tile, publish it or complete and store the tile
-  auto item = [&](int ii, typename Fmt::Raw &slot, bool reload) {
+  auto item = [&](int ii, Buf &slot, bool reload) {
     const int tl = ii / nb, b = ii - tl * nb;
-    Fmt::mfma(slot, s, xb + b * QK, acc2);
-    if (reload) slot = load(ii + Q6M_PF);
+    if constexpr (STAGE) {
+      // only this wave uses its LDS rows, and a wave's LDS accesses run in
+      // order: the previous item's slice reads are done before these writes
+#pragma unroll
+      for (int k = 0; k < St::NCI; k++) *(u32x4 *)(sbuf + sdst[k]) = slot.c[k];
+      if (reload) slot = load(ii + Q6M_PF);
+      uint32_t sh = 0;  // where the lane's row block starts in its LDS row
+      if constexpr (Fmt::STAGE_SHIFT) {
+        const int row = min((t0 + tl) * 16 + r, N - 1);
+        sh = ((uint32_t)row * (uint32_t)nbt + (uint32_t)(kb0 + b)) * (uint32_t)Fmt::BYTES & 15u;
+      }
+      const typename Fmt::Raw R = Fmt::load(sbuf, (int64_t)(r * St::RS + sh), s);
+      Fmt::mfma(R, s, xb + b * QK, acc2);
+    } else {
+      Fmt::mfma(slot, s, xb + b * QK, acc2);
+      if (reload) slot = load(ii + Q6M_PF);
+    }
 
     if (b == nb - 1 || ii == i1 - 1) {  // end of this wave's portion of a tile
       f32x4 acc = acc2[0] + acc2[1];
@@ -721,37 +800,36 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     if (i + p < i1) item(i + p, buf[p], false);
 }
 
-template <int THREADS, class Fmt>
+template <int THREADS, class Fmt, bool STAGE>
 void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t N, int64_t K,
                     int64_t ldk, int64_t kb0, bool accumulate, size_t lds, int per_cu,
                     hipStream_t s) {
   const int64_t tiles = (N + 15) / 16;
   int64_t grid = 256 * per_cu;
   if (grid > tiles) grid = tiles;  // every workgroup owns at least one tile
-  auto kern = kq_mfma_kernel<THREADS, Fmt>;
+  auto kern = kq_mfma_kernel<THREADS, Fmt, STAGE>;
   (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), lds, s, (const uint8_t *)w, x,
                      y, mc, (int)N, (int)K, (int)(K + 8), (int)ldk, (int)kb0, accumulate ? 1 : 0);
 }
 
-// Rows of x in chunks whose padded LDS copy fits; each chunk streams all
-// weights. 12 waves per compute unit (3 per SIMD, as many as the registers
-// allow): 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
-template <class Fmt>
-void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
-                    int64_t K, hipStream_t s) {
-  // All M rows of x in every launch; when their padded LDS copy would not fit,
-  // K is split into equal chunks of whole super-blocks, each launch streaming
-  // only its columns of the weights and adding into y after the first (the
-  // weights are read once; splitting M instead would read them per split).
-  // 12 waves per compute unit (3 per SIMD, as many as the registers allow):
-  // 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
+// All M rows of x in every launch; when their padded LDS copy would not fit,
+// K is split into equal chunks of whole super-blocks, each launch streaming
+// only its columns of the weights and adding into y after the first (the
+// weights are read once; splitting M instead would read them per split).
+// 12 waves per compute unit (3 per SIMD, as many as the registers allow):
+// 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
+// Staged loads take one set of 16 LDS rows per wave (12 per compute unit);
+// they are used unless they would need more K chunks, or (Q6_K, whose staged
+// chunks may run up to 14 bytes past a block) the tensor's size is not a
+// multiple of 16 bytes.
+template <class Fmt, bool STAGE>
+void launch_kq_mfma_x(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                      int64_t K, int64_t nch, hipStream_t s) {
   constexpr size_t LDS_CU = 160 * 1024, SLACK = 512;  // SLACK: static LDS, rounding
-  const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
+  constexpr size_t SW = STAGE ? KqStage<Fmt>::WAVE_BYTES : 0;
   const int64_t units = K / QK;
-  int64_t nch = 1;
-  while ((size_t)M * ((units + nch - 1) / nch * QK + 8) * 2 > x_cap) nch++;
   int64_t kb0 = 0;
   for (int64_t c = 0; c < nch; c++) {
     const int64_t kc = (units / nch + (c < units % nch ? 1 : 0)) * QK;
@@ -759,14 +837,39 @@ void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64
     const uint16_t *xm = x + kb0 * QK;
     const int mc = (int)M;
     const bool acc = c > 0;
-    if (3 * (xb + q6m_head_bytes(4) + SLACK) <= LDS_CU)
-      launch_q6_mfma<256, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(4), 3, s);
-    else if (2 * (xb + q6m_head_bytes(6) + SLACK) <= LDS_CU)
-      launch_q6_mfma<384, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(6), 2, s);
+    const size_t l4 = xb + q6m_head_bytes(4) + 4 * SW, l6 = xb + q6m_head_bytes(6) + 6 * SW;
+    const size_t l12 = xb + q6m_head_bytes(12) + 12 * SW;
+    if (3 * (l4 + SLACK) <= LDS_CU)
+      launch_q6_mfma<256, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l4, 3, s);
+    else if (2 * (l6 + SLACK) <= LDS_CU)
+      launch_q6_mfma<384, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l6, 2, s);
     else
-      launch_q6_mfma<768, Fmt>(w, xm, y, mc, N, kc, K, kb0, acc, xb + q6m_head_bytes(12), 1, s);
+      launch_q6_mfma<768, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l12, 1, s);
     kb0 += kc / QK;
   }
+}
+
+template <class Fmt>
+void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64_t N,
+                    int64_t K, hipStream_t s) {
+  constexpr size_t LDS_CU = 160 * 1024, SLACK = 512;
+  const int64_t units = K / QK;
+  auto chunks = [&](size_t x_cap) {
+    int64_t n = 1;
+    while ((size_t)M * ((units + n - 1) / n * QK + 8) * 2 > x_cap) n++;
+    return n;
+  };
+  const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
+  const int64_t nch = chunks(x_cap);
+  const int64_t nch_st = chunks(x_cap - 12 * KqStage<Fmt>::WAVE_BYTES);
+  const bool fits = !Fmt::STAGE_SHIFT || (N * units) % 8 == 0;
+  if constexpr (Fmt::STAGE_OK) {
+    if (fits && nch_st == nch) {
+      launch_kq_mfma_x<Fmt, true>(w, x, y, M, N, K, nch, s);
+      return;
+    }
+  }
+  launch_kq_mfma_x<Fmt, false>(w, x, y, M, N, K, nch, s);
 }
 
 // ---------------------------------------------------------------------------
