@@ -666,10 +666,27 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     sdst[k] = (uint32_t)(srow[k] * St::RS + 16 * sj[k]);
   }
   uint8_t *sbuf = stage + (size_t)wave * St::WAVE_BYTES;
-  auto load = [&](int i) {
-    const int ic = max(min(i, i1 - 1), 0);  // past the range: a valid dummy
-    const int tl = ic / nb;
-    const int blk = kb0 + (ic - tl * nb);
+  // The compute and load streams walk (tile, block) positions with counters
+  // (no division per item). Addresses are a wave-uniform tile base plus 32-bit
+  // lane offsets (16 rows of one tile).
+  struct Pos {
+    int tl, b;
+  };
+  auto pos_of = [&](int i) {
+    const int tl = i / nb;
+    return Pos{tl, i - tl * nb};
+  };
+  auto step = [&](Pos &p) {
+    if (++p.b == nb) {
+      p.b = 0;
+      p.tl++;
+    }
+  };
+  const uint32_t rowbytes = (uint32_t)nbt * Fmt::BYTES;
+  auto load_at = [&](Pos p) {
+    const uint8_t *tb = w + (int64_t)(t0 + p.tl) * 16 * rowbytes;  // 16-byte aligned
+    const int lastr = N - 1 - (t0 + p.tl) * 16;                     // rows past N repeat it
+    const uint32_t boff = (uint32_t)(kb0 + p.b) * Fmt::BYTES;
     if constexpr (STAGE) {
       // a row's chunks start at its block rounded down to 16 bytes; for Q6_K
       // the last chunk may run up to 14 bytes past the block, which stays
@@ -677,18 +694,27 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
       typename St::Raw R;
 #pragma unroll
       for (int k = 0; k < St::NCI; k++) {
-        const int row = min((t0 + tl) * 16 + srow[k], N - 1);
-        int64_t g = ((int64_t)row * nbt + blk) * Fmt::BYTES;
-        if constexpr (Fmt::STAGE_SHIFT) g &= ~(int64_t)15;
-        R.c[k] = *(const u32x4 *)(w + g + 16 * sj[k]);
+        uint32_t g = (uint32_t)min(srow[k], lastr) * rowbytes + boff;
+        if constexpr (Fmt::STAGE_SHIFT) g &= ~15u;
+        R.c[k] = *(const u32x4 *)(tb + g + 16 * sj[k]);
       }
       return R;
     } else {
-      const int row = min((t0 + tl) * 16 + r, N - 1);
-      return Fmt::load(w, ((int64_t)row * nbt + blk) * Fmt::BYTES, s);
+      return Fmt::load(tb, (int64_t)((uint32_t)min(r, lastr) * rowbytes + boff), s);
     }
   };
-  typedef decltype(load(0)) Buf;
+  typedef decltype(load_at(Pos{0, 0})) Buf;
+  // load stream: items from i0 on; past the range it reloads the range's last
+  // item (a valid dummy)
+  int lnext = i0;
+  Pos lp = pos_of(i0);
+  const Pos lend = pos_of(max(i1 - 1, 0));
+  auto load_next = [&]() {
+    const Pos p = lnext < i1 ? lp : lend;
+    lnext++;
+    step(lp);
+    return load_at(p);
+  };
   // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
   // apart), eight 16-byte loads in flight per thread; the first batch of x
   // loads goes out before the first weight loads, so its stores wait for x only
@@ -714,7 +740,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
   x_load(0);
   Buf buf[Q6M_PF];
 #pragma unroll
-  for (int p = 0; p < Q6M_PF; p++) buf[p] = load(i0 + p);
+  for (int p = 0; p < Q6M_PF; p++) buf[p] = load_next();
   x_store(0);
   for (int base = 8 * THREADS; base < total; base += 8 * THREADS) {
     x_load(base);
@@ -727,14 +753,16 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // one item: decode the slice, 8 MFMAs; at the end of this wave's portion of
   // a tile, publish it or complete and store the tile
+  Pos cp = pos_of(i0);  // compute stream
   auto item = [&](int ii, Buf &slot, bool reload) {
-    const int tl = ii / nb, b = ii - tl * nb;
+    const int tl = cp.tl, b = cp.b;
+    step(cp);
     if constexpr (STAGE) {
       // only this wave uses its LDS rows, and a wave's LDS accesses run in
       // order: the previous item's slice reads are done before these writes
 #pragma unroll
       for (int k = 0; k < St::NCI; k++) *(u32x4 *)(sbuf + sdst[k]) = slot.c[k];
-      if (reload) slot = load(ii + Q6M_PF);
+      if (reload) slot = load_next();
       uint32_t sh = 0;  // where the lane's row block starts in its LDS row
       if constexpr (Fmt::STAGE_SHIFT) {
         const int row = min((t0 + tl) * 16 + r, N - 1);
@@ -744,7 +772,7 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
       Fmt::mfma(R, s, xb + b * QK, acc2);
     } else {
       Fmt::mfma(slot, s, xb + b * QK, acc2);
-      if (reload) slot = load(ii + Q6M_PF);
+      if (reload) slot = load_next();
     }
 
     if (b == nb - 1 || ii == i1 - 1) {  // end of this wave's portion of a tile
