@@ -230,6 +230,27 @@ def test_q4k_gemv_gate_up_m8_full():
     say("  rel err", e)
 
 
+@pytest.mark.parametrize("qtype,N,K", [(4, 48, 20480), (5, 48, 20480), (6, 48, 20480),
+                                       (4, 40, 20480), (5, 40, 20480), (6, 40, 20480),
+                                       (6, 41, 20736)])
+def test_mfma_gemv_k_chunks(qtype, N, K):
+    """M = 4, bf16 x, where four x rows of K columns do not fit the LDS: K is
+    split into two chunks (two launches, the second adding into y). With
+    80 super-blocks per row the staged loads still fit beside each chunk, so
+    Q4_K / Q5_K / Q6_K run staged and chunked (N = 40: a ragged last tile);
+    with 81 per row and N = 41 the Q6_K tensor's size is not a multiple of
+    16 bytes and the direct loads run instead."""
+    M = 4
+    rng = np.random.default_rng(qtype * 1000 + N + K)
+    gen, gemv = {4: (synth.q4k_blocks, qdm.q4k_gemv), 5: (synth.q5k_blocks, qdm.q5k_gemv),
+                 6: (synth.q6k_blocks, qdm.q6k_gemv)}[qtype]
+    w = gen(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    say("mfma gemv K chunks", qtype, N, K)
+    y = host(gemv(dev_bytes(w), dev_x(x), N, K))
+    check_gemv(y, qtype, w, x, N, K, "bf16", "q%dk_gemv M=4 N=%d K=%d" % (qtype, N, K))
+
+
 # --------------------------------------------------------------------------
 # Q5_K dequant and GEMV
 # --------------------------------------------------------------------------
