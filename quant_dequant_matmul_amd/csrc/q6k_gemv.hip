@@ -361,6 +361,14 @@ __host__ __device__ constexpr size_t q6m_head_bytes(int waves) {
   return (size_t)waves * WAVE * sizeof(f32x4) + Q6M_FLAGS;
 }
 
+// LDS for M rows of x with K columns: rows of K + 8 bf16 (16 bytes of padding)
+// in whole KiB, the unit of one wave's LDS-direct copy.
+__host__ __device__ constexpr size_t kq_x_bytes(int64_t M, int64_t K) {
+  return (size_t)((M * (K / 8 + 1) + WAVE - 1) / WAVE) * 1024;
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
 __device__ __forceinline__ uint32_t q6m_codes(uint32_t ql, uint32_t qh, int g) {
   // four 6-bit codes of group g as bytes: low nibble (g < 2) or high nibble of
   // ql, and bits 2g, 2g + 1 of qh as bits 4, 5
@@ -716,36 +724,25 @@ __global__ __launch_bounds__(THREADS) void kq_mfma_kernel(const uint8_t *__restr
     return load_at(p);
   };
   // stage x rows [0, M) with row stride xs (K + 8 elements: rows start 4 banks
-  // apart), eight 16-byte loads in flight per thread; the first batch of x
-  // loads goes out before the first weight loads, so its stores wait for x only
-  const int cpr = K / 8, total = M * cpr;
-  u32x4 xv[8];
-  auto x_load = [&](int base) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int c = min(base + j * THREADS + tid, total - 1);
-      const int m = c / cpr;
-      xv[j] = *(const u32x4 *)(x + (int64_t)m * ldk + 8 * (c - m * cpr));
+  // apart) by LDS-direct copies, all in flight at once: 16-byte slot sl of the
+  // staged rows is chunk sl % (K/8 + 1) of row sl / (K/8 + 1) (a row's padding
+  // slot repeats its last chunk), one KiB of consecutive slots per wave copy;
+  // the last copy's slots past the rows repeat the last one (the LDS holds
+  // whole KiB). The weight loads of the first items follow; the barrier waits
+  // for every copy.
+  {
+    const int spr = K / 8 + 1, nslot = M * spr, ncopy = (nslot + WAVE - 1) / WAVE;
+    for (int i = wave; i < ncopy; i += WAVES) {  // uniform
+      const int sl = min(i * WAVE + lane, nslot - 1);
+      const int m = sl / spr;
+      const int j = min(sl - m * spr, spr - 2);
+      __builtin_amdgcn_global_load_lds((const void *)(x + (int64_t)m * ldk + 8 * j),
+                                       (lds_ptr_t)((uint8_t *)xl + 1024 * i), 16, 0, 0);
     }
-  };
-  auto x_store = [&](int base) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      // unconditional: a clamped chunk rewrites the last chunk with its own value
-      const int c = min(base + j * THREADS + tid, total - 1);
-      const int m = c / cpr;
-      *(u32x4 *)(xl + m * xs + 8 * (c - m * cpr)) = xv[j];
-    }
-  };
-  x_load(0);
+  }
   Buf buf[Q6M_PF];
 #pragma unroll
   for (int p = 0; p < Q6M_PF; p++) buf[p] = load_next();
-  x_store(0);
-  for (int base = 8 * THREADS; base < total; base += 8 * THREADS) {
-    x_load(base);
-    x_store(base);
-  }
   __syncthreads();
 
   const uint16_t *xb = xl + min(r, M - 1) * xs;
@@ -861,7 +858,7 @@ void launch_kq_mfma_x(const void *w, const uint16_t *x, float *y, int64_t M, int
   int64_t kb0 = 0;
   for (int64_t c = 0; c < nch; c++) {
     const int64_t kc = (units / nch + (c < units % nch ? 1 : 0)) * QK;
-    const size_t xb = (size_t)M * (kc + 8) * 2;
+    const size_t xb = kq_x_bytes(M, kc);
     const uint16_t *xm = x + kb0 * QK;
     const int mc = (int)M;
     const bool acc = c > 0;
@@ -884,7 +881,7 @@ void launch_kq_mfma(const void *w, const uint16_t *x, float *y, int64_t M, int64
   const int64_t units = K / QK;
   auto chunks = [&](size_t x_cap) {
     int64_t n = 1;
-    while ((size_t)M * ((units + n - 1) / n * QK + 8) * 2 > x_cap) n++;
+    while (kq_x_bytes(M, (units + n - 1) / n * QK) > x_cap) n++;
     return n;
   };
   const size_t x_cap = LDS_CU - SLACK - q6m_head_bytes(16);
