@@ -336,8 +336,9 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 // e = 0..1, gives the lane's weights at positions 128h + 32g + l0 + 8e + j,
 // j = 0..7, as the A operand; the B operand is x row (lane % 16) at the same
 // positions, from LDS (rows of x past M repeat row M - 1; their outputs are
-// not stored). The matrix core pairs A and B by (lane / 16, j), so any K order
-// that both sides share gives the same contraction.
+// not stored; the rows are staged with LDS-direct copies). The matrix core
+// pairs A and B by (lane / 16, j), so any K order that both sides share gives
+// the same contraction.
 // Work split: workgroup b owns an even share of the 16-row tiles, and its
 // waves split the share's (tile, super-block) items into equal contiguous
 // ranges, so every wave streams the same number of super-blocks. A tile cut
@@ -345,9 +346,9 @@ void launch_chunk(const void *w, const void *x, float *y, int64_t N, int64_t K, 
 // super-block: the waves that continue it publish their portion (the first
 // portion of their range) in LDS, and the first wave adds those portions in
 // wave order before it stores. Loads run Q6M_PF items ahead.
-// Staged loads: a lane's slice is scattered over one row (16 rows per load
-// instruction, several instructions per line), so an item's lines are fetched
-// again and again. When staging, the wave instead loads the item's 16 row
+// Staged loads: a lane's slice is scattered over one row, so every load
+// instruction touches all 16 rows and each line of an item is requested by
+// several instructions. When staging, the wave instead loads the item's 16 row
 // blocks as consecutive 16-byte chunks (consecutive lanes read consecutive
 // bytes of a row), writes them to its own LDS rows and reads the slices back
 // from there; the next item's loads go out as soon as the chunks are written.
