@@ -188,15 +188,29 @@ def bench_roofs(torch, qdm):
     mhz = float(np.median(ck[:, 0] / ck[:, 1] * 100.0))
     flops = wgs * 4 * iters * 8 * 32768.0
     ms_empty = time_batch(torch, lambda i: lib.qdm_probe_empty(wgs, st), 1, 2000)
+    # the same launch as the 64 nodes of one captured graph, per node: what a
+    # graph replay adds or saves per kernel against back-to-back launches
+    NODES = 64
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(NODES):
+            lib.qdm_probe_empty(wgs, cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    ms_node = time_batch(torch, lambda i: graph.replay(), 1, 50) / NODES
+    del graph
     return {"hbm_read_GBps": big / ms_hbm / 1e6, "mall_read_GBps": small / ms_mall / 1e6,
             "read_us_by_size_hbm": reads,
             "mfma_bf16_TFLOPs": flops / ms_mfma / 1e9,
             "mfma_shader_clock_MHz": mhz,
             "empty_launch_us": ms_empty * 1e3,
+            "graph_empty_node_us": ms_node * 1e3,
             "notes": "read: qdm_probe_read (a contiguous slice per workgroup), C ABI launches back to back; mfma: qdm_probe_mfma (%d workgroups x 4 waves x %d x 8 "
                      "v_mfma_f32_32x32x16_bf16); clock = s_memtime / s_memrealtime ticks x "
-                     "100 MHz; empty: back-to-back C ABI launches of %d idle workgroups"
-                     % (wgs, iters, wgs)}
+                     "100 MHz; empty: back-to-back C ABI launches of %d idle workgroups; "
+                     "graph node: the same launch replayed as %d nodes of one captured graph"
+                     % (wgs, iters, wgs, NODES)}
 
 
 def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
