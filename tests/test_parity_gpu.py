@@ -230,6 +230,24 @@ def test_q4k_gemv_gate_up_m8_full():
     say("  rel err", e)
 
 
+@pytest.mark.parametrize("qtype,M,N,K", [(4, 2, 1, 768), (4, 16, 5, 2048), (5, 2, 15, 768),
+                                         (5, 16, 1, 2048), (6, 2, 5, 2048), (6, 16, 15, 2048),
+                                         (6, 3, 5, 768), (8, 2, 1, 512), (8, 16, 15, 2048)])
+def test_mfma_gemv_single_ragged_tile(qtype, M, N, K):
+    """bf16 x, M >= 2, fewer than 16 weight rows: one tile whose rows past N
+    repeat row N - 1 in the loads and are not stored (Q6_K with K = 2048 runs
+    the staged loads, with K = 768 the direct ones)."""
+    rng = np.random.default_rng(qtype * 100 + M * 10 + N + K)
+    gen, gemv = {4: (synth.q4k_blocks, qdm.q4k_gemv), 5: (synth.q5k_blocks, qdm.q5k_gemv),
+                 6: (synth.q6k_blocks, qdm.q6k_gemv), 8: (synth.q80_blocks, qdm.q80_gemv)}[qtype]
+    w = gen(rng, N, K)
+    x = synth.normal_bf16(rng, (M, K))
+    say("mfma gemv single tile", qtype, M, N, K)
+    y = host(gemv(dev_bytes(w), dev_x(x), N, K))
+    assert y.shape == (M, N)
+    check_gemv(y, qtype, w, x, N, K, "bf16", "q%d gemv M=%d N=%d K=%d" % (qtype, M, N, K))
+
+
 @pytest.mark.parametrize("qtype,N,K", [(4, 48, 20480), (5, 48, 20480), (6, 48, 20480),
                                        (4, 40, 20480), (5, 40, 20480), (6, 40, 20480),
                                        (6, 41, 20736)])
