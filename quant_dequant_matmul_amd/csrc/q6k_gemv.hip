@@ -845,7 +845,8 @@ void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t 
 // only its columns of the weights and adding into y after the first (the
 // weights are read once; splitting M instead would read them per split).
 // 12 waves per compute unit (3 per SIMD, as many as the registers allow):
-// 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows.
+// 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows (1 of 8
+// when K is split into chunks).
 // Staged loads take one set of 16 LDS rows per wave (12 per compute unit);
 // they are used unless they would need more K chunks, or (Q6_K, whose staged
 // chunks may run up to 14 bytes past a block) the tensor's size is not a
@@ -864,11 +865,15 @@ void launch_kq_mfma_x(const void *w, const uint16_t *x, float *y, int64_t M, int
     const int mc = (int)M;
     const bool acc = c > 0;
     const size_t l4 = xb + q6m_head_bytes(4) + 4 * SW, l6 = xb + q6m_head_bytes(6) + 6 * SW;
-    const size_t l12 = xb + q6m_head_bytes(12) + 12 * SW;
+    const size_t l8 = xb + q6m_head_bytes(8) + 8 * SW, l12 = xb + q6m_head_bytes(12) + 12 * SW;
     if (3 * (l4 + SLACK) <= LDS_CU)
       launch_q6_mfma<256, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l4, 3, s);
     else if (2 * (l6 + SLACK) <= LDS_CU)
       launch_q6_mfma<384, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l6, 2, s);
+    else if (nch > 1)
+      // K in chunks (one workgroup per CU holding a long x chunk): 8 waves, 2
+      // per SIMD, were faster than 12 (Q5_K K=17408 N=5120 M=8: 38.0 -> 36.2 us)
+      launch_q6_mfma<512, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l8, 1, s);
     else
       launch_q6_mfma<768, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l12, 1, s);
     kb0 += kc / QK;
