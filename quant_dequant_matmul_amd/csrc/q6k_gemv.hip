@@ -443,6 +443,7 @@ struct MfQ6 {
   // staged copy: a row's block is copied as the 14 aligned 16-byte chunks that
   // cover it (it starts at an even offset), rows 240 bytes apart in LDS
   static constexpr bool STAGE_OK = true;
+  static constexpr int ONE_CU_WAVES = 12;
   static constexpr int STAGE_CPR = 14, STAGE_RS = 240;
   static constexpr bool STAGE_SHIFT = true;
   typedef Q6Raw Raw;
@@ -493,6 +494,7 @@ struct MfQ4 {
   static constexpr int BYTES = Q5 ? Q5K_BYTES : Q4K_BYTES;
   static constexpr int QOFF = Q5 ? 48 : 16;
   static constexpr bool STAGE_OK = true;
+  static constexpr int ONE_CU_WAVES = 12;
   static constexpr int STAGE_CPR = BYTES / 16, STAGE_RS = BYTES;
   static constexpr bool STAGE_SHIFT = false;
   struct Raw {
@@ -566,6 +568,9 @@ struct MfQ8 {
   // direct loads: the staged copy (five chunks per lane) spills registers at
   // 12 waves per compute unit and measured slower
   static constexpr bool STAGE_OK = false;
+  // 8 waves when one workgroup fills a CU (each item is 4.25 KiB; with 12
+  // waves more loads queue: K=5120 N=7168 M=8 14.5 -> 13.3 us)
+  static constexpr int ONE_CU_WAVES = 8;
   static constexpr int STAGE_CPR = BYTES / 16, STAGE_RS = BYTES;
   static constexpr bool STAGE_SHIFT = false;
   struct Raw {
@@ -846,7 +851,7 @@ void launch_q6_mfma(const void *w, const uint16_t *x, float *y, int mc, int64_t 
 // weights are read once; splitting M instead would read them per split).
 // 12 waves per compute unit (3 per SIMD, as many as the registers allow):
 // 3 workgroups of 4 waves, 2 of 6, or 1 of 12, whichever LDS allows (1 of 8
-// when K is split into chunks).
+// when K is split into chunks, and for Q8_0).
 // Staged loads take one set of 16 LDS rows per wave (12 per compute unit);
 // they are used unless they would need more K chunks, or (Q6_K, whose staged
 // chunks may run up to 14 bytes past a block) the tensor's size is not a
@@ -870,9 +875,10 @@ void launch_kq_mfma_x(const void *w, const uint16_t *x, float *y, int64_t M, int
       launch_q6_mfma<256, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l4, 3, s);
     else if (2 * (l6 + SLACK) <= LDS_CU)
       launch_q6_mfma<384, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l6, 2, s);
-    else if (nch > 1)
-      // K in chunks (one workgroup per CU holding a long x chunk): 8 waves, 2
-      // per SIMD, were faster than 12 (Q5_K K=17408 N=5120 M=8: 38.0 -> 36.2 us)
+    else if (nch > 1 || Fmt::ONE_CU_WAVES == 8)
+      // one workgroup per CU with 8 waves (2 per SIMD) rather than 12: faster
+      // when K is split into chunks (Q5_K K=17408 N=5120 M=8: 38.0 -> 36.2 us)
+      // and for the formats that ask for it
       launch_q6_mfma<512, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l8, 1, s);
     else
       launch_q6_mfma<768, Fmt, STAGE>(w, xm, y, mc, N, kc, K, kb0, acc, l12, 1, s);
