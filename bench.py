@@ -300,8 +300,42 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
         reps_ms.append(a.elapsed_time(b) / 20)
     median5_ms = float(np.median(reps_ms[2:]))
 
-    # Graph-replayed steps: one graph holds one step per weight copy (the
-    # decode loop of an engine replays captured launches).
+    # Per-kernel launch duration: back-to-back launches of one kernel through
+    # the C ABI with pre-marshalled arguments (the queue stays ahead of the
+    # GPU), in 5 batches each bracketed by two events on the launch stream;
+    # the median batch mean is reported. Each shape rotates over its own
+    # copies, at least twice the 256 MB last-level cache in total (25 for QKV,
+    # 6 for gate+up, 11 for down). Every leg starts from the same state (20 ms
+    # idle, then one launch per copy) and is short (5 batches of 10 launches,
+    # about 1 ms for gate+up): one kernel alone streaming at full rate slows
+    # the GPU within milliseconds (gate+up batches rose from 18.4 to 24 us
+    # over 200 launches, 27 us over 1000), which the step, mixing lighter
+    # kernels, does not do; its duration in the step is about 18 us.
+    stream = eager_stream
+    kernels = {}
+    nb = 5 * 10
+    for name, K, N in DECODE:
+        shape_copies = copies_for(host_w[name].nbytes)
+        ws = [dev_w[c][name] for c in range(ncopy)]
+        ws += [ws[0].clone() for _ in range(max(0, shape_copies - ncopy))]
+        args = [(ctypes.c_void_p(wc.data_ptr()), ctypes.c_void_p(dev_x[name].data_ptr()),
+                 qdm.QDM_BF16, ctypes.c_void_p(ys[name].data_ptr()), 1, N, K, stream)
+                for wc in ws]
+        nb_shape = nb
+        torch.cuda.synchronize()
+        time.sleep(0.02)
+        bm = batch_means(torch, lambda i: lib.q4k_gemv(*args[i]), len(args), nb_shape)
+        ms = float(np.median(bm))
+        b = gemv_bytes(N, K)
+        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb_shape,
+                         "copies": len(args), "GBps": b / ms / 1e6,
+                         "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS, "rel_err": errs[name],
+                         "batch_ms": [round(v, 5) for v in bm]}
+        del ws, args
+
+    # Graph-replayed steps, last (their check of the replayed results against
+    # the oracle leaves the GPU idle): one graph holds one step per weight copy
+    # (the decode loop of an engine replays captured launches).
     graph, graph_ms_per_step, graph_steps = None, None, 0
     if with_graph:
         graph = torch.cuda.CUDAGraph()
@@ -338,33 +372,7 @@ def bench_decode(torch, qdm, synth, oracle, steps, warmup, with_graph=True):
             gc.enable()
         graph_ms_per_step = g0.elapsed_time(g1) / (reps * ncopy)
         graph_steps = reps * ncopy
-
-    # Per-kernel launch duration: back-to-back launches of one kernel through
-    # the C ABI with pre-marshalled arguments (the queue stays ahead of the
-    # GPU), in 5 batches each bracketed by two events on the launch stream;
-    # the median batch mean is reported. Each shape rotates over its own
-    # copies, at least twice the 256 MB last-level cache in total (25 for QKV,
-    # 6 for gate+up, 11 for down).
-    stream = eager_stream
-    kernels = {}
-    nb = max(20, steps)
     del graph
-    for name, K, N in DECODE:
-        shape_copies = copies_for(host_w[name].nbytes)
-        ws = [dev_w[c][name] for c in range(ncopy)]
-        ws += [ws[0].clone() for _ in range(max(0, shape_copies - ncopy))]
-        args = [(ctypes.c_void_p(wc.data_ptr()), ctypes.c_void_p(dev_x[name].data_ptr()),
-                 qdm.QDM_BF16, ctypes.c_void_p(ys[name].data_ptr()), 1, N, K, stream)
-                for wc in ws]
-        nb_shape = max(nb, 2 * len(args))
-        bm = batch_means(torch, lambda i: lib.q4k_gemv(*args[i]), len(args), nb_shape)
-        ms = float(np.median(bm))
-        b = gemv_bytes(N, K)
-        kernels[name] = {"K": K, "N": N, "bytes": b, "avg_ms": ms, "launches": nb_shape,
-                         "copies": len(args), "GBps": b / ms / 1e6,
-                         "frac_hbm_peak": b / ms / 1e6 / HBM_PEAK_GBS, "rel_err": errs[name],
-                         "batch_ms": [round(v, 5) for v in bm]}
-        del ws, args
     step_bytes = sum(gemv_bytes(N, K) for _, K, N in DECODE)
     del dev_w
     return {"ms_per_step": total_ms / steps, "step_bytes": step_bytes, "copies": ncopy,
