@@ -432,12 +432,25 @@ __device__ __forceinline__ void store_direct(const f32x16 (&acc)[8][2], float *y
 // beside the accumulators, which are only read, and the quarter goes out as
 // store_direct writes a whole tile. A tile whose partial never arrived is
 // written as NaN.
+// PREFETCH: the next quarter of the first partial (unit - 1's) is loaded while
+// the current one is added and stored, so the quarters cost one memory latency
+// instead of four. That pays when owners finish at different times (at least
+// as many tiles as units: M = 4096, N = 17408, 725 -> 706 us); when every owner
+// finishes at once (M = 512) the epilogues share HBM and the deeper queue was
+// slower (14 -> 24 us per epilogue), so those calls keep one quarter in flight.
+template <bool PREFETCH>
 __device__ __forceinline__ void store_summed(const f32x16 (&acc)[8][2], float *yt, int ldy,
                                              int rows, int cols, const float *__restrict__ part0,
                                              int nparts, bool poison) {
   const YOut o = y_out(yt, ldy, rows, cols);
   int t = (int)threadIdx.x;
   asm volatile("" : "+v"(t));
+  const f32x4 *src0 = (const f32x4 *)part0 + t;
+  f32x4 pn[16];
+  if constexpr (PREFETCH) {
+#pragma unroll
+    for (int gg = 0; gg < 16; gg++) pn[gg] = src0[gg * GEMM_THREADS];
+  }
 #pragma unroll
   for (int qt = 0; qt < 4; qt++) {
     f32x4 sum[16];
@@ -446,7 +459,19 @@ __device__ __forceinline__ void store_summed(const f32x16 (&acc)[8][2], float *y
       const int i = 2 * qt + (gg >> 3), j = (gg >> 2) & 1, v0 = 4 * (gg & 3);
       sum[gg] = f32x4{acc[i][j][v0], acc[i][j][v0 + 1], acc[i][j][v0 + 2], acc[i][j][v0 + 3]};
     }
-    for (int k = 0; k < nparts; k++) {
+    int k = 0;
+    if constexpr (PREFETCH) {
+      // nparts >= 1: the owner's sum plus unit - 1's partial, then the next
+      // quarter of that partial goes in flight
+#pragma unroll
+      for (int gg = 0; gg < 16; gg++) sum[gg] += pn[gg];
+      if (qt < 3) {
+#pragma unroll
+        for (int gg = 0; gg < 16; gg++) pn[gg] = src0[(16 * (qt + 1) + gg) * GEMM_THREADS];
+      }
+      k = 1;
+    }
+    for (; k < nparts; k++) {
       const f32x4 *src = (const f32x4 *)(part0 - (size_t)k * BM * BN) + t;
       f32x4 p[16];
 #pragma unroll
@@ -481,6 +506,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
   const int64_t total = (int64_t)ntm * ntn * P;
   const int unit = blockIdx.x;
   const int64_t begin = total * unit / units, end = total * (unit + 1) / units;
+  const bool spread = (int64_t)ntm * ntn >= units;  // at least one whole tile per unit
 
   f32x16 acc[8][2];
   uint32_t *pending = nullptr;  // flag of a partial tile stored but not yet published
@@ -543,8 +569,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void q4k_gemm_kernel(
     }
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    store_summed(acc, yt, N, M - m0, N - n0, partials + (size_t)(unit - 1) * BM * BN,
-                 unit - lowest, timed_out != 0u);
+    // the first partial is unit - 1's; spread: owners finish at different times
+    if (spread)
+      store_summed<true>(acc, yt, N, M - m0, N - n0, partials + (size_t)(unit - 1) * BM * BN,
+                         unit - lowest, timed_out != 0u);
+    else
+      store_summed<false>(acc, yt, N, M - m0, N - n0, partials + (size_t)(unit - 1) * BM * BN,
+                          unit - lowest, timed_out != 0u);
   }
   if (pending != nullptr) publish_partial(pending);  // the last segment left a partial
 }
